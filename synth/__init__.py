@@ -1,0 +1,171 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle side.
+
+This module holds no arithmetic of the operator: it only draws inputs.
+Values come from ``synth_gen.c`` (counter-based SplitMix64 draws,
+Box-Muller normals), so a tensor is a pure function of
+(seed, tensor id, flat index) and any row range can be regenerated alone.
+
+Tensor ids: x / x1 = 0, x2 = 1, gamma = 2, beta = 3, smooth1 = 4,
+smooth2 = 5, outlier columns = 6.
+
+Workloads (shapes and distributions of the operator pages' use cases):
+
+===========  ==========================================================
+rmsnorm_dq   RmsNormDynamicQuant, x fp16 [64,1024] N(0,1), seed 0,
+             gamma U(0.5,1.5), no beta, eps 1e-6, no smooth, int8 out
+v2_square    AddRmsNormDynamicQuantV2 bf16 [4096,4096], seed 1, beta
+             N(0,0.1), smooth1 U(0.5,2), mask [T,F], int8
+v2_decode    bf16 [32,16384], seed 2, smooth1+2, mask [T,T], two int8
+v2_outlier   bf16 [16384,8192], seed 3, 82 outlier columns x30 on x1
+             and x2, smooth1+2, mask absent, two int8 outputs
+v2_int4      fp16 [65536,5120], seed 4, smooth1 only, mask [T,F],
+             y1 int4 (two codes per byte, low nibble first)
+===========  ==========================================================
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "synth_gen.c")
+_LIB = os.path.join(_HERE, "libsynth_gen.so")
+
+DTYPES = {"bf16": 0, "fp16": 1}
+NORMAL, UNIFORM = 0, 1
+TID = {"x1": 0, "x2": 1, "gamma": 2, "beta": 3, "smooth1": 4, "smooth2": 5, "outlier": 6}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-Wall", "-Wextra",
+             "-Werror", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        lib.synth_fill.argtypes = [
+            ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+            ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+            ctypes.c_double, ctypes.c_int, ctypes.c_void_p]
+        lib.synth_fill.restype = ctypes.c_int
+        lib.synth_pick_columns.argtypes = [
+            ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+            ctypes.c_void_p]
+        lib.synth_pick_columns.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def fill(seed, tid, dist, p0, p1, dtype, rows, cols, row_offset=0, outlier=None,
+         factor=1.0, out=None):
+    """16-bit storage patterns of rows [row_offset, row_offset+rows) of a tensor."""
+    if out is None:
+        out = np.empty((rows, cols), dtype=np.uint16)
+    assert out.dtype == np.uint16 and out.flags.c_contiguous and out.size == rows * cols
+    if outlier is not None:
+        outlier = np.ascontiguousarray(outlier, dtype=np.uint8)
+        assert outlier.size == cols
+    rc = _load().synth_fill(
+        int(seed), int(tid), int(dist), float(p0), float(p1), DTYPES[dtype], int(rows),
+        int(cols), int(row_offset), None if outlier is None else outlier.ctypes.data,
+        float(factor), _threads(), out.ctypes.data)
+    if rc != 0:
+        raise ValueError("synth_fill rejected its arguments")
+    return out
+
+
+def pick_columns(seed, tid, n, k) -> np.ndarray:
+    """0/1 flags of k distinct columns out of n (seeded partial Fisher-Yates)."""
+    scratch = np.empty(n, dtype=np.int64)
+    flags = np.empty(n, dtype=np.uint8)
+    if _load().synth_pick_columns(int(seed), int(tid), int(n), int(k), scratch.ctypes.data,
+                                  flags.ctypes.data) != 0:
+        raise ValueError("bad column pick")
+    return flags
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    op: str  # "v2" (AddRmsNormDynamicQuantV2) or "rmsnorm" (RmsNormDynamicQuant)
+    rows: int
+    cols: int
+    dtype: str
+    seed: int
+    mask: tuple | None
+    has_beta: bool
+    n_smooth: int
+    y_types: tuple = ("int8", "int8")
+    outlier_frac: float = 0.0
+    outlier_factor: float = 30.0
+    eps: float = 1e-6
+    note: str = field(default="", compare=False)
+
+    @property
+    def n_outlier(self) -> int:
+        return int(round(self.outlier_frac * self.cols))
+
+
+WORKLOADS = {
+    "rmsnorm_dq": Workload("rmsnorm_dq", "rmsnorm", 64, 1024, "fp16", 0, None, False, 0,
+                           ("int8", "int8")),
+    "v2_square": Workload("v2_square", "v2", 4096, 4096, "bf16", 1, (True, False), True, 1),
+    "v2_decode": Workload("v2_decode", "v2", 32, 16384, "bf16", 2, (True, True), True, 2),
+    "v2_outlier": Workload("v2_outlier", "v2", 16384, 8192, "bf16", 3, None, True, 2,
+                           outlier_frac=0.01),
+    "v2_int4": Workload("v2_int4", "v2", 65536, 5120, "fp16", 4, (True, False), True, 1,
+                        ("int4", "int8")),
+}
+
+
+def params(w: Workload, cols=None, seed=None):
+    """gamma, beta, smooth1, smooth2 ([cols] each, None when absent)."""
+    cols = w.cols if cols is None else cols
+    seed = w.seed if seed is None else seed
+    g = fill(seed, TID["gamma"], UNIFORM, 0.5, 1.5, w.dtype, 1, cols)[0]
+    b = fill(seed, TID["beta"], NORMAL, 0.0, 0.1, w.dtype, 1, cols)[0] if w.has_beta else None
+    s1 = fill(seed, TID["smooth1"], UNIFORM, 0.5, 2.0, w.dtype, 1, cols)[0] \
+        if w.n_smooth >= 1 else None
+    s2 = fill(seed, TID["smooth2"], UNIFORM, 0.5, 2.0, w.dtype, 1, cols)[0] \
+        if w.n_smooth >= 2 else None
+    return g, b, s1, s2
+
+
+def inputs(w: Workload, rows=None, row_offset=0, cols=None, seed=None):
+    """x1 (and x2 for the V2 op) for a row range, N(0,1) with outlier columns."""
+    rows = w.rows if rows is None else rows
+    cols = w.cols if cols is None else cols
+    seed = w.seed if seed is None else seed
+    flags = None
+    if w.outlier_frac > 0:
+        flags = pick_columns(seed, TID["outlier"], cols, int(round(w.outlier_frac * cols)))
+    x1 = fill(seed, TID["x1"], NORMAL, 0.0, 1.0, w.dtype, rows, cols, row_offset, flags,
+              w.outlier_factor)
+    x2 = None
+    if w.op == "v2":
+        x2 = fill(seed, TID["x2"], NORMAL, 0.0, 1.0, w.dtype, rows, cols, row_offset, flags,
+                  w.outlier_factor)
+    return x1, x2
