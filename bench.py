@@ -1,0 +1,211 @@
+"""Benchmark of the fused AddRmsNorm + per-row dynamic quantization kernel.
+
+One step = one launch of the whole operator (load + add + xOut, RmsNorm,
+smooth scaling, row maxima, scales, quantize + pack + store) over one batch
+of synthetic inputs already resident in HBM.  The default workload is
+AddRmsNormDynamicQuantV2 on bf16 [16384, 8192] with 1% outlier columns,
+two smooth scales and two INT8 outputs (plus scales and xOut).
+
+Prints ONE JSON line with the achieved HBM bandwidth (algorithmic bytes /
+average launch time, HIP events on the launch stream), its fraction of the
+MI355X HBM3E peak, and the CPU oracle timed on a bounded sample of the same
+workload on the host cores.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload v2_outlier]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+
+def alg_bytes(w, active, rows=None):
+    """Bytes the operator must move: inputs read once, outputs written once,
+    parameter vectors read once.  `active`: which quantized outputs exist."""
+    rows = w.rows if rows is None else rows
+    n, b = w.cols, 2
+    n_in = 2 if w.op == "v2" else 1
+    per_row = n_in * b * n + (b * n if w.op == "v2" else 0)
+    for k, act in enumerate(active):
+        if act:
+            bits = 4 if w.y_types[k] == "int4" else 8
+            per_row += n * bits // 8 + 4
+    params = (1 + int(w.has_beta) + w.n_smooth) * b * n
+    return rows * per_row + params
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "int4_dynamic_quantization_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def make_case(w, torch, adq, synth, dev):
+    x1, x2 = synth.inputs(w)
+    g, b, s1, s2 = synth.params(w)
+    d = lambda a: None if a is None else torch.from_numpy(a.view("int16")).view(
+        {"bf16": torch.bfloat16, "fp16": torch.float16}[w.dtype]).to(dev)
+    if w.op == "v2":
+        ex, outs = adq.plan_add_rms_norm_dynamic_quant_v2(
+            d(x1), d(x2), d(g), d(b), d(s1), d(s2), w.eps, w.mask, w.y_types[0], w.y_types[1])
+    else:
+        ex, outs = adq.plan_rms_norm_dynamic_quant(d(x1), d(g), d(b), d(s1), w.eps,
+                                                   w.y_types[0])
+    ws = (torch.empty(ex.workspace_size, dtype=torch.uint8, device=dev)
+          if ex.workspace_size else None)
+    if w.op == "v2":
+        active = [outs["y1"] is not None, outs["y2"] is not None]
+    else:
+        active = [True, False]
+    return ex, ws, (x1, x2, g, b, s1, s2), active
+
+
+def cpu_baseline(w, active, host_inputs, budget_s: float):
+    """The oracle (plain C, one thread) on the first rows of the same inputs,
+    as many rows as fit the time budget after a short pilot."""
+    import oracle
+    x1, x2, g, b, s1, s2 = host_inputs
+
+    def run(rows):
+        t0 = time.perf_counter()
+        if w.op == "v2":
+            oracle.add_rms_norm_dq_v2(x1[:rows], x2[:rows], g, b, s1, s2, w.eps, w.mask,
+                                      w.y_types[0], w.y_types[1], w.dtype, want_pre=False)
+        else:
+            oracle.rms_norm_dq(x1[:rows], g, b, s1, w.eps, w.y_types[0], w.dtype,
+                               want_pre=False)
+        return time.perf_counter() - t0
+
+    pilot = min(w.rows, 16)
+    t = run(pilot)
+    rows = int(max(pilot, min(w.rows, budget_s / max(t / pilot, 1e-9))))
+    t = run(rows)
+    gbs = alg_bytes(w, active, rows) / t / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} of {w.rows} rows of the same seeded inputs, "
+                      f"{t:.2f} s, single-threaded plain-C fp64 oracle "
+                      f"({rows / t:.0f} rows/s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v2_outlier")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this operator is row-local and this build runs on a "
+              f"single MI355X, so --gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import int4_dynamic_quantization_amd as adq
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    first = make_case(w, torch, adq, synth, dev)
+    active = first[3]
+    footprint = alg_bytes(w, active)
+    # Rotate input/output sets so that each launch streams from HBM rather
+    # than the 256 MB last-level cache.
+    n_sets = max(1, math.ceil(512e6 / footprint))
+    print(f"[bench] workload {w.name} {w.rows}x{w.cols} {w.dtype}: {footprint / 1e6:.1f} MB "
+          f"per launch, {n_sets} rotating set(s)", file=sys.stderr, flush=True)
+    cases = [first] + [make_case(w, torch, adq, synth, dev) for _ in range(n_sets - 1)]
+    print(f"[bench] plan: {cases[0][0].describe()}", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        ex, ws, _, _ = cases[i % n_sets]
+        ex.run(ws, stream)
+    torch.cuda.synchronize()
+
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    events[0].record(stream)
+    for i in range(args.steps):
+        ex, ws, _, _ = cases[i % n_sets]
+        ex.run(ws, stream)
+        events[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
+    ms = sum(per_launch_ms) / args.steps
+    gbs = footprint / (ms * 1e-3) / 1e9
+    print(f"[bench] {args.steps} launches: avg {ms * 1e3:.1f} us, min "
+          f"{min(per_launch_ms) * 1e3:.1f} us, max {max(per_launch_ms) * 1e3:.1f} us, "
+          f"wall {wall * 1e3:.1f} ms", file=sys.stderr, flush=True)
+
+    traffic = measured_traffic(w.name)
+    result = {
+        "metric": "achieved HBM GB/s (% of peak), AddRmsNorm+DynQuant bf16 16384x8192",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "op": "AddRmsNormDynamicQuantV2" if w.op == "v2" else "RmsNormDynamicQuant",
+            "rows": w.rows, "cols": w.cols, "storage": w.dtype,
+            "outputs": [t for t, a in zip(w.y_types, active) if a],
+            "outlier_columns": w.n_outlier, "smooth_scales": w.n_smooth,
+            "algorithmic_bytes_per_step": footprint,
+            "rows_per_s": round(w.rows / (ms * 1e-3)),
+            "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "parallelism": "single GPU",
+        },
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+    }
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline(w, active, cases[0][2], args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    for ex, _, _, _ in cases:
+        ex.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

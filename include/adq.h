@@ -1,0 +1,191 @@
+/*
+ * libaddrmsnorm_dq — fused (Add)RmsNorm + per-row symmetric dynamic
+ * quantization for AMD Instinct MI355X (gfx950).
+ *
+ * Operators (Huawei Ascend CANN operator pages, read as specification):
+ *
+ *  AddRmsNormDynamicQuantV2 — "aclnnAddRmsNormDynamicQuantV2", Formula:
+ *      x        = x1 + x2                                  (xOut)
+ *      y        = x / Rms(x) * gamma + beta,  Rms(x) = sqrt(mean_j x_j^2 + epsilon)
+ *      input_k  = y * smoothScale_k   (y when smoothScale_k is absent)
+ *      scale_k  = row_max(|input_k|) / 127  (INT8 output)  or  / 7  (INT4 output)
+ *      y_k      = round(input_k / scale_k)
+ *    Mean and max run over the last dimension (length n) of each row.
+ *
+ *  RmsNormDynamicQuant — "aclnnRmsNormDynamicQuant", formula section: the
+ *    same without the add and without xOut, one quantized output and an
+ *    optional smoothScales vector.
+ *
+ * Readings where the pages leave the arithmetic open (fixed by this
+ * library): the add and all later steps run in fp32 on the unrounded sum;
+ * only stored values are rounded (xOut to the input type, round to nearest
+ * even; scales to fp32); round() is round-half-to-even; codes lie in
+ * [-127, 127] or [-7, 7]; a row whose maximum is 0 gets scale 0 and codes 0;
+ * epsilon is applied as the nearest fp32 value; beta absent = 0.
+ *
+ * Calling convention (the pages' two-phase form, "aclnnXxxGetWorkspaceSize"
+ * then "aclnnXxx"): phase 1 validates every argument synchronously on the
+ * host, chooses the kernel, and returns the workspace size and an executor;
+ * phase 2 enqueues the work on a HIP stream and returns without waiting.
+ *
+ * Tensors: `adq_tensor` describes caller-owned DEVICE memory, dense
+ * row-major ("ND" in the pages' Constraints), up to 8 dimensions.  The
+ * library keeps the pointers inside the executor: the caller must keep the
+ * memory alive and unchanged in place until the phase-2 work has finished.
+ * Leading dimensions are flattened to rows M; the last dimension is n.
+ *
+ * Dtypes: x1, x2, xOut, gamma, beta, smooth scales: one of ADQ_F16 or
+ * ADQ_BF16 (all the same).  Scales: ADQ_F32.  Quantized outputs: ADQ_INT8
+ * (shape [..., n]) or ADQ_INT4X2 (shape [..., n/2], n even; byte j of a row
+ * holds column 2j in its low nibble and column 2j+1 in its high nibble, each
+ * a 4-bit two's complement code).  Each output's dtype selects its Q.
+ *
+ * Errors: every call returns an adq_status; adq_last_error() returns a
+ * thread-local message for the last non-OK status of the calling thread.
+ * Phase 2 never allocates and never synchronizes.
+ *
+ * Determinism: results are bitwise reproducible run to run (fixed
+ * reduction order, no floating-point atomics), as the pages' Constraints
+ * sections require of both operators.
+ */
+#ifndef ADQ_H
+#define ADQ_H
+
+#include <stdbool.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum adq_dtype {
+  ADQ_F16 = 1,
+  ADQ_BF16 = 2,
+  ADQ_F32 = 3,
+  ADQ_INT8 = 4,
+  ADQ_INT4X2 = 5 /* two INT4 codes per byte, even column in the low nibble */
+} adq_dtype;
+
+#define ADQ_MAX_DIMS 8
+
+/* A caller-owned, contiguous, row-major device tensor. */
+typedef struct adq_tensor {
+  void* data;     /* device address; must not be NULL for a present tensor */
+  int32_t dtype;  /* adq_dtype */
+  int32_t ndim;   /* 1 .. ADQ_MAX_DIMS (0 allowed for a scale of one row) */
+  int64_t shape[ADQ_MAX_DIMS];
+} adq_tensor;
+
+typedef enum adq_status {
+  ADQ_OK = 0,
+  ADQ_ERR_NULLPTR = 1,       /* a required tensor, its data, or an out-pointer is NULL */
+  ADQ_ERR_PARAM_INVALID = 2, /* shape, dtype pairing, empty tensor, mask rule, ... */
+  ADQ_ERR_UNSUPPORTED = 3,   /* a dtype outside the supported set */
+  ADQ_ERR_WORKSPACE = 4,     /* phase 2: workspace missing or smaller than phase 1 said */
+  ADQ_ERR_RUNTIME = 5        /* no usable HIP device, or a HIP launch error */
+} adq_status;
+
+/* Opaque, library-owned plan of one call; reusable for repeated launches
+ * with the same tensors until adq_executor_destroy(). */
+typedef struct adq_executor adq_executor;
+
+/*
+ * AddRmsNormDynamicQuantV2, phase 1.
+ *
+ * x1, x2        [..., n] F16 or BF16, same shape and dtype; required.
+ * gamma         [n] same dtype; required.
+ * beta          [n] same dtype, or NULL (beta = 0).
+ * smooth_scale1 [n] same dtype, or NULL.  smooth_scale2 likewise.
+ * epsilon       added to mean(x^2) inside the square root.
+ * output_mask   NULL (outputMaskOptional absent) or bool[2].
+ * y1_out, y2_out      [..., n] ADQ_INT8 or [..., n/2] ADQ_INT4X2.
+ * scale1_out, scale2_out  F32 with M elements (shape [...] or [M]).
+ * x_out         [..., n] same dtype as x1; required.
+ * workspace_size, executor: out-pointers; *executor must later be passed to
+ *               adq_executor_destroy().
+ *
+ * Which outputs are produced ("aclnnAddRmsNormDynamicQuantV2", Formula
+ * cases and Constraints):
+ *   output_mask given: y1/scale1 iff mask[0], y2/scale2 iff mask[1];
+ *     rejected (ADQ_ERR_PARAM_INVALID) when smooth_scale1 is given and
+ *     mask[0] is false, when smooth_scale2 is given and mask[1] is false,
+ *     or when both flags are false.
+ *   output_mask NULL: y1/scale1 always; y2/scale2 iff both smooth scales
+ *     are given; rejected when smooth_scale2 is given without smooth_scale1.
+ * An output that is produced needs its tensors (else ADQ_ERR_NULLPTR).  An
+ * output that is not produced may be NULL; if given, it is never written.
+ * Empty tensors (a zero dimension) are rejected ("aclnnRmsNormDynamicQuant",
+ * Constraints: no empty input or output).
+ */
+adq_status adq_add_rms_norm_dynamic_quant_v2_get_workspace_size(
+    const adq_tensor* x1, const adq_tensor* x2, const adq_tensor* gamma,
+    const adq_tensor* beta, const adq_tensor* smooth_scale1, const adq_tensor* smooth_scale2,
+    double epsilon, const bool* output_mask, const adq_tensor* y1_out,
+    const adq_tensor* y2_out, const adq_tensor* scale1_out, const adq_tensor* scale2_out,
+    const adq_tensor* x_out, uint64_t* workspace_size, adq_executor** executor);
+
+/*
+ * AddRmsNormDynamicQuantV2, phase 2: enqueue the work on `hip_stream` (a
+ * hipStream_t; NULL = the default stream of the executor's device).
+ * `workspace` is caller-owned device memory of at least the phase-1 size
+ * (may be NULL when that size is 0).  Concurrent launches that share a
+ * workspace must be ordered by the caller.  Returns without waiting.
+ */
+adq_status adq_add_rms_norm_dynamic_quant_v2(void* workspace, uint64_t workspace_size,
+                                             adq_executor* executor, void* hip_stream);
+
+/*
+ * RmsNormDynamicQuant, phase 1.
+ * x [..., n] F16/BF16; gamma [n]; beta [n] or NULL; smooth_scales [n] or
+ * NULL; y_out [..., n] ADQ_INT8 or [..., n/2] ADQ_INT4X2; scale_out F32
+ * with M elements.  Same validation and errors as the V2 call.
+ */
+adq_status adq_rms_norm_dynamic_quant_get_workspace_size(
+    const adq_tensor* x, const adq_tensor* gamma, const adq_tensor* beta,
+    const adq_tensor* smooth_scales, double epsilon, const adq_tensor* y_out,
+    const adq_tensor* scale_out, uint64_t* workspace_size, adq_executor** executor);
+
+/* RmsNormDynamicQuant, phase 2; as adq_add_rms_norm_dynamic_quant_v2. */
+adq_status adq_rms_norm_dynamic_quant(void* workspace, uint64_t workspace_size,
+                                      adq_executor* executor, void* hip_stream);
+
+/* Free an executor (NULL is a no-op).  Launched work is not affected. */
+void adq_executor_destroy(adq_executor* executor);
+
+/*
+ * Kernel path of an executor.  ADQ_PATH_AUTO is chosen by phase 1 from the
+ * shape; the others force a path (for tests and tuning).  ADQ_PATH_ROW:
+ * one workgroup per row, 128-bit accesses (n % 8 == 0, 16-byte aligned
+ * tensors, n <= 16384).  ADQ_PATH_SPLIT: several workgroups per row (same
+ * conditions; few-row shapes).  ADQ_PATH_GENERIC: any n and alignment.
+ */
+typedef enum adq_path {
+  ADQ_PATH_AUTO = 0,
+  ADQ_PATH_ROW = 1,
+  ADQ_PATH_SPLIT = 2,
+  ADQ_PATH_GENERIC = 3
+} adq_path;
+
+/*
+ * Re-plan `executor` for `path` and return its workspace size.  Returns
+ * ADQ_ERR_PARAM_INVALID when the shape does not meet that path's
+ * conditions (the executor is then unchanged).
+ */
+adq_status adq_executor_set_path(adq_executor* executor, int32_t path,
+                                 uint64_t* workspace_size);
+
+/*
+ * Write a one-line description of the plan (path, kernel variant, block,
+ * grid) into buf (NUL-terminated, truncated to len).  Returns the chosen
+ * path (adq_path), or -1 for a NULL executor.
+ */
+int32_t adq_executor_describe(const adq_executor* executor, char* buf, uint64_t len);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* adq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADQ_H */

@@ -1,0 +1,480 @@
+// C-ABI of libaddrmsnorm_dq: argument validation, kernel planning and launch.
+//
+// Two-phase form of the operator pages ("aclnnAddRmsNormDynamicQuantV2" and
+// "aclnnRmsNormDynamicQuant": a GetWorkspaceSize call that checks the
+// arguments and builds an executor, then the call that runs it on a
+// stream).  Output validity and the outputMask rules follow the V2 page's
+// Formula cases and Constraints section.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "adq.h"
+#include "adq_internal.h"
+
+namespace adq {
+
+hipError_t launch_row_bf16(const Variant&, int, int, int, const Args&, hipStream_t);
+hipError_t launch_row_f16(const Variant&, int, int, int, const Args&, hipStream_t);
+int row_occupancy_bf16(const Variant&, int, int);
+int row_occupancy_f16(const Variant&, int, int);
+
+hipError_t launch_row(const Variant& v, int vpt, int block, int grid, const Args& a,
+                      hipStream_t s) {
+  return v.elem == kBF16 ? launch_row_bf16(v, vpt, block, grid, a, s)
+                         : launch_row_f16(v, vpt, block, grid, a, s);
+}
+
+int row_max_blocks_per_cu(const Variant& v, int vpt, int block) {
+  return v.elem == kBF16 ? row_occupancy_bf16(v, vpt, block) : row_occupancy_f16(v, vpt, block);
+}
+
+}  // namespace adq
+
+namespace {
+
+using adq::Args;
+using adq::Variant;
+
+thread_local std::string g_last_error;
+
+adq_status fail(adq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+adq_status ok() {
+  g_last_error.clear();
+  return ADQ_OK;
+}
+
+enum Op { kOpV2 = 1, kOpRmsNorm = 2 };
+
+}  // namespace
+
+struct adq_executor {
+  int op;
+  Variant var;
+  Args args;
+  int64_t m;
+  int device;
+  int cus;
+  bool vector_ok;  // n % 8 == 0, aligned tensors, n small enough for the row kernel
+  int path;
+  int vpt;
+  int block;
+  int grid;
+  int splits;
+  uint64_t ws_bytes;
+};
+
+namespace {
+
+int64_t numel(const adq_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+bool is_half(int32_t dt) { return dt == ADQ_F16 || dt == ADQ_BF16; }
+
+const char* dtype_name(int32_t dt) {
+  switch (dt) {
+    case ADQ_F16: return "F16";
+    case ADQ_BF16: return "BF16";
+    case ADQ_F32: return "F32";
+    case ADQ_INT8: return "INT8";
+    case ADQ_INT4X2: return "INT4X2";
+    default: return "unknown";
+  }
+}
+
+// Basic well-formedness of a present tensor.
+adq_status check_tensor(const adq_tensor* t, const char* name) {
+  if (!t->data) return fail(ADQ_ERR_NULLPTR, "%s: data pointer is NULL", name);
+  if (t->ndim < 0 || t->ndim > ADQ_MAX_DIMS)
+    return fail(ADQ_ERR_PARAM_INVALID, "%s: ndim %d outside 0..%d", name, t->ndim, ADQ_MAX_DIMS);
+  for (int i = 0; i < t->ndim; ++i) {
+    if (t->shape[i] < 0) return fail(ADQ_ERR_PARAM_INVALID, "%s: negative dimension", name);
+    if (t->shape[i] == 0)
+      return fail(ADQ_ERR_PARAM_INVALID, "%s: empty tensors are not supported", name);
+  }
+  return ADQ_OK;
+}
+
+bool same_shape(const adq_tensor* a, const adq_tensor* b) {
+  if (a->ndim != b->ndim) return false;
+  for (int i = 0; i < a->ndim; ++i)
+    if (a->shape[i] != b->shape[i]) return false;
+  return true;
+}
+
+// gamma / beta / smooth: [n], same dtype as x.
+adq_status check_param(const adq_tensor* t, const char* name, int32_t dt, int64_t n) {
+  adq_status st = check_tensor(t, name);
+  if (st != ADQ_OK) return st;
+  if (t->dtype != dt)
+    return fail(ADQ_ERR_PARAM_INVALID, "%s: dtype %s differs from the input's %s", name,
+                dtype_name(t->dtype), dtype_name(dt));
+  if (t->ndim != 1 || t->shape[0] != n)
+    return fail(ADQ_ERR_PARAM_INVALID, "%s: expected shape [%lld]", name, (long long)n);
+  return ADQ_OK;
+}
+
+// A produced quantized output and its scale.
+adq_status check_output(const adq_tensor* y, const adq_tensor* s, const char* yname,
+                        const char* sname, const adq_tensor* x, int* qkind) {
+  if (!y) return fail(ADQ_ERR_NULLPTR, "%s is required for this call", yname);
+  if (!s) return fail(ADQ_ERR_NULLPTR, "%s is required for this call", sname);
+  adq_status st = check_tensor(y, yname);
+  if (st != ADQ_OK) return st;
+  st = check_tensor(s, sname);
+  if (st != ADQ_OK) return st;
+  const int64_t n = x->shape[x->ndim - 1];
+  if (y->dtype == ADQ_INT8) {
+    *qkind = adq::kQInt8;
+  } else if (y->dtype == ADQ_INT4X2) {
+    *qkind = adq::kQInt4;
+    if (n % 2 != 0)
+      return fail(ADQ_ERR_PARAM_INVALID, "%s: INT4X2 needs an even last dimension (n = %lld)",
+                  yname, (long long)n);
+  } else {
+    return fail(ADQ_ERR_UNSUPPORTED, "%s: dtype %s; expected INT8 or INT4X2", yname,
+                dtype_name(y->dtype));
+  }
+  if (y->ndim != x->ndim)
+    return fail(ADQ_ERR_PARAM_INVALID, "%s: rank differs from the input's", yname);
+  for (int i = 0; i + 1 < x->ndim; ++i)
+    if (y->shape[i] != x->shape[i])
+      return fail(ADQ_ERR_PARAM_INVALID, "%s: leading dimensions differ from the input's", yname);
+  const int64_t last = *qkind == adq::kQInt4 ? n / 2 : n;
+  if (y->shape[y->ndim - 1] != last)
+    return fail(ADQ_ERR_PARAM_INVALID, "%s: last dimension %lld, expected %lld", yname,
+                (long long)y->shape[y->ndim - 1], (long long)last);
+  if (s->dtype != ADQ_F32)
+    return fail(ADQ_ERR_PARAM_INVALID, "%s: dtype %s; expected F32", sname,
+                dtype_name(s->dtype));
+  if (numel(s) != numel(x) / n)
+    return fail(ADQ_ERR_PARAM_INVALID, "%s: %lld elements, expected one per row (%lld)", sname,
+                (long long)numel(s), (long long)(numel(x) / n));
+  return ADQ_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return p == nullptr || (uintptr_t)p % a == 0; }
+
+struct DeviceInfo {
+  int cus = 0;
+};
+
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+adq_status current_device(int* dev, int* cus) {
+  int d = -1;
+  if (hipGetDevice(&d) != hipSuccess || d < 0) {
+    (void)hipGetLastError();
+    return fail(ADQ_ERR_RUNTIME, "no HIP device available");
+  }
+  if (d >= 64) return fail(ADQ_ERR_RUNTIME, "device index %d out of range", d);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev[d].cus == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess ||
+        n <= 0) {
+      (void)hipGetLastError();
+      return fail(ADQ_ERR_RUNTIME, "cannot query the compute-unit count of device %d", d);
+    }
+    g_dev[d].cus = n;
+  }
+  *dev = d;
+  *cus = g_dev[d].cus;
+  return ADQ_OK;
+}
+
+int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+// Row-kernel geometry: vectors per thread and block size for n / 8 vectors.
+bool row_geometry(int64_t nvec, int* vpt, int* block) {
+  if (nvec <= 0) return false;
+  if (nvec <= 64) {
+    *vpt = 1, *block = 64;
+  } else if (nvec <= 2048) {
+    *vpt = 2, *block = round_up((int)((nvec + 1) / 2), 64);
+  } else {
+    return false;
+  }
+  return true;
+}
+
+adq_status plan(adq_executor* e, int path) {
+  const int64_t n = e->args.n;
+  if (path == ADQ_PATH_AUTO) {
+    int vpt = 0, block = 0;
+    path = e->vector_ok && row_geometry(n / 8, &vpt, &block) ? ADQ_PATH_ROW : ADQ_PATH_GENERIC;
+  }
+  if (path == ADQ_PATH_ROW) {
+    int vpt = 0, block = 0;
+    if (!e->vector_ok || !row_geometry(n / 8, &vpt, &block))
+      return fail(ADQ_ERR_PARAM_INVALID,
+                  "row path needs n %% 8 == 0, n <= 16384 and 16-byte aligned tensors");
+    const int occ = adq::row_max_blocks_per_cu(e->var, vpt, block);
+    if (occ <= 0) return fail(ADQ_ERR_RUNTIME, "row kernel does not fit block %d", block);
+    const int64_t slots = (int64_t)occ * e->cus;
+    const int64_t per = (e->m + slots - 1) / slots;
+    e->path = ADQ_PATH_ROW;
+    e->vpt = vpt;
+    e->block = block;
+    e->grid = (int)((e->m + per - 1) / per);
+    e->splits = 1;
+    e->ws_bytes = 0;
+    return ADQ_OK;
+  }
+  if (path == ADQ_PATH_GENERIC) {
+    e->path = ADQ_PATH_GENERIC;
+    e->vpt = 0;
+    e->block = 256;
+    e->grid = (int)(e->m < (int64_t)e->cus * 8 ? e->m : (int64_t)e->cus * 8);
+    e->splits = 1;
+    e->ws_bytes = 0;
+    return ADQ_OK;
+  }
+  if (path == ADQ_PATH_SPLIT)
+    return fail(ADQ_ERR_PARAM_INVALID, "split-row path is not available in this build");
+  return fail(ADQ_ERR_PARAM_INVALID, "unknown path %d", path);
+}
+
+// Shared tail of both phase-1 calls.
+adq_status finish_plan(adq_executor* proto, uint64_t* workspace_size, adq_executor** executor) {
+  adq_status st = current_device(&proto->device, &proto->cus);
+  if (st != ADQ_OK) return st;
+  const Args& a = proto->args;
+  proto->vector_ok = a.n % 8 == 0 && aligned(a.x1, 16) && aligned(a.x2, 16) &&
+                     aligned(a.x_out, 16) && aligned(a.gamma, 16) && aligned(a.beta, 16) &&
+                     aligned(a.smooth1, 16) && aligned(a.smooth2, 16) && aligned(a.y1, 8) &&
+                     aligned(a.y2, 8);
+  st = plan(proto, ADQ_PATH_AUTO);
+  if (st != ADQ_OK) return st;
+  adq_executor* e = new (std::nothrow) adq_executor(*proto);
+  if (!e) return fail(ADQ_ERR_RUNTIME, "out of host memory");
+  *workspace_size = e->ws_bytes;
+  *executor = e;
+  return ok();
+}
+
+adq_status run(void* workspace, uint64_t workspace_size, adq_executor* e, void* stream, int op) {
+  if (!e) return fail(ADQ_ERR_NULLPTR, "executor is NULL");
+  if (e->op != op) return fail(ADQ_ERR_PARAM_INVALID, "executor was built for another operator");
+  if (workspace_size < e->ws_bytes || (e->ws_bytes > 0 && !workspace))
+    return fail(ADQ_ERR_WORKSPACE, "workspace of %llu bytes, %llu needed",
+                (unsigned long long)workspace_size, (unsigned long long)e->ws_bytes);
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(ADQ_ERR_RUNTIME, "no HIP device available");
+  }
+  if (cur != e->device && hipSetDevice(e->device) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(ADQ_ERR_RUNTIME, "cannot select device %d", e->device);
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t err = hipErrorInvalidValue;
+  switch (e->path) {
+    case ADQ_PATH_ROW: err = adq::launch_row(e->var, e->vpt, e->block, e->grid, e->args, s); break;
+    case ADQ_PATH_GENERIC: err = adq::launch_generic(e->var, e->block, e->grid, e->args, s); break;
+    default: break;
+  }
+  if (cur != e->device) (void)hipSetDevice(cur);
+  if (err != hipSuccess)
+    return fail(ADQ_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(err));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+adq_status adq_add_rms_norm_dynamic_quant_v2_get_workspace_size(
+    const adq_tensor* x1, const adq_tensor* x2, const adq_tensor* gamma,
+    const adq_tensor* beta, const adq_tensor* smooth_scale1, const adq_tensor* smooth_scale2,
+    double epsilon, const bool* output_mask, const adq_tensor* y1_out,
+    const adq_tensor* y2_out, const adq_tensor* scale1_out, const adq_tensor* scale2_out,
+    const adq_tensor* x_out, uint64_t* workspace_size, adq_executor** executor) {
+  if (!workspace_size || !executor)
+    return fail(ADQ_ERR_NULLPTR, "workspace_size and executor out-pointers are required");
+  *executor = nullptr;
+  *workspace_size = 0;
+  if (!x1 || !x2 || !gamma || !x_out)
+    return fail(ADQ_ERR_NULLPTR, "x1, x2, gamma and x_out are required");
+  adq_status st;
+  if ((st = check_tensor(x1, "x1")) != ADQ_OK) return st;
+  if (!is_half(x1->dtype))
+    return fail(ADQ_ERR_UNSUPPORTED, "x1: dtype %s; expected F16 or BF16", dtype_name(x1->dtype));
+  if (x1->ndim < 1) return fail(ADQ_ERR_PARAM_INVALID, "x1: needs at least one dimension");
+  if ((st = check_tensor(x2, "x2")) != ADQ_OK) return st;
+  if ((st = check_tensor(x_out, "x_out")) != ADQ_OK) return st;
+  if (x2->dtype != x1->dtype || x_out->dtype != x1->dtype)
+    return fail(ADQ_ERR_PARAM_INVALID, "x2 and x_out must have x1's dtype");
+  if (!same_shape(x1, x2) || !same_shape(x1, x_out))
+    return fail(ADQ_ERR_PARAM_INVALID, "x1, x2 and x_out must have the same shape");
+  const int64_t n = x1->shape[x1->ndim - 1];
+  if (n > INT32_MAX) return fail(ADQ_ERR_PARAM_INVALID, "last dimension too large");
+  if ((st = check_param(gamma, "gamma", x1->dtype, n)) != ADQ_OK) return st;
+  if (beta && (st = check_param(beta, "beta", x1->dtype, n)) != ADQ_OK) return st;
+  if (smooth_scale1 && (st = check_param(smooth_scale1, "smooth_scale1", x1->dtype, n)) != ADQ_OK)
+    return st;
+  if (smooth_scale2 && (st = check_param(smooth_scale2, "smooth_scale2", x1->dtype, n)) != ADQ_OK)
+    return st;
+  if (!(epsilon == epsilon) || epsilon > 3.4e38 || epsilon < -3.4e38)
+    return fail(ADQ_ERR_PARAM_INVALID, "epsilon must be a finite value");
+
+  // Which outputs exist: V2 Formula cases; Constraints rules on the mask.
+  const bool has1 = smooth_scale1 != nullptr, has2 = smooth_scale2 != nullptr;
+  bool act1, act2;
+  if (output_mask) {
+    if (has1 && !output_mask[0])
+      return fail(ADQ_ERR_PARAM_INVALID, "smooth_scale1 is given, so output_mask[0] must be true");
+    if (has2 && !output_mask[1])
+      return fail(ADQ_ERR_PARAM_INVALID, "smooth_scale2 is given, so output_mask[1] must be true");
+    if (!output_mask[0] && !output_mask[1])
+      return fail(ADQ_ERR_PARAM_INVALID, "output_mask[0] and output_mask[1] cannot both be false");
+    act1 = output_mask[0];
+    act2 = output_mask[1];
+  } else {
+    if (has2 && !has1)
+      return fail(ADQ_ERR_PARAM_INVALID,
+                  "without output_mask, smooth_scale2 needs smooth_scale1 as well");
+    act1 = true;
+    act2 = has1 && has2;
+  }
+  int q1 = adq::kQNone, q2 = adq::kQNone;
+  if (act1 && (st = check_output(y1_out, scale1_out, "y1_out", "scale1_out", x1, &q1)) != ADQ_OK)
+    return st;
+  if (act2 && (st = check_output(y2_out, scale2_out, "y2_out", "scale2_out", x1, &q2)) != ADQ_OK)
+    return st;
+
+  adq_executor e{};
+  e.op = kOpV2;
+  e.m = numel(x1) / n;
+  Args& a = e.args;
+  a.x1 = x1->data;
+  a.x2 = x2->data;
+  a.gamma = gamma->data;
+  a.beta = beta ? beta->data : nullptr;
+  a.x_out = x_out->data;
+  a.rows = e.m;
+  a.n = (int32_t)n;
+  a.eps = (float)epsilon;
+  a.inv_n = (float)(1.0 / (double)n);
+  // The kernels always produce slot 1 and optionally slot 2; a lone second
+  // output (mask [false, true]) runs in slot 1 with the second smooth scale.
+  if (act1) {
+    a.smooth1 = has1 ? smooth_scale1->data : nullptr;
+    a.y1 = y1_out->data;
+    a.scale1 = static_cast<float*>(scale1_out->data);
+    if (act2) {
+      a.smooth2 = has2 ? smooth_scale2->data : nullptr;
+      a.y2 = y2_out->data;
+      a.scale2 = static_cast<float*>(scale2_out->data);
+    }
+    e.var = Variant{x1->dtype == ADQ_BF16 ? adq::kBF16 : adq::kF16, 2, q1, act2 ? q2 : adq::kQNone};
+  } else {
+    a.smooth1 = has2 ? smooth_scale2->data : nullptr;
+    a.y1 = y2_out->data;
+    a.scale1 = static_cast<float*>(scale2_out->data);
+    e.var = Variant{x1->dtype == ADQ_BF16 ? adq::kBF16 : adq::kF16, 2, q2, adq::kQNone};
+  }
+  return finish_plan(&e, workspace_size, executor);
+}
+
+adq_status adq_add_rms_norm_dynamic_quant_v2(void* workspace, uint64_t workspace_size,
+                                             adq_executor* executor, void* hip_stream) {
+  return run(workspace, workspace_size, executor, hip_stream, kOpV2);
+}
+
+adq_status adq_rms_norm_dynamic_quant_get_workspace_size(
+    const adq_tensor* x, const adq_tensor* gamma, const adq_tensor* beta,
+    const adq_tensor* smooth_scales, double epsilon, const adq_tensor* y_out,
+    const adq_tensor* scale_out, uint64_t* workspace_size, adq_executor** executor) {
+  if (!workspace_size || !executor)
+    return fail(ADQ_ERR_NULLPTR, "workspace_size and executor out-pointers are required");
+  *executor = nullptr;
+  *workspace_size = 0;
+  if (!x || !gamma) return fail(ADQ_ERR_NULLPTR, "x and gamma are required");
+  adq_status st;
+  if ((st = check_tensor(x, "x")) != ADQ_OK) return st;
+  if (!is_half(x->dtype))
+    return fail(ADQ_ERR_UNSUPPORTED, "x: dtype %s; expected F16 or BF16", dtype_name(x->dtype));
+  if (x->ndim < 1) return fail(ADQ_ERR_PARAM_INVALID, "x: needs at least one dimension");
+  const int64_t n = x->shape[x->ndim - 1];
+  if (n > INT32_MAX) return fail(ADQ_ERR_PARAM_INVALID, "last dimension too large");
+  if ((st = check_param(gamma, "gamma", x->dtype, n)) != ADQ_OK) return st;
+  if (beta && (st = check_param(beta, "beta", x->dtype, n)) != ADQ_OK) return st;
+  if (smooth_scales && (st = check_param(smooth_scales, "smooth_scales", x->dtype, n)) != ADQ_OK)
+    return st;
+  if (!(epsilon == epsilon) || epsilon > 3.4e38 || epsilon < -3.4e38)
+    return fail(ADQ_ERR_PARAM_INVALID, "epsilon must be a finite value");
+  int q = adq::kQNone;
+  if ((st = check_output(y_out, scale_out, "y_out", "scale_out", x, &q)) != ADQ_OK) return st;
+
+  adq_executor e{};
+  e.op = kOpRmsNorm;
+  e.m = numel(x) / n;
+  Args& a = e.args;
+  a.x1 = x->data;
+  a.gamma = gamma->data;
+  a.beta = beta ? beta->data : nullptr;
+  a.smooth1 = smooth_scales ? smooth_scales->data : nullptr;
+  a.y1 = y_out->data;
+  a.scale1 = static_cast<float*>(scale_out->data);
+  a.rows = e.m;
+  a.n = (int32_t)n;
+  a.eps = (float)epsilon;
+  a.inv_n = (float)(1.0 / (double)n);
+  e.var = Variant{x->dtype == ADQ_BF16 ? adq::kBF16 : adq::kF16, 1, q, adq::kQNone};
+  return finish_plan(&e, workspace_size, executor);
+}
+
+adq_status adq_rms_norm_dynamic_quant(void* workspace, uint64_t workspace_size,
+                                      adq_executor* executor, void* hip_stream) {
+  return run(workspace, workspace_size, executor, hip_stream, kOpRmsNorm);
+}
+
+void adq_executor_destroy(adq_executor* executor) { delete executor; }
+
+adq_status adq_executor_set_path(adq_executor* executor, int32_t path, uint64_t* workspace_size) {
+  if (!executor || !workspace_size) return fail(ADQ_ERR_NULLPTR, "executor and workspace_size are required");
+  adq_executor trial = *executor;
+  adq_status st = plan(&trial, path);
+  if (st != ADQ_OK) return st;
+  *executor = trial;
+  *workspace_size = trial.ws_bytes;
+  return ok();
+}
+
+int32_t adq_executor_describe(const adq_executor* e, char* buf, uint64_t len) {
+  if (!e) return -1;
+  if (buf && len > 0) {
+    static const char* names[] = {"auto", "row", "split", "generic"};
+    snprintf(buf, (size_t)len,
+             "path=%s elem=%s nin=%d q1=%d q2=%d rows=%lld n=%d vpt=%d block=%d grid=%d "
+             "splits=%d workspace=%llu cus=%d",
+             names[e->path & 3], e->var.elem == adq::kBF16 ? "bf16" : "fp16", e->var.nin,
+             e->var.q1, e->var.q2, (long long)e->m, e->args.n, e->vpt, e->block, e->grid,
+             e->splits, (unsigned long long)e->ws_bytes, e->cus);
+  }
+  return e->path;
+}
+
+const char* adq_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

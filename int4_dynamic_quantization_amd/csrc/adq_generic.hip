@@ -1,0 +1,149 @@
+// Generic kernel: the same operator for any row length n (including n not a
+// multiple of 8) and any 2-byte-aligned pointers.  One workgroup per row at
+// a time, elementwise 16-bit accesses, three passes that re-read the row's
+// inputs from cache.  This is the correctness path for shapes the vector
+// kernels do not take; the arithmetic per element is the same as theirs:
+// fp32 add, sum of squares, rinv = 1/sqrt(ss/n + eps), y = fma(x*rinv,
+// gamma, beta), input_k = y * smooth_k, scale_k = max|input_k| / Q,
+// code = round_half_even(input_k * (1/scale_k)).
+//
+// Operator: "aclnnAddRmsNormDynamicQuantV2", Formula section, and
+// "aclnnRmsNormDynamicQuant", formula section.
+#include <type_traits>
+
+#include "adq_device.h"
+
+namespace adq {
+
+namespace {
+
+template <int E>
+__device__ __forceinline__ float ld1(const void* p, int64_t i) {
+  return widen1<E>(reinterpret_cast<const uint16_t*>(p)[i]);
+}
+
+template <int E>
+__device__ __forceinline__ float param(const void* p, int64_t j, float absent) {
+  return p ? ld1<E>(p, j) : absent;
+}
+
+template <int E, int NIN, int Q1, int Q2>
+__global__ void __launch_bounds__(256) generic_kernel(const Args a) {
+  constexpr bool kTwo = Q2 != kQNone;
+  const int tid = threadIdx.x;
+  const int bs = blockDim.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nwaves = bs >> 6;
+  const int64_t n = a.n;
+  __shared__ float red_ss[16];
+  __shared__ float red_mx[2][16];
+
+  for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+    const int64_t off = row * n;
+    auto xval = [&](int64_t j) {
+      float v = ld1<E>(a.x1, off + j);
+      if constexpr (NIN == 2) v += ld1<E>(a.x2, off + j);
+      return v;
+    };
+    // pass 1: x = x1 + x2, xOut, sum of squares
+    float ss = 0.0f;
+    for (int64_t j = tid; j < n; j += bs) {
+      const float v = xval(j);
+      if constexpr (NIN == 2) reinterpret_cast<uint16_t*>(a.x_out)[off + j] = narrow1<E>(v);
+      ss = __builtin_fmaf(v, v, ss);
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red_ss[wave] = ss;
+    __syncthreads();
+    float tot = 0.0f;
+    for (int w = 0; w < nwaves; ++w) tot += red_ss[w];
+    const float rinv = 1.0f / __builtin_sqrtf(tot / (float)a.n + a.eps);
+
+    auto inputs = [&](int64_t j, float& in1, float& in2) {
+      const float y = __builtin_fmaf(xval(j) * rinv, param<E>(a.gamma, j, 0.0f),
+                                     param<E>(a.beta, j, 0.0f));
+      in1 = y * param<E>(a.smooth1, j, 1.0f);
+      in2 = kTwo ? y * param<E>(a.smooth2, j, 1.0f) : 0.0f;
+    };
+    // pass 2: row maxima
+    float m1 = 0.0f, m2 = 0.0f;
+    for (int64_t j = tid; j < n; j += bs) {
+      float i1, i2;
+      inputs(j, i1, i2);
+      m1 = fmaxf(m1, fabsf(i1));
+      m2 = fmaxf(m2, fabsf(i2));
+    }
+    m1 = wave_max(m1);
+    m2 = wave_max(m2);
+    if (lane == 0) red_mx[0][wave] = m1, red_mx[1][wave] = m2;
+    __syncthreads();
+    float M1 = 0.0f, M2 = 0.0f;
+    for (int w = 0; w < nwaves; ++w) M1 = fmaxf(M1, red_mx[0][w]), M2 = fmaxf(M2, red_mx[1][w]);
+    const RowScale r1 = row_scale<Q1>(M1);
+    const RowScale r2 = row_scale<kTwo ? Q2 : kQInt8>(M2);
+    if (tid == 0) {
+      a.scale1[row] = r1.scale;
+      if constexpr (kTwo) a.scale2[row] = r2.scale;
+    }
+    auto code = [](float in, const RowScale& rs) -> uint32_t {
+      return rs.slow ? code_bits_div(in, rs.scale) : code_bits(in, rs.inv);
+    };
+    // pass 3: codes, one column pair per thread step
+    const int64_t pairs = (n + 1) / 2;
+    for (int64_t p = tid; p < pairs; p += bs) {
+      const int64_t j0 = 2 * p, j1 = 2 * p + 1;
+      const bool has1 = j1 < n;
+      float a0, b0, a1 = 0.0f, b1 = 0.0f;
+      inputs(j0, a0, b0);
+      if (has1) inputs(j1, a1, b1);
+      auto put = [&](void* out, int q, float v0, float v1, const RowScale& rs) {
+        const uint32_t c0 = code(v0, rs), c1 = code(v1, rs);
+        if (q == kQInt8) {
+          int8_t* o = reinterpret_cast<int8_t*>(out) + off;
+          o[j0] = (int8_t)(c0 & 0xFFu);
+          if (has1) o[j1] = (int8_t)(c1 & 0xFFu);
+        } else {  // n is even for INT4 outputs
+          reinterpret_cast<uint8_t*>(out)[row * (n / 2) + p] =
+              (uint8_t)((c0 & 0x0Fu) | ((c1 & 0x0Fu) << 4));
+        }
+      };
+      put(a.y1, Q1, a0, a1, r1);
+      if constexpr (kTwo) put(a.y2, Q2, b0, b1, r2);
+    }
+  }
+}
+
+template <int E, int NIN, int Q1, int Q2>
+hipError_t launch_one(int block, int grid, const Args& a, hipStream_t s) {
+  hipLaunchKernelGGL((generic_kernel<E, NIN, Q1, Q2>), dim3(grid), dim3(block), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int E>
+hipError_t launch_elem(const Variant& v, int block, int grid, const Args& a, hipStream_t s) {
+  if (v.nin == 1) {
+    if (v.q2 != kQNone) return hipErrorInvalidValue;
+    if (v.q1 == kQInt8) return launch_one<E, 1, kQInt8, kQNone>(block, grid, a, s);
+    if (v.q1 == kQInt4) return launch_one<E, 1, kQInt4, kQNone>(block, grid, a, s);
+    return hipErrorInvalidValue;
+  }
+  if (v.q1 == kQInt8 && v.q2 == kQNone) return launch_one<E, 2, kQInt8, kQNone>(block, grid, a, s);
+  if (v.q1 == kQInt4 && v.q2 == kQNone) return launch_one<E, 2, kQInt4, kQNone>(block, grid, a, s);
+  if (v.q1 == kQInt8 && v.q2 == kQInt8) return launch_one<E, 2, kQInt8, kQInt8>(block, grid, a, s);
+  if (v.q1 == kQInt8 && v.q2 == kQInt4) return launch_one<E, 2, kQInt8, kQInt4>(block, grid, a, s);
+  if (v.q1 == kQInt4 && v.q2 == kQInt8) return launch_one<E, 2, kQInt4, kQInt8>(block, grid, a, s);
+  if (v.q1 == kQInt4 && v.q2 == kQInt4) return launch_one<E, 2, kQInt4, kQInt4>(block, grid, a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_generic(const Variant& v, int block, int grid, const Args& a,
+                          hipStream_t stream) {
+  if (block < 64 || block > 256 || block % 64 != 0 || grid < 1) return hipErrorInvalidValue;
+  return v.elem == kBF16 ? launch_elem<kBF16>(v, block, grid, a, stream)
+                         : launch_elem<kF16>(v, block, grid, a, stream);
+}
+
+}  // namespace adq

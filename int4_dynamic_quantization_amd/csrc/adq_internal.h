@@ -1,0 +1,67 @@
+// Internal interface between the C-ABI host layer (adq_api.cpp) and the
+// HIP kernels (adq_row.hip, adq_split.hip, adq_generic.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace adq {
+
+enum ElemType : int { kBF16 = 0, kF16 = 1 };
+// What one quantized output slot produces: nothing, INT8 codes (one per
+// byte, scale = max/127) or INT4 codes (two per byte, scale = max/7).
+enum QuantKind : int { kQNone = 0, kQInt8 = 1, kQInt4 = 2 };
+
+// Everything a launch needs; passed by value as the kernel argument.
+// Pointers are device addresses.  x2 == nullptr selects the single-input
+// RmsNormDynamicQuant form (no add, no x_out).  Output slot 1 is always
+// produced; slot 2 only when q2 != kQNone.  An absent beta reads as 0, an
+// absent smooth scale as 1.
+struct Args {
+  const void* x1;
+  const void* x2;
+  const void* gamma;
+  const void* beta;
+  const void* smooth1;
+  const void* smooth2;
+  void* x_out;
+  void* y1;
+  void* y2;
+  float* scale1;
+  float* scale2;
+  int64_t rows;
+  int32_t n;
+  float eps;
+  float inv_n;  // 1/n rounded to float
+};
+
+// Kernel families.
+enum Path : int { kPathRow = 1, kPathSplit = 2, kPathGeneric = 3 };
+
+// Compile-time variant of the row and split kernels.
+struct Variant {
+  int elem;  // ElemType
+  int nin;   // 1 or 2 inputs
+  int q1;    // QuantKind of output slot 1 (never kQNone)
+  int q2;    // QuantKind of output slot 2
+};
+
+// Row kernel: one workgroup per row at a time, `vpt` 8-element vectors per
+// thread, grid-strided over rows.  vpt in {1, 2}.
+hipError_t launch_row(const Variant& v, int vpt, int block, int grid, const Args& a,
+                      hipStream_t stream);
+int row_max_blocks_per_cu(const Variant& v, int vpt, int block);
+
+// Split-row kernel: `splits` workgroups share one row.  `ws` is the
+// launch's workspace (split_workspace_bytes), `epoch` a value unique to
+// this launch.
+hipError_t launch_split(const Variant& v, int vpt, int block, int splits, const Args& a,
+                        void* ws, uint64_t epoch, hipStream_t stream);
+int split_max_blocks_per_cu(const Variant& v, int vpt, int block);
+uint64_t split_workspace_bytes(int64_t rows, int splits);
+
+// Generic kernel: any n (odd widths, unaligned pointers); correctness path.
+hipError_t launch_generic(const Variant& v, int block, int grid, const Args& a,
+                          hipStream_t stream);
+
+}  // namespace adq

@@ -1,0 +1,281 @@
+// Row kernel: fused (Add)RmsNorm + one or two per-row dynamic quantizations.
+//
+// Operator: "aclnnAddRmsNormDynamicQuantV2", Formula section (x = x1 + x2;
+// y = x / Rms(x) * gamma + beta; input_k = y * smoothScale_k;
+// scale_k = row_max(|input_k|) / 127 or / 7; y_k = round(input_k / scale_k))
+// and "aclnnRmsNormDynamicQuant", formula section (single input).
+//
+// Layout: every tensor is dense row-major.  A workgroup of `block` threads
+// owns a whole row at a time: thread t holds the 8-element column vectors
+// t, t + block, ..., t + (VPT-1) * block, so each wavefront load or store
+// instruction covers one contiguous 1 KiB (16-bit data) span.  Workgroups
+// stride over rows (grid <= rows); the next row's x1/x2 are loaded into
+// registers while the current row is computed, so each element of x1 and
+// x2 is read from HBM exactly once and every output is written once.
+//
+// Per row:
+//   A  load + add in fp32, store xOut (round to nearest even), sum of squares
+//   -- workgroup sum (DPP + readlane per wave, LDS across waves, fixed order)
+//   B  rinv = 1 / sqrt(ss / n + eps); y = fma(x * rinv, gamma, beta);
+//      input_k = y * smooth_k; row max of |input_k|
+//   -- workgroup max
+//   C  scale_k = max_k / Q_k; code = round_half_even(input_k * (1/scale_k));
+//      pack (INT8: 1 byte, INT4: 1 nibble, even column low) and store.
+//
+// VPT (8-column vectors per thread) is 1 or 2, so a row of up to 16384
+// columns fits one workgroup of at most 1024 threads.  The parameters
+// (gamma, beta, smooth) stay in registers as packed 16-bit values for the
+// whole row loop and are converted at use.
+#pragma once
+
+#include <type_traits>
+
+#include "adq_device.h"
+
+namespace adq {
+
+// Keeps the compiler from hoisting per-use conversions of a loop-invariant
+// register out of the row loop (which would hold fp32 copies and spill).
+__device__ __forceinline__ void opaque(u32x4& v) { asm volatile("" : "+v"(v)); }
+
+// Codes of one 8-column vector into an INT8 (8 bytes) or INT4X2 (4 bytes)
+// output row, at vector index j of that row.
+template <int Q>
+__device__ __forceinline__ void store_codes(const float (&in)[8], const RowScale& rs,
+                                            rsrc_t out, uint32_t j) {
+  uint32_t q[8];
+  if (!rs.slow) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = code_bits(in[e], rs.inv);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = code_bits_div(in[e], rs.scale);
+  }
+  if constexpr (Q == kQInt8) {
+    __builtin_amdgcn_raw_buffer_store_b64(pack_int8x8(q), out, j * 8u, 0, kStream);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(pack_int4x8(q), out, j * 4u, 0, kStream);
+  }
+}
+
+template <int E, int NIN, int Q1, int Q2, int VPT>
+__global__ void __launch_bounds__(1024) row_kernel(const Args a) {
+  static_assert(VPT == 1 || VPT == 2, "row kernel holds at most 16 columns per thread");
+  constexpr bool kTwo = Q2 != kQNone;
+  constexpr int kQ2 = kTwo ? Q2 : kQInt8;
+  const int tid = threadIdx.x;
+  const int bs = blockDim.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nwaves = bs >> 6;
+  const uint32_t n = (uint32_t)a.n;
+  const uint32_t row_bytes = n * 2u;  // 16-bit elements
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  const u32x4 one4 = u32x4{kOnePair<E>, kOnePair<E>, kOnePair<E>, kOnePair<E>};
+
+  __shared__ float red_ss[16];
+  __shared__ float red_mx[2][16];
+
+  // This thread's 8-column vectors: j = tid + k * bs.  Vectors past the end
+  // of the row read as 0 and their stores are dropped by the buffer range
+  // check (the row is a whole number of 16-byte vectors).
+  uint32_t vj[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) vj[k] = (uint32_t)(tid + k * bs);
+
+  // Parameters, kept as 16-bit pairs (1 for an absent smooth scale).
+  auto load_param = [&](const void* p, int k, u32x4 absent) -> u32x4 {
+    if (!p) return absent;
+    return __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(p, row_bytes), vj[k] * 16u, 0, 0);
+  };
+  u32x4 pg[VPT], pb[VPT], p1[VPT], p2[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    pg[k] = load_param(a.gamma, k, zero4);
+    pb[k] = load_param(a.beta, k, zero4);
+    p1[k] = load_param(a.smooth1, k, one4);
+    p2[k] = kTwo ? load_param(a.smooth2, k, one4) : zero4;
+  }
+
+  auto load_row = [&](int64_t row, u32x4 (&c1)[VPT], u32x4 (&c2)[VPT]) {
+    const rsrc_t r1 = make_rsrc(row_ptr(a.x1, row, row_bytes), row_bytes);
+    const rsrc_t r2 = make_rsrc(row_ptr(a.x2, row, row_bytes), row_bytes);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      c1[k] = __builtin_amdgcn_raw_buffer_load_b128(r1, vj[k] * 16u, 0, kStream);
+      if constexpr (NIN == 2)
+        c2[k] = __builtin_amdgcn_raw_buffer_load_b128(r2, vj[k] * 16u, 0, kStream);
+    }
+  };
+
+  int64_t row = blockIdx.x;
+  if (row >= a.rows) return;
+  u32x4 c1[VPT], c2[VPT];
+  load_row(row, c1, c2);
+
+  // One row: prefetch the next, compute and store this one.  The first row
+  // is peeled off the loop so that every entry to the loop header has the
+  // same outstanding memory operations (loads, then stores); the wait for
+  // the prefetched row then need not wait for the stores.
+  auto body = [&](int64_t row) {
+    // Prefetch this workgroup's next row (the last row again when there is
+    // none, so the loads are unconditional).
+    u32x4 n1[VPT], n2[VPT];
+    const int64_t next = row + gridDim.x < a.rows ? row + gridDim.x : a.rows - 1;
+    load_row(next, n1, n2);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) opaque(pg[k]), opaque(pb[k]), opaque(p1[k]), opaque(p2[k]);
+
+    // ---- A: x = x1 + x2 (fp32), xOut, sum of squares
+    float x[VPT][8];
+    float ss = 0.0f;
+    const rsrc_t rxo = make_rsrc(row_ptr(a.x_out, row, row_bytes), row_bytes);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        f32x2 v = widen2<E>(c1[k][w]);
+        if constexpr (NIN == 2) v += widen2<E>(c2[k][w]);
+        x[k][2 * w] = v.x;
+        x[k][2 * w + 1] = v.y;
+        acc = __builtin_fmaf(v.x, v.x, acc);
+        acc = __builtin_fmaf(v.y, v.y, acc);
+      }
+      ss += acc;
+      if constexpr (NIN == 2) {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{narrow2<E>(x[k][0], x[k][1]), narrow2<E>(x[k][2], x[k][3]),
+                  narrow2<E>(x[k][4], x[k][5]), narrow2<E>(x[k][6], x[k][7])},
+            rxo, vj[k] * 16u, 0, kStream);
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red_ss[wave] = ss;
+    __syncthreads();
+    float tot = 0.0f;
+    for (int w = 0; w < nwaves; ++w) tot += red_ss[w];
+    const float rinv = __builtin_amdgcn_rsqf(__builtin_fmaf(tot, a.inv_n, a.eps));
+
+    // ---- B: y = x * rinv * gamma + beta, quantizer inputs, row maxima
+    float in1[VPT][8], in2[VPT][8];
+    float m1 = 0.0f, m2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f32x2 g = widen2<E>(pg[k][w]), b = widen2<E>(pb[k][w]);
+        const f32x2 s1 = widen2<E>(p1[k][w]);
+        const float y0 = __builtin_fmaf(x[k][2 * w] * rinv, g.x, b.x);
+        const float y1 = __builtin_fmaf(x[k][2 * w + 1] * rinv, g.y, b.y);
+        in1[k][2 * w] = y0 * s1.x;
+        in1[k][2 * w + 1] = y1 * s1.y;
+        m1 = fmaxf(m1, fmaxf(fabsf(in1[k][2 * w]), fabsf(in1[k][2 * w + 1])));
+        if constexpr (kTwo) {
+          const f32x2 s2 = widen2<E>(p2[k][w]);
+          in2[k][2 * w] = y0 * s2.x;
+          in2[k][2 * w + 1] = y1 * s2.y;
+          m2 = fmaxf(m2, fmaxf(fabsf(in2[k][2 * w]), fabsf(in2[k][2 * w + 1])));
+        }
+      }
+    }
+    m1 = wave_max(m1);
+    if constexpr (kTwo) m2 = wave_max(m2);
+    if (lane == 0) {
+      red_mx[0][wave] = m1;
+      if constexpr (kTwo) red_mx[1][wave] = m2;
+    }
+    __syncthreads();
+    float M1 = 0.0f, M2 = 0.0f;
+    for (int w = 0; w < nwaves; ++w) {
+      M1 = fmaxf(M1, red_mx[0][w]);
+      if constexpr (kTwo) M2 = fmaxf(M2, red_mx[1][w]);
+    }
+
+    // ---- C: scales, codes, packed stores
+    const RowScale r1 = row_scale<Q1>(M1);
+    const RowScale r2 = row_scale<kQ2>(M2);
+    if (tid == 0) {
+      a.scale1[row] = r1.scale;
+      if constexpr (kTwo) a.scale2[row] = r2.scale;
+    }
+    const uint32_t y1_bytes = Q1 == kQInt4 ? n / 2u : n;
+    const rsrc_t ry1 = make_rsrc(row_ptr(a.y1, row, y1_bytes), y1_bytes);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) store_codes<Q1>(in1[k], r1, ry1, vj[k]);
+    if constexpr (kTwo) {
+      const uint32_t y2_bytes = kQ2 == kQInt4 ? n / 2u : n;
+      const rsrc_t ry2 = make_rsrc(row_ptr(a.y2, row, y2_bytes), y2_bytes);
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) store_codes<kQ2>(in2[k], r2, ry2, vj[k]);
+    }
+
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) c1[k] = n1[k], c2[k] = n2[k];
+  };
+  body(row);
+  for (row += gridDim.x; row < a.rows; row += gridDim.x) body(row);
+}
+
+// ---- launch table for one element type
+
+template <int E, int NIN, int Q1, int Q2, int VPT>
+struct RowInst {
+  static hipError_t launch(int block, int grid, const Args& a, hipStream_t s) {
+    hipLaunchKernelGGL((row_kernel<E, NIN, Q1, Q2, VPT>), dim3(grid), dim3(block), 0, s, a);
+    return hipGetLastError();
+  }
+  static int occupancy(int block) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_kernel<E, NIN, Q1, Q2, VPT>, block,
+                                                     0) != hipSuccess)
+      return 0;
+    return n;
+  }
+};
+
+// Calls f.template operator()<Inst>() for the instance matching (nin, q1,
+// q2, vpt); returns false when no such instance exists.
+template <int E, template <int, int, int, int, int> class Inst, typename F>
+bool dispatch_variant(int nin, int q1, int q2, int vpt, F&& f) {
+#define ADQ_VPT_CASES(NIN_, Q1_, Q2_)                                       \
+  switch (vpt) {                                                            \
+    case 1: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 1>>(); return true; \
+    case 2: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 2>>(); return true; \
+    default: return false;                                                  \
+  }
+  if (nin == 1) {
+    if (q2 != kQNone) return false;
+    if (q1 == kQInt8) { ADQ_VPT_CASES(1, kQInt8, kQNone) }
+    if (q1 == kQInt4) { ADQ_VPT_CASES(1, kQInt4, kQNone) }
+    return false;
+  }
+  if (nin != 2) return false;
+  if (q1 == kQInt8 && q2 == kQNone) { ADQ_VPT_CASES(2, kQInt8, kQNone) }
+  if (q1 == kQInt4 && q2 == kQNone) { ADQ_VPT_CASES(2, kQInt4, kQNone) }
+  if (q1 == kQInt8 && q2 == kQInt8) { ADQ_VPT_CASES(2, kQInt8, kQInt8) }
+  if (q1 == kQInt8 && q2 == kQInt4) { ADQ_VPT_CASES(2, kQInt8, kQInt4) }
+  if (q1 == kQInt4 && q2 == kQInt8) { ADQ_VPT_CASES(2, kQInt4, kQInt8) }
+  if (q1 == kQInt4 && q2 == kQInt4) { ADQ_VPT_CASES(2, kQInt4, kQInt4) }
+#undef ADQ_VPT_CASES
+  return false;
+}
+
+// Entry points for one element type, used by launch_row() in adq_api.cpp.
+#define ADQ_DEFINE_ROW_ENTRY(E, SUFFIX)                                                     \
+  hipError_t launch_row_##SUFFIX(const Variant& v, int vpt, int block, int grid,           \
+                                 const Args& a, hipStream_t s) {                           \
+    hipError_t err = hipErrorInvalidValue;                                                 \
+    dispatch_variant<E, RowInst>(v.nin, v.q1, v.q2, vpt, [&]<typename I>() {               \
+      err = I::launch(block, grid, a, s);                                                  \
+    });                                                                                    \
+    return err;                                                                            \
+  }                                                                                        \
+  int row_occupancy_##SUFFIX(const Variant& v, int vpt, int block) {                       \
+    int occ = 0;                                                                           \
+    dispatch_variant<E, RowInst>(v.nin, v.q1, v.q2, vpt,                                   \
+                                 [&]<typename I>() { occ = I::occupancy(block); });        \
+    return occ;                                                                            \
+  }
+
+}  // namespace adq

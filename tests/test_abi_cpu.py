@@ -1,0 +1,212 @@
+"""Host-side checks of the C-ABI library that need no GPU.
+
+ - the library loads and exports every function include/adq.h declares;
+ - phase-1 validation: every error status, and the output-mask truth table
+   of the V2 page (Formula cases + Constraints), driven through the C-ABI
+   with placeholder device addresses.  No kernel is launched: phase 1 only
+   inspects descriptors.  On a machine without a GPU a well-formed call ends
+   in ADQ_ERR_RUNTIME ("no HIP device"); with one it returns ADQ_OK and an
+   executor, which is destroyed without running.
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import int4_dynamic_quantization_amd as adq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ACCEPTED = (adq.OK, adq.ERR_RUNTIME)
+
+# placeholder device addresses, 256-byte aligned and distinct
+_next = [0x10000000]
+
+
+def fake(shape, dtype):
+    t = adq.Tensor()
+    t.data = _next[0]
+    _next[0] += 1 << 24
+    t.dtype = dtype
+    t.ndim = len(shape)
+    for i, s in enumerate(shape):
+        t.shape[i] = s
+    return t
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "adq.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(adq_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) == 8, names
+    assert set(names) == set(adq.EXPORTED)
+    for name in names:
+        assert hasattr(adq.lib, name), name
+    # and the symbols come from this library, not a loaded dependency
+    handle = ctypes.CDLL(adq.LIB_PATH)
+    for name in names:
+        assert ctypes.cast(getattr(handle, name), ctypes.c_void_p).value
+
+
+def v2_call(x1=None, x2=None, gamma=None, beta=None, s1=None, s2=None, eps=1e-6, mask=None,
+            y1=None, y2=None, sc1=None, sc2=None, xo=None, out_ptrs=True):
+    m = None if mask is None else (ctypes.c_bool * 2)(*mask)
+    ws = ctypes.c_uint64(0)
+    ex = ctypes.c_void_p(None)
+    r = lambda t: None if t is None else ctypes.byref(t)
+    st = adq.lib.adq_add_rms_norm_dynamic_quant_v2_get_workspace_size(
+        r(x1), r(x2), r(gamma), r(beta), r(s1), r(s2), eps, m, r(y1), r(y2), r(sc1), r(sc2),
+        r(xo), ctypes.byref(ws) if out_ptrs else None, ctypes.byref(ex) if out_ptrs else None)
+    if ex.value:
+        adq.lib.adq_executor_destroy(ex)
+    return st
+
+
+def full_v2(M=4, N=64, dt=adq.BF16, q1=adq.INT8, q2=adq.INT8, smooth=2):
+    n1 = N // 2 if q1 == adq.INT4X2 else N
+    n2 = N // 2 if q2 == adq.INT4X2 else N
+    return dict(
+        x1=fake([M, N], dt), x2=fake([M, N], dt), gamma=fake([N], dt), beta=fake([N], dt),
+        s1=fake([N], dt) if smooth >= 1 else None, s2=fake([N], dt) if smooth >= 2 else None,
+        y1=fake([M, n1], q1), y2=fake([M, n2], q2), sc1=fake([M], adq.F32),
+        sc2=fake([M], adq.F32), xo=fake([M, N], dt))
+
+
+def test_valid_call_accepted():
+    assert v2_call(**full_v2()) in ACCEPTED
+    assert v2_call(**full_v2(dt=adq.F16, q1=adq.INT4X2)) in ACCEPTED
+    # leading dims flattened, scale with shape [...]
+    a = full_v2()
+    a.update(x1=fake([2, 3, 64], adq.BF16), x2=fake([2, 3, 64], adq.BF16),
+             xo=fake([2, 3, 64], adq.BF16), y1=fake([2, 3, 64], adq.INT8),
+             y2=fake([2, 3, 64], adq.INT8), sc1=fake([2, 3], adq.F32), sc2=fake([6], adq.F32))
+    assert v2_call(**a) in ACCEPTED
+
+
+def test_mask_truth_table_through_phase_one():
+    with open(os.path.join(ROOT, "tests", "golden", "mask_table.json")) as f:
+        rows = json.load(f)["rows"]
+    for mask, has1, has2, valid, y1, y2 in rows:
+        a = full_v2()
+        if not has1:
+            a["s1"] = None
+        if not has2:
+            a["s2"] = None
+        st = v2_call(mask=mask, **a)
+        if not valid:
+            assert st == adq.ERR_PARAM_INVALID, (mask, has1, has2, adq.last_error())
+            continue
+        assert st in ACCEPTED, (mask, has1, has2, adq.last_error())
+        # an output that is produced is required; one that is not may be NULL
+        for k, active in ((1, y1), (2, y2)):
+            b = dict(a)
+            b[f"y{k}"] = None
+            st = v2_call(mask=mask, **b)
+            if active:
+                assert st == adq.ERR_NULLPTR, (mask, has1, has2, k)
+            else:
+                assert st in ACCEPTED, (mask, has1, has2, k, adq.last_error())
+
+
+@pytest.mark.parametrize("field", ["x1", "x2", "gamma", "xo"])
+def test_required_tensor_missing(field):
+    a = full_v2()
+    a[field] = None
+    assert v2_call(**a) == adq.ERR_NULLPTR
+
+
+def test_null_data_pointer_and_out_pointers():
+    a = full_v2()
+    a["gamma"].data = None
+    assert v2_call(**a) == adq.ERR_NULLPTR
+    assert v2_call(out_ptrs=False, **full_v2()) == adq.ERR_NULLPTR
+
+
+@pytest.mark.parametrize("field", ["x1", "x2", "xo", "gamma", "y1", "sc1"])
+def test_empty_tensor_rejected(field):
+    a = full_v2()
+    t = a[field]
+    t.shape[0] = 0
+    assert v2_call(**a) == adq.ERR_PARAM_INVALID
+    assert "empty" in adq.last_error()
+
+
+def test_shape_and_dtype_mismatches():
+    cases = []
+    a = full_v2(); a["x2"] = fake([4, 32], adq.BF16); cases.append(a)
+    a = full_v2(); a["x2"] = fake([4, 64], adq.F16); cases.append(a)
+    a = full_v2(); a["xo"] = fake([4, 64], adq.F16); cases.append(a)
+    a = full_v2(); a["gamma"] = fake([63], adq.BF16); cases.append(a)
+    a = full_v2(); a["beta"] = fake([64], adq.F16); cases.append(a)
+    a = full_v2(); a["s2"] = fake([1, 64], adq.BF16); cases.append(a)
+    a = full_v2(); a["y1"] = fake([4, 32], adq.INT8); cases.append(a)
+    a = full_v2(); a["y2"] = fake([4, 64], adq.INT4X2); cases.append(a)
+    a = full_v2(); a["y1"] = fake([3, 64], adq.INT8); cases.append(a)
+    a = full_v2(); a["sc1"] = fake([5], adq.F32); cases.append(a)
+    a = full_v2(); a["sc2"] = fake([4], adq.F16); cases.append(a)
+    for i, c in enumerate(cases):
+        assert v2_call(**c) == adq.ERR_PARAM_INVALID, (i, adq.last_error())
+
+
+def test_odd_width_int4_rejected():
+    a = full_v2(N=63, q1=adq.INT4X2)
+    a["y1"] = fake([4, 31], adq.INT4X2)
+    assert v2_call(**a) == adq.ERR_PARAM_INVALID
+    # INT8 accepts odd widths (generic kernel)
+    assert v2_call(**full_v2(N=63)) in ACCEPTED
+
+
+def test_unsupported_dtypes():
+    a = full_v2()
+    for t in ("x1", "x2", "xo"):
+        a[t] = fake([4, 64], adq.F32)
+    assert v2_call(**a) == adq.ERR_UNSUPPORTED
+    a = full_v2()
+    a["y1"] = fake([4, 64], adq.F16)
+    assert v2_call(**a) == adq.ERR_UNSUPPORTED
+
+
+def test_bad_epsilon():
+    assert v2_call(eps=float("nan"), **full_v2()) == adq.ERR_PARAM_INVALID
+    assert v2_call(eps=float("inf"), **full_v2()) == adq.ERR_PARAM_INVALID
+
+
+def rms_call(x, gamma, beta, smooth, y, sc, eps=1e-6):
+    ws = ctypes.c_uint64(0)
+    ex = ctypes.c_void_p(None)
+    r = lambda t: None if t is None else ctypes.byref(t)
+    st = adq.lib.adq_rms_norm_dynamic_quant_get_workspace_size(
+        r(x), r(gamma), r(beta), r(smooth), eps, r(y), r(sc), ctypes.byref(ws), ctypes.byref(ex))
+    if ex.value:
+        adq.lib.adq_executor_destroy(ex)
+    return st
+
+
+def test_rms_norm_dq_validation():
+    x, g = fake([64, 1024], adq.F16), fake([1024], adq.F16)
+    y, sc = fake([64, 1024], adq.INT8), fake([64], adq.F32)
+    assert rms_call(x, g, None, None, y, sc) in ACCEPTED
+    assert rms_call(x, g, None, fake([1024], adq.F16), fake([64, 512], adq.INT4X2),
+                    sc) in ACCEPTED
+    assert rms_call(x, None, None, None, y, sc) == adq.ERR_NULLPTR
+    assert rms_call(x, g, None, None, None, sc) == adq.ERR_NULLPTR
+    assert rms_call(x, g, None, None, y, None) == adq.ERR_NULLPTR
+    assert rms_call(x, fake([1024], adq.BF16), None, None, y, sc) == adq.ERR_PARAM_INVALID
+    assert rms_call(fake([0, 1024], adq.F16), g, None, None, y, sc) == adq.ERR_PARAM_INVALID
+    assert rms_call(x, g, None, None, fake([64, 1024], adq.F32), sc) == adq.ERR_UNSUPPORTED
+
+
+def test_phase_two_and_helpers_reject_null_executor():
+    assert adq.lib.adq_add_rms_norm_dynamic_quant_v2(None, 0, None, None) == adq.ERR_NULLPTR
+    assert adq.lib.adq_rms_norm_dynamic_quant(None, 0, None, None) == adq.ERR_NULLPTR
+    ws = ctypes.c_uint64(0)
+    assert adq.lib.adq_executor_set_path(None, 0, ctypes.byref(ws)) == adq.ERR_NULLPTR
+    assert adq.lib.adq_executor_describe(None, None, 0) == -1
+    adq.lib.adq_executor_destroy(None)
+    assert isinstance(adq.last_error(), str)

@@ -1,0 +1,391 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle on the
+same seeded inputs.
+
+Workloads at their full sizes: element-by-element against the oracle where
+it finishes in seconds (rmsnorm_dq, v2_square, v2_decode); on sampled rows
+plus whole-tensor properties for v2_outlier (16384 x 8192) and v2_int4
+(65536 x 5120).  Then ragged shapes, the option matrix, degenerate rows,
+determinism, streams and forced kernel paths.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import int4_dynamic_quantization_amd as adq
+import oracle
+import synth
+from gpu_helpers import (codes_of, compare_rms, compare_v2, dev, host, host_bits, oracle_v2,
+                         run_rms, run_v2)
+from helpers import check_codes, check_scales, from_bits, to_bits, unpack_int4
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    torch.cuda.init()
+    yield
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+# ---- workloads --------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["rmsnorm_dq", "v2_square", "v2_decode"])
+def test_workload_full_parity(name):
+    w = synth.WORKLOADS[name]
+    _announce(f"{name} {w.rows}x{w.cols} {w.dtype}")
+    x1, x2 = synth.inputs(w)
+    g, b, s1, s2 = synth.params(w)
+    if w.op == "rmsnorm":
+        outs, desc = run_rms(x1, g, b, s1, w.eps, w.y_types[0], w.dtype)
+        ora = oracle.rms_norm_dq(x1, g, b, s1, w.eps, w.y_types[0], w.dtype)
+        compare_rms(outs, ora, w.y_types[0])
+        return
+    outs, desc = run_v2(x1, x2, g, b, s1, s2, w.eps, w.mask, w.y_types, w.dtype)
+    ora = oracle_v2(x1, x2, g, b, s1, s2, w.eps, w.mask, w.y_types, w.dtype)
+    compare_v2(outs, ora, w.y_types)
+    for k in (1, 2):
+        if not ora["active"][k - 1]:
+            assert outs[f"y{k}"] is None
+
+
+def _sample_rows(m, seed, n_rand=192):
+    rng = np.random.default_rng(seed)
+    rows = set(range(64)) | set(range(m - 64, m)) | set(rng.choice(m, n_rand, replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+def _exact_sum_rounded(x1, x2, dtype):
+    """x1 + x2 rounded once to the storage type.  fp16: numpy's float64 ->
+    float16 conversion (the float64 sum is exact).  bf16: torch's float32 ->
+    bfloat16 conversion where the float64 sum is a float32 value, and the
+    oracle's rounding for the few sums that are not (very different
+    magnitudes)."""
+    s = from_bits(x1, dtype) + from_bits(x2, dtype)
+    if dtype == "fp16":
+        return s.astype(np.float16).view(np.uint16)
+    f = s.astype(np.float32)
+    out = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    inexact = f.astype(np.float64) != s
+    for idx in zip(*np.nonzero(inexact)):
+        out[idx] = oracle.round_to_storage(float(s[idx]), dtype)
+    return out
+
+
+@pytest.mark.parametrize("name", ["v2_outlier", "v2_int4"])
+def test_workload_full_size_sampled_and_properties(name):
+    w = synth.WORKLOADS[name]
+    _announce(f"{name} {w.rows}x{w.cols} {w.dtype}")
+    x1, x2 = synth.inputs(w)
+    g, b, s1, s2 = synth.params(w)
+    outs, desc = run_v2(x1, x2, g, b, s1, s2, w.eps, w.mask, w.y_types, w.dtype)
+    assert "path=row" in desc, desc
+    # sampled rows, element by element against the oracle
+    rows = _sample_rows(w.rows, w.seed)
+    ora = oracle_v2(x1[rows], x2[rows], g, b, s1, s2, w.eps, w.mask, w.y_types, w.dtype)
+    compare_v2(outs, ora, w.y_types, rows=rows)
+    # every row: xOut is the correctly rounded sum; per-row code properties
+    xo = host_bits(outs["x_out"])
+    chunk = 4096
+    for r0 in range(0, w.rows, chunk):
+        r1 = min(w.rows, r0 + chunk)
+        assert np.array_equal(xo[r0:r1], _exact_sum_rounded(x1[r0:r1], x2[r0:r1], w.dtype))
+    for k in (1, 2):
+        if not ora["active"][k - 1]:
+            continue
+        q = oracle.QMAX[w.y_types[k - 1]]
+        sc = host(outs[f"scale{k}"]).reshape(-1)
+        assert np.all(np.isfinite(sc)) and np.all(sc > 0)
+        for r0 in range(0, w.rows, chunk):
+            c = codes_of(outs[f"y{k}"][r0:r0 + chunk], w.y_types[k - 1]).astype(np.int32)
+            assert np.all(np.abs(c).max(axis=1) == q)
+            assert c.min() >= -q and c.max() <= q
+
+
+# ---- golden rows on the GPU (zero tolerance except flagged real ties) -------
+
+with open(os.path.join(GOLDEN, "worked_rows.json")) as f:
+    _CASES = json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _CASES, ids=[c["name"] for c in _CASES])
+def test_golden_rows_on_gpu(case):
+    dt = case["dtype"]
+    bits = lambda k: None if case.get(k) is None else to_bits(case[k], dt)
+    exp = case["expect"]
+    if case["op"] == "rmsnorm":
+        outs, _ = run_rms(bits("x1"), bits("gamma"), bits("beta"), bits("smooth1"), case["eps"],
+                          case["y_types"][0], dt)
+        got = {"y1": outs["y"], "scale1": outs["scale"]}
+    else:
+        outs, _ = run_v2(bits("x1"), bits("x2"), bits("gamma"), bits("beta"), bits("smooth1"),
+                         bits("smooth2"), case["eps"], case["mask"], case["y_types"], dt)
+        got = outs
+        assert np.array_equal(host_bits(outs["x_out"]), to_bits(exp["x_out"], dt))
+    ora = _run_oracle_case(case)
+    for k in (1, 2):
+        if f"code{k}" not in exp:
+            continue
+        c = codes_of(got[f"y{k}"], case["y_types"][k - 1]).astype(np.int64)
+        want = np.array(exp[f"code{k}"])
+        ok = np.array(exp.get("near_tie_ok", np.zeros_like(want, bool)))
+        assert np.all((c == want) | (ok & (np.abs(c - want) <= 1))), (c, want)
+        check_scales(host(got[f"scale{k}"]).reshape(-1), ora[f"scale{k}"])
+        if f"packed{k}" in exp:
+            assert np.array_equal(host(got[f"y{k}"]), np.array(exp[f"packed{k}"], np.uint8))
+
+
+def _run_oracle_case(c):
+    dt = c["dtype"]
+    bits = lambda k: None if c.get(k) is None else to_bits(c[k], dt)
+    if c["op"] == "rmsnorm":
+        r = oracle.rms_norm_dq(bits("x1"), bits("gamma"), bits("beta"), bits("smooth1"),
+                               c["eps"], c["y_types"][0], dt)
+        return {"scale1": r["scale"], "code1": r["code"]}
+    return oracle.add_rms_norm_dq_v2(bits("x1"), bits("x2"), bits("gamma"), bits("beta"),
+                                     bits("smooth1"), bits("smooth2"), c["eps"], c["mask"],
+                                     c["y_types"][0], c["y_types"][1], dt)
+
+
+# ---- shapes -----------------------------------------------------------------
+
+def _case_inputs(m, n, dtype, seed, n_smooth=2, beta=True, outlier=0.0):
+    w = synth.Workload("case", "v2", m, n, dtype, seed, None, beta, n_smooth,
+                       outlier_frac=outlier)
+    x1, x2 = synth.inputs(w)
+    g, b, s1, s2 = synth.params(w)
+    return x1, x2, g, b, s1, s2
+
+
+SHAPES = [(1, 8), (3, 8), (257, 16), (3, 24), (5, 100 * 8), (3, 1000), (257, 1000),
+          (2, 5120), (3, 16384), (1, 1), (3, 7), (4, 2), (257, 100), (2, 16392), (1, 20000),
+          (2, 65536), (64, 1032)]
+
+
+@pytest.mark.parametrize("m,n", SHAPES)
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_ragged_shapes(m, n, dtype):
+    _announce(f"shape {m}x{n} {dtype}")
+    y_types = ("int8", "int4") if n % 2 == 0 else ("int8", "int8")
+    x1, x2, g, b, s1, s2 = _case_inputs(m, n, dtype, seed=1000 + m * 7 + n)
+    outs, desc = run_v2(x1, x2, g, b, s1, s2, 1e-6, (True, True), y_types, dtype)
+    ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, (True, True), y_types, dtype)
+    compare_v2(outs, ora, y_types)
+    vec = n % 8 == 0 and n <= 16384
+    assert ("path=row" in desc) == vec, desc
+
+
+# ---- the option matrix --------------------------------------------------------
+
+with open(os.path.join(GOLDEN, "mask_table.json")) as f:
+    _MASK_ROWS = [r for r in json.load(f)["rows"] if r[3]]
+
+
+@pytest.mark.parametrize("row", _MASK_ROWS, ids=lambda r: f"mask{r[0]}-s1{r[1]}-s2{r[2]}")
+@pytest.mark.parametrize("y_types", [("int8", "int8"), ("int4", "int8"), ("int8", "int4"),
+                                     ("int4", "int4")])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_option_matrix(row, y_types, dtype):
+    mask, has1, has2, _, act1, act2 = row
+    m, n = 5, 264
+    x1, x2, g, b, s1, s2 = _case_inputs(m, n, dtype, seed=77)
+    s1 = s1 if has1 else None
+    s2 = s2 if has2 else None
+    # canaries in every output tensor: outputs that are not produced stay untouched
+    canary = {}
+    for k in (1, 2):
+        width = n // 2 if y_types[k - 1] == "int4" else n
+        t = torch.full((m, width), 0x5A, dtype=torch.uint8 if y_types[k - 1] == "int4"
+                       else torch.int8, device="cuda")
+        canary[f"y{k}"] = t
+        canary[f"scale{k}"] = torch.full((m,), 1234.5, dtype=torch.float32, device="cuda")
+    outs, _ = run_v2(x1, x2, g, b, s1, s2, 1e-6, mask, y_types, dtype, outputs=canary)
+    ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, mask, y_types, dtype)
+    assert ora["active"] == (act1, act2)
+    compare_v2(outs, ora, y_types)
+    for k, act in ((1, act1), (2, act2)):
+        if not act:
+            assert torch.all(outs[f"y{k}"].view(torch.uint8) == 0x5A)
+            assert torch.all(outs[f"scale{k}"] == 1234.5)
+
+
+@pytest.mark.parametrize("y_type", ["int8", "int4"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("smooth", [False, True])
+@pytest.mark.parametrize("n", [1024, 1000])
+def test_rms_norm_dq_variants(y_type, dtype, smooth, n):
+    w = synth.Workload("rms", "rmsnorm", 33, n, dtype, 5, None, True, 1 if smooth else 0)
+    x, _ = synth.inputs(w)
+    g, b, s1, _ = synth.params(w)
+    outs, _ = run_rms(x, g, b, s1, 1e-6, y_type, dtype)
+    ora = oracle.rms_norm_dq(x, g, b, s1, 1e-6, y_type, dtype)
+    compare_rms(outs, ora, y_type)
+
+
+def test_rms_norm_dq_beta_zeros_equals_absent():
+    w = synth.WORKLOADS["rmsnorm_dq"]
+    x, _ = synth.inputs(w)
+    g, _, _, _ = synth.params(w)
+    zeros = np.zeros(w.cols, np.uint16)
+    a, _ = run_rms(x, g, None, None, w.eps, "int8", w.dtype)
+    z, _ = run_rms(x, g, zeros, None, w.eps, "int8", w.dtype)
+    assert torch.equal(a["y"], z["y"]) and torch.equal(a["scale"], z["scale"])
+
+
+# ---- degenerate rows -------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("n", [64, 63])
+def test_zero_rows(dtype, n):
+    """gamma = beta = 0 (row max 0), and x = 0 with eps = 0 (0/0 in the norm):
+    scale 0 and all codes 0."""
+    m = 3
+    x1, x2, g, b, s1, s2 = _case_inputs(m, n, dtype, seed=5)
+    zero = np.zeros(n, np.uint16)
+    outs, _ = run_v2(x1, x2, zero, zero, None, None, 1e-6, (True, True), ("int8", "int8"),
+                     dtype)
+    for k in (1, 2):
+        assert torch.all(outs[f"scale{k}"] == 0) and torch.all(outs[f"y{k}"] == 0)
+    zx = np.zeros((m, n), np.uint16)
+    outs, _ = run_v2(zx, zx, g, zero, None, None, 0.0, None, ("int8", "int8"), dtype)
+    ora = oracle_v2(zx, zx, g, zero, None, None, 0.0, None, ("int8", "int8"), dtype)
+    assert np.all(ora["scale1"] == 0) and np.all(ora["code1"] == 0)
+    assert torch.all(outs["scale1"] == 0) and torch.all(outs["y1"] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_ties_zero_tolerance(dtype):
+    """gamma = 0 makes y = beta exactly, so every .5 value is an exact tie and
+    the codes must round half to even with no tolerance."""
+    n, m = 64, 2
+    rng = np.random.default_rng(3)
+    halves = np.concatenate([[127.0], rng.integers(-126, 126, n - 1) + 0.5])
+    beta = to_bits(halves, dtype)
+    x1 = to_bits(rng.integers(-4, 5, (m, n)).astype(np.float64), dtype)
+    x2 = to_bits(np.ones((m, n)), dtype)
+    zero = np.zeros(n, np.uint16)
+    outs, _ = run_v2(x1, x2, zero, beta, None, None, 1e-6, (True, False), ("int8", "int8"),
+                     dtype)
+    want = np.rint(halves).astype(np.int8)  # numpy rint: half to even
+    got = host(outs["y1"])
+    assert np.array_equal(got, np.tile(want, (m, 1)))
+    assert torch.all(outs["scale1"] == 1.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_tiny_scale_division_path(dtype):
+    """A row maximum so small that 1/scale overflows float: the kernels
+    quantize by division; results still match the oracle."""
+    n, m = 64, 2
+    rng = np.random.default_rng(4)
+    tiny = 2.0 ** -120 if dtype == "bf16" else 2.0 ** -20
+    beta = to_bits(np.round(rng.uniform(-8, 8, n)) * tiny, dtype)
+    x1, x2, g, b, s1, s2 = _case_inputs(m, n, dtype, seed=6, n_smooth=0)
+    zero = np.zeros(n, np.uint16)
+    for yt in ("int8", "int4"):
+        outs, _ = run_v2(x1, x2, zero, beta, None, None, 1e-6, (True, False), (yt, "int8"),
+                         dtype)
+        ora = oracle_v2(x1, x2, zero, beta, None, None, 1e-6, (True, False), (yt, "int8"),
+                        dtype)
+        assert np.array_equal(host(outs["scale1"]), ora["scale1"])
+        check_codes(codes_of(outs["y1"], yt), ora["code1"], ora["pre1"])
+
+
+def test_fp16_sum_overflow_to_inf_in_xout():
+    n, m = 64, 2
+    big = np.full((m, n), 60000.0)
+    big[:, 1::2] = -1.0
+    x1 = to_bits(big, "fp16")
+    x2 = to_bits(big, "fp16")
+    g = to_bits(np.ones(n), "fp16")
+    outs, _ = run_v2(x1, x2, g, None, None, None, 1e-6, None, ("int8", "int8"), "fp16")
+    ora = oracle_v2(x1, x2, g, None, None, None, 1e-6, None, ("int8", "int8"), "fp16")
+    assert np.all(ora["x_out"][:, 0::2] == 0x7C00)
+    compare_v2(outs, ora, ("int8", "int8"))
+
+
+# ---- execution properties --------------------------------------------------------------
+
+def test_determinism_bitwise():
+    w = synth.WORKLOADS["v2_square"]
+    x1, x2 = synth.inputs(w)
+    g, b, s1, s2 = synth.params(w)
+    ex, outs = adq.plan_add_rms_norm_dynamic_quant_v2(
+        dev(x1, w.dtype), dev(x2, w.dtype), dev(g, w.dtype), dev(b, w.dtype), dev(s1, w.dtype),
+        None, w.eps, w.mask)
+    ex.run()
+    first = {k: v.clone() for k, v in outs.items() if v is not None}
+    for _ in range(3):
+        for v in outs.values():
+            if v is not None:
+                v.zero_()
+        ex.run()
+        torch.cuda.synchronize()
+        for k, v in first.items():
+            assert torch.equal(outs[k], v), k
+    ex.close()
+
+
+def test_generic_path_matches_oracle_on_vector_shape():
+    x1, x2, g, b, s1, s2 = _case_inputs(9, 4096, "bf16", seed=8)
+    for path in (adq.PATH_ROW, adq.PATH_GENERIC):
+        outs, desc = run_v2(x1, x2, g, b, s1, s2, 1e-6, None, ("int8", "int4"), "bf16",
+                            path=path)
+        ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, None, ("int8", "int4"), "bf16")
+        compare_v2(outs, ora, ("int8", "int4"))
+
+
+def test_launch_on_side_stream_and_executor_reuse():
+    x1, x2, g, b, s1, s2 = _case_inputs(40, 2048, "fp16", seed=9)
+    dx1, dx2 = dev(x1, "fp16"), dev(x2, "fp16")
+    ex, outs = adq.plan_add_rms_norm_dynamic_quant_v2(
+        dx1, dx2, dev(g, "fp16"), dev(b, "fp16"), dev(s1, "fp16"), dev(s2, "fp16"), 1e-6, None)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ex.run(None, s)
+    s.synchronize()
+    ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, None, ("int8", "int8"), "fp16")
+    compare_v2(outs, ora, ("int8", "int8"))
+    # same executor, new values in the same input buffers
+    y1, y2, _, _, _, _ = _case_inputs(40, 2048, "fp16", seed=10)
+    dx1.copy_(dev(y1, "fp16"))
+    dx2.copy_(dev(y2, "fp16"))
+    ex.run()
+    torch.cuda.synchronize()
+    ora = oracle_v2(y1, y2, g, b, s1, s2, 1e-6, None, ("int8", "int8"), "fp16")
+    compare_v2(outs, ora, ("int8", "int8"))
+    ex.close()
+
+
+def test_set_path_rejects_ineligible_shape():
+    x1, x2, g, b, s1, s2 = _case_inputs(2, 100, "bf16", seed=11)
+    ex, _ = adq.plan_add_rms_norm_dynamic_quant_v2(
+        dev(x1, "bf16"), dev(x2, "bf16"), dev(g, "bf16"), None, None, None, 1e-6, None)
+    assert "path=generic" in ex.describe()
+    with pytest.raises(adq.AdqError) as e:
+        ex.set_path(adq.PATH_ROW)
+    assert e.value.status == adq.ERR_PARAM_INVALID
+    assert "path=generic" in ex.describe()
+    ex.close()
+
+
+def test_leading_dims_flattened():
+    x1, x2, g, b, s1, s2 = _case_inputs(12, 512, "bf16", seed=12)
+    d1 = dev(x1, "bf16").view(3, 4, 512)
+    d2 = dev(x2, "bf16").view(3, 4, 512)
+    y1, y2, sc1, sc2, xo = adq.add_rms_norm_dynamic_quant_v2(
+        d1, d2, dev(g, "bf16"), dev(b, "bf16"), dev(s1, "bf16"), dev(s2, "bf16"), 1e-6)
+    torch.cuda.synchronize()
+    assert y1.shape == (3, 4, 512) and sc1.shape == (3, 4)
+    ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, None, ("int8", "int8"), "bf16")
+    outs = {"x_out": xo.view(12, 512), "y1": y1.view(12, 512), "y2": y2.view(12, 512),
+            "scale1": sc1.view(12), "scale2": sc2.view(12)}
+    compare_v2(outs, ora, ("int8", "int8"))
