@@ -122,6 +122,9 @@ def main():
     ap.add_argument("--workload", default="v2_outlier")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead: time a plain device-to-device copy of MIB MiB (reference "
+                         "for achievable bandwidth and for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this operator is row-local and this build runs on a "
@@ -129,6 +132,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        calibrate_copy(torch, args.calibrate_copy, args.steps, args.warmup)
+        return
     import int4_dynamic_quantization_amd as adq
     import synth
 
@@ -152,21 +158,22 @@ def main():
         ex.run(ws, stream)
     torch.cuda.synchronize()
 
-    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # Timed region: K back-to-back launches between two HIP events recorded
+    # on the launch stream; the average launch duration is their span / K.
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    events[0].record(stream)
+    start.record(stream)
     for i in range(args.steps):
         ex, ws, _, _ = cases[i % n_sets]
         ex.run(ws, stream)
-        events[i + 1].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_launch_ms = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
-    ms = sum(per_launch_ms) / args.steps
+    ms = start.elapsed_time(end) / args.steps
     gbs = footprint / (ms * 1e-3) / 1e9
-    print(f"[bench] {args.steps} launches: avg {ms * 1e3:.1f} us, min "
-          f"{min(per_launch_ms) * 1e3:.1f} us, max {max(per_launch_ms) * 1e3:.1f} us, "
+    print(f"[bench] {args.steps} launches: avg {ms * 1e3:.1f} us per launch, "
           f"wall {wall * 1e3:.1f} ms", file=sys.stderr, flush=True)
 
     traffic = measured_traffic(w.name)
@@ -205,6 +212,28 @@ def main():
     for ex, _, _, _ in cases:
         ex.close()
     print(json.dumps(result), flush=True)
+
+
+def calibrate_copy(torch, mib: int, steps: int, warmup: int) -> None:
+    """A plain copy of `mib` MiB: reads and writes `mib` MiB per launch."""
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        dst.copy_(src)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "steps": steps,
+                      "ms_per_copy": round(ms, 6),
+                      "gbs_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 if __name__ == "__main__":

@@ -7,8 +7,8 @@ streams.  The C functions are exposed under their own names (without the
 ``rms_norm_dynamic_quant`` additionally run both phases on torch tensors
 and allocate the outputs.
 
-If the shared library has not been built, importing this package raises
-ImportError: there is no fallback implementation.
+The shared library is loaded on first use (``lib``); if it has not been
+built, that raises ImportError: there is no fallback implementation.
 """
 from __future__ import annotations
 
@@ -103,11 +103,25 @@ def _load():
     return lib
 
 
-lib = _load()
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def __getattr__(name):
+    # module attribute `lib`: the loaded C-ABI library (loaded on first use)
+    if name == "lib":
+        return _lib()
+    raise AttributeError(name)
 
 
 def last_error() -> str:
-    return lib.adq_last_error().decode()
+    return _lib().adq_last_error().decode()
 
 
 def _check(status: int) -> None:
@@ -161,26 +175,26 @@ class Executor:
 
     def set_path(self, path: int) -> int:
         ws = ctypes.c_uint64(0)
-        _check(lib.adq_executor_set_path(self.handle, int(path), ctypes.byref(ws)))
+        _check(_lib().adq_executor_set_path(self.handle, int(path), ctypes.byref(ws)))
         self.workspace_size = int(ws.value)
         return self.workspace_size
 
     def describe(self) -> str:
         buf = ctypes.create_string_buffer(512)
-        lib.adq_executor_describe(self.handle, buf, len(buf))
+        _lib().adq_executor_describe(self.handle, buf, len(buf))
         return buf.value.decode()
 
     def run(self, workspace=None, stream=None) -> None:
         ws_ptr = None if workspace is None else workspace.data_ptr()
         ws_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
         s = None if stream is None else stream.cuda_stream
-        fn = (lib.adq_add_rms_norm_dynamic_quant_v2 if self.op == "v2"
-              else lib.adq_rms_norm_dynamic_quant)
+        fn = (_lib().adq_add_rms_norm_dynamic_quant_v2 if self.op == "v2"
+              else _lib().adq_rms_norm_dynamic_quant)
         _check(fn(ws_ptr, ws_size, self.handle, s))
 
     def close(self) -> None:
         if self.handle:
-            lib.adq_executor_destroy(self.handle)
+            _lib().adq_executor_destroy(self.handle)
             self.handle = None
 
     def __del__(self):
@@ -201,7 +215,7 @@ def add_rms_norm_dynamic_quant_v2_get_workspace_size(
     handle = ctypes.c_void_p(None)
     descs = (x1, x2, gamma, beta, smooth_scale1, smooth_scale2, y1_out, y2_out, scale1_out,
              scale2_out, x_out)
-    _check(lib.adq_add_rms_norm_dynamic_quant_v2_get_workspace_size(
+    _check(_lib().adq_add_rms_norm_dynamic_quant_v2_get_workspace_size(
         _ref(x1), _ref(x2), _ref(gamma), _ref(beta), _ref(smooth_scale1), _ref(smooth_scale2),
         float(epsilon), mask, _ref(y1_out), _ref(y2_out), _ref(scale1_out), _ref(scale2_out),
         _ref(x_out), ctypes.byref(ws), ctypes.byref(handle)))
@@ -213,7 +227,7 @@ def rms_norm_dynamic_quant_get_workspace_size(x, gamma, beta, smooth_scales, eps
     ws = ctypes.c_uint64(0)
     handle = ctypes.c_void_p(None)
     descs = (x, gamma, beta, smooth_scales, y_out, scale_out)
-    _check(lib.adq_rms_norm_dynamic_quant_get_workspace_size(
+    _check(_lib().adq_rms_norm_dynamic_quant_get_workspace_size(
         _ref(x), _ref(gamma), _ref(beta), _ref(smooth_scales), float(epsilon), _ref(y_out),
         _ref(scale_out), ctypes.byref(ws), ctypes.byref(handle)))
     return Executor(handle, ws.value, "rmsnorm", descs)

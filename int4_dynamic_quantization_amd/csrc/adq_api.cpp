@@ -204,10 +204,17 @@ adq_status current_device(int* dev, int* cus) {
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
 // Row-kernel geometry: vectors per thread and block size for n / 8 vectors.
+#ifndef ADQ_VPT1_MAX_NVEC
+#define ADQ_VPT1_MAX_NVEC 64
+#endif
+#ifndef ADQ_MAX_WG_PER_CU
+#define ADQ_MAX_WG_PER_CU 0
+#endif
+
 bool row_geometry(int64_t nvec, int* vpt, int* block) {
   if (nvec <= 0) return false;
-  if (nvec <= 64) {
-    *vpt = 1, *block = 64;
+  if (nvec <= ADQ_VPT1_MAX_NVEC) {
+    *vpt = 1, *block = round_up((int)nvec, 64);
   } else if (nvec <= 2048) {
     *vpt = 2, *block = round_up((int)((nvec + 1) / 2), 64);
   } else {
@@ -227,7 +234,8 @@ adq_status plan(adq_executor* e, int path) {
     if (!e->vector_ok || !row_geometry(n / 8, &vpt, &block))
       return fail(ADQ_ERR_PARAM_INVALID,
                   "row path needs n %% 8 == 0, n <= 16384 and 16-byte aligned tensors");
-    const int occ = adq::row_max_blocks_per_cu(e->var, vpt, block);
+    int occ = adq::row_max_blocks_per_cu(e->var, vpt, block);
+    if (ADQ_MAX_WG_PER_CU > 0 && occ > ADQ_MAX_WG_PER_CU) occ = ADQ_MAX_WG_PER_CU;
     if (occ <= 0) return fail(ADQ_ERR_RUNTIME, "row kernel does not fit block %d", block);
     const int64_t slots = (int64_t)occ * e->cus;
     const int64_t per = (e->m + slots - 1) / slots;

@@ -33,8 +33,16 @@ __device__ __forceinline__ void* row_ptr(void* base, int64_t row, uint32_t row_b
   return static_cast<char*>(base) + row * (int64_t)row_bytes;
 }
 
-// Cache policy of streamed (read-once / write-once) accesses: non-temporal.
-constexpr int kStream = 2;
+// Cache policy bits of streamed (read-once / write-once) buffer accesses:
+// 2 = non-temporal.
+#ifndef ADQ_LOAD_POLICY
+#define ADQ_LOAD_POLICY 2
+#endif
+#ifndef ADQ_STORE_POLICY
+#define ADQ_STORE_POLICY 2
+#endif
+constexpr int kStreamLoad = ADQ_LOAD_POLICY;
+constexpr int kStreamStore = ADQ_STORE_POLICY;
 
 // Two packed 16-bit values (element 0 in the low half) -> two floats.
 template <int E>
@@ -118,11 +126,6 @@ __device__ __forceinline__ uint32_t code_bits(float a, float inv) {
   return __float_as_uint(__builtin_fmaf(a, inv, kMagic));
 }
 
-// Division form for rows whose scale is so small that 1/scale overflows.
-__device__ __forceinline__ uint32_t code_bits_div(float a, float scale) {
-  return __float_as_uint(a / scale + kMagic);
-}
-
 // Low bytes of four words -> one word (byte i from word i).
 __device__ __forceinline__ uint32_t gather4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
   const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u);
@@ -148,19 +151,39 @@ constexpr float kQMax = Q == kQInt4 ? 7.0f : 127.0f;
 
 // scale = row max / Q (correctly rounded); inv = v_rcp_f32(scale), within
 // 1 ulp of 1/scale and exact for powers of two; 0 for an all-zero row.
+// When 1/scale overflows (scale below about 2^-128) the quantizer inputs
+// and the scale are both multiplied by boost = 2^64 (exact) before the
+// reciprocal, so one fma per code serves every row.
 struct RowScale {
   float scale;
   float inv;
-  bool slow;  // 1/scale overflowed (scale below 2^-126): quantize by division
+  float boost;  // 1, or 2^64 for rows with a tiny scale
 };
 
 template <int Q>
 __device__ __forceinline__ RowScale row_scale(float m) {
   RowScale r;
   r.scale = m / kQMax<Q>;
-  r.inv = r.scale > 0.0f ? __builtin_amdgcn_rcpf(r.scale) : 0.0f;
-  r.slow = !(r.inv <= 3.4028234e38f);
+  r.boost = 1.0f;
+  r.inv = 0.0f;
+  if (r.scale > 0.0f) {
+    r.inv = __builtin_amdgcn_rcpf(r.scale);
+    if (!(r.inv <= 3.4028234e38f)) {
+      r.boost = 18446744073709551616.0f;  // 2^64
+      r.inv = __builtin_amdgcn_rcpf(r.scale * r.boost);
+    }
+  }
   return r;
+}
+
+// Scales a row's quantizer inputs by rs.boost (register-only; taken for
+// rows with a tiny scale).
+template <int N>
+__device__ __forceinline__ void apply_boost(float (&in)[N], const RowScale& rs) {
+  if (rs.boost != 1.0f) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) in[e] *= rs.boost;
+  }
 }
 
 }  // namespace adq

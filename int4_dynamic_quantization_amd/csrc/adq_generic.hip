@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(256) generic_kernel(const Args a) {
       if constexpr (kTwo) a.scale2[row] = r2.scale;
     }
     auto code = [](float in, const RowScale& rs) -> uint32_t {
-      return rs.slow ? code_bits_div(in, rs.scale) : code_bits(in, rs.inv);
+      return code_bits(in * rs.boost, rs.inv);
     };
     // pass 3: codes, one column pair per thread step
     const int64_t pairs = (n + 1) / 2;

@@ -32,6 +32,10 @@
 
 #include "adq_device.h"
 
+#ifndef ADQ_ROW_PREFETCH_DEPTH
+#define ADQ_ROW_PREFETCH_DEPTH 1
+#endif
+
 namespace adq {
 
 // Keeps the compiler from hoisting per-use conversions of a loop-invariant
@@ -39,22 +43,17 @@ namespace adq {
 __device__ __forceinline__ void opaque(u32x4& v) { asm volatile("" : "+v"(v)); }
 
 // Codes of one 8-column vector into an INT8 (8 bytes) or INT4X2 (4 bytes)
-// output row, at vector index j of that row.
+// output row, at vector index j of that row.  `in` is already boosted.
 template <int Q>
-__device__ __forceinline__ void store_codes(const float (&in)[8], const RowScale& rs,
-                                            rsrc_t out, uint32_t j) {
+__device__ __forceinline__ void store_codes(const float (&in)[8], float inv, rsrc_t out,
+                                            uint32_t j) {
   uint32_t q[8];
-  if (!rs.slow) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = code_bits(in[e], rs.inv);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = code_bits_div(in[e], rs.scale);
-  }
+  for (int e = 0; e < 8; ++e) q[e] = code_bits(in[e], inv);
   if constexpr (Q == kQInt8) {
-    __builtin_amdgcn_raw_buffer_store_b64(pack_int8x8(q), out, j * 8u, 0, kStream);
+    __builtin_amdgcn_raw_buffer_store_b64(pack_int8x8(q), out, j * 8u, 0, kStreamStore);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b32(pack_int4x8(q), out, j * 4u, 0, kStream);
+    __builtin_amdgcn_raw_buffer_store_b32(pack_int4x8(q), out, j * 4u, 0, kStreamStore);
   }
 }
 
@@ -102,27 +101,39 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
     const rsrc_t r2 = make_rsrc(row_ptr(a.x2, row, row_bytes), row_bytes);
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      c1[k] = __builtin_amdgcn_raw_buffer_load_b128(r1, vj[k] * 16u, 0, kStream);
+      c1[k] = __builtin_amdgcn_raw_buffer_load_b128(r1, vj[k] * 16u, 0, kStreamLoad);
       if constexpr (NIN == 2)
-        c2[k] = __builtin_amdgcn_raw_buffer_load_b128(r2, vj[k] * 16u, 0, kStream);
+        c2[k] = __builtin_amdgcn_raw_buffer_load_b128(r2, vj[k] * 16u, 0, kStreamLoad);
     }
   };
 
+  // Rows this workgroup loads ahead of the one it computes (1 or 2).
+  constexpr int kDepth = ADQ_ROW_PREFETCH_DEPTH;
+  static_assert(kDepth == 1 || kDepth == 2, "prefetch depth 1 or 2");
+  const int64_t last = a.rows - 1;
+  auto clamp_row = [&](int64_t r) { return r < a.rows ? r : last; };
+
   int64_t row = blockIdx.x;
   if (row >= a.rows) return;
-  u32x4 c1[VPT], c2[VPT];
-  load_row(row, c1, c2);
+  // Raw x1/x2 vectors of rows in flight.  Depth 1: set A holds the row being
+  // computed and the next row is loaded into fresh registers at the start of
+  // each row.  Depth 2: sets A and B alternate; a set is refilled with the
+  // row two steps ahead as soon as pass A has consumed it, so no register
+  // copies (which would force a wait on the newest loads) are needed.
+  u32x4 a1[VPT], a2[VPT], b1[VPT], b2[VPT];
+  load_row(row, a1, a2);
+  if constexpr (kDepth == 2) load_row(clamp_row(row + gridDim.x), b1, b2);
 
-  // One row: prefetch the next, compute and store this one.  The first row
-  // is peeled off the loop so that every entry to the loop header has the
-  // same outstanding memory operations (loads, then stores); the wait for
-  // the prefetched row then need not wait for the stores.
-  auto body = [&](int64_t row) {
-    // Prefetch this workgroup's next row (the last row again when there is
-    // none, so the loads are unconditional).
+  // One row.  The first row is peeled off the loop so that every entry to
+  // the loop header has the same outstanding memory operations (loads, then
+  // stores); the wait for a prefetched row then need not wait for stores.
+  auto body = [&](int64_t row, u32x4 (&c1)[VPT], u32x4 (&c2)[VPT]) {
     u32x4 n1[VPT], n2[VPT];
-    const int64_t next = row + gridDim.x < a.rows ? row + gridDim.x : a.rows - 1;
-    load_row(next, n1, n2);
+    if constexpr (kDepth == 1) {
+      // Prefetch the next row (the last row again when there is none, so
+      // the loads are unconditional).
+      load_row(clamp_row(row + gridDim.x), n1, n2);
+    }
 #pragma unroll
     for (int k = 0; k < VPT; ++k) opaque(pg[k]), opaque(pb[k]), opaque(p1[k]), opaque(p2[k]);
 
@@ -147,9 +158,10 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
         __builtin_amdgcn_raw_buffer_store_b128(
             u32x4{narrow2<E>(x[k][0], x[k][1]), narrow2<E>(x[k][2], x[k][3]),
                   narrow2<E>(x[k][4], x[k][5]), narrow2<E>(x[k][6], x[k][7])},
-            rxo, vj[k] * 16u, 0, kStream);
+            rxo, vj[k] * 16u, 0, kStreamStore);
       }
     }
+    if constexpr (kDepth == 2) load_row(clamp_row(row + 2 * (int64_t)gridDim.x), c1, c2);
     ss = wave_sum(ss);
     if (lane == 0) red_ss[wave] = ss;
     __syncthreads();
@@ -199,22 +211,42 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
       a.scale1[row] = r1.scale;
       if constexpr (kTwo) a.scale2[row] = r2.scale;
     }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      apply_boost(in1[k], r1);
+      if constexpr (kTwo) apply_boost(in2[k], r2);
+    }
     const uint32_t y1_bytes = Q1 == kQInt4 ? n / 2u : n;
     const rsrc_t ry1 = make_rsrc(row_ptr(a.y1, row, y1_bytes), y1_bytes);
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) store_codes<Q1>(in1[k], r1, ry1, vj[k]);
+    for (int k = 0; k < VPT; ++k) store_codes<Q1>(in1[k], r1.inv, ry1, vj[k]);
     if constexpr (kTwo) {
       const uint32_t y2_bytes = kQ2 == kQInt4 ? n / 2u : n;
       const rsrc_t ry2 = make_rsrc(row_ptr(a.y2, row, y2_bytes), y2_bytes);
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) store_codes<kQ2>(in2[k], r2, ry2, vj[k]);
+      for (int k = 0; k < VPT; ++k) store_codes<kQ2>(in2[k], r2.inv, ry2, vj[k]);
     }
 
+    if constexpr (kDepth == 1) {
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) c1[k] = n1[k], c2[k] = n2[k];
+      for (int k = 0; k < VPT; ++k) c1[k] = n1[k], c2[k] = n2[k];
+    }
   };
-  body(row);
-  for (row += gridDim.x; row < a.rows; row += gridDim.x) body(row);
+  if constexpr (kDepth == 1) {
+    body(row, a1, a2);
+    for (row += gridDim.x; row < a.rows; row += gridDim.x) body(row, a1, a2);
+  } else {
+    // Two rows peeled (one per set) so that the loop is entered after the
+    // same sequence of memory operations as its back edge.
+    body(row, a1, a2);
+    if ((row += gridDim.x) >= a.rows) return;
+    body(row, b1, b2);
+    for (row += gridDim.x; row < a.rows; row += gridDim.x) {
+      body(row, a1, a2);
+      if ((row += gridDim.x) >= a.rows) break;
+      body(row, b1, b2);
+    }
+  }
 }
 
 // ---- launch table for one element type
