@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -75,7 +76,9 @@ struct adq_executor {
   int block;
   int grid;
   int splits;
+  int row_groups;
   uint64_t ws_bytes;
+  uint64_t last_epoch;
 };
 
 namespace {
@@ -203,6 +206,20 @@ adq_status current_device(int* dev, int* cus) {
 
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
+// Per-launch epochs for the split-row exchange: unique within the process,
+// starting from a value mixed from the clock and an address so that stale
+// workspace contents from another process do not repeat them.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> counter{[] {
+    uint64_t z = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
+                 (uint64_t)(uintptr_t)&g_last_error;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+  }()};
+  return counter.fetch_add(0x9E3779B97F4A7C15ULL, std::memory_order_relaxed);
+}
+
 // Row-kernel geometry: vectors per thread and block size for n / 8 vectors.
 #ifndef ADQ_VPT1_MAX_NVEC
 #define ADQ_VPT1_MAX_NVEC 64
@@ -223,11 +240,63 @@ bool row_geometry(int64_t nvec, int* vpt, int* block) {
   return true;
 }
 
+#ifndef ADQ_SPLIT_TARGET_WG_PER_CU
+#define ADQ_SPLIT_TARGET_WG_PER_CU 2
+#endif
+
+// Split-row geometry: S workgroups of `block` threads (one 8-column vector
+// per thread, two for rows above 1024 * 8 * 64 columns) per row, enough of
+// them to give every CU about ADQ_SPLIT_TARGET_WG_PER_CU workgroups, and all
+// resident at once.  Rows are processed 8 * row_groups at a time.
+bool split_geometry(adq_executor* e) {
+  const int64_t nvec = e->args.n / 8;
+  const int64_t rows8 = (e->m + 7) / 8 * 8;
+  int64_t want = (int64_t)e->cus * ADQ_SPLIT_TARGET_WG_PER_CU / rows8;  // splits per row
+  if (want < 1) want = 1;
+  int vpt = 1;
+  int64_t block = round_up((int)((nvec + want - 1) / want), 64);
+  if (block < 64) block = 64;
+  if (block > 1024) {
+    vpt = 2;
+    block = round_up((int)((nvec + 2 * want - 1) / (2 * want)), 64);
+    if (block > 1024) block = 1024;
+  }
+  const int64_t chunk = block * vpt;
+  const int64_t splits = (nvec + chunk - 1) / chunk;
+  if (splits > 64) return false;
+  const int occ = adq::split_max_blocks_per_cu(e->var, vpt, (int)block);
+  if (occ <= 0) return false;
+  const int64_t capacity = (int64_t)occ * e->cus;
+  int64_t groups = (e->m + 7) / 8;
+  if (groups * 8 * splits > capacity) groups = capacity / (8 * splits);
+  if (groups < 1) return false;
+  e->vpt = vpt;
+  e->block = (int)block;
+  e->splits = (int)splits;
+  e->row_groups = (int)groups;
+  e->grid = (int)(8 * groups * splits);
+  e->ws_bytes = adq::split_workspace_bytes(e->m, (int)splits);
+  return true;
+}
+
+#ifndef ADQ_SPLIT_MAX_ROWS
+#define ADQ_SPLIT_MAX_ROWS 64
+#endif
+
 adq_status plan(adq_executor* e, int path) {
   const int64_t n = e->args.n;
   if (path == ADQ_PATH_AUTO) {
+    // Row kernel when it fits a row and there are enough rows to occupy the
+    // GPU; split-row for few rows of at least 2048 columns and for rows
+    // longer than the row kernel takes; generic otherwise.
     int vpt = 0, block = 0;
-    path = e->vector_ok && row_geometry(n / 8, &vpt, &block) ? ADQ_PATH_ROW : ADQ_PATH_GENERIC;
+    const bool row_ok = e->vector_ok && row_geometry(n / 8, &vpt, &block);
+    const bool few_rows = e->m <= ADQ_SPLIT_MAX_ROWS && n >= 2048;
+    if (e->vector_ok && (!row_ok || few_rows)) {
+      adq_executor trial = *e;
+      if (split_geometry(&trial)) path = ADQ_PATH_SPLIT;
+    }
+    if (path == ADQ_PATH_AUTO) path = row_ok ? ADQ_PATH_ROW : ADQ_PATH_GENERIC;
   }
   if (path == ADQ_PATH_ROW) {
     int vpt = 0, block = 0;
@@ -244,6 +313,7 @@ adq_status plan(adq_executor* e, int path) {
     e->block = block;
     e->grid = (int)((e->m + per - 1) / per);
     e->splits = 1;
+    e->row_groups = 0;
     e->ws_bytes = 0;
     return ADQ_OK;
   }
@@ -253,11 +323,18 @@ adq_status plan(adq_executor* e, int path) {
     e->block = 256;
     e->grid = (int)(e->m < (int64_t)e->cus * 8 ? e->m : (int64_t)e->cus * 8);
     e->splits = 1;
+    e->row_groups = 0;
     e->ws_bytes = 0;
     return ADQ_OK;
   }
-  if (path == ADQ_PATH_SPLIT)
-    return fail(ADQ_ERR_PARAM_INVALID, "split-row path is not available in this build");
+  if (path == ADQ_PATH_SPLIT) {
+    if (!e->vector_ok)
+      return fail(ADQ_ERR_PARAM_INVALID,
+                  "split-row path needs n %% 8 == 0 and 16-byte aligned tensors");
+    if (!split_geometry(e)) return fail(ADQ_ERR_RUNTIME, "split-row kernel does not fit");
+    e->path = ADQ_PATH_SPLIT;
+    return ADQ_OK;
+  }
   return fail(ADQ_ERR_PARAM_INVALID, "unknown path %d", path);
 }
 
@@ -285,6 +362,8 @@ adq_status run(void* workspace, uint64_t workspace_size, adq_executor* e, void* 
   if (workspace_size < e->ws_bytes || (e->ws_bytes > 0 && !workspace))
     return fail(ADQ_ERR_WORKSPACE, "workspace of %llu bytes, %llu needed",
                 (unsigned long long)workspace_size, (unsigned long long)e->ws_bytes);
+  if (e->ws_bytes > 0 && (uintptr_t)workspace % 8 != 0)
+    return fail(ADQ_ERR_WORKSPACE, "workspace must be 8-byte aligned");
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess) {
     (void)hipGetLastError();
@@ -299,6 +378,11 @@ adq_status run(void* workspace, uint64_t workspace_size, adq_executor* e, void* 
   switch (e->path) {
     case ADQ_PATH_ROW: err = adq::launch_row(e->var, e->vpt, e->block, e->grid, e->args, s); break;
     case ADQ_PATH_GENERIC: err = adq::launch_generic(e->var, e->block, e->grid, e->args, s); break;
+    case ADQ_PATH_SPLIT:
+      e->last_epoch = next_epoch();
+      err = adq::launch_split(e->var, e->vpt, e->block, e->splits, e->row_groups, e->args,
+                              workspace, e->last_epoch, s);
+      break;
     default: break;
   }
   if (cur != e->device) (void)hipSetDevice(cur);
@@ -475,10 +559,11 @@ int32_t adq_executor_describe(const adq_executor* e, char* buf, uint64_t len) {
     static const char* names[] = {"auto", "row", "split", "generic"};
     snprintf(buf, (size_t)len,
              "path=%s elem=%s nin=%d q1=%d q2=%d rows=%lld n=%d vpt=%d block=%d grid=%d "
-             "splits=%d workspace=%llu cus=%d",
+             "splits=%d row_groups=%d workspace=%llu cus=%d epoch=%llu",
              names[e->path & 3], e->var.elem == adq::kBF16 ? "bf16" : "fp16", e->var.nin,
              e->var.q1, e->var.q2, (long long)e->m, e->args.n, e->vpt, e->block, e->grid,
-             e->splits, (unsigned long long)e->ws_bytes, e->cus);
+             e->splits, e->row_groups, (unsigned long long)e->ws_bytes, e->cus,
+             (unsigned long long)e->last_epoch);
   }
   return e->path;
 }

@@ -52,11 +52,12 @@ hipError_t launch_row(const Variant& v, int vpt, int block, int grid, const Args
                       hipStream_t stream);
 int row_max_blocks_per_cu(const Variant& v, int vpt, int block);
 
-// Split-row kernel: `splits` workgroups share one row.  `ws` is the
-// launch's workspace (split_workspace_bytes), `epoch` a value unique to
-// this launch.
-hipError_t launch_split(const Variant& v, int vpt, int block, int splits, const Args& a,
-                        void* ws, uint64_t epoch, hipStream_t stream);
+// Split-row kernel: `splits` workgroups share each row (a chunk of block *
+// vpt 8-column vectors each); grid = 8 * row_groups * splits, launched
+// cooperatively.  `ws` is the launch's workspace (split_workspace_bytes,
+// 8-byte aligned, any contents), `epoch` a value unique to this launch.
+hipError_t launch_split(const Variant& v, int vpt, int block, int splits, int row_groups,
+                        const Args& a, void* ws, uint64_t epoch, hipStream_t stream);
 int split_max_blocks_per_cu(const Variant& v, int vpt, int block);
 uint64_t split_workspace_bytes(int64_t rows, int splits);
 

@@ -36,18 +36,38 @@ def host(t) -> np.ndarray:
     return t.cpu().numpy()
 
 
+def workspace(ex, fill=None):
+    """Workspace for an executor: uninitialised memory by default (the
+    split-row exchange needs no clearing), or filled with a byte value."""
+    if not ex.workspace_size:
+        return None
+    ws = torch.empty(ex.workspace_size, dtype=torch.uint8, device="cuda")
+    if fill is not None:
+        ws.fill_(fill)
+    return ws
+
+
+def check_no_timeout(ex, ws):
+    """The split-row kernel records the epoch of a launch whose exchange wait
+    gave up in the first workspace word; it must not be this launch's."""
+    if ws is None:
+        return
+    epoch = int(ex.describe().split("epoch=")[1].split()[0])
+    word0 = int(ws[:8].cpu().numpy().view(np.uint64)[0])
+    assert word0 != epoch, "split-row exchange wait timed out"
+
+
 def run_v2(x1, x2, g, b, s1, s2, eps, mask, y_types, dtype, path=adq.PATH_AUTO, stream=None,
-           outputs=None):
+           outputs=None, ws_fill=None):
     """Run AddRmsNormDynamicQuantV2 on host arrays; returns (outs, describe)."""
     ex, outs = adq.plan_add_rms_norm_dynamic_quant_v2(
         dev(x1, dtype), dev(x2, dtype), dev(g, dtype), dev(b, dtype), dev(s1, dtype),
         dev(s2, dtype), eps, mask, y_types[0], y_types[1], outputs=outputs, path=path)
-    ws = None
-    if ex.workspace_size:
-        ws = torch.zeros(ex.workspace_size, dtype=torch.uint8, device="cuda")
+    ws = workspace(ex, ws_fill)
     ex.run(ws, stream)
     torch.cuda.synchronize()
     desc = ex.describe()
+    check_no_timeout(ex, ws)
     ex.close()
     return outs, desc
 
@@ -55,12 +75,11 @@ def run_v2(x1, x2, g, b, s1, s2, eps, mask, y_types, dtype, path=adq.PATH_AUTO, 
 def run_rms(x, g, b, s, eps, y_type, dtype, path=adq.PATH_AUTO):
     ex, outs = adq.plan_rms_norm_dynamic_quant(dev(x, dtype), dev(g, dtype), dev(b, dtype),
                                                dev(s, dtype), eps, y_type, path=path)
-    ws = None
-    if ex.workspace_size:
-        ws = torch.zeros(ex.workspace_size, dtype=torch.uint8, device="cuda")
+    ws = workspace(ex)
     ex.run(ws)
     torch.cuda.synchronize()
     desc = ex.describe()
+    check_no_timeout(ex, ws)
     ex.close()
     return outs, desc
 

@@ -18,7 +18,7 @@ import int4_dynamic_quantization_amd as adq
 import oracle
 import synth
 from gpu_helpers import (codes_of, compare_rms, compare_v2, dev, host, host_bits, oracle_v2,
-                         run_rms, run_v2)
+                         run_rms, run_v2, workspace)
 from helpers import check_codes, check_scales, from_bits, to_bits, unpack_int4
 
 pytestmark = pytest.mark.gpu
@@ -55,6 +55,10 @@ def test_workload_full_parity(name):
     for k in (1, 2):
         if not ora["active"][k - 1]:
             assert outs[f"y{k}"] is None
+    # every workload also through each kernel that takes its shape
+    for path in (adq.PATH_ROW, adq.PATH_SPLIT, adq.PATH_GENERIC):
+        outs, desc = run_v2(x1, x2, g, b, s1, s2, w.eps, w.mask, w.y_types, w.dtype, path=path)
+        compare_v2(outs, ora, w.y_types)
 
 
 def _sample_rows(m, seed, n_rand=192):
@@ -179,8 +183,12 @@ def test_ragged_shapes(m, n, dtype):
     outs, desc = run_v2(x1, x2, g, b, s1, s2, 1e-6, (True, True), y_types, dtype)
     ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, (True, True), y_types, dtype)
     compare_v2(outs, ora, y_types)
-    vec = n % 8 == 0 and n <= 16384
-    assert ("path=row" in desc) == vec, desc
+    if n % 8 != 0:
+        assert "path=generic" in desc, desc
+    elif n > 16384 or (m <= 64 and n >= 2048):
+        assert "path=split" in desc, desc
+    else:
+        assert "path=row" in desc, desc
 
 
 # ---- the option matrix --------------------------------------------------------
@@ -348,9 +356,10 @@ def test_launch_on_side_stream_and_executor_reuse():
     dx1, dx2 = dev(x1, "fp16"), dev(x2, "fp16")
     ex, outs = adq.plan_add_rms_norm_dynamic_quant_v2(
         dx1, dx2, dev(g, "fp16"), dev(b, "fp16"), dev(s1, "fp16"), dev(s2, "fp16"), 1e-6, None)
+    ws = workspace(ex)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        ex.run(None, s)
+        ex.run(ws, s)
     s.synchronize()
     ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, None, ("int8", "int8"), "fp16")
     compare_v2(outs, ora, ("int8", "int8"))
@@ -358,7 +367,7 @@ def test_launch_on_side_stream_and_executor_reuse():
     y1, y2, _, _, _, _ = _case_inputs(40, 2048, "fp16", seed=10)
     dx1.copy_(dev(y1, "fp16"))
     dx2.copy_(dev(y2, "fp16"))
-    ex.run()
+    ex.run(ws)
     torch.cuda.synchronize()
     ora = oracle_v2(y1, y2, g, b, s1, s2, 1e-6, None, ("int8", "int8"), "fp16")
     compare_v2(outs, ora, ("int8", "int8"))
