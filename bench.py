@@ -67,17 +67,18 @@ def measured_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def make_case(w, torch, adq, synth, dev):
+def make_case(w, torch, adq, synth, dev, path=0):
     x1, x2 = synth.inputs(w)
     g, b, s1, s2 = synth.params(w)
     d = lambda a: None if a is None else torch.from_numpy(a.view("int16")).view(
         {"bf16": torch.bfloat16, "fp16": torch.float16}[w.dtype]).to(dev)
     if w.op == "v2":
         ex, outs = adq.plan_add_rms_norm_dynamic_quant_v2(
-            d(x1), d(x2), d(g), d(b), d(s1), d(s2), w.eps, w.mask, w.y_types[0], w.y_types[1])
+            d(x1), d(x2), d(g), d(b), d(s1), d(s2), w.eps, w.mask, w.y_types[0], w.y_types[1],
+            path=path)
     else:
         ex, outs = adq.plan_rms_norm_dynamic_quant(d(x1), d(g), d(b), d(s1), w.eps,
-                                                   w.y_types[0])
+                                                   w.y_types[0], path=path)
     ws = (torch.empty(ex.workspace_size, dtype=torch.uint8, device=dev)
           if ex.workspace_size else None)
     if w.op == "v2":
@@ -122,6 +123,11 @@ def main():
     ap.add_argument("--workload", default="v2_outlier")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--path", choices=["auto", "row", "split", "generic"], default="auto",
+                    help="kernel path (default: the library's own choice)")
+    ap.add_argument("--no-rotate", action="store_true",
+                    help="reuse one input/output set (cache-warm) instead of rotating sets "
+                         "that do not fit the last-level cache")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead: time a plain device-to-device copy of MIB MiB (reference "
                          "for achievable bandwidth and for scaling HBM byte counters)")
@@ -141,15 +147,17 @@ def main():
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    first = make_case(w, torch, adq, synth, dev)
+    path = {"auto": adq.PATH_AUTO, "row": adq.PATH_ROW, "split": adq.PATH_SPLIT,
+            "generic": adq.PATH_GENERIC}[args.path]
+    first = make_case(w, torch, adq, synth, dev, path)
     active = first[3]
     footprint = alg_bytes(w, active)
     # Rotate input/output sets so that each launch streams from HBM rather
     # than the 256 MB last-level cache.
-    n_sets = max(1, math.ceil(512e6 / footprint))
+    n_sets = 1 if args.no_rotate else max(1, math.ceil(512e6 / footprint))
     print(f"[bench] workload {w.name} {w.rows}x{w.cols} {w.dtype}: {footprint / 1e6:.1f} MB "
           f"per launch, {n_sets} rotating set(s)", file=sys.stderr, flush=True)
-    cases = [first] + [make_case(w, torch, adq, synth, dev) for _ in range(n_sets - 1)]
+    cases = [first] + [make_case(w, torch, adq, synth, dev, path) for _ in range(n_sets - 1)]
     print(f"[bench] plan: {cases[0][0].describe()}", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
 
@@ -200,6 +208,9 @@ def main():
             "rows_per_s": round(w.rows / (ms * 1e-3)),
             "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "parallelism": "single GPU",
+            "kernel_path": first[0].describe().split()[0].split("=")[1],
+            "cache": "warm (one set)" if n_sets == 1 and args.no_rotate else
+                     f"cold ({n_sets} rotating sets)" if n_sets > 1 else "cold (footprint > LLC)",
         },
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),

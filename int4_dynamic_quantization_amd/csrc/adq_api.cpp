@@ -20,19 +20,20 @@
 
 namespace adq {
 
-hipError_t launch_row_bf16(const Variant&, int, int, int, const Args&, hipStream_t);
-hipError_t launch_row_f16(const Variant&, int, int, int, const Args&, hipStream_t);
-int row_occupancy_bf16(const Variant&, int, int);
-int row_occupancy_f16(const Variant&, int, int);
+hipError_t launch_row_bf16(const Variant&, int, int, int, int, const Args&, hipStream_t);
+hipError_t launch_row_f16(const Variant&, int, int, int, int, const Args&, hipStream_t);
+int row_occupancy_bf16(const Variant&, int, int, int);
+int row_occupancy_f16(const Variant&, int, int, int);
 
-hipError_t launch_row(const Variant& v, int vpt, int block, int grid, const Args& a,
+hipError_t launch_row(const Variant& v, int vpt, int depth, int block, int grid, const Args& a,
                       hipStream_t s) {
-  return v.elem == kBF16 ? launch_row_bf16(v, vpt, block, grid, a, s)
-                         : launch_row_f16(v, vpt, block, grid, a, s);
+  return v.elem == kBF16 ? launch_row_bf16(v, vpt, depth, block, grid, a, s)
+                         : launch_row_f16(v, vpt, depth, block, grid, a, s);
 }
 
-int row_max_blocks_per_cu(const Variant& v, int vpt, int block) {
-  return v.elem == kBF16 ? row_occupancy_bf16(v, vpt, block) : row_occupancy_f16(v, vpt, block);
+int row_max_blocks_per_cu(const Variant& v, int vpt, int depth, int block) {
+  return v.elem == kBF16 ? row_occupancy_bf16(v, vpt, depth, block)
+                         : row_occupancy_f16(v, vpt, depth, block);
 }
 
 }  // namespace adq
@@ -73,6 +74,7 @@ struct adq_executor {
   bool vector_ok;  // n % 8 == 0, aligned tensors, n small enough for the row kernel
   int path;
   int vpt;
+  int depth;
   int block;
   int grid;
   int splits;
@@ -227,6 +229,12 @@ uint64_t next_epoch() {
 #ifndef ADQ_MAX_WG_PER_CU
 #define ADQ_MAX_WG_PER_CU 0
 #endif
+#ifndef ADQ_DEPTH2_MAX_N
+#define ADQ_DEPTH2_MAX_N 6144
+#endif
+#ifndef ADQ_DEPTH2_MIN_ROWS_PER_WG
+#define ADQ_DEPTH2_MIN_ROWS_PER_WG 16
+#endif
 
 bool row_geometry(int64_t nvec, int* vpt, int* block) {
   if (nvec <= 0) return false;
@@ -271,6 +279,7 @@ bool split_geometry(adq_executor* e) {
   if (groups * 8 * splits > capacity) groups = capacity / (8 * splits);
   if (groups < 1) return false;
   e->vpt = vpt;
+  e->depth = 1;
   e->block = (int)block;
   e->splits = (int)splits;
   e->row_groups = (int)groups;
@@ -279,16 +288,21 @@ bool split_geometry(adq_executor* e) {
   return true;
 }
 
+// Few-row shapes stay on the row kernel: on gfx950 one workgroup streaming
+// a whole row (up to 16384 columns) beats S workgroups that must exchange
+// partial results twice through agent-coherent memory, and the cooperative
+// launch the exchange needs costs more than the kernel itself.  Set above 0
+// to send shapes with at most this many rows (and n >= 2048) to the
+// split-row kernel.
 #ifndef ADQ_SPLIT_MAX_ROWS
-#define ADQ_SPLIT_MAX_ROWS 64
+#define ADQ_SPLIT_MAX_ROWS 0
 #endif
 
 adq_status plan(adq_executor* e, int path) {
   const int64_t n = e->args.n;
   if (path == ADQ_PATH_AUTO) {
-    // Row kernel when it fits a row and there are enough rows to occupy the
-    // GPU; split-row for few rows of at least 2048 columns and for rows
-    // longer than the row kernel takes; generic otherwise.
+    // Row kernel when it holds a row; split-row for longer rows; generic
+    // for rows that are not whole 16-byte vectors or unaligned tensors.
     int vpt = 0, block = 0;
     const bool row_ok = e->vector_ok && row_geometry(n / 8, &vpt, &block);
     const bool few_rows = e->m <= ADQ_SPLIT_MAX_ROWS && n >= 2048;
@@ -303,12 +317,21 @@ adq_status plan(adq_executor* e, int path) {
     if (!e->vector_ok || !row_geometry(n / 8, &vpt, &block))
       return fail(ADQ_ERR_PARAM_INVALID,
                   "row path needs n %% 8 == 0, n <= 16384 and 16-byte aligned tensors");
-    int occ = adq::row_max_blocks_per_cu(e->var, vpt, block);
-    if (ADQ_MAX_WG_PER_CU > 0 && occ > ADQ_MAX_WG_PER_CU) occ = ADQ_MAX_WG_PER_CU;
-    if (occ <= 0) return fail(ADQ_ERR_RUNTIME, "row kernel does not fit block %d", block);
-    const int64_t slots = (int64_t)occ * e->cus;
-    const int64_t per = (e->m + slots - 1) / slots;
+    // Prefetch depth 2 (two rows in flight per workgroup) pays for short
+    // rows streamed many times per workgroup; longer rows keep depth 1.
+    int depth = 1, occ = 0;
+    int64_t per = 0;
+    for (int d = 1; d <= 2; ++d) {
+      occ = adq::row_max_blocks_per_cu(e->var, vpt, d, block);
+      if (ADQ_MAX_WG_PER_CU > 0 && occ > ADQ_MAX_WG_PER_CU) occ = ADQ_MAX_WG_PER_CU;
+      if (occ <= 0) return fail(ADQ_ERR_RUNTIME, "row kernel does not fit block %d", block);
+      const int64_t slots = (int64_t)occ * e->cus;
+      per = (e->m + slots - 1) / slots;
+      depth = d;
+      if (!(n <= ADQ_DEPTH2_MAX_N && per >= ADQ_DEPTH2_MIN_ROWS_PER_WG)) break;
+    }
     e->path = ADQ_PATH_ROW;
+    e->depth = depth;
     e->vpt = vpt;
     e->block = block;
     e->grid = (int)((e->m + per - 1) / per);
@@ -320,6 +343,7 @@ adq_status plan(adq_executor* e, int path) {
   if (path == ADQ_PATH_GENERIC) {
     e->path = ADQ_PATH_GENERIC;
     e->vpt = 0;
+    e->depth = 1;
     e->block = 256;
     e->grid = (int)(e->m < (int64_t)e->cus * 8 ? e->m : (int64_t)e->cus * 8);
     e->splits = 1;
@@ -376,7 +400,9 @@ adq_status run(void* workspace, uint64_t workspace_size, adq_executor* e, void* 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t err = hipErrorInvalidValue;
   switch (e->path) {
-    case ADQ_PATH_ROW: err = adq::launch_row(e->var, e->vpt, e->block, e->grid, e->args, s); break;
+    case ADQ_PATH_ROW:
+      err = adq::launch_row(e->var, e->vpt, e->depth, e->block, e->grid, e->args, s);
+      break;
     case ADQ_PATH_GENERIC: err = adq::launch_generic(e->var, e->block, e->grid, e->args, s); break;
     case ADQ_PATH_SPLIT:
       e->last_epoch = next_epoch();
@@ -558,10 +584,10 @@ int32_t adq_executor_describe(const adq_executor* e, char* buf, uint64_t len) {
   if (buf && len > 0) {
     static const char* names[] = {"auto", "row", "split", "generic"};
     snprintf(buf, (size_t)len,
-             "path=%s elem=%s nin=%d q1=%d q2=%d rows=%lld n=%d vpt=%d block=%d grid=%d "
+             "path=%s elem=%s nin=%d q1=%d q2=%d rows=%lld n=%d vpt=%d depth=%d block=%d grid=%d "
              "splits=%d row_groups=%d workspace=%llu cus=%d epoch=%llu",
              names[e->path & 3], e->var.elem == adq::kBF16 ? "bf16" : "fp16", e->var.nin,
-             e->var.q1, e->var.q2, (long long)e->m, e->args.n, e->vpt, e->block, e->grid,
+             e->var.q1, e->var.q2, (long long)e->m, e->args.n, e->vpt, e->depth, e->block, e->grid,
              e->splits, e->row_groups, (unsigned long long)e->ws_bytes, e->cus,
              (unsigned long long)e->last_epoch);
   }

@@ -32,8 +32,8 @@
 
 #include "adq_device.h"
 
-#ifndef ADQ_ROW_PREFETCH_DEPTH
-#define ADQ_ROW_PREFETCH_DEPTH 1
+#ifndef ADQ_ROW_BLOCKED
+#define ADQ_ROW_BLOCKED 0
 #endif
 
 namespace adq {
@@ -57,8 +57,11 @@ __device__ __forceinline__ void store_codes(const float (&in)[8], float inv, rsr
   }
 }
 
-template <int E, int NIN, int Q1, int Q2, int VPT>
+// GEO packs the thread geometry: VPT = GEO & 0xF (8-column vectors per
+// thread), prefetch depth = GEO >> 4 (rows loaded ahead: 1 or 2).
+template <int E, int NIN, int Q1, int Q2, int GEO>
 __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
+  constexpr int VPT = GEO & 0xF;
   static_assert(VPT == 1 || VPT == 2, "row kernel holds at most 16 columns per thread");
   constexpr bool kTwo = Q2 != kQNone;
   constexpr int kQ2 = kTwo ? Q2 : kQInt8;
@@ -108,13 +111,24 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
   };
 
   // Rows this workgroup loads ahead of the one it computes (1 or 2).
-  constexpr int kDepth = ADQ_ROW_PREFETCH_DEPTH;
+  constexpr int kDepth = GEO >> 4;
   static_assert(kDepth == 1 || kDepth == 2, "prefetch depth 1 or 2");
-  const int64_t last = a.rows - 1;
-  auto clamp_row = [&](int64_t r) { return r < a.rows ? r : last; };
+  // Rows of this workgroup: strided (blockIdx.x, + gridDim.x, ...) or one
+  // contiguous block of rows.
+#if ADQ_ROW_BLOCKED
+  const int64_t per = (a.rows + gridDim.x - 1) / gridDim.x;
+  const int64_t first = (int64_t)blockIdx.x * per;
+  const int64_t rend = first + per < a.rows ? first + per : a.rows;
+  const int64_t step = 1;
+#else
+  const int64_t first = blockIdx.x;
+  const int64_t rend = a.rows;
+  const int64_t step = gridDim.x;
+#endif
+  auto clamp_row = [&](int64_t r) { return r < rend ? r : rend - 1; };
 
-  int64_t row = blockIdx.x;
-  if (row >= a.rows) return;
+  int64_t row = first;
+  if (row >= rend) return;
   // Raw x1/x2 vectors of rows in flight.  Depth 1: set A holds the row being
   // computed and the next row is loaded into fresh registers at the start of
   // each row.  Depth 2: sets A and B alternate; a set is refilled with the
@@ -122,7 +136,7 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
   // copies (which would force a wait on the newest loads) are needed.
   u32x4 a1[VPT], a2[VPT], b1[VPT], b2[VPT];
   load_row(row, a1, a2);
-  if constexpr (kDepth == 2) load_row(clamp_row(row + gridDim.x), b1, b2);
+  if constexpr (kDepth == 2) load_row(clamp_row(row + step), b1, b2);
 
   // One row.  The first row is peeled off the loop so that every entry to
   // the loop header has the same outstanding memory operations (loads, then
@@ -132,7 +146,7 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
     if constexpr (kDepth == 1) {
       // Prefetch the next row (the last row again when there is none, so
       // the loads are unconditional).
-      load_row(clamp_row(row + gridDim.x), n1, n2);
+      load_row(clamp_row(row + step), n1, n2);
     }
 #pragma unroll
     for (int k = 0; k < VPT; ++k) opaque(pg[k]), opaque(pb[k]), opaque(p1[k]), opaque(p2[k]);
@@ -161,7 +175,7 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
             rxo, vj[k] * 16u, 0, kStreamStore);
       }
     }
-    if constexpr (kDepth == 2) load_row(clamp_row(row + 2 * (int64_t)gridDim.x), c1, c2);
+    if constexpr (kDepth == 2) load_row(clamp_row(row + 2 * step), c1, c2);
     ss = wave_sum(ss);
     if (lane == 0) red_ss[wave] = ss;
     __syncthreads();
@@ -234,16 +248,16 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
   };
   if constexpr (kDepth == 1) {
     body(row, a1, a2);
-    for (row += gridDim.x; row < a.rows; row += gridDim.x) body(row, a1, a2);
+    for (row += step; row < rend; row += step) body(row, a1, a2);
   } else {
     // Two rows peeled (one per set) so that the loop is entered after the
     // same sequence of memory operations as its back edge.
     body(row, a1, a2);
-    if ((row += gridDim.x) >= a.rows) return;
+    if ((row += step) >= rend) return;
     body(row, b1, b2);
-    for (row += gridDim.x; row < a.rows; row += gridDim.x) {
+    for (row += step; row < rend; row += step) {
       body(row, a1, a2);
-      if ((row += gridDim.x) >= a.rows) break;
+      if ((row += step) >= rend) break;
       body(row, b1, b2);
     }
   }
@@ -251,15 +265,15 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
 
 // ---- launch table for one element type
 
-template <int E, int NIN, int Q1, int Q2, int VPT>
+template <int E, int NIN, int Q1, int Q2, int GEO>
 struct RowInst {
   static hipError_t launch(int block, int grid, const Args& a, hipStream_t s) {
-    hipLaunchKernelGGL((row_kernel<E, NIN, Q1, Q2, VPT>), dim3(grid), dim3(block), 0, s, a);
+    hipLaunchKernelGGL((row_kernel<E, NIN, Q1, Q2, GEO>), dim3(grid), dim3(block), 0, s, a);
     return hipGetLastError();
   }
   static int occupancy(int block) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_kernel<E, NIN, Q1, Q2, VPT>, block,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_kernel<E, NIN, Q1, Q2, GEO>, block,
                                                      0) != hipSuccess)
       return 0;
     return n;
@@ -267,14 +281,16 @@ struct RowInst {
 };
 
 // Calls f.template operator()<Inst>() for the instance matching (nin, q1,
-// q2, vpt); returns false when no such instance exists.
+// q2, geo); returns false when no such instance exists.  geo = vpt | depth << 4.
 template <int E, template <int, int, int, int, int> class Inst, typename F>
-bool dispatch_variant(int nin, int q1, int q2, int vpt, F&& f) {
-#define ADQ_VPT_CASES(NIN_, Q1_, Q2_)                                       \
-  switch (vpt) {                                                            \
-    case 1: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 1>>(); return true; \
-    case 2: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 2>>(); return true; \
-    default: return false;                                                  \
+bool dispatch_variant(int nin, int q1, int q2, int geo, F&& f) {
+#define ADQ_VPT_CASES(NIN_, Q1_, Q2_)                                                \
+  switch (geo) {                                                                     \
+    case 0x11: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 0x11>>(); return true; \
+    case 0x12: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 0x12>>(); return true; \
+    case 0x21: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 0x21>>(); return true; \
+    case 0x22: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 0x22>>(); return true; \
+    default: return false;                                                           \
   }
   if (nin == 1) {
     if (q2 != kQNone) return false;
@@ -295,17 +311,17 @@ bool dispatch_variant(int nin, int q1, int q2, int vpt, F&& f) {
 
 // Entry points for one element type, used by launch_row() in adq_api.cpp.
 #define ADQ_DEFINE_ROW_ENTRY(E, SUFFIX)                                                     \
-  hipError_t launch_row_##SUFFIX(const Variant& v, int vpt, int block, int grid,           \
+  hipError_t launch_row_##SUFFIX(const Variant& v, int vpt, int depth, int block, int grid, \
                                  const Args& a, hipStream_t s) {                           \
     hipError_t err = hipErrorInvalidValue;                                                 \
-    dispatch_variant<E, RowInst>(v.nin, v.q1, v.q2, vpt, [&]<typename I>() {               \
+    dispatch_variant<E, RowInst>(v.nin, v.q1, v.q2, vpt | depth << 4, [&]<typename I>() {  \
       err = I::launch(block, grid, a, s);                                                  \
     });                                                                                    \
     return err;                                                                            \
   }                                                                                        \
-  int row_occupancy_##SUFFIX(const Variant& v, int vpt, int block) {                       \
+  int row_occupancy_##SUFFIX(const Variant& v, int vpt, int depth, int block) {            \
     int occ = 0;                                                                           \
-    dispatch_variant<E, RowInst>(v.nin, v.q1, v.q2, vpt,                                   \
+    dispatch_variant<E, RowInst>(v.nin, v.q1, v.q2, vpt | depth << 4,                      \
                                  [&]<typename I>() { occ = I::occupancy(block); });        \
     return occ;                                                                            \
   }

@@ -185,7 +185,7 @@ def test_ragged_shapes(m, n, dtype):
     compare_v2(outs, ora, y_types)
     if n % 8 != 0:
         assert "path=generic" in desc, desc
-    elif n > 16384 or (m <= 64 and n >= 2048):
+    elif n > 16384:
         assert "path=split" in desc, desc
     else:
         assert "path=row" in desc, desc
