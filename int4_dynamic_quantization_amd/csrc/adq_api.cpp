@@ -20,20 +20,19 @@
 
 namespace adq {
 
-hipError_t launch_row_bf16(const Variant&, int, int, int, int, const Args&, hipStream_t);
-hipError_t launch_row_f16(const Variant&, int, int, int, int, const Args&, hipStream_t);
-int row_occupancy_bf16(const Variant&, int, int, int);
-int row_occupancy_f16(const Variant&, int, int, int);
+hipError_t launch_row_bf16(const Variant&, int, int, int, const Args&, hipStream_t);
+hipError_t launch_row_f16(const Variant&, int, int, int, const Args&, hipStream_t);
+int row_occupancy_bf16(const Variant&, int, int);
+int row_occupancy_f16(const Variant&, int, int);
 
-hipError_t launch_row(const Variant& v, int vpt, int depth, int block, int grid, const Args& a,
+hipError_t launch_row(const Variant& v, int vpt, int block, int grid, const Args& a,
                       hipStream_t s) {
-  return v.elem == kBF16 ? launch_row_bf16(v, vpt, depth, block, grid, a, s)
-                         : launch_row_f16(v, vpt, depth, block, grid, a, s);
+  return v.elem == kBF16 ? launch_row_bf16(v, vpt, block, grid, a, s)
+                         : launch_row_f16(v, vpt, block, grid, a, s);
 }
 
-int row_max_blocks_per_cu(const Variant& v, int vpt, int depth, int block) {
-  return v.elem == kBF16 ? row_occupancy_bf16(v, vpt, depth, block)
-                         : row_occupancy_f16(v, vpt, depth, block);
+int row_max_blocks_per_cu(const Variant& v, int vpt, int block) {
+  return v.elem == kBF16 ? row_occupancy_bf16(v, vpt, block) : row_occupancy_f16(v, vpt, block);
 }
 
 }  // namespace adq
@@ -74,7 +73,6 @@ struct adq_executor {
   bool vector_ok;  // n % 8 == 0, aligned tensors, n small enough for the row kernel
   int path;
   int vpt;
-  int depth;
   int block;
   int grid;
   int splits;
@@ -229,11 +227,17 @@ uint64_t next_epoch() {
 #ifndef ADQ_MAX_WG_PER_CU
 #define ADQ_MAX_WG_PER_CU 0
 #endif
-#ifndef ADQ_DEPTH2_MAX_N
-#define ADQ_DEPTH2_MAX_N 6144
+#ifndef ADQ_ROW_GRID_MULT
+#define ADQ_ROW_GRID_MULT 1
 #endif
-#ifndef ADQ_DEPTH2_MIN_ROWS_PER_WG
-#define ADQ_DEPTH2_MIN_ROWS_PER_WG 16
+#ifndef ADQ_SHORT_ROW_MAX_N
+#define ADQ_SHORT_ROW_MAX_N 6144
+#endif
+#ifndef ADQ_SHORT_ROW_MIN_ROWS_PER_WG
+#define ADQ_SHORT_ROW_MIN_ROWS_PER_WG 16
+#endif
+#ifndef ADQ_SHORT_ROW_GRID_MULT
+#define ADQ_SHORT_ROW_GRID_MULT 24
 #endif
 
 bool row_geometry(int64_t nvec, int* vpt, int* block) {
@@ -279,7 +283,6 @@ bool split_geometry(adq_executor* e) {
   if (groups * 8 * splits > capacity) groups = capacity / (8 * splits);
   if (groups < 1) return false;
   e->vpt = vpt;
-  e->depth = 1;
   e->block = (int)block;
   e->splits = (int)splits;
   e->row_groups = (int)groups;
@@ -317,21 +320,21 @@ adq_status plan(adq_executor* e, int path) {
     if (!e->vector_ok || !row_geometry(n / 8, &vpt, &block))
       return fail(ADQ_ERR_PARAM_INVALID,
                   "row path needs n %% 8 == 0, n <= 16384 and 16-byte aligned tensors");
-    // Prefetch depth 2 (two rows in flight per workgroup) pays for short
-    // rows streamed many times per workgroup; longer rows keep depth 1.
-    int depth = 1, occ = 0;
-    int64_t per = 0;
-    for (int d = 1; d <= 2; ++d) {
-      occ = adq::row_max_blocks_per_cu(e->var, vpt, d, block);
-      if (ADQ_MAX_WG_PER_CU > 0 && occ > ADQ_MAX_WG_PER_CU) occ = ADQ_MAX_WG_PER_CU;
-      if (occ <= 0) return fail(ADQ_ERR_RUNTIME, "row kernel does not fit block %d", block);
-      const int64_t slots = (int64_t)occ * e->cus;
+    int occ = adq::row_max_blocks_per_cu(e->var, vpt, block);
+    if (ADQ_MAX_WG_PER_CU > 0 && occ > ADQ_MAX_WG_PER_CU) occ = ADQ_MAX_WG_PER_CU;
+    if (occ <= 0) return fail(ADQ_ERR_RUNTIME, "row kernel does not fit block %d", block);
+    // A grid that fills every slot once (each workgroup then streams
+    // rows / slots rows) suits long rows.  Short rows (up to 6144 columns)
+    // that would be streamed 16 or more times per workgroup go faster with
+    // ADQ_SHORT_ROW_GRID_MULT times as many workgroups of a few rows each,
+    // which the dispatcher hands to CUs as they free up.
+    int64_t slots = (int64_t)occ * e->cus * ADQ_ROW_GRID_MULT;
+    int64_t per = (e->m + slots - 1) / slots;
+    if (n <= ADQ_SHORT_ROW_MAX_N && per >= ADQ_SHORT_ROW_MIN_ROWS_PER_WG) {
+      slots *= ADQ_SHORT_ROW_GRID_MULT;
       per = (e->m + slots - 1) / slots;
-      depth = d;
-      if (!(n <= ADQ_DEPTH2_MAX_N && per >= ADQ_DEPTH2_MIN_ROWS_PER_WG)) break;
     }
     e->path = ADQ_PATH_ROW;
-    e->depth = depth;
     e->vpt = vpt;
     e->block = block;
     e->grid = (int)((e->m + per - 1) / per);
@@ -343,7 +346,6 @@ adq_status plan(adq_executor* e, int path) {
   if (path == ADQ_PATH_GENERIC) {
     e->path = ADQ_PATH_GENERIC;
     e->vpt = 0;
-    e->depth = 1;
     e->block = 256;
     e->grid = (int)(e->m < (int64_t)e->cus * 8 ? e->m : (int64_t)e->cus * 8);
     e->splits = 1;
@@ -401,7 +403,7 @@ adq_status run(void* workspace, uint64_t workspace_size, adq_executor* e, void* 
   hipError_t err = hipErrorInvalidValue;
   switch (e->path) {
     case ADQ_PATH_ROW:
-      err = adq::launch_row(e->var, e->vpt, e->depth, e->block, e->grid, e->args, s);
+      err = adq::launch_row(e->var, e->vpt, e->block, e->grid, e->args, s);
       break;
     case ADQ_PATH_GENERIC: err = adq::launch_generic(e->var, e->block, e->grid, e->args, s); break;
     case ADQ_PATH_SPLIT:
@@ -584,10 +586,10 @@ int32_t adq_executor_describe(const adq_executor* e, char* buf, uint64_t len) {
   if (buf && len > 0) {
     static const char* names[] = {"auto", "row", "split", "generic"};
     snprintf(buf, (size_t)len,
-             "path=%s elem=%s nin=%d q1=%d q2=%d rows=%lld n=%d vpt=%d depth=%d block=%d grid=%d "
+             "path=%s elem=%s nin=%d q1=%d q2=%d rows=%lld n=%d vpt=%d block=%d grid=%d "
              "splits=%d row_groups=%d workspace=%llu cus=%d epoch=%llu",
              names[e->path & 3], e->var.elem == adq::kBF16 ? "bf16" : "fp16", e->var.nin,
-             e->var.q1, e->var.q2, (long long)e->m, e->args.n, e->vpt, e->depth, e->block, e->grid,
+             e->var.q1, e->var.q2, (long long)e->m, e->args.n, e->vpt, e->block, e->grid,
              e->splits, e->row_groups, (unsigned long long)e->ws_bytes, e->cus,
              (unsigned long long)e->last_epoch);
   }

@@ -47,10 +47,10 @@ struct Variant {
 };
 
 // Row kernel: one workgroup per row at a time, `vpt` 8-element vectors per
-// thread (1 or 2), `depth` rows loaded ahead (1 or 2), grid-strided over rows.
-hipError_t launch_row(const Variant& v, int vpt, int depth, int block, int grid, const Args& a,
+// thread (1 or 2), grid-strided over rows, next row prefetched.
+hipError_t launch_row(const Variant& v, int vpt, int block, int grid, const Args& a,
                       hipStream_t stream);
-int row_max_blocks_per_cu(const Variant& v, int vpt, int depth, int block);
+int row_max_blocks_per_cu(const Variant& v, int vpt, int block);
 
 // Split-row kernel: `splits` workgroups share each row (a chunk of block *
 // vpt 8-column vectors each); grid = 8 * row_groups * splits, launched

@@ -57,11 +57,8 @@ __device__ __forceinline__ void store_codes(const float (&in)[8], float inv, rsr
   }
 }
 
-// GEO packs the thread geometry: VPT = GEO & 0xF (8-column vectors per
-// thread), prefetch depth = GEO >> 4 (rows loaded ahead: 1 or 2).
-template <int E, int NIN, int Q1, int Q2, int GEO>
+template <int E, int NIN, int Q1, int Q2, int VPT>
 __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
-  constexpr int VPT = GEO & 0xF;
   static_assert(VPT == 1 || VPT == 2, "row kernel holds at most 16 columns per thread");
   constexpr bool kTwo = Q2 != kQNone;
   constexpr int kQ2 = kTwo ? Q2 : kQInt8;
@@ -110,9 +107,6 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
     }
   };
 
-  // Rows this workgroup loads ahead of the one it computes (1 or 2).
-  constexpr int kDepth = GEO >> 4;
-  static_assert(kDepth == 1 || kDepth == 2, "prefetch depth 1 or 2");
   // Rows of this workgroup: strided (blockIdx.x, + gridDim.x, ...) or one
   // contiguous block of rows.
 #if ADQ_ROW_BLOCKED
@@ -129,25 +123,18 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
 
   int64_t row = first;
   if (row >= rend) return;
-  // Raw x1/x2 vectors of rows in flight.  Depth 1: set A holds the row being
-  // computed and the next row is loaded into fresh registers at the start of
-  // each row.  Depth 2: sets A and B alternate; a set is refilled with the
-  // row two steps ahead as soon as pass A has consumed it, so no register
-  // copies (which would force a wait on the newest loads) are needed.
-  u32x4 a1[VPT], a2[VPT], b1[VPT], b2[VPT];
-  load_row(row, a1, a2);
-  if constexpr (kDepth == 2) load_row(clamp_row(row + step), b1, b2);
+  u32x4 c1[VPT], c2[VPT];  // raw x1/x2 vectors of the row being computed
+  load_row(row, c1, c2);
 
-  // One row.  The first row is peeled off the loop so that every entry to
-  // the loop header has the same outstanding memory operations (loads, then
-  // stores); the wait for a prefetched row then need not wait for stores.
-  auto body = [&](int64_t row, u32x4 (&c1)[VPT], u32x4 (&c2)[VPT]) {
+  // One row: prefetch the next, compute and store this one.  The first row
+  // is peeled off the loop so that every entry to the loop header has the
+  // same outstanding memory operations (loads, then stores); the wait for
+  // the prefetched row then need not wait for stores.
+  auto body = [&](int64_t row) {
+    // Prefetch this workgroup's next row (its last row again when there is
+    // none, so the loads are unconditional).
     u32x4 n1[VPT], n2[VPT];
-    if constexpr (kDepth == 1) {
-      // Prefetch the next row (the last row again when there is none, so
-      // the loads are unconditional).
-      load_row(clamp_row(row + step), n1, n2);
-    }
+    load_row(clamp_row(row + step), n1, n2);
 #pragma unroll
     for (int k = 0; k < VPT; ++k) opaque(pg[k]), opaque(pb[k]), opaque(p1[k]), opaque(p2[k]);
 
@@ -175,7 +162,6 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
             rxo, vj[k] * 16u, 0, kStreamStore);
       }
     }
-    if constexpr (kDepth == 2) load_row(clamp_row(row + 2 * step), c1, c2);
     ss = wave_sum(ss);
     if (lane == 0) red_ss[wave] = ss;
     __syncthreads();
@@ -241,39 +227,24 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
       for (int k = 0; k < VPT; ++k) store_codes<kQ2>(in2[k], r2.inv, ry2, vj[k]);
     }
 
-    if constexpr (kDepth == 1) {
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) c1[k] = n1[k], c2[k] = n2[k];
-    }
+    for (int k = 0; k < VPT; ++k) c1[k] = n1[k], c2[k] = n2[k];
   };
-  if constexpr (kDepth == 1) {
-    body(row, a1, a2);
-    for (row += step; row < rend; row += step) body(row, a1, a2);
-  } else {
-    // Two rows peeled (one per set) so that the loop is entered after the
-    // same sequence of memory operations as its back edge.
-    body(row, a1, a2);
-    if ((row += step) >= rend) return;
-    body(row, b1, b2);
-    for (row += step; row < rend; row += step) {
-      body(row, a1, a2);
-      if ((row += step) >= rend) break;
-      body(row, b1, b2);
-    }
-  }
+  body(row);
+  for (row += step; row < rend; row += step) body(row);
 }
 
 // ---- launch table for one element type
 
-template <int E, int NIN, int Q1, int Q2, int GEO>
+template <int E, int NIN, int Q1, int Q2, int VPT>
 struct RowInst {
   static hipError_t launch(int block, int grid, const Args& a, hipStream_t s) {
-    hipLaunchKernelGGL((row_kernel<E, NIN, Q1, Q2, GEO>), dim3(grid), dim3(block), 0, s, a);
+    hipLaunchKernelGGL((row_kernel<E, NIN, Q1, Q2, VPT>), dim3(grid), dim3(block), 0, s, a);
     return hipGetLastError();
   }
   static int occupancy(int block) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_kernel<E, NIN, Q1, Q2, GEO>, block,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_kernel<E, NIN, Q1, Q2, VPT>, block,
                                                      0) != hipSuccess)
       return 0;
     return n;
@@ -281,16 +252,14 @@ struct RowInst {
 };
 
 // Calls f.template operator()<Inst>() for the instance matching (nin, q1,
-// q2, geo); returns false when no such instance exists.  geo = vpt | depth << 4.
+// q2, vpt); returns false when no such instance exists.
 template <int E, template <int, int, int, int, int> class Inst, typename F>
-bool dispatch_variant(int nin, int q1, int q2, int geo, F&& f) {
-#define ADQ_VPT_CASES(NIN_, Q1_, Q2_)                                                \
-  switch (geo) {                                                                     \
-    case 0x11: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 0x11>>(); return true; \
-    case 0x12: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 0x12>>(); return true; \
-    case 0x21: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 0x21>>(); return true; \
-    case 0x22: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 0x22>>(); return true; \
-    default: return false;                                                           \
+bool dispatch_variant(int nin, int q1, int q2, int vpt, F&& f) {
+#define ADQ_VPT_CASES(NIN_, Q1_, Q2_)                                         \
+  switch (vpt) {                                                              \
+    case 1: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 1>>(); return true; \
+    case 2: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 2>>(); return true; \
+    default: return false;                                                    \
   }
   if (nin == 1) {
     if (q2 != kQNone) return false;
@@ -311,17 +280,17 @@ bool dispatch_variant(int nin, int q1, int q2, int geo, F&& f) {
 
 // Entry points for one element type, used by launch_row() in adq_api.cpp.
 #define ADQ_DEFINE_ROW_ENTRY(E, SUFFIX)                                                     \
-  hipError_t launch_row_##SUFFIX(const Variant& v, int vpt, int depth, int block, int grid, \
+  hipError_t launch_row_##SUFFIX(const Variant& v, int vpt, int block, int grid,           \
                                  const Args& a, hipStream_t s) {                           \
     hipError_t err = hipErrorInvalidValue;                                                 \
-    dispatch_variant<E, RowInst>(v.nin, v.q1, v.q2, vpt | depth << 4, [&]<typename I>() {  \
+    dispatch_variant<E, RowInst>(v.nin, v.q1, v.q2, vpt, [&]<typename I>() {               \
       err = I::launch(block, grid, a, s);                                                  \
     });                                                                                    \
     return err;                                                                            \
   }                                                                                        \
-  int row_occupancy_##SUFFIX(const Variant& v, int vpt, int depth, int block) {            \
+  int row_occupancy_##SUFFIX(const Variant& v, int vpt, int block) {                       \
     int occ = 0;                                                                           \
-    dispatch_variant<E, RowInst>(v.nin, v.q1, v.q2, vpt | depth << 4,                      \
+    dispatch_variant<E, RowInst>(v.nin, v.q1, v.q2, vpt,                                   \
                                  [&]<typename I>() { occ = I::occupancy(block); });        \
     return occ;                                                                            \
   }
