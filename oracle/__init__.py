@@ -17,6 +17,7 @@ Pins (what checks this oracle against something other than itself) are in
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -44,29 +45,46 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def _configure(lib):
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    ci = ctypes.c_int
+    lib.oracle_storage_value.argtypes = [ctypes.c_uint16, ci]
+    lib.oracle_storage_value.restype = ctypes.c_double
+    lib.oracle_round_to_storage.argtypes = [ctypes.c_double, ci]
+    lib.oracle_round_to_storage.restype = ctypes.c_uint16
+    lib.oracle_v2_outputs.argtypes = [p, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci)]
+    lib.oracle_v2_outputs.restype = ci
+    lib.oracle_add_rms_norm_dq.argtypes = [
+        i64, i64, ci, p, p, p, p, p, p, ctypes.c_double, ci, ci,
+        p, p, p, p, p, p, p, p]
+    lib.oracle_add_rms_norm_dq.restype = ci
+    lib.oracle_pack_int4.argtypes = [i64, i64, p, p]
+    lib.oracle_pack_int4.restype = ci
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB):
             build(force=False)
-        lib = ctypes.CDLL(_LIB)
-        p = ctypes.c_void_p
-        i64 = ctypes.c_int64
-        ci = ctypes.c_int
-        lib.oracle_storage_value.argtypes = [ctypes.c_uint16, ci]
-        lib.oracle_storage_value.restype = ctypes.c_double
-        lib.oracle_round_to_storage.argtypes = [ctypes.c_double, ci]
-        lib.oracle_round_to_storage.restype = ctypes.c_uint16
-        lib.oracle_v2_outputs.argtypes = [p, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci)]
-        lib.oracle_v2_outputs.restype = ci
-        lib.oracle_add_rms_norm_dq.argtypes = [
-            i64, i64, ci, p, p, p, p, p, p, ctypes.c_double, ci, ci,
-            p, p, p, p, p, p, p, p]
-        lib.oracle_add_rms_norm_dq.restype = ci
-        lib.oracle_pack_int4.argtypes = [i64, i64, p, p]
-        lib.oracle_pack_int4.restype = ci
-        _lib = lib
+        _lib = _configure(ctypes.CDLL(_LIB))
     return _lib
+
+
+@contextlib.contextmanager
+def use_library(path: str):
+    """Route every oracle call to another build of adq_oracle.c (used by the
+    tests that plant mistakes in a copy of the oracle and check that the pins
+    catch them)."""
+    global _lib
+    saved = _lib
+    _lib = _configure(ctypes.CDLL(path))
+    try:
+        yield
+    finally:
+        _lib = saved
 
 
 def _ptr(a):

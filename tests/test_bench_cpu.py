@@ -1,0 +1,49 @@
+"""bench.py on the CPU: algorithmic-byte accounting of every workload, and
+the single-GPU contract of its command line."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# bytes per launch: inputs read once + outputs written once + parameter vectors once,
+# worked out by hand for each workload
+EXPECTED = {
+    # 64 rows * (2*1024 read + 1024 + 4) + gamma 2*1024
+    "rmsnorm_dq": ([True, False], 64 * (2 * 1024 + 1024 + 4) + 2 * 1024),
+    # 4096 * (2*2*4096 + 2*4096 + 4096 + 4) + (gamma, beta, s1) 3*2*4096
+    "v2_square": ([True, False], 4096 * (4 * 4096 + 2 * 4096 + 4096 + 4) + 3 * 2 * 4096),
+    # 32 * (4*16384 + 2*16384 + 2*(16384 + 4)) + 4*2*16384
+    "v2_decode": ([True, True], 32 * (4 * 16384 + 2 * 16384 + 2 * (16384 + 4)) + 4 * 2 * 16384),
+    "v2_outlier": ([True, True], 16384 * (4 * 8192 + 2 * 8192 + 2 * (8192 + 4)) + 4 * 2 * 8192),
+    # INT4: 5120/2 bytes of codes per row
+    "v2_int4": ([True, False], 65536 * (4 * 5120 + 2 * 5120 + 2560 + 4) + 3 * 2 * 5120),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXPECTED))
+def test_algorithmic_bytes(name):
+    active, want = EXPECTED[name]
+    assert bench.alg_bytes(synth.WORKLOADS[name], active) == want
+
+
+def test_headline_bytes_value():
+    assert bench.alg_bytes(synth.WORKLOADS["v2_outlier"], [True, True]) == 1_073_938_432
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_traffic_record_matches_its_hash_or_is_ignored():
+    t = bench.measured_traffic("v2_outlier")
+    assert t is None or t > bench.alg_bytes(synth.WORKLOADS["v2_outlier"], [True, True]) * 0.99
+    assert bench.measured_traffic("no_such_workload") is None

@@ -1,0 +1,80 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of oracle/adq_oracle.c (a dropped
+term, a misplaced epsilon, a wrong sign, constant, index, rounding mode,
+packing order or validity rule), builds it on the CPU, routes the oracle
+wrapper to it and runs the pin checks of test_oracle_pins.py until one
+fails.  A mutant that passes every pin would mean the pins cannot tell it
+from the formulas; the test fails in that case.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
+                   "adq_oracle.c")
+
+MUTANTS = [
+    ("beta dropped", "double b = beta ? oracle_storage_value(beta[j], dtype) : 0.0;",
+     "double b = 0.0;"),
+    ("epsilon outside the root", "sqrt(ss / (double)n + eps)", "sqrt(ss / (double)n) + eps"),
+    ("sum instead of mean", "sqrt(ss / (double)n + eps)", "sqrt(ss + eps)"),
+    ("x1 - x2", "v += oracle_storage_value(x2[off + j], dtype)",
+     "v -= oracle_storage_value(x2[off + j], dtype)"),
+    ("wrong divisor for the scale", "(float)(m / Q)", "(float)(m / (Q + 1.0))"),
+    ("round half away from zero", "double c = nearbyint(v);", "double c = round(v);"),
+    ("smooth scale ignored", "y[j] * oracle_storage_value(smooth[k][j], dtype) : y[j]",
+     "y[j] : y[j]"),
+    ("smooth scales swapped", "const uint16_t* smooth[2] = {smooth1, smooth2};",
+     "const uint16_t* smooth[2] = {smooth2, smooth1};"),
+    ("signed instead of absolute maximum", "if (fabs(in) > m) m = fabs(in);",
+     "if (in > m) m = in;"),
+    ("nibbles swapped", "(uint8_t)(lo | (hi << 4))", "(uint8_t)(hi | (lo << 4))"),
+    ("smooth2 without smooth1 accepted", "if (has_s2 && !has_s1) return 0;", ""),
+    ("mask[0] rule dropped", "if (has_s1 && !mask[0]) return 0;", ""),
+    ("gamma indexed backwards", "oracle_storage_value(gamma[j], dtype)",
+     "oracle_storage_value(gamma[n - 1 - j], dtype)"),
+    ("xOut truncated", "double q = nearbyint(m / quantum);", "double q = floor(m / quantum);"),
+    ("no clamp of the scale to float", "const float sc = (float)(m / Q);",
+     "const double sc = m / Q;"),
+]
+
+
+def _battery():
+    checks = [("mask table", pins.test_mask_truth_table)]
+    checks += [(f"worked row {c['name']}", lambda c=c: pins.test_worked_rows(c))
+               for c in pins._CASES]
+    checks += [
+        ("closed forms", pins.test_closed_form_constant_and_one_hot_rows),
+        ("int4 packing", pins.test_pack_int4_nibble_order),
+        ("rms_norm vs torch", pins.test_rmsnorm_step_matches_torch_rms_norm),
+        ("xOut bf16", lambda: pins.test_xout_is_correctly_rounded_sum("bf16")),
+        ("xOut fp16", lambda: pins.test_xout_is_correctly_rounded_sum("fp16")),
+    ]
+    checks += [(f"brute force {s}", lambda s=s: pins.test_brute_force_tiny_rows(s))
+               for s in range(6)]
+    return checks
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old}"
+    mutant = tmp_path / "mutant.c"
+    mutant.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", str(mutant), "-o",
+                           str(lib), "-lm"])
+    caught = None
+    with oracle.use_library(str(lib)):
+        for label, check in _battery():
+            try:
+                check()
+            except Exception:  # an assertion, or a rejected call
+                caught = label
+                break
+    assert caught is not None, f"no pin catches the mutant '{name}'"
