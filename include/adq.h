@@ -149,6 +149,34 @@ adq_status adq_rms_norm_dynamic_quant_get_workspace_size(
 adq_status adq_rms_norm_dynamic_quant(void* workspace, uint64_t workspace_size,
                                       adq_executor* executor, void* hip_stream);
 
+/*
+ * INT8 x INT8 GEMM with per-row and per-column scales: the consumer of the
+ * quantized activations.  With y1Out = round(input1 / scale1Out) (the V2
+ * Formula), input1 ~ y1Out * scale1Out row by row, and a linear layer whose
+ * weights are quantized per output column (w ~ w_q * w_scale) computes
+ *
+ *   out[..., j] = (sum_k a[..., k] * w[j, k]) * a_scale[...] * w_scale[j] + bias[j]
+ *
+ * a        [..., k] ADQ_INT8, row-major, 16-byte aligned (e.g. y1_out)
+ * a_scale  F32 with one value per row of a (e.g. scale1_out)
+ * w        [n, k] ADQ_INT8, row-major (each output's weights contiguous), 16-byte aligned
+ * w_scale  [n] F32
+ * bias     [n] F32, or NULL
+ * out      [..., n] F32, BF16 or F16 (rounded to nearest even from fp32)
+ * k must be a multiple of 16 and at most 131072 (the integer sum stays in
+ * int32).  The integer sum is exact; the epilogue is
+ * ((float)sum * a_scale) * w_scale + bias in fp32.  Workspace size is 0.
+ * Errors as for the other phase-1 calls.
+ */
+adq_status adq_w8a8_gemm_get_workspace_size(const adq_tensor* a, const adq_tensor* a_scale,
+                                            const adq_tensor* w, const adq_tensor* w_scale,
+                                            const adq_tensor* bias, const adq_tensor* out,
+                                            uint64_t* workspace_size, adq_executor** executor);
+
+/* GEMM phase 2; as adq_add_rms_norm_dynamic_quant_v2. */
+adq_status adq_w8a8_gemm(void* workspace, uint64_t workspace_size, adq_executor* executor,
+                         void* hip_stream);
+
 /* Free an executor (NULL is a no-op).  Launched work is not affected. */
 void adq_executor_destroy(adq_executor* executor);
 

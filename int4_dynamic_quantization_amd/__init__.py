@@ -33,6 +33,8 @@ EXPORTED = (
     "adq_add_rms_norm_dynamic_quant_v2",
     "adq_rms_norm_dynamic_quant_get_workspace_size",
     "adq_rms_norm_dynamic_quant",
+    "adq_w8a8_gemm_get_workspace_size",
+    "adq_w8a8_gemm",
     "adq_executor_destroy",
     "adq_executor_set_path",
     "adq_executor_describe",
@@ -85,6 +87,8 @@ def _load():
     lib.adq_rms_norm_dynamic_quant_get_workspace_size.argtypes = [
         P, P, P, P, ctypes.c_double, P, P, u64p, exp]
     lib.adq_rms_norm_dynamic_quant.argtypes = [vp, ctypes.c_uint64, vp, vp]
+    lib.adq_w8a8_gemm_get_workspace_size.argtypes = [P, P, P, P, P, P, u64p, exp]
+    lib.adq_w8a8_gemm.argtypes = [vp, ctypes.c_uint64, vp, vp]
     lib.adq_executor_destroy.argtypes = [vp]
     lib.adq_executor_destroy.restype = None
     lib.adq_executor_set_path.argtypes = [vp, ctypes.c_int32, u64p]
@@ -95,7 +99,7 @@ def _load():
     for name in ("adq_add_rms_norm_dynamic_quant_v2_get_workspace_size",
                  "adq_add_rms_norm_dynamic_quant_v2",
                  "adq_rms_norm_dynamic_quant_get_workspace_size", "adq_rms_norm_dynamic_quant",
-                 "adq_executor_set_path"):
+                 "adq_w8a8_gemm_get_workspace_size", "adq_w8a8_gemm", "adq_executor_set_path"):
         getattr(lib, name).restype = ctypes.c_int
     runtimes = _hip_runtimes_mapped()
     if len(runtimes) > 1:
@@ -188,8 +192,9 @@ class Executor:
         ws_ptr = None if workspace is None else workspace.data_ptr()
         ws_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
         s = None if stream is None else stream.cuda_stream
-        fn = (_lib().adq_add_rms_norm_dynamic_quant_v2 if self.op == "v2"
-              else _lib().adq_rms_norm_dynamic_quant)
+        fn = {"v2": _lib().adq_add_rms_norm_dynamic_quant_v2,
+              "rmsnorm": _lib().adq_rms_norm_dynamic_quant,
+              "gemm": _lib().adq_w8a8_gemm}[self.op]
         _check(fn(ws_ptr, ws_size, self.handle, s))
 
     def close(self) -> None:
@@ -331,3 +336,36 @@ def rms_norm_dynamic_quant(x, gamma, beta=None, smooth_scales=None, epsilon=1e-6
     ex.run(ws, stream)
     ex.close()
     return outs["y"], outs["scale"]
+
+
+def w8a8_gemm_get_workspace_size(a, a_scale, w, w_scale, bias, out) -> Executor:
+    """GEMM phase 1 on adq_tensor descriptors (bias may be None)."""
+    ws = ctypes.c_uint64(0)
+    handle = ctypes.c_void_p(None)
+    _check(_lib().adq_w8a8_gemm_get_workspace_size(
+        _ref(a), _ref(a_scale), _ref(w), _ref(w_scale), _ref(bias), _ref(out), ctypes.byref(ws),
+        ctypes.byref(handle)))
+    return Executor(handle, ws.value, "gemm", (a, a_scale, w, w_scale, bias, out))
+
+
+def plan_w8a8_gemm(a, a_scale, w, w_scale, bias=None, out_dtype=None, out=None):
+    """Allocate out (unless given) and run GEMM phase 1 on torch tensors:
+    a int8 [..., k], a_scale float32 (one per row), w int8 [n, k],
+    w_scale float32 [n], bias float32 [n] or None."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(tuple(a.shape[:-1]) + (w.shape[0],),
+                          dtype=out_dtype or torch.bfloat16, device=a.device)
+    d = describe_tensor
+    ex = w8a8_gemm_get_workspace_size(d(a, INT8), d(a_scale), d(w, INT8), d(w_scale), d(bias),
+                                      d(out))
+    ex._keep = (ex._keep, a, a_scale, w, w_scale, bias, out)
+    return ex, out
+
+
+def w8a8_gemm(a, a_scale, w, w_scale, bias=None, out_dtype=None, stream=None):
+    """Both GEMM phases on torch tensors; returns out."""
+    ex, out = plan_w8a8_gemm(a, a_scale, w, w_scale, bias, out_dtype)
+    ex.run(None, stream)
+    ex.close()
+    return out

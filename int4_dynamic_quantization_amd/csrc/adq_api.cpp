@@ -59,7 +59,7 @@ adq_status ok() {
   return ADQ_OK;
 }
 
-enum Op { kOpV2 = 1, kOpRmsNorm = 2 };
+enum Op { kOpV2 = 1, kOpRmsNorm = 2, kOpGemm = 3 };
 
 }  // namespace
 
@@ -67,6 +67,8 @@ struct adq_executor {
   int op;
   Variant var;
   Args args;
+  adq::GemmArgs gemm;
+  int gemm_tile;
   int64_t m;
   int device;
   int cus;
@@ -226,6 +228,9 @@ uint64_t next_epoch() {
 #endif
 #ifndef ADQ_MAX_WG_PER_CU
 #define ADQ_MAX_WG_PER_CU 0
+#endif
+#ifndef ADQ_GEMM_BIG_TILE
+#define ADQ_GEMM_BIG_TILE 1
 #endif
 #ifndef ADQ_ROW_GRID_MULT
 #define ADQ_ROW_GRID_MULT 1
@@ -401,6 +406,13 @@ adq_status run(void* workspace, uint64_t workspace_size, adq_executor* e, void* 
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t err = hipErrorInvalidValue;
+  if (op == kOpGemm) {
+    err = adq::launch_w8a8(e->gemm, e->gemm_tile, s);
+    if (cur != e->device) (void)hipSetDevice(cur);
+    if (err != hipSuccess)
+      return fail(ADQ_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(err));
+    return ok();
+  }
   switch (e->path) {
     case ADQ_PATH_ROW:
       err = adq::launch_row(e->var, e->vpt, e->block, e->grid, e->args, s);
@@ -569,10 +581,92 @@ adq_status adq_rms_norm_dynamic_quant(void* workspace, uint64_t workspace_size,
   return run(workspace, workspace_size, executor, hip_stream, kOpRmsNorm);
 }
 
+adq_status adq_w8a8_gemm_get_workspace_size(const adq_tensor* a, const adq_tensor* a_scale,
+                                            const adq_tensor* w, const adq_tensor* w_scale,
+                                            const adq_tensor* bias, const adq_tensor* out,
+                                            uint64_t* workspace_size, adq_executor** executor) {
+  if (!workspace_size || !executor)
+    return fail(ADQ_ERR_NULLPTR, "workspace_size and executor out-pointers are required");
+  *executor = nullptr;
+  *workspace_size = 0;
+  if (!a || !a_scale || !w || !w_scale || !out)
+    return fail(ADQ_ERR_NULLPTR, "a, a_scale, w, w_scale and out are required");
+  adq_status st;
+  if ((st = check_tensor(a, "a")) != ADQ_OK) return st;
+  if ((st = check_tensor(w, "w")) != ADQ_OK) return st;
+  if ((st = check_tensor(a_scale, "a_scale")) != ADQ_OK) return st;
+  if ((st = check_tensor(w_scale, "w_scale")) != ADQ_OK) return st;
+  if ((st = check_tensor(out, "out")) != ADQ_OK) return st;
+  if (bias && (st = check_tensor(bias, "bias")) != ADQ_OK) return st;
+  if (a->dtype != ADQ_INT8 || w->dtype != ADQ_INT8)
+    return fail(ADQ_ERR_UNSUPPORTED, "a and w must be INT8");
+  if (a_scale->dtype != ADQ_F32 || w_scale->dtype != ADQ_F32 || (bias && bias->dtype != ADQ_F32))
+    return fail(ADQ_ERR_UNSUPPORTED, "a_scale, w_scale and bias must be F32");
+  int out_type;
+  if (out->dtype == ADQ_F32) out_type = adq::kGemmOutF32;
+  else if (out->dtype == ADQ_BF16) out_type = adq::kGemmOutBF16;
+  else if (out->dtype == ADQ_F16) out_type = adq::kGemmOutF16;
+  else return fail(ADQ_ERR_UNSUPPORTED, "out must be F32, BF16 or F16");
+  if (a->ndim < 1 || w->ndim != 2)
+    return fail(ADQ_ERR_PARAM_INVALID, "a is [..., k] and w is [n, k]");
+  const int64_t k = a->shape[a->ndim - 1];
+  const int64_t m = numel(a) / k;
+  const int64_t n = w->shape[0];
+  if (w->shape[1] != k) return fail(ADQ_ERR_PARAM_INVALID, "w must be [n, k] with a's k");
+  if (k % 16 != 0) return fail(ADQ_ERR_PARAM_INVALID, "k must be a multiple of 16");
+  if (k > (1 << 17)) return fail(ADQ_ERR_PARAM_INVALID, "k above 131072 could overflow int32");
+  if (numel(a_scale) != m) return fail(ADQ_ERR_PARAM_INVALID, "a_scale needs one value per row");
+  if (w_scale->ndim != 1 || w_scale->shape[0] != n)
+    return fail(ADQ_ERR_PARAM_INVALID, "w_scale must be [n]");
+  if (bias && (bias->ndim != 1 || bias->shape[0] != n))
+    return fail(ADQ_ERR_PARAM_INVALID, "bias must be [n]");
+  if (out->ndim != a->ndim) return fail(ADQ_ERR_PARAM_INVALID, "out must be [..., n]");
+  for (int i = 0; i + 1 < a->ndim; ++i)
+    if (out->shape[i] != a->shape[i])
+      return fail(ADQ_ERR_PARAM_INVALID, "out's leading dimensions must match a's");
+  if (out->shape[out->ndim - 1] != n) return fail(ADQ_ERR_PARAM_INVALID, "out must be [..., n]");
+  if (!aligned(a->data, 16) || !aligned(w->data, 16))
+    return fail(ADQ_ERR_PARAM_INVALID, "a and w must be 16-byte aligned");
+  adq_executor e{};
+  e.op = kOpGemm;
+  st = current_device(&e.device, &e.cus);
+  if (st != ADQ_OK) return st;
+  e.gemm.a = static_cast<const int8_t*>(a->data);
+  e.gemm.a_scale = static_cast<const float*>(a_scale->data);
+  e.gemm.w = static_cast<const int8_t*>(w->data);
+  e.gemm.w_scale = static_cast<const float*>(w_scale->data);
+  e.gemm.bias = bias ? static_cast<const float*>(bias->data) : nullptr;
+  e.gemm.out = out->data;
+  e.gemm.m = m;
+  e.gemm.n = n;
+  e.gemm.k = k;
+  e.gemm.out_type = out_type;
+  e.m = m;
+  // large tiles once there are enough of them to fill the CUs
+  const int64_t big = ((m + 255) / 256) * ((n + 255) / 256);
+  e.gemm_tile = big >= e.cus ? ADQ_GEMM_BIG_TILE : adq::kGemmTile128;
+  adq_executor* ex = new (std::nothrow) adq_executor(e);
+  if (!ex) return fail(ADQ_ERR_RUNTIME, "out of host memory");
+  *executor = ex;
+  return ok();
+}
+
+adq_status adq_w8a8_gemm(void* workspace, uint64_t workspace_size, adq_executor* executor,
+                         void* hip_stream) {
+  return run(workspace, workspace_size, executor, hip_stream, kOpGemm);
+}
+
 void adq_executor_destroy(adq_executor* executor) { delete executor; }
 
 adq_status adq_executor_set_path(adq_executor* executor, int32_t path, uint64_t* workspace_size) {
   if (!executor || !workspace_size) return fail(ADQ_ERR_NULLPTR, "executor and workspace_size are required");
+  if (executor->op == kOpGemm) {
+    if (path == ADQ_PATH_AUTO) {
+      *workspace_size = 0;
+      return ok();
+    }
+    return fail(ADQ_ERR_PARAM_INVALID, "the GEMM has a single kernel path");
+  }
   adq_executor trial = *executor;
   adq_status st = plan(&trial, path);
   if (st != ADQ_OK) return st;
@@ -583,6 +677,13 @@ adq_status adq_executor_set_path(adq_executor* executor, int32_t path, uint64_t*
 
 int32_t adq_executor_describe(const adq_executor* e, char* buf, uint64_t len) {
   if (!e) return -1;
+  if (e->op == kOpGemm) {
+    if (buf && len > 0)
+      snprintf(buf, (size_t)len, "path=gemm m=%lld n=%lld k=%lld tile=%d out=%d cus=%d",
+               (long long)e->gemm.m, (long long)e->gemm.n, (long long)e->gemm.k,
+               e->gemm_tile == adq::kGemmTile256 ? 256 : 128, e->gemm.out_type, e->cus);
+    return ADQ_PATH_AUTO;
+  }
   if (buf && len > 0) {
     static const char* names[] = {"auto", "row", "split", "generic"};
     snprintf(buf, (size_t)len,

@@ -65,4 +65,22 @@ uint64_t split_workspace_bytes(int64_t rows, int splits);
 hipError_t launch_generic(const Variant& v, int block, int grid, const Args& a,
                           hipStream_t stream);
 
+// INT8 x INT8 GEMM with per-row / per-column scales (consumer of the codes).
+enum GemmOut : int { kGemmOutF32 = 0, kGemmOutBF16 = 1, kGemmOutF16 = 2 };
+enum GemmTile : int { kGemmTile128 = 1, kGemmTile256 = 2 };
+
+struct GemmArgs {
+  const int8_t* a;        // [m, k] row-major (activation codes)
+  const float* a_scale;   // [m]
+  const int8_t* w;        // [n, k] row-major (weight codes)
+  const float* w_scale;   // [n]
+  const float* bias;      // [n] or nullptr
+  void* out;              // [m, n] row-major, out_type
+  int64_t m, n, k;
+  int32_t out_type;       // GemmOut
+};
+
+// k % 16 == 0, 16-byte aligned a and w.
+hipError_t launch_w8a8(const GemmArgs& g, int tile, hipStream_t stream);
+
 }  // namespace adq

@@ -61,6 +61,8 @@ def _configure(lib):
     lib.oracle_add_rms_norm_dq.restype = ci
     lib.oracle_pack_int4.argtypes = [i64, i64, p, p]
     lib.oracle_pack_int4.restype = ci
+    lib.oracle_w8a8_gemm_at.argtypes = [i64, p, p, i64, p, p, p, p, p, p, p]
+    lib.oracle_w8a8_gemm_at.restype = ci
     return lib
 
 
@@ -196,3 +198,36 @@ def rms_norm_dq(x, gamma, beta=None, smooth=None, eps=1e-6, y_type="int8", dtype
     if y_type == "int4":
         res["packed"] = pack_int4(out["code1"])
     return res
+
+
+def w8a8_gemm_at(a, a_scale, w, w_scale, bias, rows, cols):
+    """Outputs (row rows[t], column cols[t]) of the INT8 GEMM with scales:
+    returns (exact int64 sums, double outputs)."""
+    a = np.ascontiguousarray(a, dtype=np.int8)
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    k = a.shape[-1]
+    a = a.reshape(-1, k)
+    assert w.shape[1] == k
+    sa = np.ascontiguousarray(a_scale, dtype=np.float32).reshape(-1)
+    sw = np.ascontiguousarray(w_scale, dtype=np.float32).reshape(-1)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32).reshape(-1)
+    mi = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+    ni = np.ascontiguousarray(cols, dtype=np.int64).reshape(-1)
+    assert mi.size == ni.size
+    assert (mi >= 0).all() and (mi < a.shape[0]).all() and (ni >= 0).all() and (ni < w.shape[0]).all()
+    sums = np.empty(mi.size, np.int64)
+    out = np.empty(mi.size, np.float64)
+    if _load().oracle_w8a8_gemm_at(mi.size, _ptr(mi), _ptr(ni), k, _ptr(a), _ptr(sa), _ptr(w),
+                                   _ptr(sw), _ptr(b), _ptr(sums), _ptr(out)) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return sums, out
+
+
+def w8a8_gemm(a, a_scale, w, w_scale, bias=None):
+    """Every output of the INT8 GEMM with scales: (sums [m, n], out [m, n])."""
+    m = int(np.prod(np.shape(a)[:-1]))
+    n = np.shape(w)[0]
+    rows = np.repeat(np.arange(m), n)
+    cols = np.tile(np.arange(n), m)
+    sums, out = w8a8_gemm_at(a, a_scale, w, w_scale, bias, rows, cols)
+    return sums.reshape(m, n), out.reshape(m, n)

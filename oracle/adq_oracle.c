@@ -226,3 +226,31 @@ int oracle_pack_int4(int64_t rows, int64_t n, const int8_t* codes, uint8_t* out)
     }
   return 0;
 }
+
+/* --- the consumer of the codes: INT8 x INT8 GEMM with scales ------------- */
+
+/*
+ * With y1Out = round(input1 / scale1Out) ("aclnnAddRmsNormDynamicQuantV2",
+ * Formula), input1 is approximated by y1Out * scale1Out row by row; a linear
+ * layer with per-output-column weight scales then computes, for each
+ * requested output (row mi[t], column ni[t]):
+ *   sums[t] = sum_k a[mi[t], k] * w[ni[t], k]          (exact, int64)
+ *   out[t]  = sums[t] * a_scale[mi[t]] * w_scale[ni[t]] + bias[ni[t]]   (double)
+ * a is [rows, k] and w is [n, k], both row-major int8; bias may be NULL.
+ */
+int oracle_w8a8_gemm_at(int64_t count, const int64_t* mi, const int64_t* ni, int64_t k,
+                        const int8_t* a, const float* a_scale, const int8_t* w,
+                        const float* w_scale, const float* bias, int64_t* sums, double* out) {
+  if (count < 0 || k <= 0 || !mi || !ni || !a || !a_scale || !w || !w_scale) return -1;
+  for (int64_t t = 0; t < count; ++t) {
+    const int8_t* ar = a + mi[t] * k;
+    const int8_t* wr = w + ni[t] * k;
+    int64_t s = 0;
+    for (int64_t j = 0; j < k; ++j) s += (int64_t)ar[j] * (int64_t)wr[j];
+    if (sums) sums[t] = s;
+    if (out)
+      out[t] = (double)s * (double)a_scale[mi[t]] * (double)w_scale[ni[t]] +
+               (bias ? (double)bias[ni[t]] : 0.0);
+  }
+  return 0;
+}

@@ -37,7 +37,8 @@ _LIB = os.path.join(_HERE, "libsynth_gen.so")
 
 DTYPES = {"bf16": 0, "fp16": 1}
 NORMAL, UNIFORM = 0, 1
-TID = {"x1": 0, "x2": 1, "gamma": 2, "beta": 3, "smooth1": 4, "smooth2": 5, "outlier": 6}
+TID = {"x1": 0, "x2": 1, "gamma": 2, "beta": 3, "smooth1": 4, "smooth2": 5, "outlier": 6,
+       "a_codes": 7, "a_scale": 8, "w_codes": 9, "w_scale": 10, "bias": 11}
 
 _lib = None
 
@@ -67,6 +68,14 @@ def _load():
             ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
             ctypes.c_void_p]
         lib.synth_pick_columns.restype = ctypes.c_int
+        lib.synth_fill_int8.argtypes = [
+            ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        lib.synth_fill_int8.restype = ctypes.c_int
+        lib.synth_fill_f32.argtypes = [
+            ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+            ctypes.c_int64, ctypes.c_void_p]
+        lib.synth_fill_f32.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -169,3 +178,52 @@ def inputs(w: Workload, rows=None, row_offset=0, cols=None, seed=None):
         x2 = fill(seed, TID["x2"], NORMAL, 0.0, 1.0, w.dtype, rows, cols, row_offset, flags,
                   w.outlier_factor)
     return x1, x2
+
+
+def int8_codes(seed, tid, rows, cols, lo=-127, hi=127, row_offset=0) -> np.ndarray:
+    """Uniform integers in [lo, hi], int8 [rows, cols]."""
+    out = np.empty((rows, cols), dtype=np.int8)
+    if _load().synth_fill_int8(int(seed), int(tid), int(lo), int(hi), int(rows), int(cols),
+                               int(row_offset), out.ctypes.data) != 0:
+        raise ValueError("synth_fill_int8 rejected its arguments")
+    return out
+
+
+def f32(seed, tid, dist, p0, p1, n) -> np.ndarray:
+    out = np.empty(n, dtype=np.float32)
+    if _load().synth_fill_f32(int(seed), int(tid), int(dist), float(p0), float(p1), int(n),
+                              out.ctypes.data) != 0:
+        raise ValueError("synth_fill_f32 rejected its arguments")
+    return out
+
+
+@dataclass(frozen=True)
+class GemmWorkload:
+    """INT8 GEMM consuming quantized activations: a [m, k] codes with one scale
+    per row (as the operator's y1Out / scale1Out), w [n, k] codes with one
+    scale per output column."""
+    name: str
+    m: int
+    n: int
+    k: int
+    seed: int
+    out_dtype: str = "bf16"
+    has_bias: bool = False
+
+
+GEMM_WORKLOADS = {
+    # the headline activations (16384 rows of 8192) through an 8192 -> 8192 projection
+    "w8a8_gemm": GemmWorkload("w8a8_gemm", 16384, 8192, 8192, 5),
+}
+
+
+def gemm_inputs(w: GemmWorkload, m=None, lo=-127, hi=127):
+    """a codes, a_scale (U(0.01, 0.08): row max / 127 of activations of a few
+    units), w codes, w_scale (U(1e-4, 1e-3)), bias (N(0, 0.1) or None)."""
+    m = w.m if m is None else m
+    a = int8_codes(w.seed, TID["a_codes"], m, w.k, lo, hi)
+    sa = f32(w.seed, TID["a_scale"], UNIFORM, 0.01, 0.08, m)
+    wq = int8_codes(w.seed, TID["w_codes"], w.n, w.k, lo, hi)
+    sw = f32(w.seed, TID["w_scale"], UNIFORM, 1e-4, 1e-3, w.n)
+    b = f32(w.seed, TID["bias"], NORMAL, 0.0, 0.1, w.n) if w.has_bias else None
+    return a, sa, wq, sw, b

@@ -189,3 +189,29 @@ int synth_pick_columns(uint64_t seed, uint32_t tid, int64_t n, int64_t k, int64_
   }
   return 0;
 }
+
+/*
+ * Uniform integers in [lo, hi] as int8 (rows [row_offset, row_offset+rows)
+ * of the tensor (seed, tid), cols per row): draw modulo (hi - lo + 1).
+ */
+int synth_fill_int8(uint64_t seed, uint32_t tid, int lo, int hi, int64_t rows, int64_t cols,
+                    int64_t row_offset, int8_t* out) {
+  if (rows < 0 || cols < 0 || !out || lo > hi || lo < -128 || hi > 127) return -1;
+  uint64_t base = stream_base(seed, tid);
+  uint64_t span = (uint64_t)(hi - lo + 1);
+  for (int64_t r = 0; r < rows; ++r) {
+    uint64_t flat = (uint64_t)(r + row_offset) * (uint64_t)cols;
+    for (int64_t c = 0; c < cols; ++c)
+      out[r * cols + c] = (int8_t)(lo + (int)(draw(base, flat + (uint64_t)c) % span));
+  }
+  return 0;
+}
+
+/* n float32 values of the tensor (seed, tid): dist 0 normal(p0, p1), 1 uniform[p0, p1). */
+int synth_fill_f32(uint64_t seed, uint32_t tid, int dist, double p0, double p1, int64_t n,
+                   float* out) {
+  if (n < 0 || !out) return -1;
+  uint64_t base = stream_base(seed, tid);
+  for (int64_t i = 0; i < n; ++i) out[i] = (float)sample(base, (uint64_t)i, dist, p0, p1);
+  return 0;
+}

@@ -44,7 +44,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     assert set(names) == set(adq.EXPORTED)
     for name in names:
         assert hasattr(adq.lib, name), name
@@ -210,3 +210,60 @@ def test_phase_two_and_helpers_reject_null_executor():
     assert adq.lib.adq_executor_describe(None, None, 0) == -1
     adq.lib.adq_executor_destroy(None)
     assert isinstance(adq.last_error(), str)
+
+
+def gemm_call(a, sa, w, sw, bias, out, out_ptrs=True):
+    ws = ctypes.c_uint64(0)
+    ex = ctypes.c_void_p(None)
+    r = lambda t: None if t is None else ctypes.byref(t)
+    st = adq.lib.adq_w8a8_gemm_get_workspace_size(
+        r(a), r(sa), r(w), r(sw), r(bias), r(out), ctypes.byref(ws) if out_ptrs else None,
+        ctypes.byref(ex) if out_ptrs else None)
+    if ex.value:
+        adq.lib.adq_executor_destroy(ex)
+    return st
+
+
+def full_gemm(m=64, n=48, k=128, out=adq.BF16):
+    return dict(a=fake([m, k], adq.INT8), sa=fake([m], adq.F32), w=fake([n, k], adq.INT8),
+                sw=fake([n], adq.F32), bias=fake([n], adq.F32), out=fake([m, n], out))
+
+
+def test_gemm_valid_calls():
+    for out in (adq.F32, adq.BF16, adq.F16):
+        assert gemm_call(**full_gemm(out=out)) in ACCEPTED, adq.last_error()
+    a = full_gemm()
+    a["bias"] = None
+    assert gemm_call(**a) in ACCEPTED
+    a = full_gemm()
+    a.update(a=fake([2, 32, 128], adq.INT8), sa=fake([2, 32], adq.F32),
+             out=fake([2, 32, 48], adq.BF16))
+    assert gemm_call(**a) in ACCEPTED
+
+
+def test_gemm_validation():
+    for f in ("a", "sa", "w", "sw", "out"):
+        a = full_gemm()
+        a[f] = None
+        assert gemm_call(**a) == adq.ERR_NULLPTR, f
+    assert gemm_call(out_ptrs=False, **full_gemm()) == adq.ERR_NULLPTR
+    bad = []
+    a = full_gemm(k=120); a["w"] = fake([48, 120], adq.INT8); bad.append(a)  # k % 16
+    a = full_gemm(k=(1 << 17) + 16); bad.append(a)                            # k too large
+    a = full_gemm(); a["w"] = fake([48, 64], adq.INT8); bad.append(a)         # k mismatch
+    a = full_gemm(); a["sa"] = fake([63], adq.F32); bad.append(a)
+    a = full_gemm(); a["sw"] = fake([47], adq.F32); bad.append(a)
+    a = full_gemm(); a["bias"] = fake([1, 48], adq.F32); bad.append(a)
+    a = full_gemm(); a["out"] = fake([64, 47], adq.BF16); bad.append(a)
+    a = full_gemm(); a["out"] = fake([63, 48], adq.BF16); bad.append(a)
+    a = full_gemm(); a["a"].data += 8; bad.append(a)                           # alignment
+    a = full_gemm(); a["out"].shape[0] = 0; bad.append(a)
+    for i, c in enumerate(bad):
+        assert gemm_call(**c) == adq.ERR_PARAM_INVALID, (i, adq.last_error())
+    unsupported = []
+    a = full_gemm(); a["a"] = fake([64, 128], adq.F16); unsupported.append(a)
+    a = full_gemm(); a["sw"] = fake([48], adq.BF16); unsupported.append(a)
+    a = full_gemm(); a["out"] = fake([64, 48], adq.INT8); unsupported.append(a)
+    for i, c in enumerate(unsupported):
+        assert gemm_call(**c) == adq.ERR_UNSUPPORTED, (i, adq.last_error())
+    assert adq.lib.adq_w8a8_gemm(None, 0, None, None) == adq.ERR_NULLPTR

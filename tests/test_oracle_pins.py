@@ -337,3 +337,42 @@ def test_invariants_on_workloads(name, rows):
                         oracle.QMAX[w.y_types[k - 1]])
     # near-tie codes are rare on these inputs
     assert near_tie(o["pre1"], 1e-3).mean() < 0.01
+
+
+# ---- the consumer GEMM of the codes ------------------------------------------
+
+def test_gemm_worked_example():
+    with open(os.path.join(GOLDEN, "gemm_worked.json")) as f:
+        c = json.load(f)
+    sums, out = oracle.w8a8_gemm(np.array(c["a"]), np.array(c["a_scale"]), np.array(c["w"]),
+                                 np.array(c["w_scale"]), np.array(c["bias"]))
+    assert sums.tolist() == c["sums"]
+    assert out.tolist() == c["out"]
+
+
+def test_gemm_sums_match_numpy_integer_matmul():
+    rng = np.random.default_rng(21)
+    for m, n, k in ((3, 5, 16), (17, 9, 48), (8, 33, 160)):
+        a = rng.integers(-127, 128, (m, k)).astype(np.int8)
+        w = rng.integers(-127, 128, (n, k)).astype(np.int8)
+        sa = rng.uniform(0.01, 1, m).astype(np.float32)
+        sw = rng.uniform(0.01, 1, n).astype(np.float32)
+        b = rng.normal(0, 1, n).astype(np.float32)
+        sums, out = oracle.w8a8_gemm(a, sa, w, sw, b)
+        ref = a.astype(np.int64) @ w.astype(np.int64).T
+        assert np.array_equal(sums, ref)
+        want = ref * sa.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] + b
+        assert np.allclose(out, want, rtol=1e-15, atol=1e-12)
+
+
+def test_gemm_scaled_identity_closed_form():
+    """w = c * identity: out[m, j] = a[m, j] * c * a_scale[m] * w_scale[j]."""
+    rng = np.random.default_rng(22)
+    k = 32
+    a = rng.integers(-127, 128, (6, k)).astype(np.int8)
+    w = (np.eye(k) * 3).astype(np.int8)
+    sa = rng.uniform(0.1, 1, 6).astype(np.float32)
+    sw = rng.uniform(0.1, 1, k).astype(np.float32)
+    sums, out = oracle.w8a8_gemm(a, sa, w, sw)
+    assert np.array_equal(sums, 3 * a.astype(np.int64))
+    assert np.allclose(out, 3.0 * a * sa[:, None].astype(np.float64) * sw[None, :], rtol=1e-15)
