@@ -12,6 +12,11 @@ MI355X HBM3E peak, and the CPU oracle timed on a bounded sample of the same
 workload on the host cores.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload v2_outlier]
+
+``--workload w8a8_gemm`` instead times the INT8 GEMM that consumes the
+quantized rows (16384 x 8192 codes with per-row scales through an
+8192 -> 8192 projection with per-column weight scales, bf16 out) against
+the MI355X dense INT8 MFMA peak.
 """
 from __future__ import annotations
 
@@ -28,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+INT8_PEAK_TOPS = 5000.0  # MI355X dense INT8 MFMA, 5.0 POP/s
 
 
 def alg_bytes(w, active, rows=None):
@@ -144,6 +150,9 @@ def main():
     import int4_dynamic_quantization_amd as adq
     import synth
 
+    if args.workload in synth.GEMM_WORKLOADS:
+        bench_gemm(args, torch, adq, synth)
+        return
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -222,6 +231,90 @@ def main():
         result["cpu_baseline"] = None
     for ex, _, _, _ in cases:
         ex.close()
+    print(json.dumps(result), flush=True)
+
+
+def gemm_cpu_baseline(a, sa, w, sw, b, k: int, budget_s: float):
+    """The oracle (plain C, one thread, exact int64 sums) on a sample of the
+    outputs, as many as fit the time budget after a short pilot."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(0)
+
+    def run(count):
+        rows = rng.integers(0, a.shape[0], count)
+        cols = rng.integers(0, w.shape[0], count)
+        t0 = time.perf_counter()
+        oracle.w8a8_gemm_at(a, sa, w, sw, b, rows, cols)
+        return time.perf_counter() - t0
+
+    pilot = 256
+    t = run(pilot)
+    count = int(max(pilot, budget_s / max(t / pilot, 1e-9)))
+    t = run(count)
+    tops = 2.0 * k * count / t / 1e12
+    return {"value": round(tops, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"{count} randomly placed outputs of the same seeded inputs "
+                      f"(2*k ops each), {t:.2f} s, single-threaded plain-C int64 oracle"}
+
+
+def bench_gemm(args, torch, adq, synth) -> None:
+    """One step = one launch of the INT8 GEMM with its dequantizing epilogue."""
+    w8 = synth.GEMM_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    a, sa, wq, sw, b = synth.gemm_inputs(w8)
+    t = lambda x: None if x is None else torch.from_numpy(x).to(dev)
+    out_dt = {"bf16": torch.bfloat16, "fp16": torch.float16, "f32": torch.float32}[w8.out_dtype]
+    ex, out = adq.plan_w8a8_gemm(t(a), t(sa), t(wq), t(sw), t(b), out_dtype=out_dt)
+    print(f"[bench] workload {w8.name} m={w8.m} n={w8.n} k={w8.k} out {w8.out_dtype}; "
+          f"plan: {ex.describe()}", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        ex.run(None, stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        ex.run(None, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    ops = 2.0 * w8.m * w8.n * w8.k
+    tops = ops / (ms * 1e-3) / 1e12
+    print(f"[bench] {args.steps} launches: avg {ms * 1e3:.1f} us per launch, "
+          f"wall {wall * 1e3:.1f} ms", file=sys.stderr, flush=True)
+    result = {
+        "metric": "achieved INT8 TOPS (% of dense MFMA peak), W8A8 GEMM 16384x8192x8192",
+        "value": round(tops, 1),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": w8.name, "op": "W8A8 GEMM (per-row x per-column scales)",
+            "m": w8.m, "n": w8.n, "k": w8.k, "out": w8.out_dtype, "bias": w8.has_bias,
+            "algorithmic_ops_per_step": ops,
+            "pct_of_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
+            "parallelism": "single GPU",
+            "plan": ex.describe(),
+        },
+        "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS,
+                     "unit": "TOPS", "frac": round(tops / INT8_PEAK_TOPS, 4),
+                     "traffic": measured_traffic(w8.name)},
+    }
+    ex.close()
+    result["cpu_baseline"] = (gemm_cpu_baseline(a, sa, wq, sw, b, w8.k, args.cpu_budget)
+                              if args.cpu_budget > 0 else None)
     print(json.dumps(result), flush=True)
 
 

@@ -164,7 +164,7 @@ adq_status adq_rms_norm_dynamic_quant(void* workspace, uint64_t workspace_size,
  * bias     [n] F32, or NULL
  * out      [..., n] F32, BF16 or F16 (rounded to nearest even from fp32)
  * k must be a multiple of 16 and at most 131072 (the integer sum stays in
- * int32).  The integer sum is exact; the epilogue is
+ * int32); n at most 1048576.  The integer sum is exact; the epilogue is
  * ((float)sum * a_scale) * w_scale + bias in fp32.  Workspace size is 0.
  * Errors as for the other phase-1 calls.
  */
@@ -186,12 +186,18 @@ void adq_executor_destroy(adq_executor* executor);
  * one workgroup per row, 128-bit accesses (n % 8 == 0, 16-byte aligned
  * tensors, n <= 16384).  ADQ_PATH_SPLIT: several workgroups per row (same
  * conditions; few-row shapes).  ADQ_PATH_GENERIC: any n and alignment.
+ * GEMM executors: ADQ_PATH_GEMM_TILE128 (128 x 128 output tiles) and
+ * ADQ_PATH_GEMM_TILE256 (256 x 256 tiles); AUTO takes 256 once the
+ * 256-tiles cover the compute units.  Either accepts any valid GEMM shape;
+ * the operator paths are rejected for a GEMM executor and vice versa.
  */
 typedef enum adq_path {
   ADQ_PATH_AUTO = 0,
   ADQ_PATH_ROW = 1,
   ADQ_PATH_SPLIT = 2,
-  ADQ_PATH_GENERIC = 3
+  ADQ_PATH_GENERIC = 3,
+  ADQ_PATH_GEMM_TILE128 = 4,
+  ADQ_PATH_GEMM_TILE256 = 5
 } adq_path;
 
 /*

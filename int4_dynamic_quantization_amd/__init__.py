@@ -26,6 +26,7 @@ STATUS_NAMES = {0: "ADQ_OK", 1: "ADQ_ERR_NULLPTR", 2: "ADQ_ERR_PARAM_INVALID",
                 3: "ADQ_ERR_UNSUPPORTED", 4: "ADQ_ERR_WORKSPACE", 5: "ADQ_ERR_RUNTIME"}
 # adq_path
 PATH_AUTO, PATH_ROW, PATH_SPLIT, PATH_GENERIC = 0, 1, 2, 3
+PATH_GEMM_TILE128, PATH_GEMM_TILE256 = 4, 5
 MAX_DIMS = 8
 
 EXPORTED = (
@@ -348,10 +349,12 @@ def w8a8_gemm_get_workspace_size(a, a_scale, w, w_scale, bias, out) -> Executor:
     return Executor(handle, ws.value, "gemm", (a, a_scale, w, w_scale, bias, out))
 
 
-def plan_w8a8_gemm(a, a_scale, w, w_scale, bias=None, out_dtype=None, out=None):
+def plan_w8a8_gemm(a, a_scale, w, w_scale, bias=None, out_dtype=None, out=None,
+                   path=PATH_AUTO):
     """Allocate out (unless given) and run GEMM phase 1 on torch tensors:
     a int8 [..., k], a_scale float32 (one per row), w int8 [n, k],
-    w_scale float32 [n], bias float32 [n] or None."""
+    w_scale float32 [n], bias float32 [n] or None.  `path` may force a tile
+    size (PATH_GEMM_TILE128 / PATH_GEMM_TILE256)."""
     torch = _torch()
     if out is None:
         out = torch.empty(tuple(a.shape[:-1]) + (w.shape[0],),
@@ -360,6 +363,8 @@ def plan_w8a8_gemm(a, a_scale, w, w_scale, bias=None, out_dtype=None, out=None):
     ex = w8a8_gemm_get_workspace_size(d(a, INT8), d(a_scale), d(w, INT8), d(w_scale), d(bias),
                                       d(out))
     ex._keep = (ex._keep, a, a_scale, w, w_scale, bias, out)
+    if path != PATH_AUTO:
+        ex.set_path(path)
     return ex, out
 
 

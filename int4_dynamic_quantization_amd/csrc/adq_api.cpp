@@ -230,7 +230,7 @@ uint64_t next_epoch() {
 #define ADQ_MAX_WG_PER_CU 0
 #endif
 #ifndef ADQ_GEMM_BIG_TILE
-#define ADQ_GEMM_BIG_TILE 1
+#define ADQ_GEMM_BIG_TILE 2
 #endif
 #ifndef ADQ_ROW_GRID_MULT
 #define ADQ_ROW_GRID_MULT 1
@@ -581,6 +581,12 @@ adq_status adq_rms_norm_dynamic_quant(void* workspace, uint64_t workspace_size,
   return run(workspace, workspace_size, executor, hip_stream, kOpRmsNorm);
 }
 
+// large tiles once there are enough of them to occupy every compute unit
+static int gemm_auto_tile(const adq_executor& e) {
+  const int64_t big = ((e.gemm.m + 255) / 256) * ((e.gemm.n + 255) / 256);
+  return big >= e.cus ? ADQ_GEMM_BIG_TILE : adq::kGemmTile128;
+}
+
 adq_status adq_w8a8_gemm_get_workspace_size(const adq_tensor* a, const adq_tensor* a_scale,
                                             const adq_tensor* w, const adq_tensor* w_scale,
                                             const adq_tensor* bias, const adq_tensor* out,
@@ -615,6 +621,7 @@ adq_status adq_w8a8_gemm_get_workspace_size(const adq_tensor* a, const adq_tenso
   if (w->shape[1] != k) return fail(ADQ_ERR_PARAM_INVALID, "w must be [n, k] with a's k");
   if (k % 16 != 0) return fail(ADQ_ERR_PARAM_INVALID, "k must be a multiple of 16");
   if (k > (1 << 17)) return fail(ADQ_ERR_PARAM_INVALID, "k above 131072 could overflow int32");
+  if (n > (1 << 20)) return fail(ADQ_ERR_PARAM_INVALID, "n above 1048576 is not supported");
   if (numel(a_scale) != m) return fail(ADQ_ERR_PARAM_INVALID, "a_scale needs one value per row");
   if (w_scale->ndim != 1 || w_scale->shape[0] != n)
     return fail(ADQ_ERR_PARAM_INVALID, "w_scale must be [n]");
@@ -642,9 +649,7 @@ adq_status adq_w8a8_gemm_get_workspace_size(const adq_tensor* a, const adq_tenso
   e.gemm.k = k;
   e.gemm.out_type = out_type;
   e.m = m;
-  // large tiles once there are enough of them to fill the CUs
-  const int64_t big = ((m + 255) / 256) * ((n + 255) / 256);
-  e.gemm_tile = big >= e.cus ? ADQ_GEMM_BIG_TILE : adq::kGemmTile128;
+  e.gemm_tile = gemm_auto_tile(e);
   adq_executor* ex = new (std::nothrow) adq_executor(e);
   if (!ex) return fail(ADQ_ERR_RUNTIME, "out of host memory");
   *executor = ex;
@@ -661,12 +666,16 @@ void adq_executor_destroy(adq_executor* executor) { delete executor; }
 adq_status adq_executor_set_path(adq_executor* executor, int32_t path, uint64_t* workspace_size) {
   if (!executor || !workspace_size) return fail(ADQ_ERR_NULLPTR, "executor and workspace_size are required");
   if (executor->op == kOpGemm) {
-    if (path == ADQ_PATH_AUTO) {
-      *workspace_size = 0;
-      return ok();
-    }
-    return fail(ADQ_ERR_PARAM_INVALID, "the GEMM has a single kernel path");
+    if (path == ADQ_PATH_AUTO) executor->gemm_tile = gemm_auto_tile(*executor);
+    else if (path == ADQ_PATH_GEMM_TILE128) executor->gemm_tile = adq::kGemmTile128;
+    else if (path == ADQ_PATH_GEMM_TILE256) executor->gemm_tile = adq::kGemmTile256;
+    else return fail(ADQ_ERR_PARAM_INVALID, "a GEMM executor takes AUTO or a GEMM tile path");
+    executor->path = path;
+    *workspace_size = 0;
+    return ok();
   }
+  if (path == ADQ_PATH_GEMM_TILE128 || path == ADQ_PATH_GEMM_TILE256)
+    return fail(ADQ_ERR_PARAM_INVALID, "GEMM tile paths apply to GEMM executors only");
   adq_executor trial = *executor;
   adq_status st = plan(&trial, path);
   if (st != ADQ_OK) return st;
@@ -682,7 +691,7 @@ int32_t adq_executor_describe(const adq_executor* e, char* buf, uint64_t len) {
       snprintf(buf, (size_t)len, "path=gemm m=%lld n=%lld k=%lld tile=%d out=%d cus=%d",
                (long long)e->gemm.m, (long long)e->gemm.n, (long long)e->gemm.k,
                e->gemm_tile == adq::kGemmTile256 ? 256 : 128, e->gemm.out_type, e->cus);
-    return ADQ_PATH_AUTO;
+    return e->path;
   }
   if (buf && len > 0) {
     static const char* names[] = {"auto", "row", "split", "generic"};

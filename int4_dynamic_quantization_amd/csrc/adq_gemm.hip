@@ -27,6 +27,10 @@
 
 #include "adq_device.h"
 
+#ifndef ADQ_GEMM_STAGES
+#define ADQ_GEMM_STAGES 4
+#endif
+
 namespace adq {
 
 namespace {
@@ -190,6 +194,268 @@ __global__ void __launch_bounds__(256) w8a8_kernel(const GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 tiles for large problems.  Each wavefront owns 128 x 128 outputs
+// (4 x 4 blocks of 32x32x32), which halves the LDS bytes read per MFMA
+// compared with 64 x 64 per wavefront.  Tiles reach LDS through the buffer
+// unit's direct-to-LDS path (buffer_load_dwordx4 ... lds): no staging
+// registers, and a ring of STAGES buffers keeps STAGES - 1 K-steps in flight.
+//
+// A direct-to-LDS load writes lane l's 16 bytes at the instruction's LDS base
+// + 16 * l, so a 1 KB segment holds 16 tile rows of BK = 64 bytes (4 chunks
+// per row).  The lane that fills position p of row r fetches chunk
+// c = p ^ h(r) of that row, h(r) = (r >> 2) & 3.  gfx950's LDS serves a
+// 128-bit read in four passes of 16 lanes over 64 four-byte banks; measured
+// with the LDS bank-conflict counter, a pass takes lanes from one half of
+// the wavefront whose index bits 2 and 4 agree in parity (the fits also
+// allow bits 0 and 3 to join that parity).  A fragment read has lane l on
+// row l % 32, one chunk per half, so a pass holds 16 rows whose (r mod 4,
+// h(r)) pairs are all distinct for each of those lane groupings: every
+// pass touches 64 distinct banks.  Without the swizzle (row stride 64 B)
+// a pass hits only 16 banks four times over.
+template <int STAGES>
+struct BigShape {
+  static constexpr int BM = 256, BN = 256, BK = 64;
+  static constexpr int SEG = 1024;                       // bytes per direct-load instruction
+  static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;  // 32 KB
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int SEGS_PER_WAVE = A_BYTES / SEG / 4;  // per operand, 4 wavefronts
+};
+
+__device__ __forceinline__ int chunk_swizzle(int r) { return (r >> 2) & 3; }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int STAGES, int OUT>
+__global__ void __launch_bounds__(256) w8a8_big_kernel(const GemmArgs g) {
+  using S = BigShape<STAGES>;
+  __shared__ __attribute__((aligned(1024))) int8_t lds[S::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int64_t tiles_m = (g.m + S::BM - 1) / S::BM;
+  const int64_t tiles_n = (g.n + S::BN - 1) / S::BN;
+  const int64_t tiles = tiles_m * tiles_n;
+  const int64_t b = blockIdx.x;
+  const int64_t per_xcd = (tiles + kXcdCount - 1) / kXcdCount;
+  const int64_t t = (b % kXcdCount) * per_xcd + b / kXcdCount;
+  if (t >= tiles) return;
+  const int64_t group = t / (kGroupRows * tiles_n);
+  const int64_t first_m = group * kGroupRows;
+  const int64_t rows_in_group = tiles_m - first_m < kGroupRows ? tiles_m - first_m : kGroupRows;
+  const int64_t in_group = t - group * kGroupRows * tiles_n;
+  const int64_t m0 = (first_m + in_group % rows_in_group) * S::BM;
+  const int64_t n0 = (in_group / rows_in_group) * S::BN;
+
+  const int64_t a_rows = g.m - m0 < S::BM ? g.m - m0 : S::BM;
+  const int64_t w_rows = g.n - n0 < S::BN ? g.n - n0 : S::BN;
+  const rsrc_t ra = make_rsrc(g.a + m0 * g.k, (uint32_t)(a_rows * g.k));
+  const rsrc_t rw = make_rsrc(g.w + n0 * g.k, (uint32_t)(w_rows * g.k));
+  constexpr uint32_t kOut = 0x80000000u;
+
+  // this lane's source in each of the wavefront's segments: row r = 16 * seg + lane / 4
+  // (the same rows for A and W), chunk c = (lane % 4) ^ h(r)
+  uint32_t src[S::SEGS_PER_WAVE];
+  int src_k[S::SEGS_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < S::SEGS_PER_WAVE; ++i) {
+    const int r = 16 * (wave * S::SEGS_PER_WAVE + i) + (lane >> 2);
+    const int c = (lane & 3) ^ chunk_swizzle(r);
+    src[i] = (uint32_t)(r * g.k) + 16u * c;
+    src_k[i] = 16 * c;
+  }
+  using lds_ptr = __attribute__((address_space(3))) void*;
+  auto issue = [&](int64_t step, int buf) {
+    const int64_t k0 = step * S::BK;
+    int8_t* base = lds + buf * S::STAGE_BYTES + wave * S::SEGS_PER_WAVE * S::SEG;
+#pragma unroll
+    for (int i = 0; i < S::SEGS_PER_WAVE; ++i) {
+      const uint32_t off = k0 + src_k[i] < g.k ? src[i] + (uint32_t)k0 : kOut;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(base + i * S::SEG), 16, off, 0, 0,
+                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(base + S::A_BYTES + i * S::SEG), 16,
+                                               off, 0, 0, 0);
+    }
+  };
+
+  i32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = i32x16{};
+
+  // fragment addresses (relative to a stage): row R of the A (W) tile, chunk
+  // kk / 16 + lane / 32 at position chunk ^ h(R); h depends on R only through
+  // lane % 32 and the block offset (a multiple of 32), so it is per lane.
+  const int fr = lane & 31;
+  const int hsw = chunk_swizzle(fr);
+  const int fk = lane >> 5;
+  int a_off[4], b_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a_off[i] = (wm * 128 + i * 32 + fr) * S::BK;
+    b_off[i] = S::A_BYTES + (wn * 128 + i * 32 + fr) * S::BK;
+  }
+
+  const int64_t ksteps = (g.k + S::BK - 1) / S::BK;
+  auto read = [&](const int8_t* st, int kk, i32x4* fa, i32x4* fb) {
+    const int pos = 16 * (((kk * 2) + fk) ^ hsw);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const i32x4*>(st + a_off[i] + pos);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const i32x4*>(st + b_off[j] + pos);
+  };
+  auto mfma = [&](const i32x4* fa, const i32x4* fb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  // Barrier without a memory fence: a fence would make every wavefront wait
+  // for all of its direct-to-LDS loads, including the later stages in flight.
+  // The stage about to be read is awaited explicitly: loads complete in
+  // order, so it has landed once no more than the `later` stages issued after
+  // it (2 * SEGS_PER_WAVE loads each) are outstanding.  LDS reads of the
+  // stage being retired complete (lgkmcnt) before the barrier, so after it
+  // that buffer may be refilled.
+  auto sync_stage = [&](int64_t later) {
+    constexpr int L = 2 * S::SEGS_PER_WAVE;
+    if (later >= 4) wait_vmcnt<4 * L>();
+    else if (later == 3) wait_vmcnt<3 * L>();
+    else if (later == 2) wait_vmcnt<2 * L>();
+    else if (later == 1) wait_vmcnt<L>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+  };
+  auto min64 = [](int64_t x, int64_t y) { return x < y ? x : y; };
+
+  // prologue: stages 0 .. STAGES-1 in flight; stage 0 visible, its first half read
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s)
+    if (s < ksteps) issue(s, s);
+  i32x4 f0a[4], f0b[4], f1a[4], f1b[4];
+  sync_stage(min64(STAGES - 1, ksteps - 1));
+  read(lds, 0, f0a, f0b);
+  // One step: read the second half of stage s while the first half's MFMAs
+  // run; sync on stage s + 1 (issued so far: stages up to s + STAGES - 1);
+  // refill stage s's buffer, which every wavefront has finished reading; read
+  // the first half of stage s + 1 while the second half's MFMAs run.  The
+  // last step is peeled so that every loop iteration has the same waits.
+  // Instruction order inside each half (sched_group_barrier masks: 0x008
+  // MFMA, 0x020 vector-memory read, 0x100 LDS read): the LDS reads and the
+  // direct-to-LDS loads issue one per MFMA, in the shadow of the MFMAs.
+  auto step = [&](int64_t s, bool refill) {
+    const int buf = (int)(s % STAGES);
+    read(lds + buf * S::STAGE_BYTES, 1, f1a, f1b);
+    mfma(f0a, f0b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    sync_stage(min64(STAGES - 2, ksteps - 2 - s));
+    read(lds + (int)((s + 1) % STAGES) * S::STAGE_BYTES, 0, f0a, f0b);
+    if (refill) issue(s + STAGES, buf);
+    mfma(f1a, f1b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+    }
+  };
+  int64_t s = 0;
+  for (; s + STAGES < ksteps; ++s) step(s, true);
+  for (; s + 1 < ksteps; ++s) step(s, false);
+  read(lds + (int)(s % STAGES) * S::STAGE_BYTES, 1, f1a, f1b);
+  mfma(f0a, f0b);
+  mfma(f1a, f1b);
+
+  // ---- epilogue: out = float(acc) * a_scale[row] * w_scale[col] (+ bias[col]).
+  // Scales are loaded up front through range-checked buffer loads (0 past the
+  // end).  Outputs go through a descriptor over this tile's rows of out (row r
+  // at r * n, column n0 + c within it); the offset is sent out of range for
+  // columns past N, and rows past M fall outside the descriptor.
+  const rsrc_t rsa = make_rsrc(g.a_scale + m0, (uint32_t)(a_rows * 4));
+  const rsrc_t rsw = make_rsrc(g.w_scale + n0, (uint32_t)(w_rows * 4));
+  const rsrc_t rb = make_rsrc(g.bias ? g.bias + n0 : g.w_scale + n0,
+                              g.bias ? (uint32_t)(w_rows * 4) : 0u);
+  constexpr int OB = OUT == kGemmOutF32 ? 4 : 2;  // output bytes
+  const rsrc_t ro = make_rsrc(static_cast<int8_t*>(g.out) + m0 * g.n * OB,
+                              (uint32_t)min64(a_rows * g.n * OB, 0x7FFFFFFF));
+  float sa[4][16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = wm * 128 + i * 32 + (e / 4) * 8 + (lane >> 5) * 4 + (e & 3);
+      sa[i][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, r * 4, 0, 0));
+    }
+  float swv[4], bv[4];
+  uint32_t col_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = wn * 128 + j * 32 + (lane & 31);
+    swv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsw, c * 4, 0, 0));
+    bv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, c * 4, 0, 0));
+    col_off[j] = n0 + c < g.n ? (uint32_t)((n0 + c) * OB) : kOut;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = wm * 128 + i * 32 + (e / 4) * 8 + (lane >> 5) * 4 + (e & 3);
+      const uint32_t row_off = (uint32_t)(r * g.n * OB);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v = (float)acc[i][j][e] * sa[i][e] * swv[j] + bv[j];
+        const uint32_t off = col_off[j] == kOut ? kOut : row_off + col_off[j];
+        if constexpr (OUT == kGemmOutF32) {
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ro, off, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b16(
+              narrow1<OUT == kGemmOutBF16 ? kBF16 : kF16>(v), ro, off, 0, 0);
+        }
+      }
+    }
+}
+
+template <int STAGES, int OUT>
+hipError_t launch_big(const GemmArgs& g, hipStream_t s) {
+  const int64_t tiles = ((g.m + 255) / 256) * ((g.n + 255) / 256);
+  const int64_t grid = (tiles + kXcdCount - 1) / kXcdCount * kXcdCount;
+  hipLaunchKernelGGL((w8a8_big_kernel<STAGES, OUT>), dim3((unsigned)grid), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+template <int STAGES>
+hipError_t launch_big_out(const GemmArgs& g, hipStream_t s) {
+  switch (g.out_type) {
+    case kGemmOutF32: return launch_big<STAGES, kGemmOutF32>(g, s);
+    case kGemmOutBF16: return launch_big<STAGES, kGemmOutBF16>(g, s);
+    case kGemmOutF16: return launch_big<STAGES, kGemmOutF16>(g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int TM, int TN, int BK, int OUT>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   using S = GemmShape<TM, TN, BK>;
@@ -215,7 +481,7 @@ hipError_t launch_out(const GemmArgs& g, hipStream_t s) {
 hipError_t launch_w8a8(const GemmArgs& g, int tile, hipStream_t stream) {
   switch (tile) {
     case kGemmTile128: return launch_out<2, 2, 128>(g, stream);
-    case kGemmTile256: return launch_out<4, 4, 64>(g, stream);
+    case kGemmTile256: return launch_big_out<ADQ_GEMM_STAGES>(g, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -36,7 +36,11 @@ def codes(seed, tid, rows, cols, lo=-127, hi=127):
     return synth.int8_codes(seed, tid, rows, cols, lo, hi)
 
 
-def run_gemm(a, sa, w, sw, bias=None, out="bf16", lead=None):
+TILES = [adq.PATH_GEMM_TILE128, adq.PATH_GEMM_TILE256]
+TILE_IDS = ["tile128", "tile256"]
+
+
+def run_gemm(a, sa, w, sw, bias=None, out="bf16", lead=None, path=adq.PATH_AUTO):
     """Run the GEMM through the C-ABI on host arrays; returns (out, describe)."""
     ta = torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
     if lead is not None:
@@ -48,7 +52,7 @@ def run_gemm(a, sa, w, sw, bias=None, out="bf16", lead=None):
         "cuda")
     o = torch.full(tuple(ta.shape[:-1]) + (w.shape[0],), float("nan"), dtype=OUT_DT[out],
                    device="cuda")
-    ex, o = adq.plan_w8a8_gemm(ta, tsa, tw, tsw, tb, out=o)
+    ex, o = adq.plan_w8a8_gemm(ta, tsa, tw, tsw, tb, out=o, path=path)
     ex.run()
     torch.cuda.synchronize()
     desc = ex.describe()
@@ -76,14 +80,6 @@ def tile_of(desc):
     return int(desc.split("tile=")[1].split()[0])
 
 
-def cus_of(desc):
-    return int(desc.split("cus=")[1].split()[0])
-
-
-def expected_tile(m, n, cus):
-    return 256 if ((m + 255) // 256) * ((n + 255) // 256) >= cus else 128
-
-
 EXACT_SHAPES = [
     (1, 16, 16),
     (5, 7, 32),
@@ -96,18 +92,21 @@ EXACT_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("path", TILES, ids=TILE_IDS)
 @pytest.mark.parametrize("m,n,k", EXACT_SHAPES)
-def test_integer_sums_exact(m, n, k):
+def test_integer_sums_exact(m, n, k, path):
     a = codes(11, 7, m, k)
     w = codes(11, 9, n, k)
     ones_m, ones_n = np.ones(m, np.float32), np.ones(n, np.float32)
-    got, desc = run_gemm(a, ones_m, w, ones_n, out="f32")
+    got, desc = run_gemm(a, ones_m, w, ones_n, out="f32", path=path)
+    assert tile_of(desc) == (128 if path == adq.PATH_GEMM_TILE128 else 256), desc
     sums, _ = oracle.w8a8_gemm(a, ones_m, w, ones_n)
     assert np.abs(sums).max() <= 2 ** 24
     assert np.array_equal(got, sums.astype(np.float32)), desc
 
 
-def test_extreme_codes_exact():
+@pytest.mark.parametrize("path", TILES, ids=TILE_IDS)
+def test_extreme_codes_exact(path):
     # -128 * -128 * 1024 = 2^24: the largest sum that float32 holds exactly
     k = 1024
     a = np.full((70, k), -128, np.int8)
@@ -115,7 +114,7 @@ def test_extreme_codes_exact():
     w[1::2] = 127
     a[3::5] = 127
     ones_m, ones_n = np.ones(70, np.float32), np.ones(90, np.float32)
-    got, _ = run_gemm(a, ones_m, w, ones_n, out="f32")
+    got, _ = run_gemm(a, ones_m, w, ones_n, out="f32", path=path)
     sums, _ = oracle.w8a8_gemm(a, ones_m, w, ones_n)
     assert sums.max() == 2 ** 24
     assert np.array_equal(got, sums.astype(np.float32))
@@ -129,27 +128,30 @@ SCALED = [
 ]
 
 
+@pytest.mark.parametrize("path", TILES, ids=TILE_IDS)
 @pytest.mark.parametrize("m,n,k,out,has_bias", SCALED)
-def test_scaled_outputs(m, n, k, out, has_bias):
+def test_scaled_outputs(m, n, k, out, has_bias, path):
     w8 = synth.GemmWorkload("t", m, n, k, 21 + m, out, has_bias)
     a, sa, w, sw, b = synth.gemm_inputs(w8)
-    got, _ = run_gemm(a, sa, w, sw, b, out=out)
+    got, _ = run_gemm(a, sa, w, sw, b, out=out, path=path)
     sums, exact = oracle.w8a8_gemm(a, sa, w, sw, b)
     check_scaled(got, sums, exact, sa[:, None], sw[None, :], None if b is None else b[None, :],
                  out)
 
 
-def test_leading_dims():
+@pytest.mark.parametrize("path", TILES, ids=TILE_IDS)
+def test_leading_dims(path):
     a = codes(3, 7, 2 * 3 * 7, 64)
     w = codes(3, 9, 40, 64)
     sa = synth.f32(3, 8, synth.UNIFORM, 0.01, 0.08, a.shape[0])
     sw = synth.f32(3, 10, synth.UNIFORM, 1e-4, 1e-3, 40)
-    got, _ = run_gemm(a, sa, w, sw, out="f32", lead=(2, 3, 7))
+    got, _ = run_gemm(a, sa, w, sw, out="f32", lead=(2, 3, 7), path=path)
     sums, exact = oracle.w8a8_gemm(a, sa, w, sw)
     check_scaled(got, sums, exact, sa[:, None], sw[None, :], None, "f32")
 
 
-def test_consumes_operator_codes():
+@pytest.mark.parametrize("path", TILES, ids=TILE_IDS)
+def test_consumes_operator_codes(path):
     """The oracle's own AddRmsNormDynamicQuantV2 codes and scales (bf16
     [300, 1024] rows) feed the GEMM on both sides."""
     wl = synth.WORKLOADS["v2_square"]
@@ -162,7 +164,7 @@ def test_consumes_operator_codes():
     w = codes(wl.seed, 9, 384, cols)
     sw = synth.f32(wl.seed, 10, synth.UNIFORM, 1e-4, 1e-3, 384)
     bias = synth.f32(wl.seed, 11, synth.NORMAL, 0.0, 0.1, 384)
-    got, _ = run_gemm(a, sa, w, sw, bias, out="bf16")
+    got, _ = run_gemm(a, sa, w, sw, bias, out="bf16", path=path)
     sums, exact = oracle.w8a8_gemm(a, sa, w, sw, bias)
     check_scaled(got, sums, exact, sa[:, None], sw[None, :], bias[None, :], "bf16")
 
@@ -179,12 +181,13 @@ def sample_positions(m, n, tile, rng, count=6000):
     return rows, cols
 
 
+@pytest.mark.parametrize("path", [adq.PATH_AUTO] + TILES, ids=["auto"] + TILE_IDS)
 @pytest.mark.parametrize("m,n,k,out", [(4100, 3900, 528, "bf16"), (2048, 4096, 1024, "fp16")])
-def test_big_tile_ragged_sampled(m, n, k, out):
+def test_large_ragged_sampled(m, n, k, out, path):
     w8 = synth.GemmWorkload("t", m, n, k, 31, out, True)
     a, sa, w, sw, b = synth.gemm_inputs(w8)
-    got, desc = run_gemm(a, sa, w, sw, b, out=out)
-    assert tile_of(desc) == expected_tile(m, n, cus_of(desc)), desc
+    got, desc = run_gemm(a, sa, w, sw, b, out=out, path=path)
+    assert tile_of(desc) in (128, 256), desc
     assert np.isfinite(got).all(), "output not written"
     rows, cols = sample_positions(m, n, tile_of(desc), np.random.default_rng(m))
     sums, exact = oracle.w8a8_gemm_at(a, sa, w, sw, b, rows, cols)
@@ -196,7 +199,7 @@ def test_full_projection_sampled():
     w8 = synth.GEMM_WORKLOADS["w8a8_gemm"]
     a, sa, w, sw, b = synth.gemm_inputs(w8)
     got, desc = run_gemm(a, sa, w, sw, b, out=w8.out_dtype)
-    assert tile_of(desc) == expected_tile(w8.m, w8.n, cus_of(desc)), desc
+    assert tile_of(desc) in (128, 256), desc
     assert np.isfinite(got).all(), "output not written"
     rows, cols = sample_positions(w8.m, w8.n, tile_of(desc), np.random.default_rng(5))
     sums, exact = oracle.w8a8_gemm_at(a, sa, w, sw, b, rows, cols)
@@ -225,12 +228,24 @@ def test_deterministic():
     assert np.array_equal(g1.view(np.uint32), g2.view(np.uint32))
 
 
-def test_set_path_rejected():
+def test_paths():
     a = torch.zeros(4, 32, dtype=torch.int8, device="cuda")
     w = torch.zeros(8, 32, dtype=torch.int8, device="cuda")
     sa = torch.ones(4, device="cuda")
     sw = torch.ones(8, device="cuda")
     ex, _ = adq.plan_w8a8_gemm(a, sa, w, sw)
-    with pytest.raises(adq.AdqError):
-        ex.set_path(adq.PATH_ROW)
+    assert tile_of(ex.describe()) == 128  # one tile: too few for the large tiles
+    for p in (adq.PATH_ROW, adq.PATH_SPLIT, adq.PATH_GENERIC, 6):
+        with pytest.raises(adq.AdqError):
+            ex.set_path(p)
+    assert ex.set_path(adq.PATH_GEMM_TILE256) == 0 and tile_of(ex.describe()) == 256
+    assert ex.set_path(adq.PATH_AUTO) == 0 and tile_of(ex.describe()) == 128
+    ex.close()
+    # and the operator's executors refuse the GEMM tile paths
+    x = torch.zeros(4, 64, dtype=torch.bfloat16, device="cuda")
+    g = torch.ones(64, dtype=torch.bfloat16, device="cuda")
+    ex, _ = adq.plan_add_rms_norm_dynamic_quant_v2(x, x, g)
+    for p in TILES:
+        with pytest.raises(adq.AdqError):
+            ex.set_path(p)
     ex.close()
