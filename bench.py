@@ -21,7 +21,6 @@ the MI355X dense INT8 MFMA peak.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import math
@@ -51,11 +50,27 @@ def alg_bytes(w, active, rows=None):
     return rows * per_row + params
 
 
-def kernel_source_hash() -> str:
+# Sources that determine each path's kernels and launch plans (a traffic
+# record is valid only for the sources it was measured on).
+_COMMON_SOURCES = ["adq_device.h", "adq_internal.h", "adq_api.cpp"]
+_PATH_SOURCES = {
+    "operator": ["adq_row_impl.h", "adq_row_bf16.hip", "adq_row_f16.hip", "adq_split.hip",
+                 "adq_generic.hip"],
+    "gemm": ["adq_gemm.hip"],
+}
+
+
+def path_of(workload: str) -> str:
+    import synth
+    return "gemm" if workload in synth.GEMM_WORKLOADS else "operator"
+
+
+def kernel_source_hash(workload: str = "v2_outlier") -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "int4_dynamic_quantization_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
+    csrc = os.path.join(ROOT, "int4_dynamic_quantization_amd", "csrc")
+    for name in sorted(_COMMON_SOURCES + _PATH_SOURCES[path_of(workload)]):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -68,7 +83,7 @@ def measured_traffic(workload: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_hash") != kernel_source_hash():
+    if t.get("source_hash") != kernel_source_hash(workload):
         return None
     return t.get("hbm_bytes_per_launch")
 

@@ -8,13 +8,16 @@
 //
 // with the integer sum exact in int32 (|k| <= 2^17 keeps it in range).
 //
-// gfx950 design: a workgroup of 2 x 2 wavefronts computes a (64*TM) x (64*TN)
-// tile; each wavefront owns (32*TM) x (32*TN) outputs as TM x TN blocks of
-// v_mfma_i32_32x32x32_i8.  K advances in steps of BK bytes through a double
-// buffer in LDS: the next step's A and W tiles are loaded from global memory
-// into registers while the current step's MFMAs run, then written to the other
-// buffer; one barrier per step.  LDS rows are padded by 16 bytes so the
-// 16-byte fragment reads of a wavefront hit distinct banks.  Operand
+// Two kernels, both built on v_mfma_i32_32x32x32_i8 with a workgroup of 2 x 2
+// wavefronts: w8a8_kernel (128 x 128 tiles, for problems with few tiles) and
+// w8a8_big_kernel (256 x 256 tiles, described at its definition).
+//
+// w8a8_kernel: each wavefront owns (32*TM) x (32*TN) outputs as TM x TN MFMA
+// blocks.  K advances in steps of BK bytes through a double buffer in LDS:
+// the next step's A and W tiles are loaded from global memory into registers
+// while the current step's MFMAs run, then written to the other buffer; one
+// barrier per step.  LDS rows are padded by 16 bytes so the 16-byte fragment
+// reads of a wavefront hit distinct banks.  Operand
 // fragments (32x32x32 int8): A[i][k] in lane i + 32 * (k / 16), byte k % 16;
 // B[k][j] likewise with j; accumulator element e of lane l is
 // C[(e / 4) * 8 + (l / 32) * 4 + e % 4][l % 32].
@@ -27,8 +30,11 @@
 
 #include "adq_device.h"
 
+#ifndef ADQ_GEMM_BK
+#define ADQ_GEMM_BK 128
+#endif
 #ifndef ADQ_GEMM_STAGES
-#define ADQ_GEMM_STAGES 4
+#define ADQ_GEMM_STAGES 2
 #endif
 
 namespace adq {
@@ -199,31 +205,41 @@ __global__ void __launch_bounds__(256) w8a8_kernel(const GemmArgs g) {
 // (4 x 4 blocks of 32x32x32), which halves the LDS bytes read per MFMA
 // compared with 64 x 64 per wavefront.  Tiles reach LDS through the buffer
 // unit's direct-to-LDS path (buffer_load_dwordx4 ... lds): no staging
-// registers, and a ring of STAGES buffers keeps STAGES - 1 K-steps in flight.
+// registers, and a ring of STAGES buffers of BK bytes of K keeps up to
+// STAGES - 1 K-steps in flight.
 //
 // A direct-to-LDS load writes lane l's 16 bytes at the instruction's LDS base
-// + 16 * l, so a 1 KB segment holds 16 tile rows of BK = 64 bytes (4 chunks
-// per row).  The lane that fills position p of row r fetches chunk
-// c = p ^ h(r) of that row, h(r) = (r >> 2) & 3.  gfx950's LDS serves a
-// 128-bit read in four passes of 16 lanes over 64 four-byte banks; measured
-// with the LDS bank-conflict counter, a pass takes lanes from one half of
-// the wavefront whose index bits 2 and 4 agree in parity (the fits also
-// allow bits 0 and 3 to join that parity).  A fragment read has lane l on
-// row l % 32, one chunk per half, so a pass holds 16 rows whose (r mod 4,
-// h(r)) pairs are all distinct for each of those lane groupings: every
-// pass touches 64 distinct banks.  Without the swizzle (row stride 64 B)
-// a pass hits only 16 banks four times over.
-template <int STAGES>
+// + 16 * l, so a 1 KB segment holds 1024 / BK tile rows of BK / 16 chunks.
+// The lane that fills position p of row r fetches chunk c = p ^ h(r) of that
+// row: h(r) = (r >> 2) & 3 for BK = 64, (r >> 1) & 7 for BK = 128.  gfx950's
+// LDS serves a 128-bit read in four passes of 16 lanes over 64 four-byte
+// banks; measured with the LDS bank-conflict counter, a pass takes lanes
+// from one half of the wavefront whose index bits 2 and 4 agree in parity
+// (the fits also allow bits 0 and 3 to join that parity).  A fragment read
+// has lane l on row l % 32, one chunk per half, so a pass holds 16 rows; with
+// these h every pass touches 64 distinct banks for each of those lane
+// groupings (measured: no conflict cycles).  Without the swizzle a pass hits
+// only 16 (BK = 64) or 8 (BK = 128) banks.
+template <int BK_, int STAGES>
 struct BigShape {
-  static constexpr int BM = 256, BN = 256, BK = 64;
+  static constexpr int BM = 256, BN = 256, BK = BK_;
   static constexpr int SEG = 1024;                       // bytes per direct-load instruction
+  static constexpr int CPR = BK / 16;                    // 16-byte chunks per tile row
+  static constexpr int RPS = SEG / BK;                   // tile rows per segment
   static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;  // 32 KB
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int SEGS_PER_WAVE = A_BYTES / SEG / 4;  // per operand, 4 wavefronts
+  static constexpr int LOADS = 2 * SEGS_PER_WAVE;          // per wavefront per stage
+  static constexpr int NKK = BK / 32;                      // MFMA k-steps per stage
+  static_assert(BK == 64 || BK == 128, "swizzle defined for 64- and 128-byte rows");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
 };
 
-__device__ __forceinline__ int chunk_swizzle(int r) { return (r >> 2) & 3; }
+template <int BK>
+__device__ __forceinline__ int chunk_swizzle(int r) {
+  return BK == 64 ? (r >> 2) & 3 : (r >> 1) & 7;
+}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
@@ -233,9 +249,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int STAGES, int OUT>
+template <int BK, int STAGES, int OUT>
 __global__ void __launch_bounds__(256) w8a8_big_kernel(const GemmArgs g) {
-  using S = BigShape<STAGES>;
+  using S = BigShape<BK, STAGES>;
   __shared__ __attribute__((aligned(1024))) int8_t lds[S::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -263,14 +279,15 @@ __global__ void __launch_bounds__(256) w8a8_big_kernel(const GemmArgs g) {
   const rsrc_t rw = make_rsrc(g.w + n0 * g.k, (uint32_t)(w_rows * g.k));
   constexpr uint32_t kOut = 0x80000000u;
 
-  // this lane's source in each of the wavefront's segments: row r = 16 * seg + lane / 4
-  // (the same rows for A and W), chunk c = (lane % 4) ^ h(r)
+  // this lane's source in each of the wavefront's segments: row
+  // r = RPS * seg + lane / CPR (the same rows for A and W), chunk
+  // c = (lane % CPR) ^ h(r)
   uint32_t src[S::SEGS_PER_WAVE];
   int src_k[S::SEGS_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < S::SEGS_PER_WAVE; ++i) {
-    const int r = 16 * (wave * S::SEGS_PER_WAVE + i) + (lane >> 2);
-    const int c = (lane & 3) ^ chunk_swizzle(r);
+    const int r = S::RPS * (wave * S::SEGS_PER_WAVE + i) + lane / S::CPR;
+    const int c = (lane % S::CPR) ^ chunk_swizzle<BK>(r);
     src[i] = (uint32_t)(r * g.k) + 16u * c;
     src_k[i] = 16 * c;
   }
@@ -295,10 +312,10 @@ __global__ void __launch_bounds__(256) w8a8_big_kernel(const GemmArgs g) {
     for (int j = 0; j < 4; ++j) acc[i][j] = i32x16{};
 
   // fragment addresses (relative to a stage): row R of the A (W) tile, chunk
-  // kk / 16 + lane / 32 at position chunk ^ h(R); h depends on R only through
-  // lane % 32 and the block offset (a multiple of 32), so it is per lane.
+  // 2 * kk + lane / 32 at position chunk ^ h(R); h depends on R only through
+  // lane % 32 (the block offsets are multiples of 32), so it is per lane.
   const int fr = lane & 31;
-  const int hsw = chunk_swizzle(fr);
+  const int hsw = chunk_swizzle<BK>(fr);
   const int fk = lane >> 5;
   int a_off[4], b_off[4];
 #pragma unroll
@@ -326,68 +343,85 @@ __global__ void __launch_bounds__(256) w8a8_big_kernel(const GemmArgs g) {
   // for all of its direct-to-LDS loads, including the later stages in flight.
   // The stage about to be read is awaited explicitly: loads complete in
   // order, so it has landed once no more than the `later` stages issued after
-  // it (2 * SEGS_PER_WAVE loads each) are outstanding.  LDS reads of the
-  // stage being retired complete (lgkmcnt) before the barrier, so after it
-  // that buffer may be refilled.
+  // it (LOADS each) are outstanding.  LDS reads of the stage being retired
+  // complete (lgkmcnt) before the barrier, so after it that buffer may be
+  // refilled.
   auto sync_stage = [&](int64_t later) {
-    constexpr int L = 2 * S::SEGS_PER_WAVE;
-    if (later >= 4) wait_vmcnt<4 * L>();
-    else if (later == 3) wait_vmcnt<3 * L>();
-    else if (later == 2) wait_vmcnt<2 * L>();
-    else if (later == 1) wait_vmcnt<L>();
-    else wait_vmcnt<0>();
+    constexpr int L = S::LOADS;
+    if constexpr (STAGES >= 4) {
+      if (later >= 3) wait_vmcnt<3 * L>();
+      else if (later == 2) wait_vmcnt<2 * L>();
+      else if (later == 1) wait_vmcnt<L>();
+      else wait_vmcnt<0>();
+    } else if constexpr (STAGES == 3) {
+      if (later >= 2) wait_vmcnt<2 * L>();
+      else if (later == 1) wait_vmcnt<L>();
+      else wait_vmcnt<0>();
+    } else {
+      if (later >= 1) wait_vmcnt<L>();
+      else wait_vmcnt<0>();
+    }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     __asm__ __volatile__("" ::: "memory");
   };
   auto min64 = [](int64_t x, int64_t y) { return x < y ? x : y; };
 
-  // prologue: stages 0 .. STAGES-1 in flight; stage 0 visible, its first half read
+  // prologue: stages 0 .. STAGES-1 in flight; stage 0 visible, its first k-step read
 #pragma unroll
   for (int s = 0; s < STAGES; ++s)
     if (s < ksteps) issue(s, s);
-  i32x4 f0a[4], f0b[4], f1a[4], f1b[4];
+  i32x4 fa[2][4], fb[2][4];
   sync_stage(min64(STAGES - 1, ksteps - 1));
-  read(lds, 0, f0a, f0b);
-  // One step: read the second half of stage s while the first half's MFMAs
-  // run; sync on stage s + 1 (issued so far: stages up to s + STAGES - 1);
-  // refill stage s's buffer, which every wavefront has finished reading; read
-  // the first half of stage s + 1 while the second half's MFMAs run.  The
-  // last step is peeled so that every loop iteration has the same waits.
-  // Instruction order inside each half (sched_group_barrier masks: 0x008
+  read(lds, 0, fa[0], fb[0]);
+  // One step = NKK k-steps of 32 over stage s.  Each k-step reads the next
+  // k-step's fragments while its own MFMAs run; the last one first syncs on
+  // stage s + 1 (issued so far: stages up to s + STAGES - 1), reads its first
+  // k-step, and refills stage s's buffer, which every wavefront has finished
+  // reading.  Instruction order is set with sched_group_barrier (masks 0x008
   // MFMA, 0x020 vector-memory read, 0x100 LDS read): the LDS reads and the
-  // direct-to-LDS loads issue one per MFMA, in the shadow of the MFMAs.
-  auto step = [&](int64_t s, bool refill) {
+  // direct-to-LDS loads issue between MFMAs, in their shadow.  The last step
+  // is peeled so that every loop iteration has the same waits.
+  auto step = [&](int64_t s, bool last, bool refill) {
     const int buf = (int)(s % STAGES);
-    read(lds + buf * S::STAGE_BYTES, 1, f1a, f1b);
-    mfma(f0a, f0b);
+    const int8_t* cur = lds + buf * S::STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    sync_stage(min64(STAGES - 2, ksteps - 2 - s));
-    read(lds + (int)((s + 1) % STAGES) * S::STAGE_BYTES, 0, f0a, f0b);
-    if (refill) issue(s + STAGES, buf);
-    mfma(f1a, f1b);
+    for (int kk = 0; kk < S::NKK; ++kk) {
+      const int c = kk & 1, n = c ^ 1;
+      if (kk + 1 < S::NKK) {
+        read(cur, kk + 1, fa[n], fb[n]);
+        mfma(fa[c], fb[c]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-    }
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      } else if (!last) {
+        sync_stage(min64(STAGES - 2, ksteps - 2 - s));
+        read(lds + (int)((s + 1) % STAGES) * S::STAGE_BYTES, 0, fa[n], fb[n]);
+        if (refill) issue(s + STAGES, buf);
+        mfma(fa[c], fb[c]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, S::LOADS / 8, 0);
+        }
+      } else {
+        mfma(fa[c], fb[c]);
+      }
     }
   };
+  static_assert(S::NKK % 2 == 0, "fragment sets alternate within a stage");
   int64_t s = 0;
-  for (; s + STAGES < ksteps; ++s) step(s, true);
-  for (; s + 1 < ksteps; ++s) step(s, false);
-  read(lds + (int)(s % STAGES) * S::STAGE_BYTES, 1, f1a, f1b);
-  mfma(f0a, f0b);
-  mfma(f1a, f1b);
+  for (; s + STAGES < ksteps; ++s) step(s, false, true);
+  for (; s + 1 < ksteps; ++s) step(s, false, false);
+  step(s, true, false);
 
   // ---- epilogue: out = float(acc) * a_scale[row] * w_scale[col] (+ bias[col]).
   // Scales are loaded up front through range-checked buffer loads (0 past the
@@ -438,20 +472,21 @@ __global__ void __launch_bounds__(256) w8a8_big_kernel(const GemmArgs g) {
     }
 }
 
-template <int STAGES, int OUT>
+template <int BK, int STAGES, int OUT>
 hipError_t launch_big(const GemmArgs& g, hipStream_t s) {
   const int64_t tiles = ((g.m + 255) / 256) * ((g.n + 255) / 256);
   const int64_t grid = (tiles + kXcdCount - 1) / kXcdCount * kXcdCount;
-  hipLaunchKernelGGL((w8a8_big_kernel<STAGES, OUT>), dim3((unsigned)grid), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((w8a8_big_kernel<BK, STAGES, OUT>), dim3((unsigned)grid), dim3(256), 0, s,
+                     g);
   return hipGetLastError();
 }
 
-template <int STAGES>
+template <int BK, int STAGES>
 hipError_t launch_big_out(const GemmArgs& g, hipStream_t s) {
   switch (g.out_type) {
-    case kGemmOutF32: return launch_big<STAGES, kGemmOutF32>(g, s);
-    case kGemmOutBF16: return launch_big<STAGES, kGemmOutBF16>(g, s);
-    case kGemmOutF16: return launch_big<STAGES, kGemmOutF16>(g, s);
+    case kGemmOutF32: return launch_big<BK, STAGES, kGemmOutF32>(g, s);
+    case kGemmOutBF16: return launch_big<BK, STAGES, kGemmOutBF16>(g, s);
+    case kGemmOutF16: return launch_big<BK, STAGES, kGemmOutF16>(g, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -481,7 +516,7 @@ hipError_t launch_out(const GemmArgs& g, hipStream_t s) {
 hipError_t launch_w8a8(const GemmArgs& g, int tile, hipStream_t stream) {
   switch (tile) {
     case kGemmTile128: return launch_out<2, 2, 128>(g, stream);
-    case kGemmTile256: return launch_big_out<ADQ_GEMM_STAGES>(g, stream);
+    case kGemmTile256: return launch_big_out<ADQ_GEMM_BK, ADQ_GEMM_STAGES>(g, stream);
     default: return hipErrorInvalidValue;
   }
 }
