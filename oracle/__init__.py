@@ -8,7 +8,7 @@ at a time); this module only marshals numpy arrays into it.
 
 Formulas followed: "aclnnAddRmsNormDynamicQuantV2", Formula and
 Constraints sections; "aclnnRmsNormDynamicQuant", formula section
-(计算公式).  See the header of ``adq_oracle.c`` for every reading taken
+(计算公式); "aclnnAddLora", Formulas.  See the header of ``adq_oracle.c`` for every reading taken
 where the pages are silent.
 
 Pins (what checks this oracle against something other than itself) are in
@@ -63,6 +63,9 @@ def _configure(lib):
     lib.oracle_pack_int4.restype = ci
     lib.oracle_w8a8_gemm_at.argtypes = [i64, p, p, i64, p, p, p, p, p, p, p]
     lib.oracle_w8a8_gemm_at.restype = ci
+    lib.oracle_add_lora.argtypes = [i64, i64, i64, i64, i64, i64, i64, ci, p, p, p, p, p, i64,
+                                    ctypes.c_double, i64, i64, p, p, p, p]
+    lib.oracle_add_lora.restype = ci
     return lib
 
 
@@ -231,3 +234,36 @@ def w8a8_gemm(a, a_scale, w, w_scale, bias=None):
     cols = np.tile(np.arange(n), m)
     sums, out = w8a8_gemm_at(a, a_scale, w, w_scale, bias, rows, cols)
     return sums.reshape(m, n), out.reshape(m, n)
+
+
+def add_lora(y, x, weight_b, indices, weight_a=None, layer=0, scale=1.0, y_offset=0,
+             dtype="bf16", rows=None, want_pre=True):
+    """AddLora ("aclnnAddLora", Formulas) on host arrays of 16-bit storage
+    patterns: y [B, h3], x [B, h1], weight_a [W, L, h1, rank] or None,
+    weight_b [W, L, rank, h2], indices [B] int32.  Returns (out [n, h3]
+    storage patterns, pre [n, h2] slice values before rounding) for the
+    requested rows (all when rows is None)."""
+    y = np.ascontiguousarray(y, dtype=np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    wb = np.ascontiguousarray(weight_b, dtype=np.uint16)
+    wa = None if weight_a is None else np.ascontiguousarray(weight_a, dtype=np.uint16)
+    idx = np.ascontiguousarray(indices, dtype=np.int32).reshape(-1)
+    nrows, h3 = y.shape
+    h1 = x.shape[1]
+    w, nl, rank, h2 = wb.shape
+    if x.shape[0] != nrows or idx.size != nrows:
+        raise ValueError("x, y and indices disagree on the number of rows")
+    if wa is not None and wa.shape != (w, nl, h1, rank):
+        raise ValueError("weight_a must be [W, L, h1, rank]")
+    sel = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+    n = nrows if sel is None else sel.size
+    out = np.empty((n, h3), np.uint16)
+    pre = np.empty((n, h2), np.float64) if want_pre else None
+    work = np.empty(rank, np.float64)
+    rc = _load().oracle_add_lora(
+        nrows, h1, rank, h2, h3, w, nl, DTYPES[dtype], _ptr(y), _ptr(x), _ptr(wa), _ptr(wb),
+        _ptr(idx), int(layer), float(scale), int(y_offset), n, _ptr(sel), _ptr(out), _ptr(pre),
+        _ptr(work))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out, pre

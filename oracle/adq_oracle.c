@@ -1,5 +1,6 @@
 /*
- * CPU oracle for fused (Add)RmsNorm + per-row symmetric dynamic quantization.
+ * CPU oracle for fused (Add)RmsNorm + per-row symmetric dynamic quantization,
+ * the INT8 GEMM that consumes its codes, and AddLora.
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain, obviously correct
  * definition that the GPU library is checked against.  Only the test suite,
@@ -16,6 +17,10 @@
  *    the Constraints section's rules on outputMask and the smooth scales.
  *  - "aclnnRmsNormDynamicQuant", formula section (计算公式): the single-input
  *    form (no add, one output, optional smoothScales, max_val 127 for INT8).
+ *  - "aclnnAddLora", Formulas: grouped shrink / expand and slice-accumulate
+ *    (readings listed at oracle_add_lora below).
+ *  - The INT8 GEMM that consumes the quantized rows is not on the pages; it
+ *    is defined from the V2 Formula (see oracle_w8a8_gemm_at).
  *
  * Readings taken where the pages are silent (each one is also listed in the
  * design notes of the repository):
@@ -251,6 +256,77 @@ int oracle_w8a8_gemm_at(int64_t count, const int64_t* mi, const int64_t* ni, int
     if (out)
       out[t] = (double)s * (double)a_scale[mi[t]] * (double)w_scale[ni[t]] +
                (bias ? (double)bias[ni[t]] : 0.0);
+  }
+  return 0;
+}
+
+/* --- AddLora ------------------------------------------------------------- */
+
+/*
+ * "aclnnAddLora", Formulas: rows of x are grouped by their index in
+ * `indices`; for each group i the shrink Z1 = x_i . weightA[i, layerIdx]
+ * and the expand Z2 = Z1 . weightB[i, layerIdx] x scale are formed, and the
+ * result is accumulated into the slice y[:, yOffset : yOffset + ySliceSize]
+ * to give out.  Grouping only batches rows that share weights; row by row
+ * the definition is, for a row b with group g = indices[b]:
+ *   Z1[r]  = sum_k x[b, k] * A[g, layer, k, r]      (A is [W, L, h1, rank])
+ *   Z2[j]  = (sum_r Z1[r] * B[g, layer, r, j]) * scale   (B is [W, L, rank, h2])
+ *   out[b, y_offset + j] = y[b, y_offset + j] + Z2[j],  j < h2
+ *   out[b, c] = y[b, c] for every other column c of the h3-wide row.
+ * Readings taken where the page is silent (its parameter tables are lost):
+ *  - weightA absent: the shrink is skipped and Z1 = x[b, :] (h1 == rank);
+ *  - a row whose index lies outside [0, W) gets no contribution (out = y);
+ *  - arithmetic is real-valued: double throughout, out rounded once to the
+ *    storage type; scale is applied as the float nearest the given value.
+ * Rows to compute: rows[0 .. count) (all `nrows` rows when rows is NULL).
+ * `pre` (optional, [count, h2]) receives the slice values before rounding.
+ * `work` holds rank doubles.
+ */
+int oracle_add_lora(int64_t nrows, int64_t h1, int64_t rank, int64_t h2, int64_t h3, int64_t w,
+                    int64_t l, int dtype, const uint16_t* y, const uint16_t* x,
+                    const uint16_t* wa, const uint16_t* wb, const int32_t* indices,
+                    int64_t layer, double scale, int64_t y_offset, int64_t count,
+                    const int64_t* rows, uint16_t* out, double* pre, double* work) {
+  if (nrows <= 0 || h1 <= 0 || rank <= 0 || h2 <= 0 || h3 <= 0 || w <= 0 || l <= 0) return -1;
+  if (dtype != ORACLE_BF16 && dtype != ORACLE_F16) return -1;
+  if (!y || !x || !wb || !indices || !out || !work) return -1;
+  if (layer < 0 || layer >= l || y_offset < 0 || y_offset + h2 > h3) return -1;
+  if (!wa && h1 != rank) return -1;
+  const double s = (double)(float)scale;
+  const int64_t n = rows ? count : nrows;
+  for (int64_t t = 0; t < n; ++t) {
+    const int64_t b = rows ? rows[t] : t;
+    if (b < 0 || b >= nrows) return -1;
+    const uint16_t* yr = y + b * h3;
+    uint16_t* o = out + t * h3;
+    for (int64_t c = 0; c < h3; ++c) o[c] = yr[c];
+    const int64_t g = indices[b];
+    const int valid = g >= 0 && g < w;
+    if (valid) {
+      const uint16_t* xr = x + b * h1;
+      for (int64_t r = 0; r < rank; ++r) {
+        double z = 0.0;
+        if (wa) {
+          const uint16_t* a = wa + ((g * l + layer) * h1) * rank;
+          for (int64_t k = 0; k < h1; ++k)
+            z += oracle_storage_value(xr[k], dtype) * oracle_storage_value(a[k * rank + r], dtype);
+        } else {
+          z = oracle_storage_value(xr[r], dtype);
+        }
+        work[r] = z;
+      }
+    }
+    const uint16_t* bm = valid ? wb + ((g * l + layer) * rank) * h2 : NULL;
+    for (int64_t j = 0; j < h2; ++j) {
+      double v = oracle_storage_value(yr[y_offset + j], dtype);
+      if (valid) {
+        double z2 = 0.0;
+        for (int64_t r = 0; r < rank; ++r) z2 += work[r] * oracle_storage_value(bm[r * h2 + j], dtype);
+        v += z2 * s;
+        o[y_offset + j] = oracle_round_to_storage(v, dtype);
+      }
+      if (pre) pre[t * h2 + j] = v;
+    }
   }
   return 0;
 }

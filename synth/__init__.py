@@ -38,7 +38,8 @@ _LIB = os.path.join(_HERE, "libsynth_gen.so")
 DTYPES = {"bf16": 0, "fp16": 1}
 NORMAL, UNIFORM = 0, 1
 TID = {"x1": 0, "x2": 1, "gamma": 2, "beta": 3, "smooth1": 4, "smooth2": 5, "outlier": 6,
-       "a_codes": 7, "a_scale": 8, "w_codes": 9, "w_scale": 10, "bias": 11}
+       "a_codes": 7, "a_scale": 8, "w_codes": 9, "w_scale": 10, "bias": 11,
+       "lora_x": 12, "lora_y": 13, "lora_a": 14, "lora_b": 15, "lora_idx": 16}
 
 _lib = None
 
@@ -76,6 +77,10 @@ def _load():
             ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_double, ctypes.c_double,
             ctypes.c_int64, ctypes.c_void_p]
         lib.synth_fill_f32.restype = ctypes.c_int
+        lib.synth_fill_i32.argtypes = [
+            ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_void_p]
+        lib.synth_fill_i32.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -227,3 +232,66 @@ def gemm_inputs(w: GemmWorkload, m=None, lo=-127, hi=127):
     sw = f32(w.seed, TID["w_scale"], UNIFORM, 1e-4, 1e-3, w.n)
     b = f32(w.seed, TID["bias"], NORMAL, 0.0, 0.1, w.n) if w.has_bias else None
     return a, sa, wq, sw, b
+
+
+def int32s(seed, tid, lo, hi, n) -> np.ndarray:
+    """Uniform integers in [lo, hi], int32 [n]."""
+    out = np.empty(n, dtype=np.int32)
+    if _load().synth_fill_i32(int(seed), int(tid), int(lo), int(hi), int(n),
+                              out.ctypes.data) != 0:
+        raise ValueError("synth_fill_i32 rejected its arguments")
+    return out
+
+
+@dataclass(frozen=True)
+class LoraWorkload:
+    """AddLora ("aclnnAddLora"): y [rows, h3] accumulates, in its columns
+    [y_offset, y_offset + h2), scale * (x . A[g, layer]) . B[g, layer] for
+    the adapter g = indices[row]; A is [w, l, h1, rank], B [w, l, rank, h2]."""
+    name: str
+    rows: int
+    h1: int
+    rank: int
+    h2: int
+    h3: int
+    w: int
+    l: int
+    layer: int
+    y_offset: int
+    scale: float
+    dtype: str
+    seed: int
+    idx_lo: int = 0          # indices uniform in [idx_lo, idx_hi]; outside [0, w) = no adapter
+    idx_hi: int | None = None
+    has_a: bool = True
+
+
+LORA_WORKLOADS = {
+    # a prefill batch of 4096 tokens over 8 adapters (all 32 layers' weights
+    # resident), the k slice of a fused qkv output
+    "lora_prefill": LoraWorkload("lora_prefill", 4096, 4096, 16, 4096, 12288, 8, 32, 7, 4096,
+                                 0.5, "bf16", 6),
+    # decode: 64 tokens, fp16
+    "lora_decode": LoraWorkload("lora_decode", 64, 4096, 16, 4096, 12288, 8, 32, 7, 4096, 0.5,
+                                "fp16", 7),
+    # small case with ragged sizes and indices outside [0, w)
+    "lora_small": LoraWorkload("lora_small", 300, 512, 16, 384, 1024, 5, 3, 2, 128, 0.25,
+                               "bf16", 8, -1, 5),
+}
+
+
+def lora_inputs(wl: LoraWorkload, rows=None):
+    """y, x (N(0, 1)), weight_a (N(0, 0.02), or None), weight_b (N(0, 0.02))
+    as 16-bit storage patterns, and indices (int32)."""
+    rows = wl.rows if rows is None else rows
+    hi = wl.w - 1 if wl.idx_hi is None else wl.idx_hi
+    y = fill(wl.seed, TID["lora_y"], NORMAL, 0.0, 1.0, wl.dtype, rows, wl.h3)
+    x = fill(wl.seed, TID["lora_x"], NORMAL, 0.0, 1.0, wl.dtype, rows, wl.h1)
+    wa = None
+    if wl.has_a:
+        wa = fill(wl.seed, TID["lora_a"], NORMAL, 0.0, 0.02, wl.dtype, wl.w * wl.l * wl.h1,
+                  wl.rank).reshape(wl.w, wl.l, wl.h1, wl.rank)
+    wb = fill(wl.seed, TID["lora_b"], NORMAL, 0.0, 0.02, wl.dtype, wl.w * wl.l * wl.rank,
+              wl.h2).reshape(wl.w, wl.l, wl.rank, wl.h2)
+    idx = int32s(wl.seed, TID["lora_idx"], wl.idx_lo, hi, rows)
+    return y, x, wa, wb, idx

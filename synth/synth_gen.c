@@ -215,3 +215,12 @@ int synth_fill_f32(uint64_t seed, uint32_t tid, int dist, double p0, double p1, 
   for (int64_t i = 0; i < n; ++i) out[i] = (float)sample(base, (uint64_t)i, dist, p0, p1);
   return 0;
 }
+
+/* n int32 values of the tensor (seed, tid), uniform in [lo, hi] (draw modulo hi - lo + 1). */
+int synth_fill_i32(uint64_t seed, uint32_t tid, int64_t lo, int64_t hi, int64_t n, int32_t* out) {
+  if (n < 0 || !out || lo > hi || lo < INT32_MIN || hi > INT32_MAX) return -1;
+  uint64_t base = stream_base(seed, tid);
+  uint64_t span = (uint64_t)(hi - lo + 1);
+  for (int64_t i = 0; i < n; ++i) out[i] = (int32_t)(lo + (int64_t)(draw(base, (uint64_t)i) % span));
+  return 0;
+}

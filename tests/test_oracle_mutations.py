@@ -13,6 +13,7 @@ import subprocess
 import pytest
 
 import oracle
+import test_oracle_lora_pins as lora_pins
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
@@ -41,6 +42,24 @@ MUTANTS = [
     ("xOut truncated", "double q = nearbyint(m / quantum);", "double q = floor(m / quantum);"),
     ("no clamp of the scale to float", "const float sc = (float)(m / Q);",
      "const double sc = m / Q;"),
+    # AddLora
+    ("lora: layer of weightA ignored", "const uint16_t* a = wa + ((g * l + layer) * h1) * rank;",
+     "const uint16_t* a = wa + ((g * l + 0) * h1) * rank;"),
+    ("lora: layer of weightB ignored", "wb + ((g * l + layer) * rank) * h2",
+     "wb + ((g * l + 0) * rank) * h2"),
+    ("lora: weightA read transposed", "oracle_storage_value(a[k * rank + r], dtype)",
+     "oracle_storage_value(a[(k * rank + r) % h1 * rank + (k * rank + r) / h1], dtype)"),
+    ("lora: weightB row and column swapped", "oracle_storage_value(bm[r * h2 + j], dtype)",
+     "oracle_storage_value(bm[(r * h2 + j) % rank * h2 + (r * h2 + j) / rank], dtype)"),
+    ("lora: y not accumulated", "double v = oracle_storage_value(yr[y_offset + j], dtype);",
+     "double v = 0.0;"),
+    ("lora: scale not applied", "v += z2 * s;", "v += z2;"),
+    ("lora: scale kept in double", "const double s = (double)(float)scale;",
+     "const double s = scale;"),
+    ("lora: last adapter treated as none", "const int valid = g >= 0 && g < w;",
+     "const int valid = g >= 0 && g < w - 1;"),
+    ("lora: shrink skipped", "z = oracle_storage_value(xr[r], dtype);",
+     "z = oracle_storage_value(xr[rank - 1 - r], dtype);"),
 ]
 
 
@@ -57,6 +76,14 @@ def _battery():
     ]
     checks += [(f"brute force {s}", lambda s=s: pins.test_brute_force_tiny_rows(s))
                for s in range(6)]
+    checks += [
+        ("lora worked", lora_pins.test_lora_worked_example),
+        ("lora worked without weightA", lora_pins.test_lora_worked_example_without_weight_a),
+        ("lora closed form", lora_pins.test_lora_identity_expand_closed_form),
+        ("lora copies", lora_pins.test_lora_columns_outside_slice_and_unassigned_rows_are_copied),
+    ]
+    checks += [(f"lora numpy {dt} {a}", lambda dt=dt, a=a: lora_pins.test_lora_matches_numpy_products(dt, a))
+               for dt, a in (("bf16", True), ("fp16", True), ("bf16", False))]
     return checks
 
 
