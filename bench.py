@@ -16,7 +16,9 @@ workload on the host cores.
 ``--workload w8a8_gemm`` instead times the INT8 GEMM that consumes the
 quantized rows (16384 x 8192 codes with per-row scales through an
 8192 -> 8192 projection with per-column weight scales, bf16 out) against
-the MI355X dense INT8 MFMA peak.
+the MI355X dense INT8 MFMA peak.  ``--workload lora_prefill`` (or
+lora_decode) times AddLora accumulating into y in place, against HBM
+bandwidth.
 """
 from __future__ import annotations
 
@@ -57,12 +59,15 @@ _PATH_SOURCES = {
     "operator": ["adq_row_impl.h", "adq_row_bf16.hip", "adq_row_f16.hip", "adq_split.hip",
                  "adq_generic.hip"],
     "gemm": ["adq_gemm.hip"],
+    "lora": ["adq_lora.hip"],
 }
 
 
 def path_of(workload: str) -> str:
     import synth
-    return "gemm" if workload in synth.GEMM_WORKLOADS else "operator"
+    if workload in synth.GEMM_WORKLOADS:
+        return "gemm"
+    return "lora" if workload in synth.LORA_WORKLOADS else "operator"
 
 
 def kernel_source_hash(workload: str = "v2_outlier") -> str:
@@ -167,6 +172,9 @@ def main():
 
     if args.workload in synth.GEMM_WORKLOADS:
         bench_gemm(args, torch, adq, synth)
+        return
+    if args.workload in synth.LORA_WORKLOADS:
+        bench_lora(args, torch, adq, synth)
         return
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -329,6 +337,110 @@ def bench_gemm(args, torch, adq, synth) -> None:
     }
     ex.close()
     result["cpu_baseline"] = (gemm_cpu_baseline(a, sa, wq, sw, b, w8.k, args.cpu_budget)
+                              if args.cpu_budget > 0 else None)
+    print(json.dumps(result), flush=True)
+
+
+def lora_alg_bytes(wl, idx, in_place=True) -> int:
+    """Bytes AddLora must move: x read, y's slice read and written (the whole
+    of y read and out written when out is not y), the index vector, and the
+    layer's weights of each adapter that some row uses."""
+    import numpy as np
+    b = 2
+    used = len(set(int(g) for g in np.unique(idx) if 0 <= g < wl.w))
+    per_adapter = (wl.h1 * wl.rank if wl.has_a else 0) + wl.rank * wl.h2
+    rows_with = int(((idx >= 0) & (idx < wl.w)).sum())
+    y_bytes = 2 * rows_with * wl.h2 * b if in_place else 2 * wl.rows * wl.h3 * b
+    return (rows_with * wl.h1 * b + y_bytes + 4 * wl.rows + used * per_adapter * b)
+
+
+def lora_cpu_baseline(wl, host, alg_rows_bytes, budget_s: float):
+    """The oracle (plain C, one thread) on the first rows of the same inputs."""
+    import oracle
+    y, x, wa, wb, idx = host
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.add_lora(y[:rows], x[:rows], wb, idx[:rows], wa, wl.layer, wl.scale, wl.y_offset,
+                        wl.dtype, want_pre=False)
+        return time.perf_counter() - t0
+
+    pilot = min(wl.rows, 4)
+    t = run(pilot)
+    rows = int(max(pilot, min(wl.rows, budget_s / max(t / pilot, 1e-9))))
+    t = run(rows)
+    gbs = alg_rows_bytes * rows / wl.rows / t / 1e9
+    return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} of {wl.rows} rows of the same seeded inputs, {t:.2f} s, "
+                      f"single-threaded plain-C fp64 oracle ({rows / t:.1f} rows/s)"}
+
+
+def bench_lora(args, torch, adq, synth) -> None:
+    """One step = one AddLora launch accumulating into y in place."""
+    wl = synth.LORA_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    host = synth.lora_inputs(wl)
+    y, x, wa, wb, idx = host
+    td = {"bf16": torch.bfloat16, "fp16": torch.float16}[wl.dtype]
+    d = lambda a: None if a is None else torch.from_numpy(a.view("int16")).view(td).to(dev)
+    alg = lora_alg_bytes(wl, idx)
+    n_sets = 1 if args.no_rotate else max(1, math.ceil(512e6 / alg))
+    tw = (d(wb), d(wa), torch.from_numpy(idx).to(dev))
+    cases = []
+    for _ in range(n_sets):
+        ty, tx = d(y), d(x)
+        ex, _ = adq.plan_add_lora(ty, tx, tw[0], tw[2], tw[1], wl.layer, wl.scale, wl.y_offset,
+                                  out=ty)
+        cases.append((ex, ty, tx))
+    print(f"[bench] workload {wl.name}: {alg / 1e6:.1f} MB per launch, {n_sets} rotating set(s); "
+          f"plan: {cases[0][0].describe()}", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        cases[i % n_sets][0].run(None, stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        cases[i % n_sets][0].run(None, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    gbs = alg / (ms * 1e-3) / 1e9
+    print(f"[bench] {args.steps} launches: avg {ms * 1e3:.1f} us per launch, "
+          f"wall {wall * 1e3:.1f} ms", file=sys.stderr, flush=True)
+    result = {
+        "metric": f"achieved HBM GB/s (% of peak), AddLora {wl.dtype} {wl.rows} rows "
+                  f"{wl.h1}->{wl.rank}->{wl.h2}",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "op": "AddLora (in place)", "rows": wl.rows, "h1": wl.h1,
+            "rank": wl.rank, "h2": wl.h2, "h3": wl.h3, "adapters": wl.w, "layers": wl.l,
+            "storage": wl.dtype, "algorithmic_bytes_per_step": alg,
+            "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "parallelism": "single GPU", "plan": cases[0][0].describe(),
+            "cache": "warm (one set)" if n_sets == 1 else f"cold ({n_sets} rotating sets)",
+        },
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(wl.name)},
+    }
+    for ex, _, _ in cases:
+        ex.close()
+    result["cpu_baseline"] = (lora_cpu_baseline(wl, host, alg, args.cpu_budget)
                               if args.cpu_budget > 0 else None)
     print(json.dumps(result), flush=True)
 

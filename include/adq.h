@@ -63,7 +63,8 @@ typedef enum adq_dtype {
   ADQ_BF16 = 2,
   ADQ_F32 = 3,
   ADQ_INT8 = 4,
-  ADQ_INT4X2 = 5 /* two INT4 codes per byte, even column in the low nibble */
+  ADQ_INT4X2 = 5, /* two INT4 codes per byte, even column in the low nibble */
+  ADQ_INT32 = 6   /* adapter indices of AddLora */
 } adq_dtype;
 
 #define ADQ_MAX_DIMS 8
@@ -177,6 +178,44 @@ adq_status adq_w8a8_gemm_get_workspace_size(const adq_tensor* a, const adq_tenso
 adq_status adq_w8a8_gemm(void* workspace, uint64_t workspace_size, adq_executor* executor,
                          void* hip_stream);
 
+/*
+ * AddLora ("aclnnAddLora", Formulas): rows of x are grouped by their adapter
+ * index; for each row b with g = indices[b] in [0, W)
+ *
+ *   Z1 = x[b, :] . weight_a[g, layer_idx]          (shrink, h1 -> rank)
+ *   Z2 = Z1 . weight_b[g, layer_idx] * scale       (expand, rank -> h2)
+ *   out[b, y_offset + j] = y[b, y_offset + j] + Z2[j],  j < y_slice_size
+ *
+ * and every other element of out equals y (rows with an index outside
+ * [0, W) get no contribution).
+ *
+ * y          [..., h3] F16 or BF16
+ * x          [..., h1] same dtype, same leading dimensions (rows) as y
+ * weight_b   [W, L, rank, h2] same dtype, h2 == y_slice_size
+ * indices    ADQ_INT32 with one value per row (any shape)
+ * weight_a   [W, L, h1, rank] same dtype, or NULL: the shrink is skipped and
+ *            Z1 = x[b, :] (then h1 must equal rank)
+ * layer_idx  in [0, L); scale finite (applied as the nearest float);
+ *            0 <= y_offset and y_offset + y_slice_size <= h3
+ * out        same shape and dtype as y; either y itself (in place: only the
+ *            slice of rows with an adapter is written) or memory that does
+ *            not overlap y.
+ * Arithmetic in fp32 (Z1 is not rounded between the two products); each
+ * slice value is rounded once to the storage type.  W <= 2048, rank <= 1024.
+ * Workspace size is 0.  Errors as for the other phase-1 calls.
+ */
+adq_status adq_add_lora_get_workspace_size(const adq_tensor* y, const adq_tensor* x,
+                                           const adq_tensor* weight_b,
+                                           const adq_tensor* indices,
+                                           const adq_tensor* weight_a, int64_t layer_idx,
+                                           double scale, int64_t y_offset,
+                                           int64_t y_slice_size, const adq_tensor* out,
+                                           uint64_t* workspace_size, adq_executor** executor);
+
+/* AddLora phase 2; as adq_add_rms_norm_dynamic_quant_v2. */
+adq_status adq_add_lora(void* workspace, uint64_t workspace_size, adq_executor* executor,
+                        void* hip_stream);
+
 /* Free an executor (NULL is a no-op).  Launched work is not affected. */
 void adq_executor_destroy(adq_executor* executor);
 
@@ -190,6 +229,10 @@ void adq_executor_destroy(adq_executor* executor);
  * ADQ_PATH_GEMM_TILE256 (256 x 256 tiles); AUTO takes 256 once the
  * 256-tiles cover the compute units.  Either accepts any valid GEMM shape;
  * the operator paths are rejected for a GEMM executor and vice versa.
+ * AddLora executors: AUTO (the tiled kernel when the shapes and alignments
+ * allow it: h1 % 8 == 0, rank % 16 == 0 and <= 64, h2, h3 and y_offset
+ * multiples of 4, aligned tensors) or ADQ_PATH_GENERIC (one workgroup per
+ * row, any shape).
  */
 typedef enum adq_path {
   ADQ_PATH_AUTO = 0,

@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libaddrmsnorm_dq.so")
 
 # adq_dtype
-F16, BF16, F32, INT8, INT4X2 = 1, 2, 3, 4, 5
+F16, BF16, F32, INT8, INT4X2, INT32 = 1, 2, 3, 4, 5, 6
 # adq_status
 OK, ERR_NULLPTR, ERR_PARAM_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_RUNTIME = range(6)
 STATUS_NAMES = {0: "ADQ_OK", 1: "ADQ_ERR_NULLPTR", 2: "ADQ_ERR_PARAM_INVALID",
@@ -36,6 +36,8 @@ EXPORTED = (
     "adq_rms_norm_dynamic_quant",
     "adq_w8a8_gemm_get_workspace_size",
     "adq_w8a8_gemm",
+    "adq_add_lora_get_workspace_size",
+    "adq_add_lora",
     "adq_executor_destroy",
     "adq_executor_set_path",
     "adq_executor_describe",
@@ -90,6 +92,10 @@ def _load():
     lib.adq_rms_norm_dynamic_quant.argtypes = [vp, ctypes.c_uint64, vp, vp]
     lib.adq_w8a8_gemm_get_workspace_size.argtypes = [P, P, P, P, P, P, u64p, exp]
     lib.adq_w8a8_gemm.argtypes = [vp, ctypes.c_uint64, vp, vp]
+    i64 = ctypes.c_int64
+    lib.adq_add_lora_get_workspace_size.argtypes = [P, P, P, P, P, i64, ctypes.c_double, i64, i64,
+                                                    P, u64p, exp]
+    lib.adq_add_lora.argtypes = [vp, ctypes.c_uint64, vp, vp]
     lib.adq_executor_destroy.argtypes = [vp]
     lib.adq_executor_destroy.restype = None
     lib.adq_executor_set_path.argtypes = [vp, ctypes.c_int32, u64p]
@@ -100,7 +106,8 @@ def _load():
     for name in ("adq_add_rms_norm_dynamic_quant_v2_get_workspace_size",
                  "adq_add_rms_norm_dynamic_quant_v2",
                  "adq_rms_norm_dynamic_quant_get_workspace_size", "adq_rms_norm_dynamic_quant",
-                 "adq_w8a8_gemm_get_workspace_size", "adq_w8a8_gemm", "adq_executor_set_path"):
+                 "adq_w8a8_gemm_get_workspace_size", "adq_w8a8_gemm",
+                 "adq_add_lora_get_workspace_size", "adq_add_lora", "adq_executor_set_path"):
         getattr(lib, name).restype = ctypes.c_int
     runtimes = _hip_runtimes_mapped()
     if len(runtimes) > 1:
@@ -150,7 +157,7 @@ def describe_tensor(t, dtype: int | None = None, shape=None) -> Tensor:
         raise ValueError("tensors must be contiguous (row-major)")
     if dtype is None:
         dtype = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32,
-                 torch.int8: INT8, torch.uint8: INT4X2}.get(t.dtype)
+                 torch.int8: INT8, torch.uint8: INT4X2, torch.int32: INT32}.get(t.dtype)
         if dtype is None:
             raise ValueError(f"unsupported torch dtype {t.dtype}")
     shape = tuple(t.shape) if shape is None else tuple(shape)
@@ -195,7 +202,7 @@ class Executor:
         s = None if stream is None else stream.cuda_stream
         fn = {"v2": _lib().adq_add_rms_norm_dynamic_quant_v2,
               "rmsnorm": _lib().adq_rms_norm_dynamic_quant,
-              "gemm": _lib().adq_w8a8_gemm}[self.op]
+              "gemm": _lib().adq_w8a8_gemm, "lora": _lib().adq_add_lora}[self.op]
         _check(fn(ws_ptr, ws_size, self.handle, s))
 
     def close(self) -> None:
@@ -371,6 +378,43 @@ def plan_w8a8_gemm(a, a_scale, w, w_scale, bias=None, out_dtype=None, out=None,
 def w8a8_gemm(a, a_scale, w, w_scale, bias=None, out_dtype=None, stream=None):
     """Both GEMM phases on torch tensors; returns out."""
     ex, out = plan_w8a8_gemm(a, a_scale, w, w_scale, bias, out_dtype)
+    ex.run(None, stream)
+    ex.close()
+    return out
+
+
+def add_lora_get_workspace_size(y, x, weight_b, indices, weight_a, layer_idx, scale, y_offset,
+                                y_slice_size, out) -> Executor:
+    """AddLora phase 1 on adq_tensor descriptors (weight_a may be None)."""
+    ws = ctypes.c_uint64(0)
+    handle = ctypes.c_void_p(None)
+    _check(_lib().adq_add_lora_get_workspace_size(
+        _ref(y), _ref(x), _ref(weight_b), _ref(indices), _ref(weight_a), int(layer_idx),
+        float(scale), int(y_offset), int(y_slice_size), _ref(out), ctypes.byref(ws),
+        ctypes.byref(handle)))
+    return Executor(handle, ws.value, "lora", (y, x, weight_b, indices, weight_a, out))
+
+
+def plan_add_lora(y, x, weight_b, indices, weight_a=None, layer_idx=0, scale=1.0, y_offset=0,
+                  out=None, path=PATH_AUTO):
+    """AddLora phase 1 on torch tensors.  out=None allocates a new tensor;
+    pass out=y to accumulate in place."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(y)
+    d = describe_tensor
+    ex = add_lora_get_workspace_size(d(y), d(x), d(weight_b), d(indices), d(weight_a), layer_idx,
+                                     scale, y_offset, weight_b.shape[-1], d(out))
+    ex._keep = (ex._keep, y, x, weight_b, indices, weight_a, out)
+    if path != PATH_AUTO:
+        ex.set_path(path)
+    return ex, out
+
+
+def add_lora(y, x, weight_b, indices, weight_a=None, layer_idx=0, scale=1.0, y_offset=0,
+             out=None, stream=None):
+    """Both AddLora phases on torch tensors; returns out."""
+    ex, out = plan_add_lora(y, x, weight_b, indices, weight_a, layer_idx, scale, y_offset, out)
     ex.run(None, stream)
     ex.close()
     return out

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libaddrmsnorm_dq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["adq_api.cpp", "adq_row_bf16.hip", "adq_row_f16.hip", "adq_generic.hip",
-           "adq_split.hip", "adq_gemm.hip"]
+           "adq_split.hip", "adq_gemm.hip", "adq_lora.hip"]
 COMMON = ["-O3", "-fPIC", "-std=c++20", "-Wall", "-Wextra", "-Wno-unused-parameter",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 # Device code: gfx950 only, with packed-fp32 (v_pk_*_f32) generation

@@ -59,7 +59,7 @@ adq_status ok() {
   return ADQ_OK;
 }
 
-enum Op { kOpV2 = 1, kOpRmsNorm = 2, kOpGemm = 3 };
+enum Op { kOpV2 = 1, kOpRmsNorm = 2, kOpGemm = 3, kOpLora = 4 };
 
 }  // namespace
 
@@ -69,6 +69,8 @@ struct adq_executor {
   Args args;
   adq::GemmArgs gemm;
   int gemm_tile;
+  adq::LoraArgs lora;
+  bool lora_tiled_ok;
   int64_t m;
   int device;
   int cus;
@@ -100,6 +102,7 @@ const char* dtype_name(int32_t dt) {
     case ADQ_F32: return "F32";
     case ADQ_INT8: return "INT8";
     case ADQ_INT4X2: return "INT4X2";
+    case ADQ_INT32: return "INT32";
     default: return "unknown";
   }
 }
@@ -406,8 +409,11 @@ adq_status run(void* workspace, uint64_t workspace_size, adq_executor* e, void* 
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t err = hipErrorInvalidValue;
-  if (op == kOpGemm) {
-    err = adq::launch_w8a8(e->gemm, e->gemm_tile, s);
+  if (op == kOpGemm || op == kOpLora) {
+    err = op == kOpGemm ? adq::launch_w8a8(e->gemm, e->gemm_tile, s)
+                        : adq::launch_lora(e->lora, e->path == ADQ_PATH_GENERIC
+                                                        ? adq::kLoraGeneric
+                                                        : adq::kLoraTiled, s);
     if (cur != e->device) (void)hipSetDevice(cur);
     if (err != hipSuccess)
       return fail(ADQ_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(err));
@@ -661,6 +667,111 @@ adq_status adq_w8a8_gemm(void* workspace, uint64_t workspace_size, adq_executor*
   return run(workspace, workspace_size, executor, hip_stream, kOpGemm);
 }
 
+adq_status adq_add_lora_get_workspace_size(const adq_tensor* y, const adq_tensor* x,
+                                           const adq_tensor* weight_b,
+                                           const adq_tensor* indices,
+                                           const adq_tensor* weight_a, int64_t layer_idx,
+                                           double scale, int64_t y_offset,
+                                           int64_t y_slice_size, const adq_tensor* out,
+                                           uint64_t* workspace_size, adq_executor** executor) {
+  if (!workspace_size || !executor)
+    return fail(ADQ_ERR_NULLPTR, "workspace_size and executor out-pointers are required");
+  *executor = nullptr;
+  *workspace_size = 0;
+  if (!y || !x || !weight_b || !indices || !out)
+    return fail(ADQ_ERR_NULLPTR, "y, x, weight_b, indices and out are required");
+  adq_status st;
+  if ((st = check_tensor(y, "y")) != ADQ_OK) return st;
+  if ((st = check_tensor(x, "x")) != ADQ_OK) return st;
+  if ((st = check_tensor(weight_b, "weight_b")) != ADQ_OK) return st;
+  if ((st = check_tensor(indices, "indices")) != ADQ_OK) return st;
+  if ((st = check_tensor(out, "out")) != ADQ_OK) return st;
+  if (weight_a && (st = check_tensor(weight_a, "weight_a")) != ADQ_OK) return st;
+  if (!is_half(y->dtype))
+    return fail(ADQ_ERR_UNSUPPORTED, "y: dtype %s; expected F16 or BF16", dtype_name(y->dtype));
+  if (x->dtype != y->dtype || weight_b->dtype != y->dtype || out->dtype != y->dtype ||
+      (weight_a && weight_a->dtype != y->dtype))
+    return fail(ADQ_ERR_PARAM_INVALID, "x, weight_a, weight_b and out must have y's dtype");
+  if (indices->dtype != ADQ_INT32) return fail(ADQ_ERR_UNSUPPORTED, "indices must be INT32");
+  if (y->ndim < 1 || x->ndim != y->ndim)
+    return fail(ADQ_ERR_PARAM_INVALID, "x and y must have the same rank (>= 1)");
+  for (int i = 0; i + 1 < y->ndim; ++i)
+    if (x->shape[i] != y->shape[i])
+      return fail(ADQ_ERR_PARAM_INVALID, "x and y must have the same leading dimensions");
+  if (!same_shape(y, out)) return fail(ADQ_ERR_PARAM_INVALID, "out must have y's shape");
+  const int64_t h3 = y->shape[y->ndim - 1];
+  const int64_t h1 = x->shape[x->ndim - 1];
+  const int64_t rows = numel(y) / h3;
+  if (numel(indices) != rows)
+    return fail(ADQ_ERR_PARAM_INVALID, "indices needs one value per row (%lld)", (long long)rows);
+  if (weight_b->ndim != 4) return fail(ADQ_ERR_PARAM_INVALID, "weight_b must be [W, L, rank, h2]");
+  const int64_t w = weight_b->shape[0], l = weight_b->shape[1];
+  const int64_t rank = weight_b->shape[2], h2 = weight_b->shape[3];
+  if (weight_a) {
+    if (weight_a->ndim != 4 || weight_a->shape[0] != w || weight_a->shape[1] != l ||
+        weight_a->shape[2] != h1 || weight_a->shape[3] != rank)
+      return fail(ADQ_ERR_PARAM_INVALID, "weight_a must be [W, L, h1, rank] = [%lld, %lld, %lld, %lld]",
+                  (long long)w, (long long)l, (long long)h1, (long long)rank);
+  } else if (h1 != rank) {
+    return fail(ADQ_ERR_PARAM_INVALID, "without weight_a, x's last dimension must equal rank");
+  }
+  if (y_slice_size != h2)
+    return fail(ADQ_ERR_PARAM_INVALID, "y_slice_size must equal weight_b's last dimension");
+  if (y_offset < 0 || y_offset + h2 > h3)
+    return fail(ADQ_ERR_PARAM_INVALID, "the slice [y_offset, y_offset + y_slice_size) must lie in y's last dimension");
+  if (layer_idx < 0 || layer_idx >= l)
+    return fail(ADQ_ERR_PARAM_INVALID, "layer_idx outside [0, %lld)", (long long)l);
+  if (!(scale == scale) || scale > 3.4e38 || scale < -3.4e38)
+    return fail(ADQ_ERR_PARAM_INVALID, "scale must be a finite value");
+  if (w > adq::kLoraMaxAdapters)
+    return fail(ADQ_ERR_UNSUPPORTED, "at most %d adapters", adq::kLoraMaxAdapters);
+  if (rank > adq::kLoraMaxRankGeneric)
+    return fail(ADQ_ERR_UNSUPPORTED, "rank above %d", adq::kLoraMaxRankGeneric);
+  if (rows > INT32_MAX) return fail(ADQ_ERR_UNSUPPORTED, "too many rows");
+  if (!aligned(y->data, 2) || !aligned(x->data, 2) || !aligned(weight_b->data, 2) ||
+      !aligned(out->data, 2) || !aligned(indices->data, 4) ||
+      (weight_a && !aligned(weight_a->data, 2)))
+    return fail(ADQ_ERR_PARAM_INVALID, "misaligned tensor");
+  adq_executor e{};
+  e.op = kOpLora;
+  st = current_device(&e.device, &e.cus);
+  if (st != ADQ_OK) return st;
+  adq::LoraArgs& a = e.lora;
+  a.y = y->data;
+  a.x = x->data;
+  a.wa = weight_a ? weight_a->data : nullptr;
+  a.wb = weight_b->data;
+  a.indices = static_cast<const int32_t*>(indices->data);
+  a.out = out->data;
+  a.rows = rows;
+  a.h1 = h1;
+  a.rank = rank;
+  a.h2 = h2;
+  a.h3 = h3;
+  a.w = w;
+  a.l = l;
+  a.layer = layer_idx;
+  a.y_offset = y_offset;
+  a.scale = (float)scale;
+  a.elem = y->dtype == ADQ_BF16 ? adq::kBF16 : adq::kF16;
+  a.in_place = out->data == y->data;
+  e.m = rows;
+  e.lora_tiled_ok = h1 % 8 == 0 && rank % 16 == 0 && rank <= adq::kLoraMaxRankTiled &&
+                    h2 % 4 == 0 && h3 % 4 == 0 && y_offset % 4 == 0 && aligned(x->data, 16) &&
+                    (!weight_a || aligned(weight_a->data, 16)) && aligned(weight_b->data, 8) &&
+                    aligned(y->data, 8) && aligned(out->data, 8);
+  e.path = e.lora_tiled_ok ? ADQ_PATH_AUTO : ADQ_PATH_GENERIC;
+  adq_executor* ex = new (std::nothrow) adq_executor(e);
+  if (!ex) return fail(ADQ_ERR_RUNTIME, "out of host memory");
+  *executor = ex;
+  return ok();
+}
+
+adq_status adq_add_lora(void* workspace, uint64_t workspace_size, adq_executor* executor,
+                        void* hip_stream) {
+  return run(workspace, workspace_size, executor, hip_stream, kOpLora);
+}
+
 void adq_executor_destroy(adq_executor* executor) { delete executor; }
 
 adq_status adq_executor_set_path(adq_executor* executor, int32_t path, uint64_t* workspace_size) {
@@ -671,6 +782,13 @@ adq_status adq_executor_set_path(adq_executor* executor, int32_t path, uint64_t*
     else if (path == ADQ_PATH_GEMM_TILE256) executor->gemm_tile = adq::kGemmTile256;
     else return fail(ADQ_ERR_PARAM_INVALID, "a GEMM executor takes AUTO or a GEMM tile path");
     executor->path = path;
+    *workspace_size = 0;
+    return ok();
+  }
+  if (executor->op == kOpLora) {
+    if (path == ADQ_PATH_AUTO) executor->path = executor->lora_tiled_ok ? ADQ_PATH_AUTO : ADQ_PATH_GENERIC;
+    else if (path == ADQ_PATH_GENERIC) executor->path = ADQ_PATH_GENERIC;
+    else return fail(ADQ_ERR_PARAM_INVALID, "an AddLora executor takes AUTO or GENERIC");
     *workspace_size = 0;
     return ok();
   }
@@ -686,6 +804,21 @@ adq_status adq_executor_set_path(adq_executor* executor, int32_t path, uint64_t*
 
 int32_t adq_executor_describe(const adq_executor* e, char* buf, uint64_t len) {
   if (!e) return -1;
+  if (e->op == kOpLora) {
+    if (buf && len > 0) {
+      const adq::LoraArgs& a = e->lora;
+      const bool tiled = e->path != ADQ_PATH_GENERIC;
+      snprintf(buf, (size_t)len,
+               "path=%s rows=%lld h1=%lld rank=%lld h2=%lld h3=%lld adapters=%lld layers=%lld "
+               "weight_a=%d in_place=%d grid=%lld cus=%d",
+               tiled ? "lora-tiled" : "lora-generic", (long long)a.rows, (long long)a.h1,
+               (long long)a.rank, (long long)a.h2, (long long)a.h3, (long long)a.w,
+               (long long)a.l, a.wa != nullptr, a.in_place,
+               (long long)(tiled ? adq::lora_tiled_grid(a) : (a.rows < 65536 ? a.rows : 65536)),
+               e->cus);
+    }
+    return e->path;
+  }
   if (e->op == kOpGemm) {
     if (buf && len > 0)
       snprintf(buf, (size_t)len, "path=gemm m=%lld n=%lld k=%lld tile=%d out=%d cus=%d",

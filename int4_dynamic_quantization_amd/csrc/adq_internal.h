@@ -83,4 +83,35 @@ struct GemmArgs {
 // k % 16 == 0, 16-byte aligned a and w.
 hipError_t launch_w8a8(const GemmArgs& g, int tile, hipStream_t stream);
 
+// AddLora ("aclnnAddLora", Formulas): out = y with columns
+// [y_offset, y_offset + h2) of row b increased by
+// scale * (x[b] . A[g, layer]) . B[g, layer], g = indices[b]; rows whose index
+// lies outside [0, w) are left as y.  A is [w, l, h1, rank] (may be NULL:
+// then the shrink is skipped and rank == h1), B is [w, l, rank, h2].
+struct LoraArgs {
+  const void* y;
+  const void* x;
+  const void* wa;
+  const void* wb;
+  const int32_t* indices;
+  void* out;
+  int64_t rows;
+  int64_t h1, rank, h2, h3;
+  int64_t w, l, layer, y_offset;
+  float scale;
+  int elem;      // ElemType
+  int in_place;  // out == y: only the slice of rows with an adapter is written
+};
+
+enum LoraPath : int { kLoraTiled = 1, kLoraGeneric = 2 };
+constexpr int kLoraTileRows = 16;     // rows per workgroup in the tiled kernel
+constexpr int kLoraMaxAdapters = 2048;
+constexpr int kLoraMaxRankTiled = 64;
+constexpr int kLoraMaxRankGeneric = 1024;
+
+// Workgroups the tiled kernel is launched with: an upper bound on the number
+// of 16-row tiles over all groups (sum of ceil(count_g / 16) <= rows / 16 + w + 1).
+int64_t lora_tiled_grid(const LoraArgs& a);
+hipError_t launch_lora(const LoraArgs& a, int path, hipStream_t stream);
+
 }  // namespace adq

@@ -44,7 +44,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     assert set(names) == set(adq.EXPORTED)
     for name in names:
         assert hasattr(adq.lib, name), name
@@ -267,3 +267,72 @@ def test_gemm_validation():
     for i, c in enumerate(unsupported):
         assert gemm_call(**c) == adq.ERR_UNSUPPORTED, (i, adq.last_error())
     assert adq.lib.adq_w8a8_gemm(None, 0, None, None) == adq.ERR_NULLPTR
+
+
+def lora_call(y, x, wb, idx, wa, layer=1, scale=0.5, off=0, size=None, out=None,
+              out_ptrs=True):
+    ws = ctypes.c_uint64(0)
+    ex = ctypes.c_void_p(None)
+    r = lambda t: None if t is None else ctypes.byref(t)
+    size = (wb.shape[3] if wb is not None else 96) if size is None else size
+    st = adq.lib.adq_add_lora_get_workspace_size(
+        r(y), r(x), r(wb), r(idx), r(wa), layer, scale, off, size, r(out),
+        ctypes.byref(ws) if out_ptrs else None, ctypes.byref(ex) if out_ptrs else None)
+    if ex.value:
+        adq.lib.adq_executor_destroy(ex)
+    return st
+
+
+def full_lora(rows=64, h1=128, rank=16, h2=96, h3=256, w=4, layers=3, dt=adq.BF16):
+    return dict(y=fake([rows, h3], dt), x=fake([rows, h1], dt), wb=fake([w, layers, rank, h2], dt),
+                idx=fake([rows], adq.INT32), wa=fake([w, layers, h1, rank], dt),
+                out=fake([rows, h3], dt))
+
+
+def test_lora_valid_calls():
+    assert lora_call(**full_lora()) in ACCEPTED, adq.last_error()
+    assert lora_call(**full_lora(dt=adq.F16)) in ACCEPTED, adq.last_error()
+    a = full_lora(h1=16)
+    a["wa"] = None  # no shrink: h1 == rank
+    assert lora_call(**a) in ACCEPTED, adq.last_error()
+    a = full_lora()
+    a["out"] = a["y"]  # in place
+    assert lora_call(**a) in ACCEPTED
+    a = full_lora()
+    a.update(y=fake([2, 32, 256], adq.BF16), x=fake([2, 32, 128], adq.BF16),
+             out=fake([2, 32, 256], adq.BF16), idx=fake([2, 32], adq.INT32))
+    assert lora_call(**a) in ACCEPTED
+    assert lora_call(off=160, **full_lora()) in ACCEPTED  # slice ends at h3
+
+
+def test_lora_validation():
+    for f in ("y", "x", "wb", "idx", "out"):
+        a = full_lora()
+        a[f] = None
+        assert lora_call(**a) == adq.ERR_NULLPTR, f
+    assert lora_call(out_ptrs=False, **full_lora()) == adq.ERR_NULLPTR
+    bad = []
+    bad.append(dict(full_lora(), off=161))                                  # slice past h3
+    bad.append(dict(full_lora(), off=-1))
+    bad.append(dict(full_lora(), size=95))                                  # slice size != h2
+    bad.append(dict(full_lora(), layer=3))                                  # layer out of range
+    bad.append(dict(full_lora(), layer=-1))
+    bad.append(dict(full_lora(), scale=float("nan")))
+    a = full_lora(); a["wa"] = None; bad.append(a)                          # h1 != rank
+    a = full_lora(); a["wa"] = fake([4, 3, 128, 8], adq.BF16); bad.append(a)
+    a = full_lora(); a["wb"] = fake([4, 3, 16], adq.BF16); bad.append(a)
+    a = full_lora(); a["idx"] = fake([63], adq.INT32); bad.append(a)
+    a = full_lora(); a["x"] = fake([63, 128], adq.BF16); bad.append(a)
+    a = full_lora(); a["out"] = fake([64, 255], adq.BF16); bad.append(a)
+    a = full_lora(); a["x"] = fake([64, 128], adq.F16); bad.append(a)       # dtype mismatch
+    a = full_lora(); a["y"].shape[0] = 0; bad.append(a)
+    for i, c in enumerate(bad):
+        assert lora_call(**c) == adq.ERR_PARAM_INVALID, (i, adq.last_error())
+    uns = []
+    a = full_lora(); a["idx"] = fake([64], adq.INT8); uns.append(a)
+    a = full_lora(); a.update(y=fake([64, 256], adq.F32), x=fake([64, 128], adq.F32),
+                              out=fake([64, 256], adq.F32)); uns.append(a)
+    a = full_lora(w=2049); uns.append(a)
+    for i, c in enumerate(uns):
+        assert lora_call(**c) == adq.ERR_UNSUPPORTED, (i, adq.last_error())
+    assert adq.lib.adq_add_lora(None, 0, None, None) == adq.ERR_NULLPTR

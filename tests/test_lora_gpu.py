@@ -1,0 +1,211 @@
+"""Parity of AddLora ("aclnnAddLora", Formulas) on the GPU with the oracle.
+
+Bars:
+ - exact: with small-integer x, weights and y and a power-of-two scale every
+   fp32 step is exact, so the stored values equal the oracle's bit for bit
+   (the structure: grouping, layer, slice, rows without an adapter);
+ - realistic data: the kernels sum in fp32 in their own order.  For a slice
+   element with exact value v and M = |scale| * sum_r (sum_k |x_k A_kr|) |B_rj|
+   (x itself when weightA is absent), recursive fp32 summation of the shrink
+   (h1 terms) and the expand (rank terms) errs by at most
+   (h1 + rank) * 2^-24 * M; the fused multiply-add into y and the rounding to
+   the storage type add 2^-24 |v| and u |v| (u = 2^-8 bf16, 2^-11 fp16) plus
+   half the storage type's subnormal spacing:
+       |got - v| <= (h1 + rank + 4) 2^-24 M + (2^-24 + u) |v| (1 + 1e-6) + sub
+ - every element outside the slice, and every row without an adapter, equals
+   y bit for bit (outputs pre-filled with a canary when out is not y).
+"""
+import numpy as np
+import pytest
+import torch
+
+import int4_dynamic_quantization_amd as adq
+import oracle
+import synth
+from helpers import from_bits, to_bits
+
+pytestmark = pytest.mark.gpu
+
+TD = {"bf16": torch.bfloat16, "fp16": torch.float16}
+UNIT = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}
+SUB = {"bf16": 2.0 ** -134, "fp16": 2.0 ** -25}
+PATHS = [adq.PATH_AUTO, adq.PATH_GENERIC]
+PATH_IDS = ["auto", "generic"]
+
+
+def dev(bits, dt):
+    if bits is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(TD[dt]).to("cuda")
+
+
+def bits_of(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_lora(y, x, wa, wb, idx, layer, scale, off, dt, path=adq.PATH_AUTO, in_place=False,
+             lead=None):
+    ty = dev(y, dt)
+    if lead is not None:
+        ty = ty.reshape(*lead, y.shape[-1])
+    tx = dev(x, dt)
+    if lead is not None:
+        tx = tx.reshape(*lead, x.shape[-1])
+    tidx = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).to("cuda")
+    out = ty if in_place else torch.full_like(ty, float("nan"))
+    ex, out = adq.plan_add_lora(ty, tx, dev(wb, dt), tidx, dev(wa, dt), layer, scale, off, out=out,
+                                path=path)
+    ex.run()
+    torch.cuda.synchronize()
+    desc = ex.describe()
+    ex.close()
+    return bits_of(out).reshape(y.shape), desc
+
+
+def magnitude(y, x, wa, wb, idx, layer, scale, off, dt, rows=None):
+    """M of the bound above for each slice element of the given rows."""
+    rows = np.arange(y.shape[0]) if rows is None else np.asarray(rows)
+    xv = np.abs(from_bits(x[rows], dt))
+    h2 = wb.shape[-1]
+    m = np.zeros((rows.size, h2))
+    for t, b in enumerate(rows):
+        g = idx[b]
+        if 0 <= g < wb.shape[0]:
+            s1 = xv[t] if wa is None else xv[t] @ np.abs(from_bits(wa[g, layer], dt))
+            m[t] = s1 @ np.abs(from_bits(wb[g, layer], dt))
+    return m * abs(float(np.float32(scale)))
+
+
+def check_slice(got, pre, mag, h1, rank, dt):
+    gv = from_bits(got, dt)
+    tol = (h1 + rank + 4) * 2.0 ** -24 * mag + (2.0 ** -24 + UNIT[dt]) * np.abs(pre) * (1 + 1e-6) \
+        + SUB[dt]
+    err = np.abs(gv - pre)
+    bad = err > tol
+    assert not bad.any(), f"{int(bad.sum())} slice values beyond the bound; worst {err.max():.3e}"
+
+
+def check_outside(got, y, idx, w, off, h2):
+    keep = np.ones(y.shape[1], bool)
+    keep[off:off + h2] = False
+    assert np.array_equal(got[:, keep], y[:, keep]), "columns outside the slice changed"
+    none = (idx < 0) | (idx >= w)
+    assert np.array_equal(got[none], y[none]), "rows without an adapter changed"
+
+
+def small_ints(seed, tid, shape, lo, hi, dt):
+    v = synth.int8_codes(seed, tid, int(np.prod(shape[:-1])), shape[-1], lo, hi)
+    return to_bits(v.astype(np.float64).reshape(shape), dt)
+
+
+EXACT = [
+    # rows, h1, rank, h2, h3, w, layers, layer, off, has_a, dt
+    (37, 64, 16, 48, 100, 3, 2, 1, 20, True, "bf16"),
+    (100, 256, 32, 128, 256, 5, 3, 2, 128, True, "fp16"),
+    (17, 16, 16, 64, 64, 2, 1, 0, 0, False, "bf16"),
+    (300, 512, 64, 96, 400, 7, 2, 0, 300, True, "bf16"),
+    (5, 30, 5, 7, 13, 2, 2, 1, 3, True, "fp16"),      # generic only (ragged)
+]
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("case", EXACT, ids=[f"{c[0]}x{c[1]}r{c[2]}" for c in EXACT])
+def test_exact_integers(case, path):
+    rows, h1, rank, h2, h3, w, layers, layer, off, has_a, dt = case
+    s = rows + h1
+    x = small_ints(s, 12, (rows, h1), -2, 2, dt)
+    y = small_ints(s, 13, (rows, h3), -8, 8, dt)
+    wa = small_ints(s, 14, (w, layers, h1, rank), -2, 2, dt) if has_a else None
+    wb = small_ints(s, 15, (w, layers, rank, h2), -2, 2, dt)
+    idx = synth.int32s(s, 16, -1, w, rows)
+    got, desc = run_lora(y, x, wa, wb, idx, layer, 0.5, off, dt, path)
+    if path == adq.PATH_AUTO and h1 % 8 == 0 and rank % 16 == 0:
+        assert "lora-tiled" in desc, desc
+    if path == adq.PATH_GENERIC or rank % 16:
+        assert "lora-generic" in desc, desc
+    ref, _ = oracle.add_lora(y, x, wb, idx, wa, layer, 0.5, off, dt)
+    assert np.array_equal(got, ref), desc
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("in_place", [False, True], ids=["out", "in_place"])
+@pytest.mark.parametrize("name", ["lora_small", "lora_decode"])
+def test_workloads(name, in_place, path):
+    wl = synth.LORA_WORKLOADS[name]
+    y, x, wa, wb, idx = synth.lora_inputs(wl)
+    got, desc = run_lora(y, x, wa, wb, idx, wl.layer, wl.scale, wl.y_offset, wl.dtype, path,
+                         in_place)
+    _, pre = oracle.add_lora(y, x, wb, idx, wa, wl.layer, wl.scale, wl.y_offset, wl.dtype)
+    check_outside(got, y, idx, wl.w, wl.y_offset, wl.h2)
+    mag = magnitude(y, x, wa, wb, idx, wl.layer, wl.scale, wl.y_offset, wl.dtype)
+    check_slice(got[:, wl.y_offset:wl.y_offset + wl.h2], pre, mag, wl.h1, wl.rank, wl.dtype)
+
+
+def test_prefill_full_size_sampled():
+    """4096 rows x 4096 -> 16 -> 4096 into a 12288-wide y, in place (the
+    benchmarked launch): 384 sampled rows against the oracle element by
+    element, every row's columns outside the slice bit for bit."""
+    wl = synth.LORA_WORKLOADS["lora_prefill"]
+    y, x, wa, wb, idx = synth.lora_inputs(wl)
+    got, desc = run_lora(y, x, wa, wb, idx, wl.layer, wl.scale, wl.y_offset, wl.dtype,
+                         in_place=True)
+    assert "lora-tiled" in desc, desc
+    check_outside(got, y, idx, wl.w, wl.y_offset, wl.h2)
+    rows = np.sort(np.random.default_rng(6).choice(wl.rows, 384, replace=False))
+    _, pre = oracle.add_lora(y, x, wb, idx, wa, wl.layer, wl.scale, wl.y_offset, wl.dtype,
+                             rows=rows)
+    mag = magnitude(y, x, wa, wb, idx, wl.layer, wl.scale, wl.y_offset, wl.dtype, rows)
+    check_slice(got[rows, wl.y_offset:wl.y_offset + wl.h2], pre, mag, wl.h1, wl.rank, wl.dtype)
+
+
+@pytest.mark.parametrize("pattern", ["one_adapter", "distinct", "none", "single_row",
+                                     "many_adapters"])
+def test_grouping_patterns(pattern):
+    rows, h1, rank, h2, h3, layers, dt = 96, 128, 16, 64, 128, 2, "bf16"
+    w = {"many_adapters": 2048, "distinct": 96}.get(pattern, 4)
+    if pattern == "single_row":
+        rows = 1
+    s = 77
+    x = small_ints(s, 12, (rows, h1), -2, 2, dt)
+    y = small_ints(s, 13, (rows, h3), -8, 8, dt)
+    wa = small_ints(s, 14, (w, layers, h1, rank), -2, 2, dt)
+    wb = small_ints(s, 15, (w, layers, rank, h2), -2, 2, dt)
+    idx = {
+        "one_adapter": np.full(rows, 2, np.int32),
+        "distinct": np.random.default_rng(1).permutation(rows).astype(np.int32),
+        "none": np.full(rows, -5, np.int32),
+        "single_row": np.array([1], np.int32),
+        "many_adapters": synth.int32s(s, 16, 0, w - 1, rows),
+    }[pattern]
+    for in_place in (False, True):
+        got, desc = run_lora(y, x, wa, wb, idx, 1, 0.25, 32, dt, in_place=in_place)
+        ref, _ = oracle.add_lora(y, x, wb, idx, wa, 1, 0.25, 32, dt)
+        assert np.array_equal(got, ref), (pattern, in_place, desc)
+
+
+def test_leading_dims_and_determinism():
+    wl = synth.LORA_WORKLOADS["lora_small"]
+    y, x, wa, wb, idx = synth.lora_inputs(wl)
+    lead = (3, 100)
+    g1, _ = run_lora(y, x, wa, wb, idx, wl.layer, wl.scale, wl.y_offset, wl.dtype, lead=lead)
+    g2, _ = run_lora(y, x, wa, wb, idx, wl.layer, wl.scale, wl.y_offset, wl.dtype)
+    assert np.array_equal(g1, g2)
+    g3, _ = run_lora(y, x, wa, wb, idx, wl.layer, wl.scale, wl.y_offset, wl.dtype)
+    assert np.array_equal(g2, g3)
+
+
+def test_paths():
+    wl = synth.LORA_WORKLOADS["lora_small"]
+    y, x, wa, wb, idx = synth.lora_inputs(wl, rows=8)
+    ty, tx = dev(y, "bf16"), dev(x, "bf16")
+    ex, _ = adq.plan_add_lora(ty, tx, dev(wb, "bf16"), torch.from_numpy(idx).cuda(),
+                              dev(wa, "bf16"), wl.layer, wl.scale, wl.y_offset)
+    assert "lora-tiled" in ex.describe()
+    for p in (adq.PATH_ROW, adq.PATH_SPLIT, adq.PATH_GEMM_TILE128):
+        with pytest.raises(adq.AdqError):
+            ex.set_path(p)
+    ex.set_path(adq.PATH_GENERIC)
+    assert "lora-generic" in ex.describe()
+    ex.set_path(adq.PATH_AUTO)
+    assert "lora-tiled" in ex.describe()
+    ex.close()
