@@ -392,19 +392,21 @@ def bench_lora(args, torch, adq, synth) -> None:
         ty, tx = d(y), d(x)
         ex, _ = adq.plan_add_lora(ty, tx, tw[0], tw[2], tw[1], wl.layer, wl.scale, wl.y_offset,
                                   out=ty)
-        cases.append((ex, ty, tx))
+        ws = (torch.empty(ex.workspace_size, dtype=torch.uint8, device=dev)
+              if ex.workspace_size else None)
+        cases.append((ex, ws, ty, tx))
     print(f"[bench] workload {wl.name}: {alg / 1e6:.1f} MB per launch, {n_sets} rotating set(s); "
           f"plan: {cases[0][0].describe()}", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
-        cases[i % n_sets][0].run(None, stream)
+        cases[i % n_sets][0].run(cases[i % n_sets][1], stream)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        cases[i % n_sets][0].run(None, stream)
+        cases[i % n_sets][0].run(cases[i % n_sets][1], stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -438,7 +440,7 @@ def bench_lora(args, torch, adq, synth) -> None:
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(wl.name)},
     }
-    for ex, _, _ in cases:
+    for ex, _, _, _ in cases:
         ex.close()
     result["cpu_baseline"] = (lora_cpu_baseline(wl, host, alg, args.cpu_budget)
                               if args.cpu_budget > 0 else None)

@@ -230,7 +230,7 @@ void adq_executor_destroy(adq_executor* executor);
  * 256-tiles cover the compute units.  Either accepts any valid GEMM shape;
  * the operator paths are rejected for a GEMM executor and vice versa.
  * AddLora executors: AUTO (the tiled kernel when the shapes and alignments
- * allow it: h1 % 8 == 0, rank % 16 == 0 and <= 64, h2, h3 and y_offset
+ * allow it: h1 % 8 == 0, rank 16, 32 or 64, h2, h3 and y_offset
  * multiples of 4, aligned tensors) or ADQ_PATH_GENERIC (one workgroup per
  * row, any shape).
  */

@@ -413,8 +413,8 @@ def plan_add_lora(y, x, weight_b, indices, weight_a=None, layer_idx=0, scale=1.0
 
 def add_lora(y, x, weight_b, indices, weight_a=None, layer_idx=0, scale=1.0, y_offset=0,
              out=None, stream=None):
-    """Both AddLora phases on torch tensors; returns out."""
+    """Both AddLora phases on torch tensors (workspace allocated here); returns out."""
     ex, out = plan_add_lora(y, x, weight_b, indices, weight_a, layer_idx, scale, y_offset, out)
-    ex.run(None, stream)
+    ex.run(_workspace(ex, y.device), stream)
     ex.close()
     return out

@@ -232,6 +232,12 @@ uint64_t next_epoch() {
 #ifndef ADQ_MAX_WG_PER_CU
 #define ADQ_MAX_WG_PER_CU 0
 #endif
+#ifndef ADQ_LORA_KSPLIT_MULT
+#define ADQ_LORA_KSPLIT_MULT 1
+#endif
+#ifndef ADQ_LORA_CHUNK_CGS
+#define ADQ_LORA_CHUNK_CGS 128
+#endif
 #ifndef ADQ_GEMM_BIG_TILE
 #define ADQ_GEMM_BIG_TILE 2
 #endif
@@ -413,7 +419,7 @@ adq_status run(void* workspace, uint64_t workspace_size, adq_executor* e, void* 
     err = op == kOpGemm ? adq::launch_w8a8(e->gemm, e->gemm_tile, s)
                         : adq::launch_lora(e->lora, e->path == ADQ_PATH_GENERIC
                                                         ? adq::kLoraGeneric
-                                                        : adq::kLoraTiled, s);
+                                                        : adq::kLoraTiled, workspace, s);
     if (cur != e->device) (void)hipSetDevice(cur);
     if (err != hipSuccess)
       return fail(ADQ_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(err));
@@ -756,13 +762,28 @@ adq_status adq_add_lora_get_workspace_size(const adq_tensor* y, const adq_tensor
   a.elem = y->dtype == ADQ_BF16 ? adq::kBF16 : adq::kF16;
   a.in_place = out->data == y->data;
   e.m = rows;
-  e.lora_tiled_ok = h1 % 8 == 0 && rank % 16 == 0 && rank <= adq::kLoraMaxRankTiled &&
+  e.lora_tiled_ok = h1 % 8 == 0 && (rank == 16 || rank == 32 || rank == 64) &&
                     h2 % 4 == 0 && h3 % 4 == 0 && y_offset % 4 == 0 && aligned(x->data, 16) &&
                     (!weight_a || aligned(weight_a->data, 16)) && aligned(weight_b->data, 8) &&
                     aligned(y->data, 8) && aligned(out->data, 8);
+  {
+    // Tiles are only known on the device (they depend on the index values);
+    // estimate them as rows / 64 plus one partial tile per adapter in use.
+    // Slices of h1 per tile (shrink) are chosen for about four workgroups
+    // per CU, each slice at least 256 k; the expand takes ranges of 128
+    // groups of 4 columns.
+    const int64_t est_tiles = (rows + adq::kLoraTileRows - 1) / adq::kLoraTileRows +
+                              (w < rows ? w : rows);
+    const int64_t want = (2 * (int64_t)e.cus + est_tiles - 1) / est_tiles;
+    auto clamp = [](int64_t v, int64_t hi) { return (int)(v < 1 ? 1 : v > hi ? hi : v); };
+    a.ksplit = clamp(ADQ_LORA_KSPLIT_MULT * want, h1 / 256 > 1 ? h1 / 256 : 1);
+    a.chunks = clamp((h2 / 4 + ADQ_LORA_CHUNK_CGS - 1) / ADQ_LORA_CHUNK_CGS, 1 << 20);
+  }
   e.path = e.lora_tiled_ok ? ADQ_PATH_AUTO : ADQ_PATH_GENERIC;
+  e.ws_bytes = e.lora_tiled_ok ? adq::lora_workspace_bytes(a) : 0;
   adq_executor* ex = new (std::nothrow) adq_executor(e);
   if (!ex) return fail(ADQ_ERR_RUNTIME, "out of host memory");
+  *workspace_size = e.ws_bytes;
   *executor = ex;
   return ok();
 }
@@ -789,7 +810,9 @@ adq_status adq_executor_set_path(adq_executor* executor, int32_t path, uint64_t*
     if (path == ADQ_PATH_AUTO) executor->path = executor->lora_tiled_ok ? ADQ_PATH_AUTO : ADQ_PATH_GENERIC;
     else if (path == ADQ_PATH_GENERIC) executor->path = ADQ_PATH_GENERIC;
     else return fail(ADQ_ERR_PARAM_INVALID, "an AddLora executor takes AUTO or GENERIC");
-    *workspace_size = 0;
+    executor->ws_bytes =
+        executor->path == ADQ_PATH_GENERIC ? 0 : adq::lora_workspace_bytes(executor->lora);
+    *workspace_size = executor->ws_bytes;
     return ok();
   }
   if (path == ADQ_PATH_GEMM_TILE128 || path == ADQ_PATH_GEMM_TILE256)
@@ -810,12 +833,11 @@ int32_t adq_executor_describe(const adq_executor* e, char* buf, uint64_t len) {
       const bool tiled = e->path != ADQ_PATH_GENERIC;
       snprintf(buf, (size_t)len,
                "path=%s rows=%lld h1=%lld rank=%lld h2=%lld h3=%lld adapters=%lld layers=%lld "
-               "weight_a=%d in_place=%d grid=%lld cus=%d",
+               "weight_a=%d in_place=%d ksplit=%d chunks=%d tiles<=%lld workspace=%llu cus=%d",
                tiled ? "lora-tiled" : "lora-generic", (long long)a.rows, (long long)a.h1,
                (long long)a.rank, (long long)a.h2, (long long)a.h3, (long long)a.w,
-               (long long)a.l, a.wa != nullptr, a.in_place,
-               (long long)(tiled ? adq::lora_tiled_grid(a) : (a.rows < 65536 ? a.rows : 65536)),
-               e->cus);
+               (long long)a.l, a.wa != nullptr, a.in_place, a.ksplit, a.chunks,
+               (long long)adq::lora_max_tiles(a), (unsigned long long)e->ws_bytes, e->cus);
     }
     return e->path;
   }

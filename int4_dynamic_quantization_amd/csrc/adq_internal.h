@@ -101,17 +101,21 @@ struct LoraArgs {
   float scale;
   int elem;      // ElemType
   int in_place;  // out == y: only the slice of rows with an adapter is written
+  int ksplit;    // tiled path: slices of h1 per tile in the shrink
+  int chunks;    // tiled path: column ranges per tile in the expand
 };
 
 enum LoraPath : int { kLoraTiled = 1, kLoraGeneric = 2 };
-constexpr int kLoraTileRows = 16;     // rows per workgroup in the tiled kernel
+constexpr int kLoraTileRows = 64;     // rows per tile in the tiled path
 constexpr int kLoraMaxAdapters = 2048;
 constexpr int kLoraMaxRankTiled = 64;
 constexpr int kLoraMaxRankGeneric = 1024;
 
-// Workgroups the tiled kernel is launched with: an upper bound on the number
-// of 16-row tiles over all groups (sum of ceil(count_g / 16) <= rows / 16 + w + 1).
-int64_t lora_tiled_grid(const LoraArgs& a);
-hipError_t launch_lora(const LoraArgs& a, int path, hipStream_t stream);
+// Tiled path: upper bound on the number of tiles (sum over adapter classes of
+// ceil(count / 64) <= rows / 64 + w + 1), and the workspace it needs (tile
+// table, grouped row order, per-slice partial shrink results).
+int64_t lora_max_tiles(const LoraArgs& a);
+uint64_t lora_workspace_bytes(const LoraArgs& a);
+hipError_t launch_lora(const LoraArgs& a, int path, void* workspace, hipStream_t stream);
 
 }  // namespace adq

@@ -6,32 +6,51 @@
 // is fp32 (products of 16-bit inputs are exact; Z1 stays fp32 between the two
 // products); the slice is rounded once to the storage type.
 //
-// Tiled kernel (the fast path): one workgroup per tile of up to 16 rows of
-// one adapter, so the rows of a tile share their weights, as the page's
-// step 1 regroups them.  Every workgroup derives the grouping itself from
-// the index vector (histogram, prefix over the adapters' tile counts, then a
-// stable ordered gather of its own rows), so a call is a single launch with
-// no workspace and a deterministic result.
-//  - shrink on MFMA (v_mfma_f32_16x16x32_{bf16,f16}): 16 rows x 16 ranks per
-//    block, K = h1 split over the 4 wavefronts and summed in wavefront order
-//    through LDS.  weightA is stored [h1, rank] (rank contiguous) while the
-//    MFMA's B operand wants 8 consecutive k per lane, so each 32 x 16 block
-//    goes through the wavefront's own 1 KB of LDS (one 16-byte write per
-//    lane, eight 16-bit reads).
-//  - expand on the vector ALU in fp32: each thread owns 4 adjacent columns
-//    of the slice for all 16 rows (accumulators in registers), reads
-//    weightB rows in 8-byte pieces and writes y's slice in 8-byte pieces;
-//    Z1 is read from LDS by broadcast.
+// Tiled path, three launches on the caller's stream:
+//  1. group: one workgroup builds the page's step 1 in the workspace: a
+//     histogram of adapter classes, a table of tiles of up to 64 rows of one
+//     class, and the rows listed class by class.  Places within a class are
+//     taken with LDS atomics, so the order of rows inside a tile may vary
+//     between runs; every row's result is computed from its own data in a
+//     fixed order, so outputs do not.
+//  2. shrink: one workgroup per (tile, slice of h1).  The slice of
+//     weightA[g, layer] (stored [h1, rank], rank contiguous) is staged in LDS
+//     transposed, 256 k at a time, so each MFMA operand is one 16-byte read;
+//     4 wavefronts each take 16 rows (v_mfma_f32_16x16x32_{bf16,f16}, the
+//     x fragments of 4 k-steps loaded together) and write fp32 partial sums
+//     to the workspace.
+//  3. expand: one workgroup per (tile, range of columns).  Z1 = the slices'
+//     partial sums added in slice order; each thread owns 4 adjacent columns,
+//     keeps their weightB values for all ranks in registers, and walks the
+//     tile's rows 8 at a time (y loaded before the arithmetic), fp32 fma,
+//     one rounding, 8-byte stores.  Rows without an adapter and, when out is
+//     not y, the columns outside the slice are copied here.
 // Generic kernel: one workgroup per row, any sizes and alignments, same
 // arithmetic with block reductions in a fixed order.
 #include "adq_device.h"
+
+#ifndef ADQ_LORA_EXPAND_WAVES
+#define ADQ_LORA_EXPAND_WAVES 3
+#endif
 
 namespace adq {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTile = kLoraTileRows;
+constexpr int kThreads = 256;         // generic, shrink and expand kernels
+constexpr int kGroupThreads = 1024;   // group kernel
+constexpr int kTile = kLoraTileRows;  // 64 rows
+constexpr int kKSub = 256;            // k per LDS stage of weightA
+// Transposed weightA rows in LDS: 256 k + 32 of padding (576 bytes, 16 banks
+// of offset per row) with the 8-k groups of rows 8..15 (mod 16) swapped in
+// pairs (group index ^ 2).  gfx950 reads 128 bits for 16 lanes per pass; for
+// every lane grouping that fits the bank-conflict measurements (one half
+// wave, parity of lane bits 2 and 4, possibly with bits 0 and 3) the 16
+// lanes of a pass then hit 16 distinct 4-bank groups.
+constexpr int kAtStride = kKSub + 32;
+constexpr int kCW = 128;              // expand: threads per row half (groups of 4 columns)
+constexpr int kHalf = kTile / 2;      // expand: rows per thread
+constexpr int kStepRows = 4;          // expand: rows per step (the next step's y is prefetched)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -50,8 +69,9 @@ __device__ __forceinline__ f32x4 mfma16(u16x8 a, u16x8 b, f32x4 c) {
   }
 }
 
-// Exclusive prefix of one int per thread over the 256-thread workgroup, in
-// thread order; `total` receives the sum.  tmp: 4 ints of LDS.
+// Exclusive prefix of one int per thread over a workgroup of NW wavefronts,
+// in thread order; `total` receives the sum.  tmp: NW ints of LDS.
+template <int NW>
 __device__ int block_exclusive_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
@@ -62,9 +82,12 @@ __device__ int block_exclusive_scan(int v, int* tmp, int* total) {
   }
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += tmp[w];
-  *total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  int base = 0, sum = 0;
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) base += tmp[w];
+    sum += tmp[w];
+  }
+  *total = sum;
   __syncthreads();
   return base + x - v;
 }
@@ -73,198 +96,336 @@ __device__ __forceinline__ int adapter_class(int32_t g, int64_t w) {
   return (g >= 0 && g < w) ? g : (int)w;
 }
 
-template <int E>
-__global__ void __launch_bounds__(kThreads) lora_tiled_kernel(const LoraArgs a) {
+__host__ __device__ inline int64_t lora_max_tiles_dev(const LoraArgs& a) {
+  return (a.rows + kTile - 1) / kTile + a.w + 1;
+}
+
+struct Workspace {
+  int* header;      // [0]: number of tiles
+  int4* table;      // per tile: {class, 0, rows, 0}
+  int32_t* rows;    // per tile, 64 slots of row ids
+  float* z1p;       // [ksplit][tile slot][rank] partial shrink sums
+};
+
+__host__ __device__ inline uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+
+// byte offsets of the table, the row list and the partial sums
+struct WsOffsets {
+  uint64_t table, rows, z1p, end;
+};
+
+__host__ __device__ inline WsOffsets ws_offsets(const LoraArgs& a) {
+  const int64_t tiles = (a.rows + kTile - 1) / kTile + a.w + 1;
+  WsOffsets o;
+  o.table = 256;
+  o.rows = align256(o.table + (uint64_t)tiles * 16);
+  o.z1p = align256(o.rows + (uint64_t)tiles * kTile * 4);
+  o.end = o.z1p +
+          (a.wa ? (uint64_t)a.ksplit * (uint64_t)tiles * kTile * (uint64_t)a.rank * 4 : 0);
+  return o;
+}
+
+inline Workspace ws_layout(void* base, const LoraArgs& a) {
+  char* p = static_cast<char*>(base);
+  const WsOffsets o = ws_offsets(a);
+  Workspace w;
+  w.header = reinterpret_cast<int*>(p);
+  w.table = reinterpret_cast<int4*>(p + o.table);
+  w.rows = reinterpret_cast<int32_t*>(p + o.rows);
+  w.z1p = reinterpret_cast<float*>(p + o.z1p);
+  return w;
+}
+
+// ---- 1. grouping
+__global__ void __launch_bounds__(kGroupThreads) lora_group_kernel(const LoraArgs a,
+                                                                   Workspace ws) {
+  constexpr int NW = kGroupThreads / 64;
   __shared__ int cnt[kLoraMaxAdapters + 1];
-  __shared__ int tstart[kLoraMaxAdapters + 1];
-  __shared__ int scan_tmp[4];
-  __shared__ int tile_info[2];
-  __shared__ int64_t rows_lds[kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t wt[4][kLoraMaxRankTiled / 16][32 * 16];
-  __shared__ __attribute__((aligned(16))) float part[4][kTile][kLoraMaxRankTiled];
-  __shared__ __attribute__((aligned(16))) float z1[kTile][kLoraMaxRankTiled];
-
+  __shared__ int cur[kLoraMaxAdapters + 1];
+  __shared__ int first_tile[kLoraMaxAdapters + 1];
+  __shared__ int scan_tmp[NW];
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   const int64_t W = a.w;
-  const int64_t B = a.rows;
-
-  // ---- grouping: adapter histogram, tiles per adapter and their prefix
-  for (int g = tid; g <= W; g += kThreads) cnt[g] = 0;
+  for (int g = tid; g <= W; g += kGroupThreads) cnt[g] = 0;
   __syncthreads();
-  const int64_t chunk = (B + kThreads - 1) / kThreads;
-  const int64_t lo = tid * chunk;
-  const int64_t hi = lo + chunk < B ? lo + chunk : B;
-  for (int64_t i = lo; i < hi; ++i) atomicAdd(&cnt[adapter_class(a.indices[i], W)], 1);
+  for (int64_t i = tid; i < a.rows; i += kGroupThreads)
+    atomicAdd(&cnt[adapter_class(a.indices[i], W)], 1);
   __syncthreads();
-  auto tiles_of = [&](int g) -> int {
-    if (g == W && a.in_place) return 0;  // rows without an adapter: nothing to write
-    return (cnt[g] + kTile - 1) / kTile;
-  };
-  const int per = (int)((W + 1 + kThreads - 1) / kThreads);
-  int local = 0;
-  for (int q = 0; q < per; ++q) {
-    const int g = tid * per + q;
-    if (g <= W) local += tiles_of(g);
-  }
-  int total = 0;
-  int run = block_exclusive_scan(local, scan_tmp, &total);
+  // rows without an adapter are only listed when out is not y (to be copied)
+  auto placed = [&](int g) -> int { return (g < W || !a.in_place) ? cnt[g] : 0; };
+  const int per = (int)((W + 1 + kGroupThreads - 1) / kGroupThreads);
+  int tl = 0, rl = 0;
   for (int q = 0; q < per; ++q) {
     const int g = tid * per + q;
     if (g <= W) {
-      tstart[g] = run;
-      run += tiles_of(g);
+      tl += (placed(g) + kTile - 1) / kTile;
+      rl += placed(g);
     }
   }
-  const int tile = (int)blockIdx.x;
-  if (tile >= total) return;  // uniform: every thread saw the same total
-  __syncthreads();
+  int ntiles = 0, nplaced = 0;
+  int tb = block_exclusive_scan<NW>(tl, scan_tmp, &ntiles);
+  int rb = block_exclusive_scan<NW>(rl, scan_tmp, &nplaced);
   for (int q = 0; q < per; ++q) {
     const int g = tid * per + q;
-    if (g <= W && tile >= tstart[g] && tile < tstart[g] + tiles_of(g)) {
-      tile_info[0] = g;
-      tile_info[1] = tile - tstart[g];
+    if (g <= W) {
+      const int n = placed(g);
+      for (int t = 0; t * kTile < n; ++t)
+        ws.table[tb + t] = int4{g, 0, n - t * kTile < kTile ? n - t * kTile : kTile, 0};
+      cur[g] = 0;
+      first_tile[g] = tb;
+      tb += (n + kTile - 1) / kTile;
+      rb += n;
     }
   }
+  if (tid == 0) ws.header[0] = ntiles;
   __syncthreads();
-  const int g = tile_info[0];
-  const int first = tile_info[1] * kTile;
-  const int nrows = cnt[g] - first < kTile ? cnt[g] - first : kTile;
-
-  // ---- this tile's rows: ranks [first, first + nrows) of adapter class g, in row order
-  int c = 0;
-  for (int64_t i = lo; i < hi; ++i) c += adapter_class(a.indices[i], W) == g;
-  int dummy;
-  int r = block_exclusive_scan(c, scan_tmp, &dummy);
-  for (int64_t i = lo; i < hi && r < first + kTile; ++i) {
-    if (adapter_class(a.indices[i], W) == g) {
-      if (r >= first) rows_lds[r - first] = i;
-      ++r;
+  for (int64_t i = tid; i < a.rows; i += kGroupThreads) {
+    const int c = adapter_class(a.indices[i], W);
+    if (c < W || !a.in_place) {
+      const int p = atomicAdd(&cur[c], 1);  // place within the class
+      ws.rows[(first_tile[c] + p / kTile) * kTile + p % kTile] = (int32_t)i;
     }
   }
-  __syncthreads();
+}
 
+// ---- 2. shrink: partial z1 over one slice of h1 for one tile
+template <int E>
+__global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a, Workspace ws) {
+  __shared__ int64_t rows_lds[kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t at[kLoraMaxRankTiled][kAtStride];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int tile = (int)(blockIdx.x / a.ksplit);
+  const int ks = (int)(blockIdx.x % a.ksplit);
+  const int ntiles = ws.header[0];
+  const int4 te = ws.table[tile < ntiles ? tile : 0];
+  const int32_t rid = ws.rows[(int64_t)tile * kTile + tid % kTile];  // with the table
+  if (tile >= ntiles) return;
+  const int g = te.x, n = te.z;
+  if (g >= a.w) return;  // rows without an adapter
+  if (tid < n) rows_lds[tid] = rid;
+  using T = uint16_t;
+  const int64_t rank = a.rank, h1 = a.h1;
+  const int nb = (int)(rank / 16);
+  const T* wa = static_cast<const T*>(a.wa) + ((g * a.l + a.layer) * h1) * rank;
+  const T* x = static_cast<const T*>(a.x);
+  const int64_t kc = ((h1 + a.ksplit - 1) / a.ksplit + 31) / 32 * 32;
+  const int64_t k_lo = ks * kc;
+  const int64_t k_hi = k_lo + kc < h1 ? k_lo + kc : h1;
+
+  const int fi = lane & 15, fk = lane >> 4;
+  const int rb = 16 * wave;  // this wavefront's rows of the tile
+  f32x4 acc[kLoraMaxRankTiled / 16];
+#pragma unroll
+  for (int b = 0; b < kLoraMaxRankTiled / 16; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  const bool row_ok = rb + fi < n;
+  const T* xrow = x + (row_ok ? rows_lds[rb + fi] : rows_lds[0]) * h1;
+  const int pieces_per_k = (int)(rank / 8);
+  for (int64_t sub = k_lo; sub < k_hi; sub += kKSub) {
+    const int sub_n = (int)(k_hi - sub < kKSub ? k_hi - sub : kKSub);
+    const int steps = (sub_n + 31) / 32;
+    // this stage's x fragments first (they do not depend on the LDS stage)
+    u16x8 xa[kKSub / 32];
+#pragma unroll
+    for (int u = 0; u < kKSub / 32; ++u) {
+      const int64_t kx = sub + 32 * u + 8 * fk;
+      xa[u] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (rb < n && row_ok && u < steps && kx < k_hi)
+        xa[u] = *reinterpret_cast<const u16x8*>(xrow + kx);
+    }
+    // stage weightA[sub .. sub + 256) transposed (zeros past the slice)
+    for (int p = tid; p < kKSub * pieces_per_k; p += kThreads) {
+      const int k = p / pieces_per_k, rg = p % pieces_per_k;
+      u16x8 v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (k < sub_n) v = *reinterpret_cast<const u16x8*>(wa + (sub + k) * rank + 8 * rg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * rg + e;
+        at[r][8 * ((k >> 3) ^ (((r >> 3) & 1) << 1)) + (k & 7)] = v[e];
+      }
+    }
+    __syncthreads();
+    if (rb < n) {  // wavefront-uniform
+#pragma unroll
+      for (int u = 0; u < kKSub / 32; ++u) {
+        if (u < steps) {
+          const int kg = 4 * u + fk;
+#pragma unroll
+          for (int b = 0; b < kLoraMaxRankTiled / 16; ++b) {
+            if (b < nb) {
+              const int r = 16 * b + fi;
+              const u16x8 bv =
+                  *reinterpret_cast<const u16x8*>(&at[r][8 * (kg ^ (((r >> 3) & 1) << 1))]);
+              acc[b] = mfma16<E>(xa[u], bv, acc[b]);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();  // before the next stage overwrites `at`
+  }
+  // element e of lane l: row rb + 4 * (l / 16) + e, rank l % 16 (+ 16 * block)
+  float* zp = ws.z1p + ((int64_t)ks * lora_max_tiles_dev(a) + tile) * kTile * rank;
+#pragma unroll
+  for (int b = 0; b < kLoraMaxRankTiled / 16; ++b)
+    if (b < nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = rb + 4 * fk + e;
+        if (i < n) zp[i * rank + 16 * b + fi] = acc[b][e];
+      }
+}
+
+// ---- 3. expand + accumulate for one tile and one range of columns
+template <int E, int R>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(R <= 32 ? ADQ_LORA_EXPAND_WAVES : 2)))
+lora_expand_kernel(const LoraArgs a, Workspace ws) {
+  __shared__ int64_t rows_lds[kTile];
+  __shared__ __attribute__((aligned(16))) float z1[kTile][R];
+  const int tid = threadIdx.x;
+  const int tile = (int)(blockIdx.x / a.chunks);
+  const int chunk = (int)(blockIdx.x % a.chunks);
+  const int ntiles = ws.header[0];
+  const int4 te = ws.table[tile < ntiles ? tile : 0];
+  const int32_t rid = ws.rows[(int64_t)tile * kTile + tid % kTile];  // with the table
+  if (tile >= ntiles) return;
+  const int g = te.x, n = te.z;
+  if (tid < n) rows_lds[tid] = rid;
   using T = uint16_t;
   const T* y = static_cast<const T*>(a.y);
   T* out = static_cast<T*>(a.out);
   const int64_t h3 = a.h3;
-
-  if (g == W) {  // no adapter (only reached when out != y): copy the rows
-    for (int i = 0; i < nrows; ++i) {
+  const int64_t ncg_row = h3 / 4;
+  const int64_t per_row = (ncg_row + a.chunks - 1) / a.chunks;
+  const int64_t c0 = chunk * per_row;
+  const int64_t c1 = c0 + per_row < ncg_row ? c0 + per_row : ncg_row;
+  __syncthreads();
+  if (g >= a.w) {  // rows without an adapter (listed only when out is not y): copy
+    for (int i = 0; i < n; ++i) {
       const int64_t row = rows_lds[i];
-      for (int64_t c4 = tid; c4 < h3 / 4; c4 += kThreads)
+      for (int64_t c4 = c0 + tid; c4 < c1; c4 += kThreads)
         *reinterpret_cast<uint2*>(out + row * h3 + 4 * c4) =
             *reinterpret_cast<const uint2*>(y + row * h3 + 4 * c4);
     }
     return;
   }
-
-  const int64_t rank = a.rank;
-  const int nb = (int)(rank / 16);
-  const T* x = static_cast<const T*>(a.x);
-
-  // ---- shrink: z1[i][r] = sum_k x[row_i][k] * A[g, layer][k][r]
+  // z1 = the slices' partial sums, in slice order (or x itself without weightA);
+  // all of a thread's partial loads are issued before any is added
+  constexpr int ZP = kTile * R / kThreads;  // elements per thread
+  const int64_t mt = lora_max_tiles_dev(a);
   if (a.wa) {
-    const T* wa = static_cast<const T*>(a.wa) + ((g * a.l + a.layer) * a.h1) * rank;
-    f32x4 acc[kLoraMaxRankTiled / 16];
+    float zs[ZP];
 #pragma unroll
-    for (int b = 0; b < kLoraMaxRankTiled / 16; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int fi = lane & 15;   // A-operand row (tile row) / B-operand column (rank)
-    const int fk = lane >> 4;   // which 8 of the 32 k
-    const bool row_ok = fi < nrows;
-    const T* xrow = x + (row_ok ? rows_lds[fi] : rows_lds[0]) * a.h1;
-    const int64_t ksteps = (a.h1 + 31) / 32;
-    for (int64_t s = wave; s < ksteps; s += 4) {
-      const int64_t k0 = 32 * s;
-      u16x8 xa = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      const int64_t kx = k0 + 8 * fk;
-      if (row_ok && kx < a.h1) xa = *reinterpret_cast<const u16x8*>(xrow + kx);
-      const int64_t kw = k0 + (lane >> 1);  // this lane's weight row
+    for (int u = 0; u < ZP; ++u) zs[u] = 0.0f;
+    for (int ks0 = 0; ks0 < a.ksplit; ks0 += 4) {
+      float p[4][ZP];
 #pragma unroll
-      for (int b = 0; b < kLoraMaxRankTiled / 16; ++b) {
-        if (b < nb) {
-          u16x8 wv = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-          if (kw < a.h1)
-            wv = *reinterpret_cast<const u16x8*>(wa + kw * rank + 16 * b + 8 * (lane & 1));
-          *reinterpret_cast<u16x8*>(&wt[wave][b][16 * (lane >> 1) + 8 * (lane & 1)]) = wv;
-          u16x8 bv;
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) bv[e] = wt[wave][b][16 * (8 * fk + e) + fi];
-          acc[b] = mfma16<E>(xa, bv, acc[b]);
+        for (int u = 0; u < ZP; ++u) {
+          const int t = tid + u * kThreads, i = t / R, r = t % R;
+          p[q][u] = (i < n && ks0 + q < a.ksplit)
+                        ? ws.z1p[(((int64_t)(ks0 + q) * mt + tile) * kTile + i) * R + r]
+                        : 0.0f;
         }
-      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int u = 0; u < ZP; ++u)
+          if (ks0 + q < a.ksplit) zs[u] = (ks0 + q == 0) ? p[q][u] : zs[u] + p[q][u];
     }
-    // partial sums of this wavefront: element e of lane l is row 4 * (l / 16) + e, rank l % 16
 #pragma unroll
-    for (int b = 0; b < kLoraMaxRankTiled / 16; ++b)
-      if (b < nb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) part[wave][4 * fk + e][16 * b + fi] = acc[b][e];
-    __syncthreads();
-    for (int t = tid; t < kTile * rank; t += kThreads) {
-      const int i = (int)(t / rank), rr = (int)(t % rank);
-      z1[i][rr] = ((part[0][i][rr] + part[1][i][rr]) + part[2][i][rr]) + part[3][i][rr];
+    for (int u = 0; u < ZP; ++u) {
+      const int t = tid + u * kThreads;
+      z1[t / R][t % R] = zs[u];
     }
   } else {
-    for (int t = tid; t < kTile * rank; t += kThreads) {
-      const int i = (int)(t / rank), rr = (int)(t % rank);
-      z1[i][rr] = i < nrows ? widen1<E>(x[rows_lds[i] * a.h1 + rr]) : 0.0f;
+    for (int t = tid; t < kTile * R; t += kThreads) {
+      const int i = t / R, r = t % R;
+      z1[i][r] = i < n ? widen1<E>(static_cast<const T*>(a.x)[rows_lds[i] * a.h1 + r]) : 0.0f;
     }
   }
   __syncthreads();
 
-  // ---- expand + accumulate: columns 4 * cg .. 4 * cg + 3 of the slice
-  const T* wb = static_cast<const T*>(a.wb) + ((g * a.l + a.layer) * rank) * a.h2;
+  const T* wb = static_cast<const T*>(a.wb) + ((g * a.l + a.layer) * R) * a.h2;
   const int64_t ncg = a.h2 / 4;
-  for (int64_t cg = tid; cg < ncg; cg += kThreads) {
-    float acc[kTile][4];
+  const int64_t per = (ncg + a.chunks - 1) / a.chunks;
+  const int64_t e0 = chunk * per;
+  const int64_t e1 = e0 + per < ncg ? e0 + per : ncg;
+  // thread -> (group of 4 columns, half of the tile's rows)
+  const int half = tid / kCW;
+  const int hr0 = half * kHalf;
+  const int hr1 = hr0 + kHalf < n ? hr0 + kHalf : n;
+  for (int64_t cg = e0 + tid % kCW; cg < e1; cg += kCW) {
+    if (hr0 >= hr1) break;
+    // weightB[r][4 cg .. 4 cg + 3]: kept in registers for rank 16, otherwise
+    // read again (from cache) for each 16 ranks of each step of rows
+    u16x4 bw16[16];
+    if constexpr (R == 16) {
 #pragma unroll
-    for (int i = 0; i < kTile; ++i)
+      for (int r = 0; r < 16; ++r) bw16[r] = *reinterpret_cast<const u16x4*>(wb + r * a.h2 + 4 * cg);
+    }
+    auto load_y = [&](int h, u16x4* yv) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[i][q] = 0.0f;
-    for (int rc = 0; rc < rank; rc += 16) {
-      float bw[16][4];
+      for (int i = 0; i < kStepRows; ++i)
+        if (h + i < hr1)
+          yv[i] = *reinterpret_cast<const u16x4*>(y + rows_lds[h + i] * h3 + a.y_offset + 4 * cg);
+    };
+    u16x4 ycur[kStepRows], ynext[kStepRows];
+    load_y(hr0, ycur);
+#pragma unroll 1
+    for (int h = hr0; h < hr1; h += kStepRows) {
+      if (h + kStepRows < hr1) load_y(h + kStepRows, ynext);  // next rows while these compute
+      float acc[kStepRows][4];
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const u16x4 v = *reinterpret_cast<const u16x4*>(wb + (rc + rr) * a.h2 + 4 * cg);
+      for (int i = 0; i < kStepRows; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) bw[rr][q] = widen1<E>(v[q]);
-      }
+        for (int q = 0; q < 4; ++q) acc[i][q] = 0.0f;
+#pragma unroll 1
+      for (int rc = 0; rc < R; rc += 16) {
+        u16x4 bw[16];
 #pragma unroll
-      for (int i = 0; i < kTile; ++i) {
-        const f32x4* zr = reinterpret_cast<const f32x4*>(&z1[i][rc]);
+        for (int r = 0; r < 16; ++r)
+          bw[r] = R == 16 ? bw16[r]
+                          : *reinterpret_cast<const u16x4*>(wb + (rc + r) * a.h2 + 4 * cg);
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 z = zr[r4];
+        for (int r4 = 0; r4 < 16; r4 += 4) {
+          float b[4][4];
 #pragma unroll
           for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              acc[i][q] = __builtin_fmaf(z[u], bw[4 * r4 + u][q], acc[i][q]);
+            for (int q = 0; q < 4; ++q) b[u][q] = widen1<E>(bw[r4 + u][q]);
+#pragma unroll
+          for (int i = 0; i < kStepRows; ++i) {
+            const f32x4 zz = *reinterpret_cast<const f32x4*>(&z1[h + i][rc + r4]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[i][q] = __builtin_fmaf(zz[u], b[u][q], acc[i][q]);
+          }
         }
       }
-    }
 #pragma unroll
-    for (int i = 0; i < kTile; ++i) {
-      if (i < nrows) {
-        const int64_t at = rows_lds[i] * h3 + a.y_offset + 4 * cg;
-        const u16x4 yv = *reinterpret_cast<const u16x4*>(y + at);
-        u16x4 o;
+      for (int i = 0; i < kStepRows; ++i) {
+        if (h + i < hr1) {
+          u16x4 o;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          o[q] = narrow1<E>(__builtin_fmaf(acc[i][q], a.scale, widen1<E>(yv[q])));
-        *reinterpret_cast<u16x4*>(out + at) = o;
+          for (int q = 0; q < 4; ++q)
+            o[q] = narrow1<E>(__builtin_fmaf(acc[i][q], a.scale, widen1<E>(ycur[i][q])));
+          *reinterpret_cast<u16x4*>(out + rows_lds[h + i] * h3 + a.y_offset + 4 * cg) = o;
+        }
       }
+#pragma unroll
+      for (int i = 0; i < kStepRows; ++i) ycur[i] = ynext[i];
     }
   }
-
-  // ---- out != y: the columns outside the slice are copied
-  if (!a.in_place) {
+  if (!a.in_place) {  // this range's columns outside the slice
     const int64_t s0 = a.y_offset / 4, s1 = (a.y_offset + a.h2) / 4;
-    for (int i = 0; i < nrows; ++i) {
+    for (int i = 0; i < n; ++i) {
       const int64_t row = rows_lds[i];
-      for (int64_t c4 = tid; c4 < h3 / 4; c4 += kThreads)
+      for (int64_t c4 = c0 + tid; c4 < c1; c4 += kThreads)
         if (c4 < s0 || c4 >= s1)
           *reinterpret_cast<uint2*>(out + row * h3 + 4 * c4) =
               *reinterpret_cast<const uint2*>(y + row * h3 + 4 * c4);
@@ -335,27 +496,43 @@ __global__ void __launch_bounds__(kThreads) lora_generic_kernel(const LoraArgs a
   }
 }
 
+template <int E, int R>
+hipError_t launch_tiled(const LoraArgs& a, const Workspace& ws, hipStream_t s) {
+  const int64_t tiles = lora_max_tiles(a);
+  hipLaunchKernelGGL(lora_group_kernel, dim3(1), dim3(kGroupThreads), 0, s, a, ws);
+  if (a.wa)
+    hipLaunchKernelGGL(lora_shrink_kernel<E>, dim3((unsigned)(tiles * a.ksplit)), dim3(kThreads),
+                       0, s, a, ws);
+  hipLaunchKernelGGL((lora_expand_kernel<E, R>), dim3((unsigned)(tiles * a.chunks)),
+                     dim3(kThreads), 0, s, a, ws);
+  return hipGetLastError();
+}
+
 template <int E>
-hipError_t launch_elem(const LoraArgs& a, int path, hipStream_t s) {
+hipError_t launch_elem(const LoraArgs& a, int path, void* workspace, hipStream_t s) {
   if (path == kLoraTiled) {
-    hipLaunchKernelGGL(lora_tiled_kernel<E>, dim3((unsigned)lora_tiled_grid(a)), dim3(kThreads),
-                       0, s, a);
-  } else {
-    const int64_t grid = a.rows < 65536 ? a.rows : 65536;
-    hipLaunchKernelGGL(lora_generic_kernel<E>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    const Workspace ws = ws_layout(workspace, a);
+    switch (a.rank) {
+      case 16: return launch_tiled<E, 16>(a, ws, s);
+      case 32: return launch_tiled<E, 32>(a, ws, s);
+      case 64: return launch_tiled<E, 64>(a, ws, s);
+      default: return hipErrorInvalidValue;
+    }
   }
+  const int64_t grid = a.rows < 65536 ? a.rows : 65536;
+  hipLaunchKernelGGL(lora_generic_kernel<E>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int64_t lora_tiled_grid(const LoraArgs& a) {
-  return (a.rows + kTile - 1) / kTile + a.w + 1;
-}
+int64_t lora_max_tiles(const LoraArgs& a) { return lora_max_tiles_dev(a); }
 
-hipError_t launch_lora(const LoraArgs& a, int path, hipStream_t stream) {
-  return a.elem == kBF16 ? launch_elem<kBF16>(a, path, stream)
-                         : launch_elem<kF16>(a, path, stream);
+uint64_t lora_workspace_bytes(const LoraArgs& a) { return ws_offsets(a).end; }
+
+hipError_t launch_lora(const LoraArgs& a, int path, void* workspace, hipStream_t stream) {
+  return a.elem == kBF16 ? launch_elem<kBF16>(a, path, workspace, stream)
+                         : launch_elem<kF16>(a, path, workspace, stream);
 }
 
 }  // namespace adq
