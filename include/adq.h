@@ -159,10 +159,10 @@ adq_status adq_rms_norm_dynamic_quant(void* workspace, uint64_t workspace_size,
  *   out[..., j] = (sum_k a[..., k] * w[j, k]) * a_scale[...] * w_scale[j] + bias[j]
  *
  * a        [..., k] ADQ_INT8, row-major, 16-byte aligned (e.g. y1_out)
- * a_scale  F32 with one value per row of a (e.g. scale1_out)
+ * a_scale  F32 with one value per row of a (e.g. scale1_out), 4-byte aligned
  * w        [n, k] ADQ_INT8, row-major (each output's weights contiguous), 16-byte aligned
- * w_scale  [n] F32
- * bias     [n] F32, or NULL
+ * w_scale  [n] F32, 4-byte aligned
+ * bias     [n] F32 (4-byte aligned), or NULL
  * out      [..., n] F32, BF16 or F16 (rounded to nearest even from fp32)
  * k must be a multiple of 16 and at most 131072 (the integer sum stays in
  * int32); n at most 1048576.  The integer sum is exact; the epilogue is
@@ -202,7 +202,11 @@ adq_status adq_w8a8_gemm(void* workspace, uint64_t workspace_size, adq_executor*
  *            not overlap y.
  * Arithmetic in fp32 (Z1 is not rounded between the two products); each
  * slice value is rounded once to the storage type.  W <= 2048, rank <= 1024.
- * Workspace size is 0.  Errors as for the other phase-1 calls.
+ * Workspace: the tiled path (see adq_path) needs one, 8-byte aligned, whose
+ * contents need not be initialised (tile table, grouped row order and
+ * partial sums, rewritten by every launch; calls that share a workspace
+ * must not overlap); the generic path needs none.  Errors as for the other
+ * phase-1 calls.
  */
 adq_status adq_add_lora_get_workspace_size(const adq_tensor* y, const adq_tensor* x,
                                            const adq_tensor* weight_b,

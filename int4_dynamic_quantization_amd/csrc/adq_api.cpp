@@ -646,6 +646,9 @@ adq_status adq_w8a8_gemm_get_workspace_size(const adq_tensor* a, const adq_tenso
   if (out->shape[out->ndim - 1] != n) return fail(ADQ_ERR_PARAM_INVALID, "out must be [..., n]");
   if (!aligned(a->data, 16) || !aligned(w->data, 16))
     return fail(ADQ_ERR_PARAM_INVALID, "a and w must be 16-byte aligned");
+  if (!aligned(a_scale->data, 4) || !aligned(w_scale->data, 4) ||
+      (bias && !aligned(bias->data, 4)) || !aligned(out->data, out->dtype == ADQ_F32 ? 4 : 2))
+    return fail(ADQ_ERR_PARAM_INVALID, "scales, bias and out must be aligned to their element size");
   adq_executor e{};
   e.op = kOpGemm;
   st = current_device(&e.device, &e.cus);

@@ -257,6 +257,7 @@ def test_gemm_validation():
     a = full_gemm(); a["out"] = fake([64, 47], adq.BF16); bad.append(a)
     a = full_gemm(); a["out"] = fake([63, 48], adq.BF16); bad.append(a)
     a = full_gemm(); a["a"].data += 8; bad.append(a)                           # alignment
+    a = full_gemm(); a["sa"].data += 2; bad.append(a)
     a = full_gemm(); a["out"].shape[0] = 0; bad.append(a)
     for i, c in enumerate(bad):
         assert gemm_call(**c) == adq.ERR_PARAM_INVALID, (i, adq.last_error())
