@@ -19,19 +19,18 @@
 //     4 wavefronts each take 16 rows (v_mfma_f32_16x16x32_{bf16,f16}, the
 //     x fragments of 4 k-steps loaded together) and write fp32 partial sums
 //     to the workspace.
-//  3. expand: one workgroup per (tile, range of columns).  Z1 = the slices'
-//     partial sums added in slice order; each thread owns 4 adjacent columns,
-//     keeps their weightB values for all ranks in registers, and walks the
-//     tile's rows 8 at a time (y loaded before the arithmetic), fp32 fma,
-//     one rounding, 8-byte stores.  Rows without an adapter and, when out is
-//     not y, the columns outside the slice are copied here.
+//  3. expand: one workgroup per (tile, 512 columns of the slice).  The
+//     tile's row pieces of y (1 KB each) are brought into LDS by direct loads
+//     issued first, so a workgroup has all of its y in flight at once without
+//     holding registers; Z1 = the slices' partial sums added in slice order;
+//     each thread owns 4 adjacent columns (weightB values for rank 16 kept in
+//     registers) and half of the tile's rows, fp32 fma into y, one rounding,
+//     8-byte stores.  Rows without an adapter and, when out is not y, the
+//     columns outside the slice are copied here.
 // Generic kernel: one workgroup per row, any sizes and alignments, same
 // arithmetic with block reductions in a fixed order.
 #include "adq_device.h"
 
-#ifndef ADQ_LORA_EXPAND_WAVES
-#define ADQ_LORA_EXPAND_WAVES 3
-#endif
 
 namespace adq {
 
@@ -49,8 +48,7 @@ constexpr int kKSub = 256;            // k per LDS stage of weightA
 // lanes of a pass then hit 16 distinct 4-bank groups.
 constexpr int kAtStride = kKSub + 32;
 constexpr int kCW = 128;              // expand: threads per row half (groups of 4 columns)
-constexpr int kHalf = kTile / 2;      // expand: rows per thread
-constexpr int kStepRows = 4;          // expand: rows per step (the next step's y is prefetched)
+constexpr int kChunkCols = 4 * kCW;   // expand: columns of the slice per workgroup
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -278,13 +276,17 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
       }
 }
 
-// ---- 3. expand + accumulate for one tile and one range of columns
+// ---- 3. expand + accumulate for one tile and one range of 512 columns
 template <int E, int R>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(R <= 32 ? ADQ_LORA_EXPAND_WAVES : 2)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 lora_expand_kernel(const LoraArgs a, Workspace ws) {
   __shared__ int64_t rows_lds[kTile];
   __shared__ __attribute__((aligned(16))) float z1[kTile][R];
+  // the tile's rows of y's slice in this column range, filled by direct-to-LDS loads
+  __shared__ __attribute__((aligned(1024))) uint16_t ys[kTile][kChunkCols];
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = (int)(blockIdx.x / a.chunks);
   const int chunk = (int)(blockIdx.x % a.chunks);
   const int ntiles = ws.header[0];
@@ -297,6 +299,7 @@ lora_expand_kernel(const LoraArgs a, Workspace ws) {
   const T* y = static_cast<const T*>(a.y);
   T* out = static_cast<T*>(a.out);
   const int64_t h3 = a.h3;
+  // this range's share of whole rows (copies when out is not y), in groups of 4 columns
   const int64_t ncg_row = h3 / 4;
   const int64_t per_row = (ncg_row + a.chunks - 1) / a.chunks;
   const int64_t c0 = chunk * per_row;
@@ -311,6 +314,24 @@ lora_expand_kernel(const LoraArgs a, Workspace ws) {
     }
     return;
   }
+  // columns [cs, ce) of the slice
+  const int64_t cs = (int64_t)chunk * kChunkCols;
+  const int64_t ce = cs + kChunkCols < a.h2 ? cs + kChunkCols : a.h2;
+
+  // y's rows of this tile and range -> LDS, one 1 KB row piece per instruction
+  // (lane l: columns cs + 8 l .. + 7); lanes past the range read nothing.
+  {
+    const rsrc_t ry = make_rsrc(y, (uint32_t)(a.rows * h3 * 2));
+    const uint32_t col_off = cs + 8 * lane < ce ? (uint32_t)((a.y_offset + cs + 8 * lane) * 2)
+                                                : 0xFFFFFFF0u;
+    using lds_ptr = __attribute__((address_space(3))) void*;
+    for (int i = wave; i < n; i += kThreads / 64) {
+      const uint32_t off = col_off == 0xFFFFFFF0u ? col_off
+                                                  : (uint32_t)(rows_lds[i] * h3 * 2) + col_off;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_ptr)&ys[i][0], 16, off, 0, 0, 0);
+    }
+  }
+
   // z1 = the slices' partial sums, in slice order (or x itself without weightA);
   // all of a thread's partial loads are issued before any is added
   constexpr int ZP = kTile * R / kThreads;  // elements per thread
@@ -347,40 +368,28 @@ lora_expand_kernel(const LoraArgs a, Workspace ws) {
       z1[i][r] = i < n ? widen1<E>(static_cast<const T*>(a.x)[rows_lds[i] * a.h1 + r]) : 0.0f;
     }
   }
+
+  // thread -> (group of 4 columns, half of the tile's rows)
+  const T* wb = static_cast<const T*>(a.wb) + ((g * a.l + a.layer) * R) * a.h2;
+  const int cgl = tid % kCW;
+  const int64_t col = cs + 4 * cgl;  // this thread's first column of the slice
+  const bool col_ok = col < ce;
+  const int half = tid / kCW;
+  u16x4 bw16[16];
+  if constexpr (R == 16) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      bw16[r] = col_ok ? *reinterpret_cast<const u16x4*>(wb + r * a.h2 + col) : u16x4{0, 0, 0, 0};
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the row pieces have landed
   __syncthreads();
 
-  const T* wb = static_cast<const T*>(a.wb) + ((g * a.l + a.layer) * R) * a.h2;
-  const int64_t ncg = a.h2 / 4;
-  const int64_t per = (ncg + a.chunks - 1) / a.chunks;
-  const int64_t e0 = chunk * per;
-  const int64_t e1 = e0 + per < ncg ? e0 + per : ncg;
-  // thread -> (group of 4 columns, half of the tile's rows)
-  const int half = tid / kCW;
-  const int hr0 = half * kHalf;
-  const int hr1 = hr0 + kHalf < n ? hr0 + kHalf : n;
-  for (int64_t cg = e0 + tid % kCW; cg < e1; cg += kCW) {
-    if (hr0 >= hr1) break;
-    // weightB[r][4 cg .. 4 cg + 3]: kept in registers for rank 16, otherwise
-    // read again (from cache) for each 16 ranks of each step of rows
-    u16x4 bw16[16];
-    if constexpr (R == 16) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) bw16[r] = *reinterpret_cast<const u16x4*>(wb + r * a.h2 + 4 * cg);
-    }
-    auto load_y = [&](int h, u16x4* yv) {
-#pragma unroll
-      for (int i = 0; i < kStepRows; ++i)
-        if (h + i < hr1)
-          yv[i] = *reinterpret_cast<const u16x4*>(y + rows_lds[h + i] * h3 + a.y_offset + 4 * cg);
-    };
-    u16x4 ycur[kStepRows], ynext[kStepRows];
-    load_y(hr0, ycur);
+  if (col_ok) {
 #pragma unroll 1
-    for (int h = hr0; h < hr1; h += kStepRows) {
-      if (h + kStepRows < hr1) load_y(h + kStepRows, ynext);  // next rows while these compute
-      float acc[kStepRows][4];
+    for (int h = half * 4; h < n; h += 8) {  // rows h .. h + 3, then the next 8
+      float acc[4][4];
 #pragma unroll
-      for (int i = 0; i < kStepRows; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[i][q] = 0.0f;
 #pragma unroll 1
@@ -388,8 +397,7 @@ lora_expand_kernel(const LoraArgs a, Workspace ws) {
         u16x4 bw[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          bw[r] = R == 16 ? bw16[r]
-                          : *reinterpret_cast<const u16x4*>(wb + (rc + r) * a.h2 + 4 * cg);
+          bw[r] = R == 16 ? bw16[r] : *reinterpret_cast<const u16x4*>(wb + (rc + r) * a.h2 + col);
 #pragma unroll
         for (int r4 = 0; r4 < 16; r4 += 4) {
           float b[4][4];
@@ -398,7 +406,7 @@ lora_expand_kernel(const LoraArgs a, Workspace ws) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) b[u][q] = widen1<E>(bw[r4 + u][q]);
 #pragma unroll
-          for (int i = 0; i < kStepRows; ++i) {
+          for (int i = 0; i < 4; ++i) {
             const f32x4 zz = *reinterpret_cast<const f32x4*>(&z1[h + i][rc + r4]);
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -408,19 +416,19 @@ lora_expand_kernel(const LoraArgs a, Workspace ws) {
         }
       }
 #pragma unroll
-      for (int i = 0; i < kStepRows; ++i) {
-        if (h + i < hr1) {
+      for (int i = 0; i < 4; ++i) {
+        if (h + i < n) {
+          const u16x4 yv = *reinterpret_cast<const u16x4*>(&ys[h + i][4 * cgl]);
           u16x4 o;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            o[q] = narrow1<E>(__builtin_fmaf(acc[i][q], a.scale, widen1<E>(ycur[i][q])));
-          *reinterpret_cast<u16x4*>(out + rows_lds[h + i] * h3 + a.y_offset + 4 * cg) = o;
+            o[q] = narrow1<E>(__builtin_fmaf(acc[i][q], a.scale, widen1<E>(yv[q])));
+          *reinterpret_cast<u16x4*>(out + rows_lds[h + i] * h3 + a.y_offset + col) = o;
         }
       }
-#pragma unroll
-      for (int i = 0; i < kStepRows; ++i) ycur[i] = ynext[i];
     }
   }
+
   if (!a.in_place) {  // this range's columns outside the slice
     const int64_t s0 = a.y_offset / 4, s1 = (a.y_offset + a.h2) / 4;
     for (int i = 0; i < n; ++i) {

@@ -103,12 +103,18 @@ def small_ints(seed, tid, shape, lo, hi, dt):
 
 EXACT = [
     # rows, h1, rank, h2, h3, w, layers, layer, off, has_a, dt
-    (37, 64, 16, 48, 100, 3, 2, 1, 20, True, "bf16"),
+    (37, 64, 16, 48, 104, 3, 2, 1, 24, True, "bf16"),
     (100, 256, 32, 128, 256, 5, 3, 2, 128, True, "fp16"),
     (17, 16, 16, 64, 64, 2, 1, 0, 0, False, "bf16"),
-    (300, 512, 64, 96, 400, 7, 2, 0, 300, True, "bf16"),
-    (5, 30, 5, 7, 13, 2, 2, 1, 3, True, "fp16"),      # generic only (ragged)
+    (300, 512, 64, 96, 400, 7, 2, 0, 296, True, "bf16"),
+    (33, 64, 16, 52, 120, 3, 2, 1, 64, True, "bf16"),   # slice width 4 (mod 8)
+    (37, 64, 16, 48, 100, 3, 2, 1, 20, True, "bf16"),   # y rows not 16-byte aligned: generic
+    (5, 30, 5, 7, 13, 2, 2, 1, 3, True, "fp16"),        # generic only (ragged)
 ]
+
+
+def tiled_expected(h1, rank, h2, h3, off):
+    return h1 % 8 == 0 and rank in (16, 32, 64) and h2 % 4 == 0 and h3 % 8 == 0 and off % 8 == 0
 
 
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
@@ -122,10 +128,8 @@ def test_exact_integers(case, path):
     wb = small_ints(s, 15, (w, layers, rank, h2), -2, 2, dt)
     idx = synth.int32s(s, 16, -1, w, rows)
     got, desc = run_lora(y, x, wa, wb, idx, layer, 0.5, off, dt, path)
-    if path == adq.PATH_AUTO and h1 % 8 == 0 and rank % 16 == 0:
-        assert "lora-tiled" in desc, desc
-    if path == adq.PATH_GENERIC or rank % 16:
-        assert "lora-generic" in desc, desc
+    tiled = path == adq.PATH_AUTO and tiled_expected(h1, rank, h2, h3, off)
+    assert ("lora-tiled" if tiled else "lora-generic") in desc, desc
     ref, _ = oracle.add_lora(y, x, wb, idx, wa, layer, 0.5, off, dt)
     assert np.array_equal(got, ref), desc
 
