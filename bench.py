@@ -93,6 +93,80 @@ def measured_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def host_threads() -> int:
+    """Host cores this process may use (at most 16: one GPU's share of the
+    host), for the multi-threaded oracle leg."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def threaded_wall(fn, n_items: int, threads: int) -> float:
+    """Wall time of fn(lo, hi) over [0, n_items) cut into `threads`
+    contiguous parts run at once (the oracle's C calls release the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+    parts = [(n_items * i // threads, n_items * (i + 1) // threads) for i in range(threads)]
+    parts = [p for p in parts if p[1] > p[0]]
+    with ThreadPoolExecutor(len(parts)) as pool:
+        t0 = time.perf_counter()
+        list(pool.map(lambda p: fn(*p), parts))
+        return time.perf_counter() - t0
+
+
+def timed_copy_us(torch, nbytes: int, steps: int = 20) -> float:
+    """Average time of a plain device copy of `nbytes` bytes (torch's copy
+    kernel), HIP events around back-to-back copies, rotating through enough
+    buffer pairs that every copy streams from HBM."""
+    sets = max(1, math.ceil(512e6 / (2 * nbytes)))
+    bufs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1),
+             torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")) for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+    for i in range(3):
+        bufs[i % sets][1].copy_(bufs[i % sets][0])
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        bufs[i % sets][1].copy_(bufs[i % sets][0])
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) / steps * 1e3
+    del bufs
+    torch.cuda.empty_cache()
+    return us
+
+
+def device_context(torch, step_bytes: int) -> dict:
+    """The device's own figures, as context for the bandwidth numbers: the
+    memory clock and bus width it reports, a plain 1 GiB device copy, and a
+    plain copy moving the same number of bytes as one step (half read, half
+    written), both timed with HIP events as read + write bytes / time."""
+    import ctypes
+    props = torch.cuda.get_device_properties(0)
+    ctx = {"device": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        # hipDeviceAttributeMemoryBusWidth = 59, hipDeviceAttributeMemoryClockRate = 60
+        # (kHz) in hip_runtime_api.h of ROCm 7
+        val = ctypes.c_int()
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 59, torch.cuda.current_device()) == 0:
+            ctx["memory_bus_bits"] = val.value
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 60, torch.cuda.current_device()) == 0:
+            ctx["memory_clock_mhz"] = val.value / 1000
+    except OSError:
+        pass
+    us = timed_copy_us(torch, 1 << 29)
+    ctx["copy_1gib_gbs"] = round(2 * (1 << 29) / us / 1e3, 1)
+    if step_bytes > 0:
+        half = step_bytes // 2
+        us = timed_copy_us(torch, half)
+        ctx["copy_same_bytes"] = {"bytes": 2 * half, "us": round(us, 1),
+                                  "gbs": round(2 * half / us / 1e3, 1)}
+    return ctx
+
+
 def make_case(w, torch, adq, synth, dev, path=0):
     x1, x2 = synth.inputs(w)
     g, b, s1, s2 = synth.params(w)
@@ -130,15 +204,31 @@ def cpu_baseline(w, active, host_inputs, budget_s: float):
                                want_pre=False)
         return time.perf_counter() - t0
 
+    def run_part(lo, hi):
+        if w.op == "v2":
+            oracle.add_rms_norm_dq_v2(x1[lo:hi], x2[lo:hi], g, b, s1, s2, w.eps, w.mask,
+                                      w.y_types[0], w.y_types[1], w.dtype, want_pre=False)
+        else:
+            oracle.rms_norm_dq(x1[lo:hi], g, b, s1, w.eps, w.y_types[0], w.dtype,
+                               want_pre=False)
+
     pilot = min(w.rows, 16)
     t = run(pilot)
     rows = int(max(pilot, min(w.rows, budget_s / max(t / pilot, 1e-9))))
     t = run(rows)
     gbs = alg_bytes(w, active, rows) / t / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} of {w.rows} rows of the same seeded inputs, "
-                      f"{t:.2f} s, single-threaded plain-C fp64 oracle "
-                      f"({rows / t:.0f} rows/s)"}
+    single = {"value": round(gbs, 4), "cores": 1,
+              "sample": f"first {rows} of {w.rows} rows, {t:.2f} s ({rows / t:.0f} rows/s)"}
+    # the same oracle, rows split over the host's cores
+    threads = host_threads()
+    rows_mt = min(w.rows, rows * threads)
+    t_mt = threaded_wall(run_part, rows_mt, threads)
+    gbs_mt = alg_bytes(w, active, rows_mt) / t_mt / 1e9
+    return {"value": round(gbs_mt, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows_mt} of {w.rows} rows of the same seeded inputs split over "
+                      f"{threads} threads, {t_mt:.2f} s wall, plain-C fp64 oracle "
+                      f"({rows_mt / t_mt:.0f} rows/s)",
+            "single_thread": single}
 
 
 def main():
@@ -248,6 +338,7 @@ def main():
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
     }
+    result["context"] = device_context(torch, footprint)
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(w, active, cases[0][2], args.cpu_budget)
     else:
@@ -276,9 +367,21 @@ def gemm_cpu_baseline(a, sa, w, sw, b, k: int, budget_s: float):
     count = int(max(pilot, budget_s / max(t / pilot, 1e-9)))
     t = run(count)
     tops = 2.0 * k * count / t / 1e12
-    return {"value": round(tops, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
-            "sample": f"{count} randomly placed outputs of the same seeded inputs "
-                      f"(2*k ops each), {t:.2f} s, single-threaded plain-C int64 oracle"}
+    single = {"value": round(tops, 6), "cores": 1,
+              "sample": f"{count} randomly placed outputs, {t:.2f} s"}
+    # the same oracle, the sampled outputs split over the host's cores
+    threads = host_threads()
+    count_mt = count * threads
+    rows = rng.integers(0, a.shape[0], count_mt)
+    cols = rng.integers(0, w.shape[0], count_mt)
+    t_mt = threaded_wall(lambda lo, hi: oracle.w8a8_gemm_at(a, sa, w, sw, b, rows[lo:hi],
+                                                            cols[lo:hi]), count_mt, threads)
+    tops_mt = 2.0 * k * count_mt / t_mt / 1e12
+    return {"value": round(tops_mt, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{count_mt} randomly placed outputs of the same seeded inputs "
+                      f"(2*k ops each) split over {threads} threads, {t_mt:.2f} s wall, "
+                      f"plain-C int64 oracle",
+            "single_thread": single}
 
 
 def bench_gemm(args, torch, adq, synth) -> None:
@@ -336,6 +439,7 @@ def bench_gemm(args, torch, adq, synth) -> None:
                      "traffic": measured_traffic(w8.name)},
     }
     ex.close()
+    result["context"] = device_context(torch, 0)
     result["cpu_baseline"] = (gemm_cpu_baseline(a, sa, wq, sw, b, w8.k, args.cpu_budget)
                               if args.cpu_budget > 0 else None)
     print(json.dumps(result), flush=True)
@@ -370,9 +474,20 @@ def lora_cpu_baseline(wl, host, alg_rows_bytes, budget_s: float):
     rows = int(max(pilot, min(wl.rows, budget_s / max(t / pilot, 1e-9))))
     t = run(rows)
     gbs = alg_rows_bytes * rows / wl.rows / t / 1e9
-    return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} of {wl.rows} rows of the same seeded inputs, {t:.2f} s, "
-                      f"single-threaded plain-C fp64 oracle ({rows / t:.1f} rows/s)"}
+    single = {"value": round(gbs, 5), "cores": 1,
+              "sample": f"first {rows} of {wl.rows} rows, {t:.2f} s ({rows / t:.1f} rows/s)"}
+    # the same oracle, rows split over the host's cores
+    threads = host_threads()
+    rows_mt = min(wl.rows, rows * threads)
+    t_mt = threaded_wall(lambda lo, hi: oracle.add_lora(
+        y[lo:hi], x[lo:hi], wb, idx[lo:hi], wa, wl.layer, wl.scale, wl.y_offset, wl.dtype,
+        want_pre=False), rows_mt, threads)
+    gbs_mt = alg_rows_bytes * rows_mt / wl.rows / t_mt / 1e9
+    return {"value": round(gbs_mt, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows_mt} of {wl.rows} rows of the same seeded inputs split over "
+                      f"{threads} threads, {t_mt:.2f} s wall, plain-C fp64 oracle "
+                      f"({rows_mt / t_mt:.1f} rows/s)",
+            "single_thread": single}
 
 
 def bench_lora(args, torch, adq, synth) -> None:
@@ -442,6 +557,7 @@ def bench_lora(args, torch, adq, synth) -> None:
     }
     for ex, _, _, _ in cases:
         ex.close()
+    result["context"] = device_context(torch, alg)
     result["cpu_baseline"] = (lora_cpu_baseline(wl, host, alg, args.cpu_budget)
                               if args.cpu_budget > 0 else None)
     print(json.dumps(result), flush=True)

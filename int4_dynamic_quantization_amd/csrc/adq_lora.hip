@@ -187,10 +187,10 @@ __global__ void __launch_bounds__(kGroupThreads) lora_group_kernel(const LoraArg
 }
 
 // ---- 2. shrink: partial z1 over one slice of h1 for one tile
-template <int E>
+template <int E, int R>
 __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a, Workspace ws) {
   __shared__ int64_t rows_lds[kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t at[kLoraMaxRankTiled][kAtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t at[R][kAtStride];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -204,8 +204,9 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
   if (g >= a.w) return;  // rows without an adapter
   if (tid < n) rows_lds[tid] = rid;
   using T = uint16_t;
-  const int64_t rank = a.rank, h1 = a.h1;
-  const int nb = (int)(rank / 16);
+  constexpr int64_t rank = R;
+  const int64_t h1 = a.h1;
+  constexpr int nb = R / 16;
   const T* wa = static_cast<const T*>(a.wa) + ((g * a.l + a.layer) * h1) * rank;
   const T* x = static_cast<const T*>(a.x);
   const int64_t kc = ((h1 + a.ksplit - 1) / a.ksplit + 31) / 32 * 32;
@@ -214,13 +215,13 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
 
   const int fi = lane & 15, fk = lane >> 4;
   const int rb = 16 * wave;  // this wavefront's rows of the tile
-  f32x4 acc[kLoraMaxRankTiled / 16];
+  f32x4 acc[nb];
 #pragma unroll
-  for (int b = 0; b < kLoraMaxRankTiled / 16; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < nb; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
   const bool row_ok = rb + fi < n;
   const T* xrow = x + (row_ok ? rows_lds[rb + fi] : rows_lds[0]) * h1;
-  const int pieces_per_k = (int)(rank / 8);
+  constexpr int pieces_per_k = R / 8;
   for (int64_t sub = k_lo; sub < k_hi; sub += kKSub) {
     const int sub_n = (int)(k_hi - sub < kKSub ? k_hi - sub : kKSub);
     const int steps = (sub_n + 31) / 32;
@@ -251,8 +252,8 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
         if (u < steps) {
           const int kg = 4 * u + fk;
 #pragma unroll
-          for (int b = 0; b < kLoraMaxRankTiled / 16; ++b) {
-            if (b < nb) {
+          for (int b = 0; b < nb; ++b) {
+            {
               const int r = 16 * b + fi;
               const u16x8 bv =
                   *reinterpret_cast<const u16x8*>(&at[r][8 * (kg ^ (((r >> 3) & 1) << 1))]);
@@ -267,8 +268,7 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
   // element e of lane l: row rb + 4 * (l / 16) + e, rank l % 16 (+ 16 * block)
   float* zp = ws.z1p + ((int64_t)ks * lora_max_tiles_dev(a) + tile) * kTile * rank;
 #pragma unroll
-  for (int b = 0; b < kLoraMaxRankTiled / 16; ++b)
-    if (b < nb)
+  for (int b = 0; b < nb; ++b)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = rb + 4 * fk + e;
@@ -287,11 +287,15 @@ lora_expand_kernel(const LoraArgs a, Workspace ws) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tile = (int)(blockIdx.x / a.chunks);
-  const int chunk = (int)(blockIdx.x % a.chunks);
+  // workgroup b runs on XCD b % 8 (the dispatcher deals workgroups to the XCDs
+  // in turn): all column ranges of a tile go to one XCD, so its partial sums
+  // are fetched into one L2
+  const int xcd = (int)(blockIdx.x % 8), j = (int)(blockIdx.x / 8);
+  const int tile = xcd + 8 * (int)(j / a.chunks);
+  const int chunk = (int)(j % a.chunks);
   const int ntiles = ws.header[0];
   const int4 te = ws.table[tile < ntiles ? tile : 0];
-  const int32_t rid = ws.rows[(int64_t)tile * kTile + tid % kTile];  // with the table
+  const int32_t rid = ws.rows[(int64_t)(tile < ntiles ? tile : 0) * kTile + tid % kTile];
   if (tile >= ntiles) return;
   const int g = te.x, n = te.z;
   if (tid < n) rows_lds[tid] = rid;
@@ -509,9 +513,9 @@ hipError_t launch_tiled(const LoraArgs& a, const Workspace& ws, hipStream_t s) {
   const int64_t tiles = lora_max_tiles(a);
   hipLaunchKernelGGL(lora_group_kernel, dim3(1), dim3(kGroupThreads), 0, s, a, ws);
   if (a.wa)
-    hipLaunchKernelGGL(lora_shrink_kernel<E>, dim3((unsigned)(tiles * a.ksplit)), dim3(kThreads),
+    hipLaunchKernelGGL((lora_shrink_kernel<E, R>), dim3((unsigned)(tiles * a.ksplit)), dim3(kThreads),
                        0, s, a, ws);
-  hipLaunchKernelGGL((lora_expand_kernel<E, R>), dim3((unsigned)(tiles * a.chunks)),
+  hipLaunchKernelGGL((lora_expand_kernel<E, R>), dim3((unsigned)((tiles + 7) / 8 * 8 * a.chunks)),
                      dim3(kThreads), 0, s, a, ws);
   return hipGetLastError();
 }
