@@ -506,7 +506,8 @@ def bench_lora(args, torch, adq, synth) -> None:
     for _ in range(n_sets):
         ty, tx = d(y), d(x)
         ex, _ = adq.plan_add_lora(ty, tx, tw[0], tw[2], tw[1], wl.layer, wl.scale, wl.y_offset,
-                                  out=ty)
+                                  out=ty, path=adq.PATH_GENERIC if args.path == "generic"
+                                  else adq.PATH_AUTO)
         ws = (torch.empty(ex.workspace_size, dtype=torch.uint8, device=dev)
               if ex.workspace_size else None)
         cases.append((ex, ws, ty, tx))

@@ -235,9 +235,6 @@ uint64_t next_epoch() {
 #ifndef ADQ_LORA_KSPLIT_MULT
 #define ADQ_LORA_KSPLIT_MULT 1
 #endif
-#ifndef ADQ_LORA_CHUNK_CGS
-#define ADQ_LORA_CHUNK_CGS 128
-#endif
 #ifndef ADQ_GEMM_BIG_TILE
 #define ADQ_GEMM_BIG_TILE 2
 #endif
@@ -774,14 +771,14 @@ adq_status adq_add_lora_get_workspace_size(const adq_tensor* y, const adq_tensor
     // Tiles are only known on the device (they depend on the index values);
     // estimate them as rows / 64 plus one partial tile per adapter in use.
     // Slices of h1 per tile (shrink) are chosen for about four workgroups
-    // per CU, each slice at least 256 k; the expand takes ranges of 128
-    // groups of 4 columns.
+    // per CU, each slice at least 256 k; the expand takes ranges of 1024
+    // columns of the slice.
     const int64_t est_tiles = (rows + adq::kLoraTileRows - 1) / adq::kLoraTileRows +
                               (w < rows ? w : rows);
     const int64_t want = (2 * (int64_t)e.cus + est_tiles - 1) / est_tiles;
     auto clamp = [](int64_t v, int64_t hi) { return (int)(v < 1 ? 1 : v > hi ? hi : v); };
     a.ksplit = clamp(ADQ_LORA_KSPLIT_MULT * want, h1 / 256 > 1 ? h1 / 256 : 1);
-    a.chunks = clamp((h2 / 4 + ADQ_LORA_CHUNK_CGS - 1) / ADQ_LORA_CHUNK_CGS, 1 << 20);
+    a.chunks = adq::lora_expand_chunks(h2);
   }
   e.path = e.lora_tiled_ok ? ADQ_PATH_AUTO : ADQ_PATH_GENERIC;
   e.ws_bytes = e.lora_tiled_ok ? adq::lora_workspace_bytes(a) : 0;

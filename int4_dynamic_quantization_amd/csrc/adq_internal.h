@@ -115,6 +115,7 @@ constexpr int kLoraMaxRankGeneric = 1024;
 // ceil(count / 64) <= rows / 64 + w + 1), and the workspace it needs (tile
 // table, grouped row order, per-slice partial shrink results).
 int64_t lora_max_tiles(const LoraArgs& a);
+int lora_expand_chunks(int64_t h2);  // column ranges per tile in the expand
 uint64_t lora_workspace_bytes(const LoraArgs& a);
 hipError_t launch_lora(const LoraArgs& a, int path, void* workspace, hipStream_t stream);
 

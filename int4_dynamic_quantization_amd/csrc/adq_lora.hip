@@ -19,14 +19,14 @@
 //     4 wavefronts each take 16 rows (v_mfma_f32_16x16x32_{bf16,f16}, the
 //     x fragments of 4 k-steps loaded together) and write fp32 partial sums
 //     to the workspace.
-//  3. expand: one workgroup per (tile, 512 columns of the slice).  The
-//     tile's row pieces of y (1 KB each) are brought into LDS by direct loads
-//     issued first, so a workgroup has all of its y in flight at once without
-//     holding registers; Z1 = the slices' partial sums added in slice order;
-//     each thread owns 4 adjacent columns (weightB values for rank 16 kept in
-//     registers) and half of the tile's rows, fp32 fma into y, one rounding,
-//     8-byte stores.  Rows without an adapter and, when out is not y, the
-//     columns outside the slice are copied here.
+//  3. expand: one workgroup per (16 rows of a tile, 1024 columns of the
+//     slice), all workgroups of a tile on one XCD.  Each thread owns 4
+//     adjacent columns: its 16 rows of y, its weightB values (rank 16: kept
+//     in registers) and the partial sums are all requested before anything
+//     waits; Z1 = the slices' partial sums added in slice order; fp32 fma
+//     chain over the ranks, fma into y, one rounding, 8-byte stores.  Rows
+//     without an adapter and, when out is not y, the columns outside the
+//     slice are copied here.
 // Generic kernel: one workgroup per row, any sizes and alignments, same
 // arithmetic with block reductions in a fixed order.
 #include "adq_device.h"
@@ -47,8 +47,6 @@ constexpr int kKSub = 256;            // k per LDS stage of weightA
 // wave, parity of lane bits 2 and 4, possibly with bits 0 and 3) the 16
 // lanes of a pass then hit 16 distinct 4-bank groups.
 constexpr int kAtStride = kKSub + 32;
-constexpr int kCW = 128;              // expand: threads per row half (groups of 4 columns)
-constexpr int kChunkCols = 4 * kCW;   // expand: columns of the slice per workgroup
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -276,29 +274,46 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
       }
 }
 
-// ---- 3. expand + accumulate for one tile and one range of 512 columns
+// ---- 3. expand + accumulate for 16 rows of one tile and 1024 columns
+// Thread t owns columns 4t .. 4t + 3 of the range.  All 16 rows' y values
+// (8 bytes each), the thread's weightB values and the partial sums are
+// requested before anything waits; then z1 (the slices' partial sums added
+// in slice order) goes to LDS, and each output is one fp32 fma chain over
+// the ranks, one fma into y, one rounding, an 8-byte store.
+constexpr int kQRows = 16;                  // rows per workgroup
+constexpr int kQuarters = kTile / kQRows;   // workgroups per tile and column range
+constexpr int kQCols = 4 * kThreads;        // columns per workgroup
+
 template <int E, int R>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-lora_expand_kernel(const LoraArgs a, Workspace ws) {
-  __shared__ int64_t rows_lds[kTile];
-  __shared__ __attribute__((aligned(16))) float z1[kTile][R];
-  // the tile's rows of y's slice in this column range, filled by direct-to-LDS loads
-  __shared__ __attribute__((aligned(1024))) uint16_t ys[kTile][kChunkCols];
+__global__ void __launch_bounds__(kThreads) lora_expand_kernel(const LoraArgs a,
+                                                                 Workspace ws) {
+  __shared__ __attribute__((aligned(16))) float z1[kQRows][R];
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // workgroup b runs on XCD b % 8 (the dispatcher deals workgroups to the XCDs
-  // in turn): all column ranges of a tile go to one XCD, so its partial sums
-  // are fetched into one L2
+  // in turn): all workgroups of a tile go to one XCD, so its partial sums
+  // and its adapter's weightB are fetched into one L2
+  const int per_tile = kQuarters * a.chunks;
   const int xcd = (int)(blockIdx.x % 8), j = (int)(blockIdx.x / 8);
-  const int tile = xcd + 8 * (int)(j / a.chunks);
-  const int chunk = (int)(j % a.chunks);
+  const int tile = xcd + 8 * (j / per_tile);
+  const int qt = (j % per_tile) / a.chunks;
+  const int chunk = (j % per_tile) % a.chunks;
+  // the tile count, the tile's entry and its row slots are read together
+  // (slots past the workspace's tiles are never read: tc < max tiles)
+  const int64_t mt = lora_max_tiles_dev(a);
+  const int tc = tile < mt ? tile : 0;
   const int ntiles = ws.header[0];
-  const int4 te = ws.table[tile < ntiles ? tile : 0];
-  const int32_t rid = ws.rows[(int64_t)(tile < ntiles ? tile : 0) * kTile + tid % kTile];
+  const int4 te = ws.table[tc];
+  const int4* rq = reinterpret_cast<const int4*>(ws.rows + (int64_t)tc * kTile + qt * kQRows);
+  int32_t rows[kQRows];
+#pragma unroll
+  for (int u = 0; u < kQRows / 4; ++u) {
+    const int4 v = rq[u];
+    rows[4 * u] = v.x, rows[4 * u + 1] = v.y, rows[4 * u + 2] = v.z, rows[4 * u + 3] = v.w;
+  }
   if (tile >= ntiles) return;
-  const int g = te.x, n = te.z;
-  if (tid < n) rows_lds[tid] = rid;
+  const int g = te.x;
+  const int n = te.z - qt * kQRows < kQRows ? te.z - qt * kQRows : kQRows;
+  if (n <= 0) return;
   using T = uint16_t;
   const T* y = static_cast<const T*>(a.y);
   T* out = static_cast<T*>(a.out);
@@ -308,127 +323,133 @@ lora_expand_kernel(const LoraArgs a, Workspace ws) {
   const int64_t per_row = (ncg_row + a.chunks - 1) / a.chunks;
   const int64_t c0 = chunk * per_row;
   const int64_t c1 = c0 + per_row < ncg_row ? c0 + per_row : ncg_row;
-  __syncthreads();
   if (g >= a.w) {  // rows without an adapter (listed only when out is not y): copy
     for (int i = 0; i < n; ++i) {
-      const int64_t row = rows_lds[i];
+      const int64_t row = rows[i];
       for (int64_t c4 = c0 + tid; c4 < c1; c4 += kThreads)
         *reinterpret_cast<uint2*>(out + row * h3 + 4 * c4) =
             *reinterpret_cast<const uint2*>(y + row * h3 + 4 * c4);
     }
     return;
   }
-  // columns [cs, ce) of the slice
-  const int64_t cs = (int64_t)chunk * kChunkCols;
-  const int64_t ce = cs + kChunkCols < a.h2 ? cs + kChunkCols : a.h2;
+  const int64_t col = (int64_t)chunk * kQCols + 4 * tid;  // first column of the slice
+  const bool col_ok = col < a.h2;
 
-  // y's rows of this tile and range -> LDS, one 1 KB row piece per instruction
-  // (lane l: columns cs + 8 l .. + 7); lanes past the range read nothing.
-  {
-    const rsrc_t ry = make_rsrc(y, (uint32_t)(a.rows * h3 * 2));
-    const uint32_t col_off = cs + 8 * lane < ce ? (uint32_t)((a.y_offset + cs + 8 * lane) * 2)
-                                                : 0xFFFFFFF0u;
-    using lds_ptr = __attribute__((address_space(3))) void*;
-    for (int i = wave; i < n; i += kThreads / 64) {
-      const uint32_t off = col_off == 0xFFFFFFF0u ? col_off
-                                                  : (uint32_t)(rows_lds[i] * h3 * 2) + col_off;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_ptr)&ys[i][0], 16, off, 0, 0, 0);
+  // y: every row's 4 values, all loads in flight together (rows*h3*2 < 2^32);
+  // lanes past the slice read nothing
+  const rsrc_t ry = make_rsrc(y, (uint32_t)(a.rows * h3 * 2));
+  const uint32_t col_off = col_ok ? (uint32_t)((a.y_offset + col) * 2) : 0xFFFFFFF0u;
+  uint2 yv[kQRows];
+#pragma unroll
+  for (int i = 0; i < kQRows; ++i) {
+    yv[i] = uint2{0u, 0u};
+    if (i < n) {
+      const uint32_t off = col_ok ? (uint32_t)(rows[i] * h3 * 2) + col_off : col_off;
+      yv[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ry, off, 0, 0));
     }
   }
 
-  // z1 = the slices' partial sums, in slice order (or x itself without weightA);
-  // all of a thread's partial loads are issued before any is added
-  constexpr int ZP = kTile * R / kThreads;  // elements per thread
-  const int64_t mt = lora_max_tiles_dev(a);
+  // weightB for this thread's columns (rank 16: held in registers), issued
+  // right behind y
+  const T* wb = static_cast<const T*>(a.wb) + ((g * a.l + a.layer) * R) * a.h2;
+  u16x4 bw16[16];
+  if constexpr (R == 16) {
+    const rsrc_t rb = make_rsrc(wb, (uint32_t)(16 * a.h2 * 2));
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      bw16[r] = __builtin_bit_cast(
+          u16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                     rb, col_ok ? (uint32_t)((r * a.h2 + col) * 2) : 0xFFFFFFF0u, 0, 0));
+  }
+
+  // z1 = the slices' partial sums, added in slice order (or x itself without
+  // weightA).  The first kZS slices are loaded together, behind y and
+  // weightB, with no wait in between; indices past the valid ones are
+  // clamped to a valid slot and their values dropped.
+  constexpr int ZP = (kQRows * R + kThreads - 1) / kThreads;  // elements per thread
+  constexpr int kZS = 16;
   if (a.wa) {
+    const int ksn = a.ksplit;
     float zs[ZP];
-#pragma unroll
-    for (int u = 0; u < ZP; ++u) zs[u] = 0.0f;
-    for (int ks0 = 0; ks0 < a.ksplit; ks0 += 4) {
-      float p[4][ZP];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int u = 0; u < ZP; ++u) {
-          const int t = tid + u * kThreads, i = t / R, r = t % R;
-          p[q][u] = (i < n && ks0 + q < a.ksplit)
-                        ? ws.z1p[(((int64_t)(ks0 + q) * mt + tile) * kTile + i) * R + r]
-                        : 0.0f;
-        }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int u = 0; u < ZP; ++u)
-          if (ks0 + q < a.ksplit) zs[u] = (ks0 + q == 0) ? p[q][u] : zs[u] + p[q][u];
-    }
+    int64_t zi[ZP];
 #pragma unroll
     for (int u = 0; u < ZP; ++u) {
       const int t = tid + u * kThreads;
-      z1[t / R][t % R] = zs[u];
+      const int i = t / R < n ? t / R : 0, r = t % R;
+      zi[u] = ((int64_t)tile * kTile + qt * kQRows + i) * R + r;
+    }
+    const int64_t kstride = mt * kTile * R;
+    float p[kZS][ZP];
+#pragma unroll
+    for (int k = 0; k < kZS; ++k)
+#pragma unroll
+      for (int u = 0; u < ZP; ++u) p[k][u] = ws.z1p[(k < ksn ? k : 0) * kstride + zi[u]];
+    // slices past the valid ones add +0 (their bits masked off): a partial
+    // sum is never -0 (the MFMA sums start from +0), so this is exact, and
+    // every load is used on every path (none is sunk behind a branch)
+#pragma unroll
+    for (int u = 0; u < ZP; ++u) {
+      zs[u] = p[0][u];
+#pragma unroll
+      for (int k = 1; k < kZS; ++k) {
+        const uint32_t keep = k < ksn ? 0xFFFFFFFFu : 0u;
+        zs[u] += __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p[k][u]) & keep);
+      }
+    }
+    for (int k = kZS; k < ksn; ++k)
+#pragma unroll
+      for (int u = 0; u < ZP; ++u) zs[u] += ws.z1p[k * kstride + zi[u]];
+#pragma unroll
+    for (int u = 0; u < ZP; ++u) {
+      const int t = tid + u * kThreads;
+      if (t < kQRows * R) z1[t / R][t % R] = t / R < n ? zs[u] : 0.0f;
     }
   } else {
-    for (int t = tid; t < kTile * R; t += kThreads) {
+    for (int t = tid; t < kQRows * R; t += kThreads) {
       const int i = t / R, r = t % R;
-      z1[i][r] = i < n ? widen1<E>(static_cast<const T*>(a.x)[rows_lds[i] * a.h1 + r]) : 0.0f;
+      z1[i][r] = i < n ? widen1<E>(static_cast<const T*>(a.x)[(int64_t)rows[i] * a.h1 + r])
+                       : 0.0f;
     }
   }
-
-  // thread -> (group of 4 columns, half of the tile's rows)
-  const T* wb = static_cast<const T*>(a.wb) + ((g * a.l + a.layer) * R) * a.h2;
-  const int cgl = tid % kCW;
-  const int64_t col = cs + 4 * cgl;  // this thread's first column of the slice
-  const bool col_ok = col < ce;
-  const int half = tid / kCW;
-  u16x4 bw16[16];
+  float b16[16][4];
   if constexpr (R == 16) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      bw16[r] = col_ok ? *reinterpret_cast<const u16x4*>(wb + r * a.h2 + col) : u16x4{0, 0, 0, 0};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) b16[r][q] = widen1<E>(bw16[r][q]);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the row pieces have landed
   __syncthreads();
-
   if (col_ok) {
-#pragma unroll 1
-    for (int h = half * 4; h < n; h += 8) {  // rows h .. h + 3, then the next 8
-      float acc[4][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kQRows; ++i) {
+      if (i < n) {
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][q] = 0.0f;
-#pragma unroll 1
-      for (int rc = 0; rc < R; rc += 16) {
-        u16x4 bw[16];
+        for (int rc = 0; rc < R; rc += 16) {
+          u16x4 bw[16];
+          if constexpr (R != 16) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          bw[r] = R == 16 ? bw16[r] : *reinterpret_cast<const u16x4*>(wb + (rc + r) * a.h2 + col);
+            for (int r = 0; r < 16; ++r)
+              bw[r] = *reinterpret_cast<const u16x4*>(wb + (rc + r) * a.h2 + col);
+          }
 #pragma unroll
-        for (int r4 = 0; r4 < 16; r4 += 4) {
-          float b[4][4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) b[u][q] = widen1<E>(bw[r4 + u][q]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const f32x4 zz = *reinterpret_cast<const f32x4*>(&z1[h + i][rc + r4]);
+          for (int r4 = 0; r4 < 16; r4 += 4) {
+            const f32x4 zz = *reinterpret_cast<const f32x4*>(&z1[i][rc + r4]);
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
-              for (int q = 0; q < 4; ++q) acc[i][q] = __builtin_fmaf(zz[u], b[u][q], acc[i][q]);
+              for (int q = 0; q < 4; ++q) {
+                const float bv = R == 16 ? b16[r4 + u][q] : widen1<E>(bw[r4 + u][q]);
+                acc[q] = __builtin_fmaf(zz[u], bv, acc[q]);
+              }
           }
         }
-      }
+        const u16x4 yq = __builtin_bit_cast(u16x4, yv[i]);
+        u16x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (h + i < n) {
-          const u16x4 yv = *reinterpret_cast<const u16x4*>(&ys[h + i][4 * cgl]);
-          u16x4 o;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            o[q] = narrow1<E>(__builtin_fmaf(acc[i][q], a.scale, widen1<E>(yv[q])));
-          *reinterpret_cast<u16x4*>(out + rows_lds[h + i] * h3 + a.y_offset + col) = o;
-        }
+        for (int q = 0; q < 4; ++q)
+          o[q] = narrow1<E>(__builtin_fmaf(acc[q], a.scale, widen1<E>(yq[q])));
+        *reinterpret_cast<u16x4*>(out + (int64_t)rows[i] * h3 + a.y_offset + col) = o;
       }
     }
   }
@@ -436,7 +457,7 @@ lora_expand_kernel(const LoraArgs a, Workspace ws) {
   if (!a.in_place) {  // this range's columns outside the slice
     const int64_t s0 = a.y_offset / 4, s1 = (a.y_offset + a.h2) / 4;
     for (int i = 0; i < n; ++i) {
-      const int64_t row = rows_lds[i];
+      const int64_t row = rows[i];
       for (int64_t c4 = c0 + tid; c4 < c1; c4 += kThreads)
         if (c4 < s0 || c4 >= s1)
           *reinterpret_cast<uint2*>(out + row * h3 + 4 * c4) =
@@ -515,8 +536,9 @@ hipError_t launch_tiled(const LoraArgs& a, const Workspace& ws, hipStream_t s) {
   if (a.wa)
     hipLaunchKernelGGL((lora_shrink_kernel<E, R>), dim3((unsigned)(tiles * a.ksplit)), dim3(kThreads),
                        0, s, a, ws);
-  hipLaunchKernelGGL((lora_expand_kernel<E, R>), dim3((unsigned)((tiles + 7) / 8 * 8 * a.chunks)),
-                     dim3(kThreads), 0, s, a, ws);
+  hipLaunchKernelGGL((lora_expand_kernel<E, R>),
+                     dim3((unsigned)((tiles + 7) / 8 * 8 * kQuarters * a.chunks)), dim3(kThreads),
+                     0, s, a, ws);
   return hipGetLastError();
 }
 
@@ -539,6 +561,11 @@ hipError_t launch_elem(const LoraArgs& a, int path, void* workspace, hipStream_t
 }  // namespace
 
 int64_t lora_max_tiles(const LoraArgs& a) { return lora_max_tiles_dev(a); }
+
+int lora_expand_chunks(int64_t h2) {
+  const int64_t c = (h2 + kQCols - 1) / kQCols;
+  return (int)(c < 1 ? 1 : c);
+}
 
 uint64_t lora_workspace_bytes(const LoraArgs& a) { return ws_offsets(a).end; }
 
