@@ -134,6 +134,25 @@ def test_exact_integers(case, path):
     assert np.array_equal(got, ref), desc
 
 
+@pytest.mark.parametrize("rank", [16, 32])
+def test_many_slices_of_h1(rank):
+    """Few rows and a long h1: the shrink splits h1 into more than 16 slices,
+    so the expand adds the partial sums beyond the first 16 in its second
+    loop.  Small integers keep every fp32 step exact: bit-exact."""
+    rows, h1, h2, h3, w, layers, layer, off, dt = 40, 8192, 64, 128, 3, 2, 1, 32, "bf16"
+    s = 4242 + rank
+    x = small_ints(s, 12, (rows, h1), -2, 2, dt)
+    y = small_ints(s, 13, (rows, h3), -8, 8, dt)
+    wa = small_ints(s, 14, (w, layers, h1, rank), -2, 2, dt)
+    wb = small_ints(s, 15, (w, layers, rank, h2), -2, 2, dt)
+    idx = synth.int32s(s, 16, -1, w, rows)
+    for in_place in (False, True):
+        got, desc = run_lora(y, x, wa, wb, idx, layer, 0.5, off, dt, in_place=in_place)
+        assert "lora-tiled" in desc and "ksplit=32" in desc, desc
+        ref, _ = oracle.add_lora(y, x, wb, idx, wa, layer, 0.5, off, dt)
+        assert np.array_equal(got, ref), (in_place, desc)
+
+
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("in_place", [False, True], ids=["out", "in_place"])
 @pytest.mark.parametrize("name", ["lora_small", "lora_decode"])
