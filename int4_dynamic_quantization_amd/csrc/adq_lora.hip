@@ -13,12 +13,13 @@
 //     taken with LDS atomics, so the order of rows inside a tile may vary
 //     between runs; every row's result is computed from its own data in a
 //     fixed order, so outputs do not.
-//  2. shrink: one workgroup per (tile, slice of h1).  The slice of
-//     weightA[g, layer] (stored [h1, rank], rank contiguous) is staged in LDS
-//     transposed, 256 k at a time, so each MFMA operand is one 16-byte read;
-//     4 wavefronts each take 16 rows (v_mfma_f32_16x16x32_{bf16,f16}, the
-//     x fragments of 4 k-steps loaded together) and write fp32 partial sums
-//     to the workspace.
+//  2. shrink: one workgroup per (tile, slice of h1), compiled per rank.  The
+//     slice of weightA[g, layer] (stored [h1, rank], rank contiguous) is
+//     staged in LDS transposed, 256 k at a time, so each MFMA operand is one
+//     16-byte read; 4 wavefronts each take 16 rows
+//     (v_mfma_f32_16x16x32_{bf16,f16}, the x fragments of a whole 256-k
+//     stage loaded before the staging) and write fp32 partial sums to the
+//     workspace.
 //  3. expand: one workgroup per (16 rows of a tile, 1024 columns of the
 //     slice), all workgroups of a tile on one XCD.  Each thread owns 4
 //     adjacent columns: its 16 rows of y, its weightB values (rank 16: kept

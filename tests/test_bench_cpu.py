@@ -47,3 +47,33 @@ def test_traffic_record_matches_its_hash_or_is_ignored():
     t = bench.measured_traffic("v2_outlier")
     assert t is None or t > bench.alg_bytes(synth.WORKLOADS["v2_outlier"], [True, True]) * 0.99
     assert bench.measured_traffic("no_such_workload") is None
+
+
+def test_threaded_wall_covers_every_item_once():
+    seen = []
+    import threading
+    lock = threading.Lock()
+
+    def part(lo, hi):
+        with lock:
+            seen.extend(range(lo, hi))
+
+    for n, t in ((10, 3), (7, 16), (1, 4), (64, 8)):
+        seen.clear()
+        assert bench.threaded_wall(part, n, t) >= 0.0
+        assert sorted(seen) == list(range(n))
+
+
+def test_host_threads_is_bounded():
+    assert 1 <= bench.host_threads() <= 16
+
+
+def test_lora_algorithmic_bytes_by_hand():
+    # lora_prefill: every row has an adapter (indices drawn from [0, 8)):
+    # x 4096*4096*2 + y slice read and written 2*4096*4096*2 + indices 4*4096
+    # + 8 adapters' layer weights (4096*16 + 16*4096) * 2
+    wl = synth.LORA_WORKLOADS["lora_prefill"]
+    idx = synth.lora_inputs(wl)[4]
+    assert ((idx >= 0) & (idx < wl.w)).all() and len(set(idx.tolist())) == 8
+    want = 4096 * 4096 * 2 + 2 * 4096 * 4096 * 2 + 4 * 4096 + 8 * (4096 * 16 + 16 * 4096) * 2
+    assert bench.lora_alg_bytes(wl, idx) == want == 102_776_832
