@@ -6,7 +6,9 @@
 // is fp32 (products of 16-bit inputs are exact; Z1 stays fp32 between the two
 // products); the slice is rounded once to the storage type.
 //
-// Tiled path, three launches on the caller's stream:
+// Tiled path, three launches on the caller's stream (two for batches of up
+// to 512 rows with weightA, where each shrink workgroup groups the rows
+// itself, in a fixed order, and the expand reads the table they write):
 //  1. group: one workgroup builds the page's step 1 in the workspace: a
 //     histogram of adapter classes, a table of tiles of up to 64 rows of one
 //     class, and the rows listed class by class.  Places within a class are
@@ -185,8 +187,83 @@ __global__ void __launch_bounds__(kGroupThreads) lora_group_kernel(const LoraArg
   }
 }
 
+// ---- 1'. grouping inside the shrink, for small batches
+// One workgroup finds the rows of one tile under a stable grouping: classes
+// in order, the rows of a class in index order, tiles of up to 64 rows —
+// the same tile count and table shape as the grouping kernel, with a fixed
+// order, so every workgroup computes the same grouping.  Up to kSmallRows
+// rows (kSmallRows / kThreads per thread, thread t holding rows in index
+// order).  On return (after a barrier): info[0] = the tile's class (-1 past
+// the last tile), info[1] = its row count, info[2] = the tile count, and
+// rows_lds[0 .. info[1]) its rows.
+constexpr int kSmallRows = 512;
+
+__device__ void group_one_tile(const LoraArgs& a, int tile, int* cnt, int* scan_tmp, int* info,
+                               int64_t* rows_lds) {
+  constexpr int NW = kThreads / 64;
+  constexpr int RPT = kSmallRows / kThreads;
+  const int tid = threadIdx.x;
+  const int64_t W = a.w;
+  int cls[RPT];
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    const int64_t i = (int64_t)tid * RPT + u;
+    cls[u] = i < a.rows ? adapter_class(a.indices[i], W) : -1;
+  }
+  for (int g = tid; g <= W; g += kThreads) cnt[g] = 0;
+  if (tid == 0) info[0] = -1;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < RPT; ++u)
+    if (cls[u] >= 0) atomicAdd(&cnt[cls[u]], 1);
+  __syncthreads();
+  // rows without an adapter are only listed when out is not y (to be copied)
+  auto placed = [&](int g) -> int { return (g < W || !a.in_place) ? cnt[g] : 0; };
+  const int per = (int)((W + 1 + kThreads - 1) / kThreads);
+  int tl = 0;
+  for (int q = 0; q < per; ++q) {
+    const int g = tid * per + q;
+    if (g <= W) tl += (placed(g) + kTile - 1) / kTile;
+  }
+  int ntiles = 0;
+  int tb = block_exclusive_scan<NW>(tl, scan_tmp, &ntiles);
+  for (int q = 0; q < per; ++q) {
+    const int g = tid * per + q;
+    if (g <= W) {
+      const int nt = (placed(g) + kTile - 1) / kTile;
+      if (tile >= tb && tile < tb + nt) {
+        const int s = tile - tb;
+        info[0] = g;
+        info[1] = placed(g) - s * kTile < kTile ? placed(g) - s * kTile : kTile;
+        info[3] = s;
+      }
+      tb += nt;
+    }
+  }
+  if (tid == 0) info[2] = ntiles;
+  __syncthreads();
+  const int g = info[0], s = info[3];
+  if (g < 0) return;  // uniform
+  int m = 0;
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) m += cls[u] == g;
+  int total = 0;
+  int r = block_exclusive_scan<NW>(m, scan_tmp, &total);  // place within the class
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    if (cls[u] == g) {
+      if (r >= s * kTile && r < (s + 1) * kTile) rows_lds[r - s * kTile] = (int64_t)tid * RPT + u;
+      ++r;
+    }
+  }
+  __syncthreads();
+}
+
 // ---- 2. shrink: partial z1 over one slice of h1 for one tile
-template <int E, int R>
+// G: the workgroup groups the rows itself (small batches, no grouping
+// launch); the workgroups of slice 0 then write their tile's table entry
+// and row slots, and workgroup 0 the tile count, for the expand.
+template <int E, int R, bool G>
 __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a, Workspace ws) {
   __shared__ int64_t rows_lds[kTile];
   __shared__ __attribute__((aligned(16))) uint16_t at[R][kAtStride];
@@ -195,13 +272,29 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
   const int wave = tid >> 6;
   const int tile = (int)(blockIdx.x / a.ksplit);
   const int ks = (int)(blockIdx.x % a.ksplit);
-  const int ntiles = ws.header[0];
-  const int4 te = ws.table[tile < ntiles ? tile : 0];
-  const int32_t rid = ws.rows[(int64_t)tile * kTile + tid % kTile];  // with the table
-  if (tile >= ntiles) return;
-  const int g = te.x, n = te.z;
-  if (g >= a.w) return;  // rows without an adapter
-  if (tid < n) rows_lds[tid] = rid;
+  int g, n;
+  if constexpr (G) {
+    __shared__ int cnt[kLoraMaxAdapters + 1];
+    __shared__ int scan_tmp[kThreads / 64];
+    __shared__ int info[4];
+    group_one_tile(a, tile, cnt, scan_tmp, info, rows_lds);
+    g = info[0], n = info[1];
+    if (blockIdx.x == 0 && tid == 0) ws.header[0] = info[2];
+    if (g < 0) return;  // past the last tile
+    if (ks == 0) {
+      if (tid == 0) ws.table[tile] = int4{g, 0, n, 0};
+      if (tid < n) ws.rows[(int64_t)tile * kTile + tid] = (int32_t)rows_lds[tid];
+    }
+    if (g >= a.w) return;  // rows without an adapter
+  } else {
+    const int ntiles = ws.header[0];
+    const int4 te = ws.table[tile < ntiles ? tile : 0];
+    const int32_t rid = ws.rows[(int64_t)tile * kTile + tid % kTile];  // with the table
+    if (tile >= ntiles) return;
+    g = te.x, n = te.z;
+    if (g >= a.w) return;  // rows without an adapter
+    if (tid < n) rows_lds[tid] = rid;
+  }
   using T = uint16_t;
   constexpr int64_t rank = R;
   const int64_t h1 = a.h1;
@@ -533,10 +626,16 @@ __global__ void __launch_bounds__(kThreads) lora_generic_kernel(const LoraArgs a
 template <int E, int R>
 hipError_t launch_tiled(const LoraArgs& a, const Workspace& ws, hipStream_t s) {
   const int64_t tiles = lora_max_tiles(a);
-  hipLaunchKernelGGL(lora_group_kernel, dim3(1), dim3(kGroupThreads), 0, s, a, ws);
-  if (a.wa)
-    hipLaunchKernelGGL((lora_shrink_kernel<E, R>), dim3((unsigned)(tiles * a.ksplit)), dim3(kThreads),
-                       0, s, a, ws);
+  if (a.wa && a.rows <= kSmallRows) {
+    // small batch: the shrink groups the rows itself (one launch fewer)
+    hipLaunchKernelGGL((lora_shrink_kernel<E, R, true>), dim3((unsigned)(tiles * a.ksplit)),
+                       dim3(kThreads), 0, s, a, ws);
+  } else {
+    hipLaunchKernelGGL(lora_group_kernel, dim3(1), dim3(kGroupThreads), 0, s, a, ws);
+    if (a.wa)
+      hipLaunchKernelGGL((lora_shrink_kernel<E, R, false>), dim3((unsigned)(tiles * a.ksplit)),
+                         dim3(kThreads), 0, s, a, ws);
+  }
   hipLaunchKernelGGL((lora_expand_kernel<E, R>),
                      dim3((unsigned)((tiles + 7) / 8 * 8 * kQuarters * a.chunks)), dim3(kThreads),
                      0, s, a, ws);

@@ -104,6 +104,7 @@ def small_ints(seed, tid, shape, lo, hi, dt):
 EXACT = [
     # rows, h1, rank, h2, h3, w, layers, layer, off, has_a, dt
     (37, 64, 16, 48, 104, 3, 2, 1, 24, True, "bf16"),
+    (700, 64, 16, 48, 104, 3, 2, 1, 24, True, "bf16"),  # above 512 rows: grouping launch
     (100, 256, 32, 128, 256, 5, 3, 2, 128, True, "fp16"),
     (17, 16, 16, 64, 64, 2, 1, 0, 0, False, "bf16"),
     (300, 512, 64, 96, 400, 7, 2, 0, 296, True, "bf16"),
