@@ -47,7 +47,10 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(OBJDIR, exist_ok=True)
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    missing = [s for s in SOURCES if not os.path.exists(os.path.join(CSRC, s))]
+    if missing:
+        raise FileNotFoundError(f"missing sources in {CSRC}: {', '.join(missing)}")
+    srcs = list(SOURCES)
     jobs = max(1, min(len(srcs), os.cpu_count() or 1, 16))
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))

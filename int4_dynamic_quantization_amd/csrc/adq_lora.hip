@@ -153,17 +153,13 @@ __global__ void __launch_bounds__(kGroupThreads) lora_group_kernel(const LoraArg
   // rows without an adapter are only listed when out is not y (to be copied)
   auto placed = [&](int g) -> int { return (g < W || !a.in_place) ? cnt[g] : 0; };
   const int per = (int)((W + 1 + kGroupThreads - 1) / kGroupThreads);
-  int tl = 0, rl = 0;
+  int tl = 0;
   for (int q = 0; q < per; ++q) {
     const int g = tid * per + q;
-    if (g <= W) {
-      tl += (placed(g) + kTile - 1) / kTile;
-      rl += placed(g);
-    }
+    if (g <= W) tl += (placed(g) + kTile - 1) / kTile;
   }
-  int ntiles = 0, nplaced = 0;
+  int ntiles = 0;
   int tb = block_exclusive_scan<NW>(tl, scan_tmp, &ntiles);
-  int rb = block_exclusive_scan<NW>(rl, scan_tmp, &nplaced);
   for (int q = 0; q < per; ++q) {
     const int g = tid * per + q;
     if (g <= W) {
@@ -173,7 +169,6 @@ __global__ void __launch_bounds__(kGroupThreads) lora_group_kernel(const LoraArg
       cur[g] = 0;
       first_tile[g] = tb;
       tb += (n + kTile - 1) / kTile;
-      rb += n;
     }
   }
   if (tid == 0) ws.header[0] = ntiles;

@@ -29,7 +29,8 @@ def from_bits(bits, dtype: str) -> np.ndarray:
     b = np.asarray(bits, dtype=np.uint16)
     if dtype == "fp16":
         return b.view(np.float16).astype(np.float64)
-    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # NaN patterns decode to NaN
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def near_tie(pre: np.ndarray, tol: float = 1e-3) -> np.ndarray:
