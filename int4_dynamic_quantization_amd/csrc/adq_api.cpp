@@ -112,10 +112,14 @@ adq_status check_tensor(const adq_tensor* t, const char* name) {
   if (!t->data) return fail(ADQ_ERR_NULLPTR, "%s: data pointer is NULL", name);
   if (t->ndim < 0 || t->ndim > ADQ_MAX_DIMS)
     return fail(ADQ_ERR_PARAM_INVALID, "%s: ndim %d outside 0..%d", name, t->ndim, ADQ_MAX_DIMS);
+  int64_t elems = 1;
   for (int i = 0; i < t->ndim; ++i) {
     if (t->shape[i] < 0) return fail(ADQ_ERR_PARAM_INVALID, "%s: negative dimension", name);
     if (t->shape[i] == 0)
       return fail(ADQ_ERR_PARAM_INVALID, "%s: empty tensors are not supported", name);
+    // element counts stay far below int64 overflow everywhere downstream
+    if (__builtin_mul_overflow(elems, t->shape[i], &elems) || elems > ((int64_t)1 << 46))
+      return fail(ADQ_ERR_PARAM_INVALID, "%s: more than 2^46 elements", name);
   }
   return ADQ_OK;
 }

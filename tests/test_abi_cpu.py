@@ -137,6 +137,17 @@ def test_empty_tensor_rejected(field):
     assert "empty" in adq.last_error()
 
 
+@pytest.mark.parametrize("shape", [[1 << 32, 1 << 32, 64], [1 << 40, 1 << 7]])
+def test_huge_element_counts_rejected(shape):
+    """Shapes whose element count overflows int64 (or exceeds 2^46) are
+    refused in phase 1, before any size is computed from them."""
+    a = full_v2()
+    for f in ("x1", "x2", "xo"):
+        a[f] = fake(shape, a[f].dtype)
+    assert v2_call(**a) == adq.ERR_PARAM_INVALID
+    assert "2^46" in adq.last_error()
+
+
 def test_shape_and_dtype_mismatches():
     cases = []
     a = full_v2(); a["x2"] = fake([4, 32], adq.BF16); cases.append(a)
