@@ -60,6 +60,16 @@ MUTANTS = [
      "const int valid = g >= 0 && g < w - 1;"),
     ("lora: shrink skipped", "z = oracle_storage_value(xr[r], dtype);",
      "z = oracle_storage_value(xr[rank - 1 - r], dtype);"),
+    # the consumer GEMM
+    ("gemm: bias dropped", "(bias ? (double)bias[ni[t]] : 0.0)", "0.0"),
+    ("gemm: activation scale ignored", "(double)a_scale[mi[t]]", "1.0"),
+    ("gemm: first column's weight scale everywhere", "(double)w_scale[ni[t]]",
+     "(double)w_scale[0]"),
+    ("gemm: weights read back to front", "(int64_t)ar[j] * (int64_t)wr[j]",
+     "(int64_t)ar[j] * (int64_t)wr[k - 1 - j]"),
+    ("gemm: activations off by one", "(int64_t)ar[j] * (int64_t)wr[j]",
+     "(int64_t)ar[(j + 1) % k] * (int64_t)wr[j]"),
+    ("gemm: sum truncated to 16 bits", "if (sums) sums[t] = s;", "s = (int16_t)s; if (sums) sums[t] = s;"),
 ]
 
 
@@ -84,6 +94,11 @@ def _battery():
     ]
     checks += [(f"lora numpy {dt} {a}", lambda dt=dt, a=a: lora_pins.test_lora_matches_numpy_products(dt, a))
                for dt, a in (("bf16", True), ("fp16", True), ("bf16", False))]
+    checks += [
+        ("gemm worked", pins.test_gemm_worked_example),
+        ("gemm numpy", pins.test_gemm_sums_match_numpy_integer_matmul),
+        ("gemm closed form", pins.test_gemm_scaled_identity_closed_form),
+    ]
     return checks
 
 
