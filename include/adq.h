@@ -44,6 +44,11 @@
  * thread-local message for the last non-OK status of the calling thread.
  * Phase 2 never allocates and never synchronizes.
  *
+ * Threads: phase-1 calls and different executors may be used from any
+ * threads at once.  One executor is run from one host thread at a time
+ * (a split-row run records its launch tag in the executor); it may be run
+ * any number of times on any streams.
+ *
  * Determinism: results are bitwise reproducible run to run (fixed
  * reduction order, no floating-point atomics), as the pages' Constraints
  * sections require of both operators.
