@@ -28,7 +28,9 @@
 //
 // Workgroup -> (row, split) mapping keeps the S workgroups of a row on one
 // XCD (workgroups are dealt to the 8 XCDs round robin), so their exchange
-// stays within one L2 when the dispatcher follows that order.
+// stays within one L2 when the dispatcher follows that order; a wait that
+// keeps failing invalidates its L2 now and then, so that a slot written
+// from another XCD is still seen.
 #include <type_traits>
 
 #include "adq_device.h"
@@ -84,6 +86,12 @@ __device__ __forceinline__ bool collect(const SplitArgs& p, int64_t row, int pha
       return true;
     }
     __builtin_amdgcn_s_sleep(1);
+    // Each XCD has its own L2, and a slot polled before it was written can
+    // stay cached there; the mapping keeps a row's workgroups on one XCD,
+    // but only through the dispatcher's order.  After every 64 unsuccessful
+    // polls (far beyond a normal wait) the wavefront invalidates its L2 so
+    // that a slot written from another XCD is read afresh.
+    if ((it & 63u) == 63u) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   v0 = v1 = 0.0f;
   return false;
