@@ -133,7 +133,7 @@ int oracle_v2_outputs(const int* mask, int has_s1, int has_s2, int* act1, int* a
     return 1;
   }
   if (has_s2 && !has_s1) return 0; /* mask absent: smooth2 needs smooth1 */
-  *act1 = 1;                       /* "outputMask[0]=True || !outputMask" */
+  *act1 = 1;                       /* mask absent: the first output always exists */
   *act2 = (has_s1 && has_s2) ? 1 : 0;
   return 1;
 }
