@@ -49,6 +49,11 @@
  * (a split-row run records its launch tag in the executor); it may be run
  * any number of times on any streams.
  *
+ * Graphs: a phase-2 call may be captured into a HIP graph and the graph
+ * replayed, on every path except the split-row one (ADQ_PATH_SPLIT): its
+ * launches tag their exchange slots with a value the host makes fresh for
+ * each call, and a replay would repeat the captured tag.
+ *
  * Determinism: results are bitwise reproducible run to run (fixed
  * reduction order, no floating-point atomics), as the pages' Constraints
  * sections require of both operators.

@@ -184,6 +184,7 @@ class Executor:
         self.workspace_size = int(workspace_size)
         self.op = op
         self._keep = keep
+        self.device = None  # torch device of the tensors, when planned from torch tensors
 
     def set_path(self, path: int) -> int:
         ws = ctypes.c_uint64(0)
@@ -197,9 +198,14 @@ class Executor:
         return buf.value.decode()
 
     def run(self, workspace=None, stream=None) -> None:
+        """Phase 2 on `stream` (a torch.cuda.Stream); by default torch's
+        current stream on the executor's device, so the launch is ordered
+        with the surrounding torch work (and can be captured in a graph)."""
         ws_ptr = None if workspace is None else workspace.data_ptr()
         ws_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
-        s = None if stream is None else stream.cuda_stream
+        if stream is None:
+            stream = _torch().cuda.current_stream(self.device)
+        s = stream.cuda_stream
         fn = {"v2": _lib().adq_add_rms_norm_dynamic_quant_v2,
               "rmsnorm": _lib().adq_rms_norm_dynamic_quant,
               "gemm": _lib().adq_w8a8_gemm, "lora": _lib().adq_add_lora}[self.op]
@@ -291,6 +297,7 @@ def plan_add_rms_norm_dynamic_quant_v2(x1, x2, gamma, beta=None, smooth_scale1=N
         None if outs["y2"] is None else d(outs["y2"], qd[2]), d(outs["scale1"]),
         d(outs["scale2"]), d(outs["x_out"]))
     ex._keep = (ex._keep, x1, x2, gamma, beta, smooth_scale1, smooth_scale2, outs)
+    ex.device = x1.device
     if path != PATH_AUTO:
         ex.set_path(path)
     return ex, outs
@@ -330,6 +337,7 @@ def plan_rms_norm_dynamic_quant(x, gamma, beta=None, smooth_scales=None, epsilon
     ex = rms_norm_dynamic_quant_get_workspace_size(
         d(x), d(gamma), d(beta), d(smooth_scales), epsilon, d(outs["y"], qd), d(outs["scale"]))
     ex._keep = (ex._keep, x, gamma, beta, smooth_scales, outs)
+    ex.device = x.device
     if path != PATH_AUTO:
         ex.set_path(path)
     return ex, outs
@@ -370,6 +378,7 @@ def plan_w8a8_gemm(a, a_scale, w, w_scale, bias=None, out_dtype=None, out=None,
     ex = w8a8_gemm_get_workspace_size(d(a, INT8), d(a_scale), d(w, INT8), d(w_scale), d(bias),
                                       d(out))
     ex._keep = (ex._keep, a, a_scale, w, w_scale, bias, out)
+    ex.device = a.device
     if path != PATH_AUTO:
         ex.set_path(path)
     return ex, out
@@ -406,6 +415,7 @@ def plan_add_lora(y, x, weight_b, indices, weight_a=None, layer_idx=0, scale=1.0
     ex = add_lora_get_workspace_size(d(y), d(x), d(weight_b), d(indices), d(weight_a), layer_idx,
                                      scale, y_offset, weight_b.shape[-1], d(out))
     ex._keep = (ex._keep, y, x, weight_b, indices, weight_a, out)
+    ex.device = y.device
     if path != PATH_AUTO:
         ex.set_path(path)
     return ex, out
