@@ -244,7 +244,7 @@ void adq_executor_destroy(adq_executor* executor);
  * 256-tiles cover the compute units.  Either accepts any valid GEMM shape;
  * the operator paths are rejected for a GEMM executor and vice versa.
  * AddLora executors: AUTO (the tiled kernel when the shapes and alignments
- * allow it: h1 % 8 == 0, rank 16, 32 or 64, h2 a multiple of 4, h3 and
+ * allow it: h1 % 8 == 0, rank 8, 16, 32, 64 or 128, h2 a multiple of 4, h3 and
  * y_offset multiples of 8, aligned tensors, y under 4 GiB) or
  * ADQ_PATH_GENERIC (one workgroup per row, any shape).
  */

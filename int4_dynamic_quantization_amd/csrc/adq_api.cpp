@@ -766,7 +766,8 @@ adq_status adq_add_lora_get_workspace_size(const adq_tensor* y, const adq_tensor
   a.elem = y->dtype == ADQ_BF16 ? adq::kBF16 : adq::kF16;
   a.in_place = out->data == y->data;
   e.m = rows;
-  e.lora_tiled_ok = h1 % 8 == 0 && (rank == 16 || rank == 32 || rank == 64) &&
+  e.lora_tiled_ok = h1 % 8 == 0 &&
+                    (rank == 8 || rank == 16 || rank == 32 || rank == 64 || rank == 128) &&
                     h2 % 4 == 0 && h3 % 8 == 0 && y_offset % 8 == 0 && aligned(x->data, 16) &&
                     (!weight_a || aligned(weight_a->data, 16)) && aligned(weight_b->data, 8) &&
                     aligned(y->data, 16) && aligned(out->data, 8) &&

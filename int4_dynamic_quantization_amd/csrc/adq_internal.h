@@ -108,7 +108,7 @@ struct LoraArgs {
 enum LoraPath : int { kLoraTiled = 1, kLoraGeneric = 2 };
 constexpr int kLoraTileRows = 64;     // rows per tile in the tiled path
 constexpr int kLoraMaxAdapters = 2048;
-constexpr int kLoraMaxRankTiled = 64;
+constexpr int kLoraMaxRankTiled = 128;
 constexpr int kLoraMaxRankGeneric = 1024;
 
 // Tiled path: upper bound on the number of tiles (sum over adapter classes of

@@ -15,19 +15,22 @@
 //     taken with LDS atomics, so the order of rows inside a tile may vary
 //     between runs; every row's result is computed from its own data in a
 //     fixed order, so outputs do not.
-//  2. shrink: one workgroup per (tile, slice of h1), compiled per rank.  The
-//     slice of weightA[g, layer] (stored [h1, rank], rank contiguous) is
-//     staged in LDS transposed, 256 k at a time, so each MFMA operand is one
-//     16-byte read; 4 wavefronts each take 16 rows
+//  2. shrink: one workgroup per (tile, slice of h1), compiled per rank (8,
+//     16, 32, 64, 128; rank 8 padded to one 16-wide block).  The slice of
+//     weightA[g, layer] (stored [h1, rank], rank contiguous) is staged in LDS
+//     transposed, 256 k at a time (128 for rank 128), so each MFMA operand is
+//     one 16-byte read; 4 wavefronts each take 16 rows
 //     (v_mfma_f32_16x16x32_{bf16,f16}, the x fragments of a whole 256-k
 //     stage loaded before the staging) and write fp32 partial sums to the
 //     workspace.
 //  3. expand: one workgroup per (16 rows of a tile, 1024 columns of the
 //     slice), all workgroups of a tile on one XCD.  Each thread owns 4
-//     adjacent columns: its 16 rows of y, its weightB values (rank 16: kept
-//     in registers) and the partial sums are all requested before anything
-//     waits; Z1 = the slices' partial sums added in slice order; fp32 fma
-//     chain over the ranks, fma into y, one rounding, 8-byte stores.  Rows
+//     adjacent columns: its 16 rows of y, its weightB values (rank <= 16:
+//     kept in registers; larger ranks: 16 at a time, every row's sums kept
+//     across the chunks) and the partial sums are all requested before
+//     anything waits; Z1 = the slices' partial sums added in slice order;
+//     fp32 fma chain over the ranks, fma into y, one rounding, 8-byte
+//     stores.  Rows
 //     without an adapter and, when out is not y, the columns outside the
 //     slice are copied here.
 // Generic kernel: one workgroup per row, any sizes and alignments, same
@@ -42,7 +45,7 @@ namespace {
 constexpr int kThreads = 256;         // generic, shrink and expand kernels
 constexpr int kGroupThreads = 1024;   // group kernel
 constexpr int kTile = kLoraTileRows;  // 64 rows
-constexpr int kKSub = 256;            // k per LDS stage of weightA
+constexpr int kKSub = 256;            // k per LDS stage of weightA (rank <= 64)
 // Transposed weightA rows in LDS: 256 k + 32 of padding (576 bytes, 16 banks
 // of offset per row) with the 8-k groups of rows 8..15 (mod 16) swapped in
 // pairs (group index ^ 2).  gfx950 reads 128 bits for 16 lanes per pass; for
@@ -50,6 +53,13 @@ constexpr int kKSub = 256;            // k per LDS stage of weightA
 // wave, parity of lane bits 2 and 4, possibly with bits 0 and 3) the 16
 // lanes of a pass then hit 16 distinct 4-bank groups.
 constexpr int kAtStride = kKSub + 32;
+// Per rank: k per stage (128 for rank 128, so the staged slice stays 40 KB)
+// and the row stride of the staged slice (the same 16-bank offset per row,
+// so the swizzle above keeps the reads conflict-free); ranks below 16 are
+// padded to one 16-wide MFMA block with zero rows.
+template <int R> constexpr int stage_k() { return R > 64 ? 128 : kKSub; }
+template <int R> constexpr int at_stride() { return stage_k<R>() + 32; }
+template <int R> constexpr int padded_rank() { return R < 16 ? 16 : R; }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -260,13 +270,19 @@ __device__ void group_one_tile(const LoraArgs& a, int tile, int* cnt, int* scan_
 // and row slots, and workgroup 0 the tile count, for the expand.
 template <int E, int R, bool G>
 __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a, Workspace ws) {
+  constexpr int RP = padded_rank<R>();
+  constexpr int KS = stage_k<R>();
   __shared__ int64_t rows_lds[kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t at[R][kAtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t at[RP][at_stride<R>()];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int tile = (int)(blockIdx.x / a.ksplit);
   const int ks = (int)(blockIdx.x % a.ksplit);
+  if constexpr (RP > R) {  // padding rows: zero once, never staged
+    for (int p = tid; p < (RP - R) * at_stride<R>(); p += kThreads)
+      at[R + p / at_stride<R>()][p % at_stride<R>()] = 0;
+  }
   int g, n;
   if constexpr (G) {
     __shared__ int cnt[kLoraMaxAdapters + 1];
@@ -293,7 +309,7 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
   using T = uint16_t;
   constexpr int64_t rank = R;
   const int64_t h1 = a.h1;
-  constexpr int nb = R / 16;
+  constexpr int nb = RP / 16;
   const T* wa = static_cast<const T*>(a.wa) + ((g * a.l + a.layer) * h1) * rank;
   const T* x = static_cast<const T*>(a.x);
   const int64_t kc = ((h1 + a.ksplit - 1) / a.ksplit + 31) / 32 * 32;
@@ -309,20 +325,20 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
   const bool row_ok = rb + fi < n;
   const T* xrow = x + (row_ok ? rows_lds[rb + fi] : rows_lds[0]) * h1;
   constexpr int pieces_per_k = R / 8;
-  for (int64_t sub = k_lo; sub < k_hi; sub += kKSub) {
-    const int sub_n = (int)(k_hi - sub < kKSub ? k_hi - sub : kKSub);
+  for (int64_t sub = k_lo; sub < k_hi; sub += KS) {
+    const int sub_n = (int)(k_hi - sub < KS ? k_hi - sub : KS);
     const int steps = (sub_n + 31) / 32;
     // this stage's x fragments first (they do not depend on the LDS stage)
-    u16x8 xa[kKSub / 32];
+    u16x8 xa[KS / 32];
 #pragma unroll
-    for (int u = 0; u < kKSub / 32; ++u) {
+    for (int u = 0; u < KS / 32; ++u) {
       const int64_t kx = sub + 32 * u + 8 * fk;
       xa[u] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
       if (rb < n && row_ok && u < steps && kx < k_hi)
         xa[u] = *reinterpret_cast<const u16x8*>(xrow + kx);
     }
-    // stage weightA[sub .. sub + 256) transposed (zeros past the slice)
-    for (int p = tid; p < kKSub * pieces_per_k; p += kThreads) {
+    // stage weightA[sub .. sub + KS) transposed (zeros past the slice)
+    for (int p = tid; p < KS * pieces_per_k; p += kThreads) {
       const int k = p / pieces_per_k, rg = p % pieces_per_k;
       u16x8 v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
       if (k < sub_n) v = *reinterpret_cast<const u16x8*>(wa + (sub + k) * rank + 8 * rg);
@@ -335,7 +351,7 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
     __syncthreads();
     if (rb < n) {  // wavefront-uniform
 #pragma unroll
-      for (int u = 0; u < kKSub / 32; ++u) {
+      for (int u = 0; u < KS / 32; ++u) {
         if (u < steps) {
           const int kg = 4 * u + fk;
 #pragma unroll
@@ -359,7 +375,7 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = rb + 4 * fk + e;
-        if (i < n) zp[i * rank + 16 * b + fi] = acc[b][e];
+        if (i < n && 16 * b + fi < R) zp[i * rank + 16 * b + fi] = acc[b][e];
       }
 }
 
@@ -438,15 +454,16 @@ __global__ void __launch_bounds__(kThreads) lora_expand_kernel(const LoraArgs a,
     }
   }
 
-  // weightB for this thread's columns (rank 16: held in registers), issued
-  // right behind y
+  // weightB for this thread's columns (rank <= 16: held in registers),
+  // issued right behind y
+  constexpr int RB = R <= 16 ? R : 1;  // ranks held in registers
   const T* wb = static_cast<const T*>(a.wb) + ((g * a.l + a.layer) * R) * a.h2;
-  u16x4 bw16[16];
-  if constexpr (R == 16) {
-    const rsrc_t rb = make_rsrc(wb, (uint32_t)(16 * a.h2 * 2));
+  u16x4 bwr[RB];
+  if constexpr (R <= 16) {
+    const rsrc_t rb = make_rsrc(wb, (uint32_t)(R * a.h2 * 2));
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      bw16[r] = __builtin_bit_cast(
+    for (int r = 0; r < R; ++r)
+      bwr[r] = __builtin_bit_cast(
           u16x4, __builtin_amdgcn_raw_buffer_load_b64(
                      rb, col_ok ? (uint32_t)((r * a.h2 + col) * 2) : 0xFFFFFFF0u, 0, 0));
   }
@@ -456,7 +473,7 @@ __global__ void __launch_bounds__(kThreads) lora_expand_kernel(const LoraArgs a,
   // weightB, with no wait in between; indices past the valid ones are
   // clamped to a valid slot and their values dropped.
   constexpr int ZP = (kQRows * R + kThreads - 1) / kThreads;  // elements per thread
-  constexpr int kZS = 16;
+  constexpr int kZS = R <= 16 ? 16 : 256 / R;  // slices loaded together (kZS * ZP <= 16)
   if (a.wa) {
     const int ksn = a.ksplit;
     float zs[ZP];
@@ -500,46 +517,74 @@ __global__ void __launch_bounds__(kThreads) lora_expand_kernel(const LoraArgs a,
                        : 0.0f;
     }
   }
-  float b16[16][4];
-  if constexpr (R == 16) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) b16[r][q] = widen1<E>(bw16[r][q]);
-  }
   __syncthreads();
+  // out = y + scale * (z1 . weightB), one fp32 fma chain over the ranks in
+  // rank order per output, one fma into y, one rounding
+  auto store_row = [&](int i, const float (&acc)[4]) {
+    const u16x4 yq = __builtin_bit_cast(u16x4, yv[i]);
+    u16x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = narrow1<E>(__builtin_fmaf(acc[q], a.scale, widen1<E>(yq[q])));
+    *reinterpret_cast<u16x4*>(out + (int64_t)rows[i] * h3 + a.y_offset + col) = o;
+  };
   if (col_ok) {
+    if constexpr (R <= 16) {
+      // weightB in registers, one row at a time
+      float br[RB][4];
 #pragma unroll
-    for (int i = 0; i < kQRows; ++i) {
-      if (i < n) {
-        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int r = 0; r < RB; ++r)
 #pragma unroll
-        for (int rc = 0; rc < R; rc += 16) {
-          u16x4 bw[16];
-          if constexpr (R != 16) {
+        for (int q = 0; q < 4; ++q) br[r][q] = widen1<E>(bwr[r][q]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              bw[r] = *reinterpret_cast<const u16x4*>(wb + (rc + r) * a.h2 + col);
-          }
+      for (int i = 0; i < kQRows; ++i) {
+        if (i < n) {
+          float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int r4 = 0; r4 < 16; r4 += 4) {
-            const f32x4 zz = *reinterpret_cast<const f32x4*>(&z1[i][rc + r4]);
+          for (int r4 = 0; r4 < R; r4 += 4) {
+            const f32x4 zz = *reinterpret_cast<const f32x4*>(&z1[i][r4]);
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const float bv = R == 16 ? b16[r4 + u][q] : widen1<E>(bw[r4 + u][q]);
-                acc[q] = __builtin_fmaf(zz[u], bv, acc[q]);
-              }
+              for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(zz[u], br[r4 + u][q], acc[q]);
+          }
+          store_row(i, acc);
+        }
+      }
+    } else {
+      // 16 ranks of weightB at a time in registers, every row's sums kept
+      // across the chunks (each weightB value is read once per workgroup)
+      float acc[kQRows][4];
+#pragma unroll
+      for (int i = 0; i < kQRows; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q] = 0.0f;
+#pragma unroll 1
+      for (int rc = 0; rc < R; rc += 16) {
+        float b[16][4];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const u16x4 v = *reinterpret_cast<const u16x4*>(wb + (rc + r) * a.h2 + col);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) b[r][q] = widen1<E>(v[q]);
+        }
+#pragma unroll
+        for (int i = 0; i < kQRows; ++i) {
+          if (i < n) {
+#pragma unroll
+            for (int r4 = 0; r4 < 16; r4 += 4) {
+              const f32x4 zz = *reinterpret_cast<const f32x4*>(&z1[i][rc + r4]);
+#pragma unroll
+              for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                  acc[i][q] = __builtin_fmaf(zz[u], b[r4 + u][q], acc[i][q]);
+            }
           }
         }
-        const u16x4 yq = __builtin_bit_cast(u16x4, yv[i]);
-        u16x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          o[q] = narrow1<E>(__builtin_fmaf(acc[q], a.scale, widen1<E>(yq[q])));
-        *reinterpret_cast<u16x4*>(out + (int64_t)rows[i] * h3 + a.y_offset + col) = o;
       }
+#pragma unroll
+      for (int i = 0; i < kQRows; ++i)
+        if (i < n) store_row(i, acc[i]);
     }
   }
 
@@ -642,9 +687,11 @@ hipError_t launch_elem(const LoraArgs& a, int path, void* workspace, hipStream_t
   if (path == kLoraTiled) {
     const Workspace ws = ws_layout(workspace, a);
     switch (a.rank) {
+      case 8: return launch_tiled<E, 8>(a, ws, s);
       case 16: return launch_tiled<E, 16>(a, ws, s);
       case 32: return launch_tiled<E, 32>(a, ws, s);
       case 64: return launch_tiled<E, 64>(a, ws, s);
+      case 128: return launch_tiled<E, 128>(a, ws, s);
       default: return hipErrorInvalidValue;
     }
   }

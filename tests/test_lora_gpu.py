@@ -108,6 +108,10 @@ EXACT = [
     (100, 256, 32, 128, 256, 5, 3, 2, 128, True, "fp16"),
     (17, 16, 16, 64, 64, 2, 1, 0, 0, False, "bf16"),
     (300, 512, 64, 96, 400, 7, 2, 0, 296, True, "bf16"),
+    (64, 64, 8, 48, 104, 3, 2, 1, 24, True, "fp16"),     # rank 8 (one padded MFMA block)
+    (17, 8, 8, 64, 64, 2, 1, 0, 0, False, "bf16"),       # rank 8 without weightA
+    (200, 256, 128, 96, 160, 3, 2, 1, 32, True, "bf16"), # rank 128 (128-k stages)
+    (600, 128, 128, 40, 64, 4, 1, 0, 8, True, "bf16"),   # rank 128, grouping launch
     (33, 64, 16, 52, 120, 3, 2, 1, 64, True, "bf16"),   # slice width 4 (mod 8)
     (37, 64, 16, 48, 100, 3, 2, 1, 20, True, "bf16"),   # y rows not 16-byte aligned: generic
     (5, 30, 5, 7, 13, 2, 2, 1, 3, True, "fp16"),        # generic only (ragged)
@@ -115,7 +119,8 @@ EXACT = [
 
 
 def tiled_expected(h1, rank, h2, h3, off):
-    return h1 % 8 == 0 and rank in (16, 32, 64) and h2 % 4 == 0 and h3 % 8 == 0 and off % 8 == 0
+    return (h1 % 8 == 0 and rank in (8, 16, 32, 64, 128) and h2 % 4 == 0 and h3 % 8 == 0
+            and off % 8 == 0)
 
 
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
@@ -135,7 +140,7 @@ def test_exact_integers(case, path):
     assert np.array_equal(got, ref), desc
 
 
-@pytest.mark.parametrize("rank", [16, 32])
+@pytest.mark.parametrize("rank", [8, 16, 32, 128])
 def test_many_slices_of_h1(rank):
     """Few rows and a long h1: the shrink splits h1 into more than 16 slices,
     so the expand adds the partial sums beyond the first 16 in its second

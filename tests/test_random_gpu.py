@@ -134,7 +134,7 @@ def test_random_lora(i):
     rng = np.random.default_rng(9900 + i)
     dt = "bf16" if rng.integers(0, 2) else "fp16"
     has_a = bool(rng.integers(0, 4))  # mostly with weightA
-    rank = [16, 32, 64, 5, 8, 16][int(rng.integers(0, 6))]
+    rank = [16, 32, 64, 5, 8, 16, 128, 24][int(rng.integers(0, 8))]
     h1 = (int(rng.integers(1, 65)) * 8 if rng.integers(0, 3) else int(rng.integers(1, 400))) \
         if has_a else rank
     h2 = int(rng.integers(1, 300))
