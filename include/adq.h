@@ -210,8 +210,10 @@ adq_status adq_w8a8_gemm(void* workspace, uint64_t workspace_size, adq_executor*
  * out        same shape and dtype as y; either y itself (in place: only the
  *            slice of rows with an adapter is written) or memory that does
  *            not overlap y.
- * Arithmetic in fp32 (Z1 is not rounded between the two products); each
- * slice value is rounded once to the storage type.  W <= 2048, rank <= 1024.
+ * Arithmetic in fp32 (Z1 is not rounded between the two products; for BF16
+ * at ranks 32, 64 and 128 the expand's sums run in the matrix unit, with Z1
+ * entering as three bf16 pieces whose sum is exactly Z1); each slice value is
+ * rounded once to the storage type.  W <= 2048, rank <= 1024.
  * Workspace: the tiled path (see adq_path) needs one, 8-byte aligned, whose
  * contents need not be initialised (tile table, grouped row order and
  * partial sums, rewritten by every launch; calls that share a workspace

@@ -32,7 +32,9 @@
 //     fp32 fma chain over the ranks, fma into y, one rounding, 8-byte
 //     stores.  Rows
 //     without an adapter and, when out is not y, the columns outside the
-//     slice are copied here.
+//     slice are copied here.  bf16 at ranks 32, 64 and 128 takes an expand
+//     on the matrix cores instead (z1 split exactly into three bf16 pieces;
+//     one workgroup per 64-row tile and 256 columns).
 // Generic kernel: one workgroup per row, any sizes and alignments, same
 // arithmetic with block reductions in a fixed order.
 #include "adq_device.h"
@@ -41,6 +43,7 @@
 namespace adq {
 
 namespace {
+
 
 constexpr int kThreads = 256;         // generic, shrink and expand kernels
 constexpr int kGroupThreads = 1024;   // group kernel
@@ -52,7 +55,6 @@ constexpr int kKSub = 256;            // k per LDS stage of weightA (rank <= 64)
 // every lane grouping that fits the bank-conflict measurements (one half
 // wave, parity of lane bits 2 and 4, possibly with bits 0 and 3) the 16
 // lanes of a pass then hit 16 distinct 4-bank groups.
-constexpr int kAtStride = kKSub + 32;
 // Per rank: k per stage (128 for rank 128, so the staged slice stays 40 KB)
 // and the row stride of the staged slice (the same 16-bank offset per row,
 // so the swizzle above keeps the reads conflict-free); ranks below 16 are
@@ -600,6 +602,283 @@ __global__ void __launch_bounds__(kThreads) lora_expand_kernel(const LoraArgs a,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Expand on the matrix cores (bf16, ranks 32, 64, 128, where the fp32 sums of
+// the kernel above are bound by the vector ALUs).  out[row][col] = y + scale
+// * sum_r z1[row][r] weightB[r][col] as v_mfma_f32_16x16x32_bf16 products:
+// each fp32 z1 value is split exactly into three bf16 pieces (hi, mid, lo;
+// 8 + 8 + 8 significant bits), every product of a piece with a weightB value
+// is exact, and the sums run in fp32 inside the matrix unit.
+//
+// One workgroup per (tile of up to 64 rows, 256 columns of the slice), all
+// workgroups of a tile on one XCD, so weightB is read once per 64 rows.  Wave
+// w takes 64 columns and every 16-row block of the tile.  MFMA operand A is
+// weightB: lane l reads the 4 adjacent columns c(l % 16) of 8 ranks with
+// 8-byte loads straight from memory, and the q-th of the 4 columns forms the
+// q-th A operand, so no transposition is needed: MFMA q yields the columns
+// c(m) + q.  With c(m) below, lane l's results are row l % 16 and columns
+// 8 (l / 16) + {0..7} and 32 + 8 (l / 16) + {0..7} of the wave's 64.
+// Operand B is z1's pieces, staged in LDS once per workgroup as three bf16
+// planes [64 rows][rank]; per chunk of 32 ranks one MFMA per piece.  y and
+// out cross LDS so that memory is read and written in whole 512-byte row
+// pieces; y is loaded after the products, which keeps the registers (and so
+// the occupancy) of the kernel low.
+constexpr int kMxCols = 256;    // columns per workgroup
+constexpr int kMxMinRank = 32;  // below, the kernel above is faster (measured)
+
+// first of the 4 columns that MFMA row m of a wave's 64 columns holds
+__device__ __forceinline__ int mx_col(int m) {
+  return 8 * (m >> 2) + 4 * (m & 1) + 32 * ((m >> 1) & 1);
+}
+// piece-plane row stride in elements: rows 16 bytes apart modulo 256 bytes,
+// so the 16-byte reads of 16 consecutive rows hit distinct banks
+template <int R> constexpr int mx_stride() { return R + 8; }
+
+int lora_mx_col_blocks(int64_t h2) {
+  const int64_t c = (h2 + kMxCols - 1) / kMxCols;
+  return (int)(c < 1 ? 1 : c);
+}
+
+template <int R>
+__global__ void __launch_bounds__(kThreads) lora_expand_mx_kernel(const LoraArgs a,
+                                                                    Workspace ws) {
+  static_assert(R >= 32 && R % 32 == 0, "ranks of 32 and above");
+  constexpr int NP = 3, ZS = mx_stride<R>();  // pieces, plane row stride
+  constexpr int RC = 32;                      // ranks per chunk
+  // LDS: z1's pieces during the products, then the tile's y / out block
+  // [64 rows][256 columns + 8] (rows 16 bytes apart modulo 256 bytes)
+  constexpr int YS = kMxCols + 8;
+  constexpr int kZBytes = NP * kTile * ZS * 2, kYBytes = kTile * YS * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kZBytes > kYBytes ? kZBytes : kYBytes];
+  auto zp = reinterpret_cast<uint16_t (*)[kTile][ZS]>(lds);
+  auto yb = reinterpret_cast<uint16_t (*)[YS]>(lds);
+  using T = uint16_t;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, lq = lane >> 4;
+  const int ncb = (int)((a.h2 + kMxCols - 1) / kMxCols);
+  const int xcd = (int)(blockIdx.x % 8), j = (int)(blockIdx.x / 8);
+  const int tile = xcd + 8 * (j / ncb), cb = j % ncb;
+  const int64_t mt = lora_max_tiles_dev(a);
+  const int tc = tile < mt ? tile : 0;
+  const int ntiles = ws.header[0];
+  const int4 te = ws.table[tc];
+  const int32_t* trows = ws.rows + (int64_t)tc * kTile;
+  int32_t myrow[4];  // this lane's row in each 16-row block
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) myrow[rb] = trows[16 * rb + m];
+  if (tile >= ntiles) return;
+  const int g = te.x, n = te.z;
+  const T* y = static_cast<const T*>(a.y);
+  T* out = static_cast<T*>(a.out);
+  const int64_t h3 = a.h3;
+  // this workgroup's share of whole rows (copies when out is not y)
+  const int64_t ncg_row = h3 / 4;
+  const int64_t per_row = (ncg_row + ncb - 1) / ncb;
+  const int64_t c0 = cb * per_row;
+  const int64_t c1 = c0 + per_row < ncg_row ? c0 + per_row : ncg_row;
+  if (g >= a.w) {  // rows without an adapter (listed only when out is not y): copy
+    for (int i = 0; i < n; ++i) {
+      const int64_t row = trows[i];
+      for (int64_t c4 = c0 + tid; c4 < c1; c4 += kThreads)
+        *reinterpret_cast<uint2*>(out + row * h3 + 4 * c4) =
+            *reinterpret_cast<const uint2*>(y + row * h3 + 4 * c4);
+    }
+    return;
+  }
+  const int rbn = (n + 15) / 16;  // row blocks holding rows (uniform)
+  const int64_t colw = (int64_t)cb * kMxCols + 64 * wave;
+
+  // weightB: this lane's 4 columns for 8 ranks of a chunk
+  const T* wb = static_cast<const T*>(a.wb) + ((g * a.l + a.layer) * R) * a.h2;
+  const rsrc_t rwb = make_rsrc(wb, (uint32_t)(R * a.h2 * 2));
+  const int64_t wc = colw + mx_col(m);
+  const bool wok = wc < a.h2;
+  const int ro = 8 * lq;  // first of the lane's 8 ranks in a chunk
+  auto load_w = [&](int rc, u16x4 (&w)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = rc + ro + e;
+      w[e] = __builtin_bit_cast(
+          u16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                     rwb, wok ? (uint32_t)((r * a.h2 + wc) * 2) : 0xFFFFFFF0u, 0, 0));
+    }
+  };
+  u16x4 wv[8];
+  load_w(0, wv);
+
+  // z1 = the slices' partial sums added in slice order (or x itself without
+  // weightA), 4 ranks per access, split into its pieces in LDS; rows past
+  // the tile's are zero
+  constexpr int NV4 = kTile * R / 4;                         // groups of 4 ranks
+  constexpr int ZP4 = (NV4 + kThreads - 1) / kThreads;       // groups per thread
+  constexpr int KB = ZP4 >= 8 ? 1 : 8 / ZP4;                // slices loaded together
+  f32x4 zs[ZP4];
+  if (a.wa) {
+    const int ksn = a.ksplit;
+    const int64_t kstride = mt * kTile * R / 4;
+    const f32x4* zb = reinterpret_cast<const f32x4*>(ws.z1p + (int64_t)tile * kTile * R);
+    int zi[ZP4];
+#pragma unroll
+    for (int u = 0; u < ZP4; ++u) {
+      const int v = tid + u * kThreads;
+      zi[u] = v < NV4 && 4 * v / R < n ? v : 0;
+      zs[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int k0 = 0; k0 < ksn; k0 += KB) {
+      f32x4 p[KB][ZP4];
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const int k = k0 + kk < ksn ? k0 + kk : k0;
+#pragma unroll
+        for (int u = 0; u < ZP4; ++u) p[kk][u] = zb[k * kstride + zi[u]];
+      }
+      // slices past the valid ones add +0 (bits masked off); each component
+      // is read into a scalar first (a bit cast taken straight from a vector
+      // component compiled to a read of component 0)
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const uint32_t keep = k0 + kk < ksn ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+        for (int u = 0; u < ZP4; ++u)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float pc = p[kk][u][c];
+            zs[u][c] += __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, pc) & keep);
+          }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < ZP4; ++u) {
+      const int v = tid + u * kThreads;
+      const int i = v < NV4 && 4 * v / R < n ? 4 * v / R : 0;
+      const u16x4 xv = *reinterpret_cast<const u16x4*>(static_cast<const T*>(a.x) +
+                                                        (int64_t)trows[i] * a.h1 + 4 * v % R);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) zs[u][c] = widen1<kBF16>(xv[c]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < ZP4; ++u) {
+    const int v = tid + u * kThreads, i = 4 * v / R, r = 4 * v % R;
+    if (v < NV4) {
+      u16x4 hi, mid, lo;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float z = i < n ? zs[u][c] : 0.0f;
+        hi[c] = narrow1<kBF16>(z);
+        const float r1 = z - widen1<kBF16>(hi[c]);
+        mid[c] = narrow1<kBF16>(r1);
+        lo[c] = narrow1<kBF16>(r1 - widen1<kBF16>(mid[c]));
+      }
+      *reinterpret_cast<u16x4*>(&zp[0][i][r]) = hi;
+      *reinterpret_cast<u16x4*>(&zp[1][i][r]) = mid;
+      *reinterpret_cast<u16x4*>(&zp[2][i][r]) = lo;
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[rb][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int rc = 0; rc < R; rc += RC) {
+    u16x4 wn[8];
+    if (rc + RC < R) load_w(rc + RC, wn);  // next chunk in flight
+    u16x8 av[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) av[q][e] = wv[e][q];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      if (rb < rbn) {
+        u16x8 bv[NP];
+#pragma unroll
+        for (int pc = 0; pc < NP; ++pc)
+          bv[pc] = *reinterpret_cast<const u16x8*>(&zp[pc][16 * rb + m][rc + ro]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int pc = 0; pc < NP; ++pc) acc[rb][q] = mfma16<kBF16>(av[q], bv[pc], acc[rb][q]);
+      }
+    }
+    if (rc + RC < R) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wv[e] = wn[e];
+    }
+  }
+
+  // out = y + scale * sum, one rounding: y goes through LDS into the MFMA
+  // layout, each lane turns its values into out in place, and the block is
+  // stored row by row as it was loaded
+  // y: the block's rows, 16 bytes per access, 32 threads per row (512
+  // contiguous bytes), issued first.  An 8-column group that starts inside
+  // the slice stays inside y's row (h3 and y_offset are multiples of 8).
+  constexpr int kYChunks = kTile * kMxCols / 8 / kThreads;  // 8 per thread
+  const rsrc_t ry = make_rsrc(y, (uint32_t)(a.rows * h3 * 2));
+  const int64_t colb = (int64_t)cb * kMxCols + 8 * (tid % 32);  // this thread's 8 columns
+  u16x8 yv[kYChunks];
+  int32_t yrow[kYChunks];
+#pragma unroll
+  for (int k = 0; k < kYChunks; ++k) {
+    const int rs = tid / 32 + 8 * k;
+    yrow[k] = trows[rs];
+    const bool ok = rs < n && colb < a.h2;
+    yv[k] = __builtin_bit_cast(
+        u16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                   ry, ok ? (uint32_t)((yrow[k] * h3 + a.y_offset + colb) * 2) : 0xFFFFFFF0u, 0,
+                   0));
+  }
+  __syncthreads();  // every wave is done with z1's pieces
+#pragma unroll
+  for (int k = 0; k < kYChunks; ++k)
+    *reinterpret_cast<u16x8*>(&yb[tid / 32 + 8 * k][8 * (tid % 32)]) = yv[k];
+  __syncthreads();
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    if (rb < rbn) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u16x8* yp = reinterpret_cast<u16x8*>(&yb[16 * rb + m][64 * wave + 8 * lq + 32 * h]);
+        const u16x8 yq = *yp;
+        u16x8 o;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          o[t] = narrow1<kBF16>(
+              __builtin_fmaf(acc[rb][t & 3][2 * h + (t >> 2)], a.scale, widen1<kBF16>(yq[t])));
+        *yp = o;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kYChunks; ++k) {
+    const int rs = tid / 32 + 8 * k;
+    if (rs < n && colb < a.h2) {
+      const u16x8 o = *reinterpret_cast<const u16x8*>(&yb[rs][8 * (tid % 32)]);
+      T* op = out + (int64_t)yrow[k] * h3 + a.y_offset + colb;
+      if (colb + 8 <= a.h2)
+        *reinterpret_cast<u16x8*>(op) = o;
+      else
+        *reinterpret_cast<u16x4*>(op) = u16x4{o[0], o[1], o[2], o[3]};
+    }
+  }
+
+  if (!a.in_place) {  // this workgroup's columns outside the slice
+    const int64_t s0 = a.y_offset / 4, s1 = (a.y_offset + a.h2) / 4;
+    for (int i = 0; i < n; ++i) {
+      const int64_t row = trows[i];
+      for (int64_t c4 = c0 + tid; c4 < c1; c4 += kThreads)
+        if (c4 < s0 || c4 >= s1)
+          *reinterpret_cast<uint2*>(out + row * h3 + 4 * c4) =
+              *reinterpret_cast<const uint2*>(y + row * h3 + 4 * c4);
+    }
+  }
+}
+
 // Sum over the workgroup in a fixed order (DPP within wavefronts, then the
 // four wavefront totals in order); every thread gets the result.
 __device__ float block_sum(float v, float* tmp) {
@@ -675,6 +954,12 @@ hipError_t launch_tiled(const LoraArgs& a, const Workspace& ws, hipStream_t s) {
     if (a.wa)
       hipLaunchKernelGGL((lora_shrink_kernel<E, R, false>), dim3((unsigned)(tiles * a.ksplit)),
                          dim3(kThreads), 0, s, a, ws);
+  }
+  if constexpr (E == kBF16 && R >= kMxMinRank) {
+    hipLaunchKernelGGL((lora_expand_mx_kernel<R>),
+                       dim3((unsigned)((tiles + 7) / 8 * 8 * lora_mx_col_blocks(a.h2))),
+                       dim3(kThreads), 0, s, a, ws);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((lora_expand_kernel<E, R>),
                      dim3((unsigned)((tiles + 7) / 8 * 8 * kQuarters * a.chunks)), dim3(kThreads),

@@ -111,11 +111,13 @@ def test_gemm_replays_match_eager():
     ex.close()
 
 
-@pytest.mark.parametrize("rows", [300, 700], ids=["grouping_in_shrink", "grouping_launch"])
-def test_lora_replays_match_eager(rows):
-    """Both tiled launch sequences; the workspace holds the previous replay's
-    table and partial sums, which every launch rewrites before reading."""
-    h1, rank, h2, h3, wn, layers, layer, off, dt = 256, 16, 192, 320, 5, 2, 1, 64, "bf16"
+@pytest.mark.parametrize("rows,rank", [(300, 16), (700, 16), (700, 64)],
+                         ids=["grouping_in_shrink", "grouping_launch", "mfma_expand"])
+def test_lora_replays_match_eager(rows, rank):
+    """Both tiled launch sequences, and the matrix-core expand (bf16, rank
+    64); the workspace holds the previous replay's table and partial sums,
+    which every launch rewrites before reading."""
+    h1, h2, h3, wn, layers, layer, off, dt = 256, 192, 320, 5, 2, 1, 64, "bf16"
     s = 80 + rows
     td = torch.bfloat16
     t = lambda bits_: torch.from_numpy(np.ascontiguousarray(bits_).view(np.int16)).view(td).cuda()

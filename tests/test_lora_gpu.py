@@ -12,9 +12,16 @@ Bars:
    the storage type add 2^-24 |v| and u |v| (u = 2^-8 bf16, 2^-11 fp16) plus
    half the storage type's subnormal spacing:
        |got - v| <= (h1 + rank + 4) 2^-24 M + (2^-24 + u) |v| (1 + 1e-6) + sub
+   In bf16 at ranks 32 and above the tiled expand sums on the matrix unit:
+   each fp32 z1 value is split exactly into three bf16 pieces, the 3 * rank
+   products with weightB are exact, and the bound takes each of their
+   additions inside the unit at up to 2^-23 relative (rounding to nearest is
+   not assumed there), so 6 * rank stands in for rank.
  - every element outside the slice, and every row without an adapter, equals
    y bit for bit (outputs pre-filled with a canary when out is not y).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -79,9 +86,16 @@ def magnitude(y, x, wa, wb, idx, layer, scale, off, dt, rows=None):
     return m * abs(float(np.float32(scale)))
 
 
-def check_slice(got, pre, mag, h1, rank, dt):
+def expand_terms(rank, dt, desc):
+    """Additions the bound charges to one expand sum (see the module notes)."""
+    mfma = dt == "bf16" and rank >= 32 and "lora-tiled" in desc
+    return 6 * rank if mfma else rank
+
+
+def check_slice(got, pre, mag, h1, rank, dt, expand=None):
     gv = from_bits(got, dt)
-    tol = (h1 + rank + 4) * 2.0 ** -24 * mag + (2.0 ** -24 + UNIT[dt]) * np.abs(pre) * (1 + 1e-6) \
+    expand = rank if expand is None else expand
+    tol = (h1 + expand + 4) * 2.0 ** -24 * mag + (2.0 ** -24 + UNIT[dt]) * np.abs(pre) * (1 + 1e-6) \
         + SUB[dt]
     err = np.abs(gv - pre)
     bad = err > tol
@@ -188,6 +202,26 @@ def test_prefill_full_size_sampled():
                              rows=rows)
     mag = magnitude(y, x, wa, wb, idx, wl.layer, wl.scale, wl.y_offset, wl.dtype, rows)
     check_slice(got[rows, wl.y_offset:wl.y_offset + wl.h2], pre, mag, wl.h1, wl.rank, wl.dtype)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("rank", [32, 64, 128])
+@pytest.mark.parametrize("rows,h2,h3,off", [(300, 384, 1024, 128), (700, 2560, 4096, 1024)],
+                         ids=["one_chunk", "three_chunks"])
+def test_ranks_realistic(rows, h2, h3, off, rank, dt):
+    """Normal data at the larger tiled ranks, against the bound: 300 rows
+    (grouping inside the shrink) and 700 rows (grouping launch), a slice of
+    384 columns (one partial column range) or 2560 (three, the last one
+    half full); indices include values outside [0, w)."""
+    wl = dataclasses.replace(synth.LORA_WORKLOADS["lora_small"], name=f"lora_r{rank}",
+                             rows=rows, rank=rank, h2=h2, h3=h3, y_offset=off, dtype=dt)
+    y, x, wa, wb, idx = synth.lora_inputs(wl)
+    got, desc = run_lora(y, x, wa, wb, idx, wl.layer, wl.scale, wl.y_offset, dt)
+    assert "lora-tiled" in desc, desc
+    _, pre = oracle.add_lora(y, x, wb, idx, wa, wl.layer, wl.scale, wl.y_offset, dt)
+    check_outside(got, y, idx, wl.w, wl.y_offset, wl.h2)
+    mag = magnitude(y, x, wa, wb, idx, wl.layer, wl.scale, wl.y_offset, dt)
+    check_slice(got[:, off:off + h2], pre, mag, wl.h1, rank, dt, expand_terms(rank, dt, desc))
 
 
 @pytest.mark.parametrize("pattern", ["one_adapter", "distinct", "none", "single_row",
