@@ -839,11 +839,13 @@ int32_t adq_executor_describe(const adq_executor* e, char* buf, uint64_t len) {
       const bool tiled = e->path != ADQ_PATH_GENERIC;
       snprintf(buf, (size_t)len,
                "path=%s rows=%lld h1=%lld rank=%lld h2=%lld h3=%lld adapters=%lld layers=%lld "
-               "weight_a=%d in_place=%d ksplit=%d chunks=%d tiles<=%lld workspace=%llu cus=%d",
+               "weight_a=%d in_place=%d ksplit=%d chunks=%d tiles<=%lld workspace=%llu cus=%d "
+               "kernels=%s",
                tiled ? "lora-tiled" : "lora-generic", (long long)a.rows, (long long)a.h1,
                (long long)a.rank, (long long)a.h2, (long long)a.h3, (long long)a.w,
                (long long)a.l, a.wa != nullptr, a.in_place, a.ksplit, a.chunks,
-               (long long)adq::lora_max_tiles(a), (unsigned long long)e->ws_bytes, e->cus);
+               (long long)adq::lora_max_tiles(a), (unsigned long long)e->ws_bytes, e->cus,
+               tiled ? adq::lora_tiled_kernels(a) : "generic");
     }
     return e->path;
   }

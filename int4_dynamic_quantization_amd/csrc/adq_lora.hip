@@ -989,6 +989,13 @@ hipError_t launch_elem(const LoraArgs& a, int path, void* workspace, hipStream_t
 
 int64_t lora_max_tiles(const LoraArgs& a) { return lora_max_tiles_dev(a); }
 
+const char* lora_tiled_kernels(const LoraArgs& a) {
+  const bool mx = a.elem == kBF16 && a.rank >= kMxMinRank;
+  if (a.wa && a.rows <= kSmallRows) return mx ? "shrink+mfma-expand" : "shrink+expand";
+  if (a.wa) return mx ? "group+shrink+mfma-expand" : "group+shrink+expand";
+  return mx ? "group+mfma-expand" : "group+expand";
+}
+
 int lora_expand_chunks(int64_t h2) {
   const int64_t c = (h2 + kQCols - 1) / kQCols;
   return (int)(c < 1 ? 1 : c);

@@ -88,7 +88,7 @@ def magnitude(y, x, wa, wb, idx, layer, scale, off, dt, rows=None):
 
 def expand_terms(rank, dt, desc):
     """Additions the bound charges to one expand sum (see the module notes)."""
-    mfma = dt == "bf16" and rank >= 32 and "lora-tiled" in desc
+    mfma = dt == "bf16" and "mfma-expand" in desc
     return 6 * rank if mfma else rank
 
 
@@ -127,6 +127,11 @@ EXACT = [
     (200, 256, 128, 96, 160, 3, 2, 1, 32, True, "bf16"), # rank 128 (128-k stages)
     (600, 128, 128, 40, 64, 4, 1, 0, 8, True, "bf16"),   # rank 128, grouping launch
     (33, 64, 16, 52, 120, 3, 2, 1, 64, True, "bf16"),   # slice width 4 (mod 8)
+    # above 512 rows (grouping launch) at ranks 8 / 16, ragged h1 and slices
+    (600, 128, 8, 44, 96, 4, 1, 0, 8, True, "fp16"),    # slice width 4 (mod 8)
+    (520, 520, 8, 100, 120, 5, 1, 0, 16, True, "bf16"), # h1 not a multiple of 256
+    (1000, 256, 16, 200, 264, 3, 2, 1, 64, True, "bf16"),
+    (777, 264, 16, 68, 136, 6, 2, 1, 40, True, "fp16"),
     (37, 64, 16, 48, 100, 3, 2, 1, 20, True, "bf16"),   # y rows not 16-byte aligned: generic
     (5, 30, 5, 7, 13, 2, 2, 1, 3, True, "fp16"),        # generic only (ragged)
 ]
@@ -184,7 +189,8 @@ def test_workloads(name, in_place, path):
     _, pre = oracle.add_lora(y, x, wb, idx, wa, wl.layer, wl.scale, wl.y_offset, wl.dtype)
     check_outside(got, y, idx, wl.w, wl.y_offset, wl.h2)
     mag = magnitude(y, x, wa, wb, idx, wl.layer, wl.scale, wl.y_offset, wl.dtype)
-    check_slice(got[:, wl.y_offset:wl.y_offset + wl.h2], pre, mag, wl.h1, wl.rank, wl.dtype)
+    check_slice(got[:, wl.y_offset:wl.y_offset + wl.h2], pre, mag, wl.h1, wl.rank, wl.dtype,
+                expand_terms(wl.rank, wl.dtype, desc))
 
 
 def test_prefill_full_size_sampled():
@@ -201,18 +207,18 @@ def test_prefill_full_size_sampled():
     _, pre = oracle.add_lora(y, x, wb, idx, wa, wl.layer, wl.scale, wl.y_offset, wl.dtype,
                              rows=rows)
     mag = magnitude(y, x, wa, wb, idx, wl.layer, wl.scale, wl.y_offset, wl.dtype, rows)
-    check_slice(got[rows, wl.y_offset:wl.y_offset + wl.h2], pre, mag, wl.h1, wl.rank, wl.dtype)
+    check_slice(got[rows, wl.y_offset:wl.y_offset + wl.h2], pre, mag, wl.h1, wl.rank, wl.dtype,
+                expand_terms(wl.rank, wl.dtype, desc))
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
-@pytest.mark.parametrize("rank", [32, 64, 128])
+@pytest.mark.parametrize("rank", [8, 16, 32, 64, 128])
 @pytest.mark.parametrize("rows,h2,h3,off", [(300, 384, 1024, 128), (700, 2560, 4096, 1024)],
                          ids=["one_chunk", "three_chunks"])
 def test_ranks_realistic(rows, h2, h3, off, rank, dt):
-    """Normal data at the larger tiled ranks, against the bound: 300 rows
+    """Normal data at every tiled rank, against the bound: 300 rows
     (grouping inside the shrink) and 700 rows (grouping launch), a slice of
-    384 columns (one partial column range) or 2560 (three, the last one
-    half full); indices include values outside [0, w)."""
+    384 columns or 2560; indices include values outside [0, w)."""
     wl = dataclasses.replace(synth.LORA_WORKLOADS["lora_small"], name=f"lora_r{rank}",
                              rows=rows, rank=rank, h2=h2, h3=h3, y_offset=off, dtype=dt)
     y, x, wa, wb, idx = synth.lora_inputs(wl)
