@@ -16,12 +16,13 @@
 //     between runs; every row's result is computed from its own data in a
 //     fixed order, so outputs do not.
 //  2. shrink: one workgroup per (tile, slice of h1), compiled per rank (8,
-//     16, 32, 64, 128; rank 8 padded to one 16-wide block).  The slice of
-//     weightA[g, layer] (stored [h1, rank], rank contiguous) is staged in LDS
-//     transposed, 256 k at a time (128 for rank 128), so each MFMA operand is
-//     one 16-byte read; 4 wavefronts each take 16 rows
-//     (v_mfma_f32_16x16x32_{bf16,f16}, the x fragments of a whole 256-k
-//     stage loaded before the staging) and write fp32 partial sums to the
+//     16, 32, 64, 128; rank 8 padded to one 16-wide block), 128 k per stage.
+//     The stage of weightA[g, layer] (stored [h1, rank], rank contiguous) is
+//     staged in LDS transposed, so each MFMA operand is one 16-byte read; the
+//     stage of x (64 rows) reaches LDS through direct-to-LDS loads in whole
+//     row pieces, double-buffered (the next stage requested before the
+//     current one is staged and multiplied); 4 wavefronts each take 16 rows
+//     (v_mfma_f32_16x16x32_{bf16,f16}) and write fp32 partial sums to the
 //     workspace.
 //  3. expand: one workgroup per (16 rows of a tile, 1024 columns of the
 //     slice), all workgroups of a tile on one XCD.  Each thread owns 4
@@ -48,20 +49,25 @@ namespace {
 constexpr int kThreads = 256;         // generic, shrink and expand kernels
 constexpr int kGroupThreads = 1024;   // group kernel
 constexpr int kTile = kLoraTileRows;  // 64 rows
-constexpr int kKSub = 256;            // k per LDS stage of weightA (rank <= 64)
-// Transposed weightA rows in LDS: 256 k + 32 of padding (576 bytes, 16 banks
+constexpr int kKSub = 128;            // k per shrink stage
+// Transposed weightA rows in LDS: 128 k + 32 of padding (320 bytes, 16 banks
 // of offset per row) with the 8-k groups of rows 8..15 (mod 16) swapped in
 // pairs (group index ^ 2).  gfx950 reads 128 bits for 16 lanes per pass; for
 // every lane grouping that fits the bank-conflict measurements (one half
 // wave, parity of lane bits 2 and 4, possibly with bits 0 and 3) the 16
-// lanes of a pass then hit 16 distinct 4-bank groups.
-// Per rank: k per stage (128 for rank 128, so the staged slice stays 40 KB)
-// and the row stride of the staged slice (the same 16-bank offset per row,
-// so the swizzle above keeps the reads conflict-free); ranks below 16 are
+// lanes of a pass then hit 16 distinct 4-bank groups.  Ranks below 16 are
 // padded to one 16-wide MFMA block with zero rows.
-template <int R> constexpr int stage_k() { return R > 64 ? 128 : kKSub; }
+template <int R> constexpr int stage_k() { return kKSub; }
 template <int R> constexpr int at_stride() { return stage_k<R>() + 32; }
 template <int R> constexpr int padded_rank() { return R < 16 ? 16 : R; }
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -274,8 +280,14 @@ template <int E, int R, bool G>
 __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a, Workspace ws) {
   constexpr int RP = padded_rank<R>();
   constexpr int KS = stage_k<R>();
+  // x stage in LDS: 64 rows of KS k, filled by direct-to-LDS loads (1 KB
+  // per instruction: RPS whole rows of CPR 16-byte chunks); the chunk c of
+  // row r sits at position c ^ (r % 16), so the 16-byte MFMA fragment reads
+  // of 16 rows hit distinct banks
+  constexpr int CPR = KS / 8, RPS = 64 / CPR, SPW = kTile / RPS / 4;
   __shared__ int64_t rows_lds[kTile];
   __shared__ __attribute__((aligned(16))) uint16_t at[RP][at_stride<R>()];
+  __shared__ __attribute__((aligned(1024))) uint16_t xs[2 * kTile * KS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -324,51 +336,96 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
 #pragma unroll
   for (int b = 0; b < nb; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
-  const bool row_ok = rb + fi < n;
-  const T* xrow = x + (row_ok ? rows_lds[rb + fi] : rows_lds[0]) * h1;
+  // this lane's chunk of x in each of its wave's segments: byte offset of
+  // the row (all ones past the tile's rows) and k of the chunk in a stage
+  const rsrc_t rx = make_rsrc(x, (uint32_t)(a.rows * h1 * 2));
+  uint32_t xo[SPW];
+  int xk[SPW];
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int r = RPS * (wave * SPW + i) + lane / CPR;
+    const int c = (lane % CPR) ^ (r & 15);
+    xk[i] = 8 * c;
+    xo[i] = r < n ? (uint32_t)(rows_lds[r] * h1 * 2) + 16u * c : 0xFFFFFFFFu;
+  }
+  using lds_ptr = __attribute__((address_space(3))) void*;
+  uint8_t* xs_wave = reinterpret_cast<uint8_t*>(xs) + wave * SPW * 1024;
+  // x stages are double-buffered: stage st + 1 is requested before stage
+  // st's weightA is staged and its products run.  Barriers carry no memory
+  // fence (which would wait for the stage in flight too): stage st is
+  // awaited explicitly (loads complete in order, so it has landed once at
+  // most the SPW loads of stage st + 1 are outstanding), LDS writes and
+  // reads complete (lgkmcnt) before each barrier.
   constexpr int pieces_per_k = R / 8;
-  for (int64_t sub = k_lo; sub < k_hi; sub += KS) {
+  constexpr int PPT = (KS * pieces_per_k + kThreads - 1) / kThreads;  // weightA pieces per thread
+  auto issue_x = [&](int64_t sub, int buf) {
+    const int sub_n = (int)(k_hi - sub < KS ? k_hi - sub : KS);
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const uint32_t off =
+          xo[i] != 0xFFFFFFFFu && xk[i] < sub_n ? xo[i] + (uint32_t)(sub * 2) : 0xFFFFFFF0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (lds_ptr)(xs_wave + buf * (kTile * KS * 2) + i * 1024), 16, off, 0, 0, 0);
+    }
+  };
+  auto barrier = [] {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+  };
+  issue_x(k_lo, 0);
+  int buf = 0;
+  for (int64_t sub = k_lo; sub < k_hi; sub += KS, buf ^= 1) {
     const int sub_n = (int)(k_hi - sub < KS ? k_hi - sub : KS);
     const int steps = (sub_n + 31) / 32;
-    // this stage's x fragments first (they do not depend on the LDS stage)
-    u16x8 xa[KS / 32];
+    const bool more = sub + KS < k_hi;
+    // weightA[sub .. sub + KS) (zeros past the slice), then the next x stage
+    u16x8 wv[PPT];
 #pragma unroll
-    for (int u = 0; u < KS / 32; ++u) {
-      const int64_t kx = sub + 32 * u + 8 * fk;
-      xa[u] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (rb < n && row_ok && u < steps && kx < k_hi)
-        xa[u] = *reinterpret_cast<const u16x8*>(xrow + kx);
-    }
-    // stage weightA[sub .. sub + KS) transposed (zeros past the slice)
-    for (int p = tid; p < KS * pieces_per_k; p += kThreads) {
+    for (int j = 0; j < PPT; ++j) {
+      const int p = tid + j * kThreads;
       const int k = p / pieces_per_k, rg = p % pieces_per_k;
-      u16x8 v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (k < sub_n) v = *reinterpret_cast<const u16x8*>(wa + (sub + k) * rank + 8 * rg);
+      wv[j] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (p < KS * pieces_per_k && k < sub_n)
+        wv[j] = *reinterpret_cast<const u16x8*>(wa + (sub + k) * rank + 8 * rg);
+    }
+    if (more) issue_x(sub + KS, buf ^ 1);
+    // weightA staged transposed
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * rg + e;
-        at[r][8 * ((k >> 3) ^ (((r >> 3) & 1) << 1)) + (k & 7)] = v[e];
+    for (int j = 0; j < PPT; ++j) {
+      const int p = tid + j * kThreads;
+      const int k = p / pieces_per_k, rg = p % pieces_per_k;
+      if (p < KS * pieces_per_k) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * rg + e;
+          at[r][8 * ((k >> 3) ^ (((r >> 3) & 1) << 1)) + (k & 7)] = wv[j][e];
+        }
       }
     }
-    __syncthreads();
+    if (more) wait_vmcnt<SPW>();
+    else wait_vmcnt<0>();
+    barrier();
+    const uint16_t* xb = xs + buf * (kTile * KS);
     if (rb < n) {  // wavefront-uniform
 #pragma unroll
       for (int u = 0; u < KS / 32; ++u) {
         if (u < steps) {
           const int kg = 4 * u + fk;
+          const u16x8 xa = *reinterpret_cast<const u16x8*>(&xb[(rb + fi) * KS + 8 * (kg ^ fi)]);
 #pragma unroll
           for (int b = 0; b < nb; ++b) {
             {
               const int r = 16 * b + fi;
               const u16x8 bv =
                   *reinterpret_cast<const u16x8*>(&at[r][8 * (kg ^ (((r >> 3) & 1) << 1))]);
-              acc[b] = mfma16<E>(xa[u], bv, acc[b]);
+              acc[b] = mfma16<E>(xa, bv, acc[b]);
             }
           }
         }
       }
     }
-    __syncthreads();  // before the next stage overwrites `at`
+    barrier();  // before the next stage overwrites `at` and this x buffer is refilled
   }
   // element e of lane l: row rb + 4 * (l / 16) + e, rank l % 16 (+ 16 * block)
   float* zp = ws.z1p + ((int64_t)ks * lora_max_tiles_dev(a) + tile) * kTile * rank;
