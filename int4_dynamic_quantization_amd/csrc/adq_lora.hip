@@ -356,8 +356,12 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
   // awaited explicitly (loads complete in order, so it has landed once at
   // most the SPW loads of stage st + 1 are outstanding), LDS writes and
   // reads complete (lgkmcnt) before each barrier.
-  constexpr int pieces_per_k = R / 8;
-  constexpr int PPT = (KS * pieces_per_k + kThreads - 1) / kThreads;  // weightA pieces per thread
+  // weightA stage: blocks of 8 k x 8 ranks, one per thread (threads t and
+  // t + 1 take neighbouring 8-k groups of the same 8 ranks), loaded as 8
+  // rows of 16 bytes, transposed in registers and written as 8 rank rows
+  // of 16 bytes: 16 lanes of a row group write 16 distinct 16-byte slots
+  constexpr int KG = KS / 8, NBLK = KG * (R / 8);
+  static_assert(NBLK <= kThreads, "one weightA block per thread");
   auto issue_x = [&](int64_t sub, int buf) {
     const int sub_n = (int)(k_hi - sub < KS ? k_hi - sub : KS);
 #pragma unroll
@@ -380,27 +384,25 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
     const int steps = (sub_n + 31) / 32;
     const bool more = sub + KS < k_hi;
     // weightA[sub .. sub + KS) (zeros past the slice), then the next x stage
-    u16x8 wv[PPT];
+    const int bkg = tid % KG, brg = tid / KG;
+    const bool blk = tid < NBLK;
+    u16x8 wv[8];
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int p = tid + j * kThreads;
-      const int k = p / pieces_per_k, rg = p % pieces_per_k;
-      wv[j] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (p < KS * pieces_per_k && k < sub_n)
-        wv[j] = *reinterpret_cast<const u16x8*>(wa + (sub + k) * rank + 8 * rg);
+    for (int e = 0; e < 8; ++e) {
+      const int k = 8 * bkg + e;
+      wv[e] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (blk && k < sub_n) wv[e] = *reinterpret_cast<const u16x8*>(wa + (sub + k) * rank + 8 * brg);
     }
     if (more) issue_x(sub + KS, buf ^ 1);
     // weightA staged transposed
+    if (blk) {
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int p = tid + j * kThreads;
-      const int k = p / pieces_per_k, rg = p % pieces_per_k;
-      if (p < KS * pieces_per_k) {
+      for (int q = 0; q < 8; ++q) {
+        u16x8 t;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * rg + e;
-          at[r][8 * ((k >> 3) ^ (((r >> 3) & 1) << 1)) + (k & 7)] = wv[j][e];
-        }
+        for (int e = 0; e < 8; ++e) t[e] = wv[e][q];
+        const int r = 8 * brg + q;
+        *reinterpret_cast<u16x8*>(&at[r][8 * (bkg ^ (((r >> 3) & 1) << 1))]) = t;
       }
     }
     if (more) wait_vmcnt<SPW>();
