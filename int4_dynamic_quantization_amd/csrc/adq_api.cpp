@@ -781,7 +781,11 @@ adq_status adq_add_lora_get_workspace_size(const adq_tensor* y, const adq_tensor
     // columns of the slice.
     const int64_t est_tiles = (rows + adq::kLoraTileRows - 1) / adq::kLoraTileRows +
                               (w < rows ? w : rows);
-    const int64_t want = (2 * (int64_t)e.cus + est_tiles - 1) / est_tiles;
+    // ... but no more than fit on the chip at once (ranks whose shrink
+    // holds fewer workgroups per CU would otherwise run a second round)
+    int64_t want = (2 * (int64_t)e.cus + est_tiles - 1) / est_tiles;
+    const int64_t fit = (int64_t)adq::lora_shrink_blocks_per_cu(a) * e.cus / est_tiles;
+    if (fit >= 1 && fit < want) want = fit;
     auto clamp = [](int64_t v, int64_t hi) { return (int)(v < 1 ? 1 : v > hi ? hi : v); };
     a.ksplit = clamp(ADQ_LORA_KSPLIT_MULT * want, h1 / 256 > 1 ? h1 / 256 : 1);
     a.chunks = adq::lora_expand_chunks(h2);

@@ -117,6 +117,7 @@ constexpr int kLoraMaxRankGeneric = 1024;
 int64_t lora_max_tiles(const LoraArgs& a);
 int lora_expand_chunks(int64_t h2);  // column ranges per tile in the expand
 const char* lora_tiled_kernels(const LoraArgs& a);  // the tiled path's launches
+int lora_shrink_blocks_per_cu(const LoraArgs& a);   // resident shrink workgroups per CU
 uint64_t lora_workspace_bytes(const LoraArgs& a);
 hipError_t launch_lora(const LoraArgs& a, int path, void* workspace, hipStream_t stream);
 

@@ -1048,6 +1048,29 @@ hipError_t launch_elem(const LoraArgs& a, int path, void* workspace, hipStream_t
 
 int64_t lora_max_tiles(const LoraArgs& a) { return lora_max_tiles_dev(a); }
 
+int lora_shrink_blocks_per_cu(const LoraArgs& a) {
+  const void* fn = nullptr;
+  const bool f16 = a.elem == kF16, g = a.wa && a.rows <= kSmallRows;
+#define ADQ_SHRINK_FN(R_)                                                                    \
+  fn = f16 ? (g ? (const void*)lora_shrink_kernel<kF16, R_, true>                          \
+                : (const void*)lora_shrink_kernel<kF16, R_, false>)                         \
+           : (g ? (const void*)lora_shrink_kernel<kBF16, R_, true>                         \
+                : (const void*)lora_shrink_kernel<kBF16, R_, false>)
+  switch (a.rank) {
+    case 8: ADQ_SHRINK_FN(8); break;
+    case 16: ADQ_SHRINK_FN(16); break;
+    case 32: ADQ_SHRINK_FN(32); break;
+    case 64: ADQ_SHRINK_FN(64); break;
+    case 128: ADQ_SHRINK_FN(128); break;
+    default: return 0;
+  }
+#undef ADQ_SHRINK_FN
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kThreads, 0) != hipSuccess)
+    return 0;
+  return blocks;
+}
+
 const char* lora_tiled_kernels(const LoraArgs& a) {
   const bool mx = a.elem == kBF16 && a.rank >= kMxMinRank;
   if (a.wa && a.rows <= kSmallRows) return mx ? "shrink+mfma-expand" : "shrink+expand";
