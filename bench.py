@@ -18,11 +18,12 @@ quantized rows (16384 x 8192 codes with per-row scales through an
 8192 -> 8192 projection with per-column weight scales, bf16 out) against
 the MI355X dense INT8 MFMA peak.  ``--workload lora_prefill`` (or
 lora_decode) times AddLora accumulating into y in place, against HBM
-bandwidth.
+bandwidth; ``--lora-rank R`` runs it at another rank.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -244,6 +245,9 @@ def main():
     ap.add_argument("--no-rotate", action="store_true",
                     help="reuse one input/output set (cache-warm) instead of rotating sets "
                          "that do not fit the last-level cache")
+    ap.add_argument("--lora-rank", type=int, default=0, metavar="R",
+                    help="AddLora workloads: use rank R (8, 16, 32, 64, 128 take the tiled "
+                         "kernels) instead of the workload's own")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead: time a plain device-to-device copy of MIB MiB (reference "
                          "for achievable bandwidth and for scaling HBM byte counters)")
@@ -493,6 +497,8 @@ def lora_cpu_baseline(wl, host, alg_rows_bytes, budget_s: float):
 def bench_lora(args, torch, adq, synth) -> None:
     """One step = one AddLora launch accumulating into y in place."""
     wl = synth.LORA_WORKLOADS[args.workload]
+    if args.lora_rank and args.lora_rank != wl.rank:
+        wl = dataclasses.replace(wl, name=f"{wl.name}_rank{args.lora_rank}", rank=args.lora_rank)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     host = synth.lora_inputs(wl)
