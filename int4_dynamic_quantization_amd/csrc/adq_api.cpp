@@ -771,7 +771,8 @@ adq_status adq_add_lora_get_workspace_size(const adq_tensor* y, const adq_tensor
                     h2 % 4 == 0 && h3 % 8 == 0 && y_offset % 8 == 0 && aligned(x->data, 16) &&
                     (!weight_a || aligned(weight_a->data, 16)) && aligned(weight_b->data, 8) &&
                     aligned(y->data, 16) && aligned(out->data, 8) &&
-                    rows * h3 * 2 < (int64_t)1 << 32 &&  // 32-bit offsets into y
+                    rows * h3 * 2 < (int64_t)1 << 32 &&  // 32-bit offsets into y,
+                    rank * h2 * 2 < (int64_t)1 << 32 &&  // into weightB[g, layer]
                     (!weight_a || rows * h1 * 2 < (int64_t)1 << 32);  // and into x
   {
     // Tiles are only known on the device (they depend on the index values);

@@ -282,3 +282,23 @@ def test_paths():
     assert ex.set_path(adq.PATH_AUTO) > 0
     assert "lora-tiled" in ex.describe()
     ex.close()
+
+
+@pytest.mark.parametrize("h2,kind", [((1 << 24) - 8, "lora-tiled"), (1 << 24, "lora-generic")])
+def test_offset_limits_select_the_kernel(h2, kind):
+    """The tiled kernels address y, x and weightB[g, layer] with 32-bit byte
+    offsets: a rank-128 weightB slice of 2^32 bytes (2^24 columns) is planned
+    on the generic kernel, one just below on the tiled kernels.  Planning
+    only (tensors left uninitialised)."""
+    rank = 128
+    y = torch.empty((2, h2), dtype=torch.bfloat16, device="cuda")
+    x = torch.empty((2, 64), dtype=torch.bfloat16, device="cuda")
+    wa = torch.empty((1, 1, 64, rank), dtype=torch.bfloat16, device="cuda")
+    wb = torch.empty((1, 1, rank, h2), dtype=torch.bfloat16, device="cuda")
+    idx = torch.zeros(2, dtype=torch.int32, device="cuda")
+    ex, _ = adq.plan_add_lora(y, x, wb, idx, wa, 0, 0.5, 0, out=y)
+    desc = ex.describe()
+    ex.close()
+    del y, x, wa, wb
+    torch.cuda.empty_cache()
+    assert kind in desc, desc
