@@ -132,6 +132,8 @@ EXACT = [
     (520, 520, 8, 100, 120, 5, 1, 0, 16, True, "bf16"), # h1 not a multiple of 256
     (1000, 256, 16, 200, 264, 3, 2, 1, 64, True, "bf16"),
     (777, 264, 16, 68, 136, 6, 2, 1, 40, True, "fp16"),
+    (50, 64, 64, 96, 160, 3, 1, 0, 32, False, "bf16"),  # matrix-core expand without weightA
+    (600, 128, 128, 64, 128, 2, 1, 0, 0, False, "bf16"),
     (37, 64, 16, 48, 100, 3, 2, 1, 20, True, "bf16"),   # y rows not 16-byte aligned: generic
     (5, 30, 5, 7, 13, 2, 2, 1, 3, True, "fp16"),        # generic only (ragged)
 ]
