@@ -253,7 +253,7 @@ def main():
                          "for achievable bandwidth and for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this operator is row-local and this build runs on a "
+        print(f"bench.py measures one GPU: the operator is row-local and the library runs on a "
               f"single MI355X, so --gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
 
