@@ -369,7 +369,7 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
       const uint32_t off =
           xo[i] != 0xFFFFFFFFu && xk[i] < sub_n ? xo[i] + (uint32_t)(sub * 2) : 0xFFFFFFF0u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (lds_ptr)(xs_wave + buf * (kTile * KS * 2) + i * 1024), 16, off, 0, 0, 0);
+          rx, (lds_ptr)(xs_wave + buf * (kTile * KS * 2) + i * 1024), 16, off, 0, 0, kStreamLoad);
     }
   };
   auto barrier = [] {
@@ -511,7 +511,8 @@ __global__ void __launch_bounds__(kThreads) lora_expand_kernel(const LoraArgs a,
     yv[i] = uint2{0u, 0u};
     if (i < n) {
       const uint32_t off = col_ok ? (uint32_t)(rows[i] * h3 * 2) + col_off : col_off;
-      yv[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ry, off, 0, 0));
+      yv[i] = __builtin_bit_cast(uint2,
+                                 __builtin_amdgcn_raw_buffer_load_b64(ry, off, 0, kStreamLoad));
     }
   }
 
@@ -581,12 +582,15 @@ __global__ void __launch_bounds__(kThreads) lora_expand_kernel(const LoraArgs a,
   __syncthreads();
   // out = y + scale * (z1 . weightB), one fp32 fma chain over the ranks in
   // rank order per output, one fma into y, one rounding
+  const rsrc_t rout = make_rsrc(out, (uint32_t)(a.rows * h3 * 2));
   auto store_row = [&](int i, const float (&acc)[4]) {
     const u16x4 yq = __builtin_bit_cast(u16x4, yv[i]);
     u16x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) o[q] = narrow1<E>(__builtin_fmaf(acc[q], a.scale, widen1<E>(yq[q])));
-    *reinterpret_cast<u16x4*>(out + (int64_t)rows[i] * h3 + a.y_offset + col) = o;
+    __builtin_amdgcn_raw_buffer_store_b64(
+        __builtin_bit_cast(u32x2, o), rout,
+        (uint32_t)(((int64_t)rows[i] * h3 + a.y_offset + col) * 2), 0, kStreamStore);
   };
   if (col_ok) {
     if constexpr (R <= 16) {
@@ -877,6 +881,7 @@ __global__ void __launch_bounds__(kThreads) lora_expand_mx_kernel(const LoraArgs
   // contiguous bytes), issued first.  An 8-column group that starts inside
   // the slice stays inside y's row (h3 and y_offset are multiples of 8).
   constexpr int kYChunks = kTile * kMxCols / 8 / kThreads;  // 8 per thread
+  const rsrc_t rout = make_rsrc(out, (uint32_t)(a.rows * h3 * 2));
   const rsrc_t ry = make_rsrc(y, (uint32_t)(a.rows * h3 * 2));
   const int64_t colb = (int64_t)cb * kMxCols + 8 * (tid % 32);  // this thread's 8 columns
   u16x8 yv[kYChunks];
@@ -889,7 +894,7 @@ __global__ void __launch_bounds__(kThreads) lora_expand_mx_kernel(const LoraArgs
     yv[k] = __builtin_bit_cast(
         u16x8, __builtin_amdgcn_raw_buffer_load_b128(
                    ry, ok ? (uint32_t)((yrow[k] * h3 + a.y_offset + colb) * 2) : 0xFFFFFFF0u, 0,
-                   0));
+                   kStreamLoad));
   }
   __syncthreads();  // every wave is done with z1's pieces
 #pragma unroll
@@ -918,11 +923,13 @@ __global__ void __launch_bounds__(kThreads) lora_expand_mx_kernel(const LoraArgs
     const int rs = tid / 32 + 8 * k;
     if (rs < n && colb < a.h2) {
       const u16x8 o = *reinterpret_cast<const u16x8*>(&yb[rs][8 * (tid % 32)]);
-      T* op = out + (int64_t)yrow[k] * h3 + a.y_offset + colb;
+      const uint32_t off = (uint32_t)(((int64_t)yrow[k] * h3 + a.y_offset + colb) * 2);
       if (colb + 8 <= a.h2)
-        *reinterpret_cast<u16x8*>(op) = o;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rout, off, 0,
+                                               kStreamStore);
       else
-        *reinterpret_cast<u16x4*>(op) = u16x4{o[0], o[1], o[2], o[3]};
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(u32x2, u16x4{o[0], o[1], o[2], o[3]}), rout, off, 0, kStreamStore);
     }
   }
 
