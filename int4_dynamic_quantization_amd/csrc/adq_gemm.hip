@@ -463,10 +463,11 @@ __global__ void __launch_bounds__(256) w8a8_big_kernel(const GemmArgs g) {
         const float v = (float)acc[i][j][e] * sa[i][e] * swv[j] + bv[j];
         const uint32_t off = col_off[j] == kOut ? kOut : row_off + col_off[j];
         if constexpr (OUT == kGemmOutF32) {
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ro, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ro, off, 0,
+                                                kStreamStore);
         } else {
           __builtin_amdgcn_raw_buffer_store_b16(
-              narrow1<OUT == kGemmOutBF16 ? kBF16 : kF16>(v), ro, off, 0, 0);
+              narrow1<OUT == kGemmOutBF16 ? kBF16 : kF16>(v), ro, off, 0, kStreamStore);
         }
       }
     }
