@@ -267,26 +267,36 @@ bool row_geometry(int64_t nvec, int* vpt, int* block) {
   return true;
 }
 
+#ifndef ADQ_SPLIT_MAX_BLOCK
+#define ADQ_SPLIT_MAX_BLOCK 512
+#endif
+#ifndef ADQ_SPLIT_MAX_WANT
+#define ADQ_SPLIT_MAX_WANT 8
+#endif
 #ifndef ADQ_SPLIT_TARGET_WG_PER_CU
 #define ADQ_SPLIT_TARGET_WG_PER_CU 2
 #endif
 
 // Split-row geometry: S workgroups of `block` threads (one 8-column vector
-// per thread, two for rows above 1024 * 8 * 64 columns) per row, enough of
-// them to give every CU about ADQ_SPLIT_TARGET_WG_PER_CU workgroups, and all
-// resident at once.  Rows are processed 8 * row_groups at a time.
+// per thread, two when a split would need more than ADQ_SPLIT_MAX_BLOCK
+// threads) per row, enough of them to give every CU about
+// ADQ_SPLIT_TARGET_WG_PER_CU workgroups but at most ADQ_SPLIT_MAX_WANT per
+// row (every split adds a partner to each exchange), and all resident at
+// once.  Rows are processed 8 * row_groups at a time.  512-thread
+// workgroups let two share a CU, so one computes while the other waits.
 bool split_geometry(adq_executor* e) {
   const int64_t nvec = e->args.n / 8;
   const int64_t rows8 = (e->m + 7) / 8 * 8;
   int64_t want = (int64_t)e->cus * ADQ_SPLIT_TARGET_WG_PER_CU / rows8;  // splits per row
+  if (want > ADQ_SPLIT_MAX_WANT) want = ADQ_SPLIT_MAX_WANT;
   if (want < 1) want = 1;
   int vpt = 1;
   int64_t block = round_up((int)((nvec + want - 1) / want), 64);
   if (block < 64) block = 64;
-  if (block > 1024) {
+  if (block > ADQ_SPLIT_MAX_BLOCK) {
     vpt = 2;
     block = round_up((int)((nvec + 2 * want - 1) / (2 * want)), 64);
-    if (block > 1024) block = 1024;
+    if (block > ADQ_SPLIT_MAX_BLOCK) block = ADQ_SPLIT_MAX_BLOCK;
   }
   const int64_t chunk = block * vpt;
   const int64_t splits = (nvec + chunk - 1) / chunk;

@@ -154,19 +154,32 @@ __global__ void __launch_bounds__(1024) split_kernel(const SplitArgs p) {
                 : (v0 + vj[k] < vend ? one4 : zero4);
   }
 
-  for (int64_t row = (int64_t)group * kXcds + xcd; row < a.rows; row += row_stride) {
-    const uint32_t row_bytes = n * 2u;
+  // the next row's chunk is requested before this row's exchanges, so its
+  // loads are in flight while the workgroup waits for the other splits
+  const uint32_t row_bytes = n * 2u;
+  u32x4 n1[VPT], n2[VPT];
+  auto load_row = [&](int64_t r) {
     const rsrc_t r1 = make_rsrc(
-        static_cast<const char*>(row_ptr(a.x1, row, row_bytes)) + (size_t)v0 * 16u, chunk_bytes16);
+        static_cast<const char*>(row_ptr(a.x1, r, row_bytes)) + (size_t)v0 * 16u, chunk_bytes16);
     const rsrc_t r2 = make_rsrc(
-        static_cast<const char*>(row_ptr(a.x2, row, row_bytes)) + (size_t)v0 * 16u, chunk_bytes16);
+        static_cast<const char*>(row_ptr(a.x2, r, row_bytes)) + (size_t)v0 * 16u, chunk_bytes16);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      n1[k] = __builtin_amdgcn_raw_buffer_load_b128(r1, vj[k] * 16u, 0, kStreamLoad);
+      if constexpr (NIN == 2)
+        n2[k] = __builtin_amdgcn_raw_buffer_load_b128(r2, vj[k] * 16u, 0, kStreamLoad);
+    }
+  };
+  const int64_t row0 = (int64_t)group * kXcds + xcd;
+  if (row0 < a.rows) load_row(row0);
+  for (int64_t row = row0; row < a.rows; row += row_stride) {
     u32x4 c1[VPT], c2[VPT];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      c1[k] = __builtin_amdgcn_raw_buffer_load_b128(r1, vj[k] * 16u, 0, kStreamLoad);
-      if constexpr (NIN == 2)
-        c2[k] = __builtin_amdgcn_raw_buffer_load_b128(r2, vj[k] * 16u, 0, kStreamLoad);
+      c1[k] = n1[k];
+      if constexpr (NIN == 2) c2[k] = n2[k];
     }
+    if (row + row_stride < a.rows) load_row(row + row_stride);
 
     // ---- A
     float x[VPT][8];
