@@ -255,12 +255,20 @@ uint64_t next_epoch() {
 #define ADQ_SHORT_ROW_GRID_MULT 24
 #endif
 
+// Rows of up to ADQ_ROW_MAX_NVEC 8-column vectors (32768 columns) fit one
+// workgroup of the row kernel (VPT 4 above 16384 columns).
+#ifndef ADQ_ROW_MAX_NVEC
+#define ADQ_ROW_MAX_NVEC 4096
+#endif
+
 bool row_geometry(int64_t nvec, int* vpt, int* block) {
   if (nvec <= 0) return false;
   if (nvec <= ADQ_VPT1_MAX_NVEC) {
     *vpt = 1, *block = round_up((int)nvec, 64);
   } else if (nvec <= 2048) {
     *vpt = 2, *block = round_up((int)((nvec + 1) / 2), 64);
+  } else if (nvec <= ADQ_ROW_MAX_NVEC) {
+    *vpt = 4, *block = round_up((int)((nvec + 3) / 4), 64);
   } else {
     return false;
   }
@@ -317,7 +325,7 @@ bool split_geometry(adq_executor* e) {
 }
 
 // Few-row shapes stay on the row kernel: on gfx950 one workgroup streaming
-// a whole row (up to 16384 columns) beats S workgroups that must exchange
+// a whole row (up to 32768 columns) beats S workgroups that must exchange
 // partial results twice through agent-coherent memory, and the cooperative
 // launch the exchange needs costs more than the kernel itself.  Set above 0
 // to send shapes with at most this many rows (and n >= 2048) to the
@@ -344,7 +352,8 @@ adq_status plan(adq_executor* e, int path) {
     int vpt = 0, block = 0;
     if (!e->vector_ok || !row_geometry(n / 8, &vpt, &block))
       return fail(ADQ_ERR_PARAM_INVALID,
-                  "row path needs n %% 8 == 0, n <= 16384 and 16-byte aligned tensors");
+                  "row path needs n %% 8 == 0, n <= %d and 16-byte aligned tensors",
+                  ADQ_ROW_MAX_NVEC * 8);
     int occ = adq::row_max_blocks_per_cu(e->var, vpt, block);
     if (ADQ_MAX_WG_PER_CU > 0 && occ > ADQ_MAX_WG_PER_CU) occ = ADQ_MAX_WG_PER_CU;
     if (occ <= 0) return fail(ADQ_ERR_RUNTIME, "row kernel does not fit block %d", block);

@@ -22,10 +22,15 @@
 //   C  scale_k = max_k / Q_k; code = round_half_even(input_k * (1/scale_k));
 //      pack (INT8: 1 byte, INT4: 1 nibble, even column low) and store.
 //
-// VPT (8-column vectors per thread) is 1 or 2, so a row of up to 16384
-// columns fits one workgroup of at most 1024 threads.  The parameters
-// (gamma, beta, smooth) stay in registers as packed 16-bit values for the
-// whole row loop and are converted at use.
+// VPT (8-column vectors per thread) is 1, 2 or 4, so a row of up to 32768
+// columns fits one workgroup of at most 1024 threads.  With VPT 1 or 2 the
+// parameters (gamma, beta, smooth) stay in registers as packed 16-bit values
+// for the whole row loop and are converted at use, and x and the quantizer
+// inputs are kept between the passes.  With VPT 4 that would not fit the
+// registers of 1024 threads: the parameters are read at use (from L2, they
+// are shared by all rows) and x and the quantizer inputs are recomputed in
+// each pass from the row's raw 16-bit data, with the same operations, so
+// every pass sees the same values.
 #pragma once
 
 #include <type_traits>
@@ -59,7 +64,8 @@ __device__ __forceinline__ void store_codes(const float (&in)[8], float inv, rsr
 
 template <int E, int NIN, int Q1, int Q2, int VPT>
 __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
-  static_assert(VPT == 1 || VPT == 2, "row kernel holds at most 16 columns per thread");
+  static_assert(VPT == 1 || VPT == 2 || VPT == 4, "row kernel holds at most 32 columns per thread");
+  constexpr bool kHold = VPT <= 2;  // x and the inputs kept between passes, next row prefetched
   constexpr bool kTwo = Q2 != kQNone;
   constexpr int kQ2 = kTwo ? Q2 : kQInt8;
   const int tid = threadIdx.x;
@@ -87,13 +93,17 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
     if (!p) return absent;
     return __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(p, row_bytes), vj[k] * 16u, 0, 0);
   };
-  u32x4 pg[VPT], pb[VPT], p1[VPT], p2[VPT];
+  constexpr int PH = kHold ? VPT : 1;  // x / input vectors kept between passes
+  // VPT 4 holds gamma and beta, and smooth1 when there is one output; the
+  // smooth scales it does not hold are read at use (from L2)
+  constexpr bool kHoldS1 = kHold || !kTwo;
+  u32x4 pg[VPT], pb[VPT], p1[kHoldS1 ? VPT : 1], p2[PH];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     pg[k] = load_param(a.gamma, k, zero4);
     pb[k] = load_param(a.beta, k, zero4);
-    p1[k] = load_param(a.smooth1, k, one4);
-    p2[k] = kTwo ? load_param(a.smooth2, k, one4) : zero4;
+    if constexpr (kHoldS1) p1[k] = load_param(a.smooth1, k, one4);
+    if constexpr (kHold) p2[k] = kTwo ? load_param(a.smooth2, k, one4) : zero4;
   }
 
   auto load_row = [&](int64_t row, u32x4 (&c1)[VPT], u32x4 (&c2)[VPT]) {
@@ -124,7 +134,7 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
   int64_t row = first;
   if (row >= rend) return;
   u32x4 c1[VPT], c2[VPT];  // raw x1/x2 vectors of the row being computed
-  load_row(row, c1, c2);
+  if constexpr (kHold) load_row(row, c1, c2);
 
   // One row: prefetch the next, compute and store this one.  The first row
   // is peeled off the loop so that every entry to the loop header has the
@@ -133,32 +143,50 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
   auto body = [&](int64_t row) {
     // Prefetch this workgroup's next row (its last row again when there is
     // none, so the loads are unconditional).
-    u32x4 n1[VPT], n2[VPT];
-    load_row(clamp_row(row + step), n1, n2);
+    // (VPT 4: the registers hold no second row, so this row is loaded here)
+    u32x4 n1[PH], n2[PH];
+    if constexpr (kHold) load_row(clamp_row(row + step), n1, n2);
+    else load_row(row, c1, c2);
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) opaque(pg[k]), opaque(pb[k]), opaque(p1[k]), opaque(p2[k]);
-
-    // ---- A: x = x1 + x2 (fp32), xOut, sum of squares
-    float x[VPT][8];
-    float ss = 0.0f;
-    const rsrc_t rxo = make_rsrc(row_ptr(a.x_out, row, row_bytes), row_bytes);
+    for (int k = 0; k < VPT; ++k) opaque(pg[k]), opaque(pb[k]);
+    if constexpr (kHoldS1) {
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      float acc = 0.0f;
+      for (int k = 0; k < VPT; ++k) opaque(p1[k]);
+    }
+    if constexpr (kHold) {
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) opaque(p2[k]);
+    }
+    // x of column vector k from the row's raw data
+    auto xvec = [&](int k, float (&xk)[8]) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         f32x2 v = widen2<E>(c1[k][w]);
         if constexpr (NIN == 2) v += widen2<E>(c2[k][w]);
-        x[k][2 * w] = v.x;
-        x[k][2 * w + 1] = v.y;
-        acc = __builtin_fmaf(v.x, v.x, acc);
-        acc = __builtin_fmaf(v.y, v.y, acc);
+        xk[2 * w] = v.x;
+        xk[2 * w + 1] = v.y;
+      }
+    };
+
+    // ---- A: x = x1 + x2 (fp32), xOut, sum of squares
+    float x[PH][8];
+    float ss = 0.0f;
+    const rsrc_t rxo = make_rsrc(row_ptr(a.x_out, row, row_bytes), row_bytes);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      float xk[8];
+      xvec(k, xk);
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (kHold) x[k][e] = xk[e];
+        acc = __builtin_fmaf(xk[e], xk[e], acc);
       }
       ss += acc;
       if constexpr (NIN == 2) {
         __builtin_amdgcn_raw_buffer_store_b128(
-            u32x4{narrow2<E>(x[k][0], x[k][1]), narrow2<E>(x[k][2], x[k][3]),
-                  narrow2<E>(x[k][4], x[k][5]), narrow2<E>(x[k][6], x[k][7])},
+            u32x4{narrow2<E>(xk[0], xk[1]), narrow2<E>(xk[2], xk[3]),
+                  narrow2<E>(xk[4], xk[5]), narrow2<E>(xk[6], xk[7])},
             rxo, vj[k] * 16u, 0, kStreamStore);
       }
     }
@@ -170,24 +198,50 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
     const float rinv = __builtin_amdgcn_rsqf(__builtin_fmaf(tot, a.inv_n, a.eps));
 
     // ---- B: y = x * rinv * gamma + beta, quantizer inputs, row maxima
-    float in1[VPT][8], in2[VPT][8];
-    float m1 = 0.0f, m2 = 0.0f;
+    // inputs of column vector k (x held or recomputed)
+    auto inputs = [&](int k, float (&i1)[8], float (&i2)[8]) {
+      float xk[8];
+      if constexpr (kHold) {
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
+        for (int e = 0; e < 8; ++e) xk[e] = x[k][e];
+      } else {
+        xvec(k, xk);
+      }
+      u32x4 p1k, p2k = zero4;
+      if constexpr (kHoldS1) p1k = p1[k];
+      else p1k = load_param(a.smooth1, k, one4);
+      if constexpr (kTwo) {
+        if constexpr (kHold) p2k = p2[k];
+        else p2k = load_param(a.smooth2, k, one4);
+      }
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const f32x2 g = widen2<E>(pg[k][w]), b = widen2<E>(pb[k][w]);
-        const f32x2 s1 = widen2<E>(p1[k][w]);
-        const float y0 = __builtin_fmaf(x[k][2 * w] * rinv, g.x, b.x);
-        const float y1 = __builtin_fmaf(x[k][2 * w + 1] * rinv, g.y, b.y);
-        in1[k][2 * w] = y0 * s1.x;
-        in1[k][2 * w + 1] = y1 * s1.y;
-        m1 = fmaxf(m1, fmaxf(fabsf(in1[k][2 * w]), fabsf(in1[k][2 * w + 1])));
+        const f32x2 s1 = widen2<E>(p1k[w]);
+        const float y0 = __builtin_fmaf(xk[2 * w] * rinv, g.x, b.x);
+        const float y1 = __builtin_fmaf(xk[2 * w + 1] * rinv, g.y, b.y);
+        i1[2 * w] = y0 * s1.x;
+        i1[2 * w + 1] = y1 * s1.y;
         if constexpr (kTwo) {
-          const f32x2 s2 = widen2<E>(p2[k][w]);
-          in2[k][2 * w] = y0 * s2.x;
-          in2[k][2 * w + 1] = y1 * s2.y;
-          m2 = fmaxf(m2, fmaxf(fabsf(in2[k][2 * w]), fabsf(in2[k][2 * w + 1])));
+          const f32x2 s2 = widen2<E>(p2k[w]);
+          i2[2 * w] = y0 * s2.x;
+          i2[2 * w + 1] = y1 * s2.y;
+        }
+      }
+    };
+    float in1[PH][8], in2[PH][8];
+    float m1 = 0.0f, m2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      float i1[8], i2[8];
+      inputs(k, i1, i2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        m1 = fmaxf(m1, fabsf(i1[e]));
+        if constexpr (kTwo) m2 = fmaxf(m2, fabsf(i2[e]));
+        if constexpr (kHold) {
+          in1[k][e] = i1[e];
+          if constexpr (kTwo) in2[k][e] = i2[e];
         }
       }
     }
@@ -211,24 +265,40 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
       a.scale1[row] = r1.scale;
       if constexpr (kTwo) a.scale2[row] = r2.scale;
     }
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      apply_boost(in1[k], r1);
-      if constexpr (kTwo) apply_boost(in2[k], r2);
-    }
     const uint32_t y1_bytes = Q1 == kQInt4 ? n / 2u : n;
     const rsrc_t ry1 = make_rsrc(row_ptr(a.y1, row, y1_bytes), y1_bytes);
+    const uint32_t y2_bytes = kQ2 == kQInt4 ? n / 2u : n;
+    const rsrc_t ry2 = make_rsrc(row_ptr(a.y2, row, kTwo ? y2_bytes : 0u), kTwo ? y2_bytes : 0u);
+    if constexpr (kHold) {
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) store_codes<Q1>(in1[k], r1.inv, ry1, vj[k]);
-    if constexpr (kTwo) {
-      const uint32_t y2_bytes = kQ2 == kQInt4 ? n / 2u : n;
-      const rsrc_t ry2 = make_rsrc(row_ptr(a.y2, row, y2_bytes), y2_bytes);
+      for (int k = 0; k < VPT; ++k) {
+        apply_boost(in1[k], r1);
+        if constexpr (kTwo) apply_boost(in2[k], r2);
+      }
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) store_codes<kQ2>(in2[k], r2.inv, ry2, vj[k]);
+      for (int k = 0; k < VPT; ++k) store_codes<Q1>(in1[k], r1.inv, ry1, vj[k]);
+      if constexpr (kTwo) {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) store_codes<kQ2>(in2[k], r2.inv, ry2, vj[k]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        float i1[8], i2[8];
+        inputs(k, i1, i2);
+        apply_boost(i1, r1);
+        store_codes<Q1>(i1, r1.inv, ry1, vj[k]);
+        if constexpr (kTwo) {
+          apply_boost(i2, r2);
+          store_codes<kQ2>(i2, r2.inv, ry2, vj[k]);
+        }
+      }
     }
 
+    if constexpr (kHold) {
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) c1[k] = n1[k], c2[k] = n2[k];
+      for (int k = 0; k < VPT; ++k) c1[k] = n1[k], c2[k] = n2[k];
+    }
   };
   body(row);
   for (row += step; row < rend; row += step) body(row);
@@ -259,6 +329,7 @@ bool dispatch_variant(int nin, int q1, int q2, int vpt, F&& f) {
   switch (vpt) {                                                              \
     case 1: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 1>>(); return true; \
     case 2: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 2>>(); return true; \
+    case 4: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 4>>(); return true; \
     default: return false;                                                    \
   }
   if (nin == 1) {

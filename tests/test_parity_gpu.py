@@ -171,7 +171,7 @@ def _case_inputs(m, n, dtype, seed, n_smooth=2, beta=True, outlier=0.0):
 
 SHAPES = [(1, 8), (3, 8), (257, 16), (3, 24), (5, 100 * 8), (3, 1000), (257, 1000),
           (2, 5120), (3, 16384), (1, 1), (3, 7), (4, 2), (257, 100), (2, 16392), (1, 20000),
-          (2, 65536), (64, 1032)]
+          (300, 24584), (2, 32768), (3, 32776), (2, 65536), (64, 1032)]
 
 
 @pytest.mark.parametrize("m,n", SHAPES)
@@ -185,10 +185,31 @@ def test_ragged_shapes(m, n, dtype):
     compare_v2(outs, ora, y_types)
     if n % 8 != 0:
         assert "path=generic" in desc, desc
-    elif n > 16384:
+    elif n > 32768:
         assert "path=split" in desc, desc
     else:
         assert "path=row" in desc, desc
+        assert ("vpt=4" in desc) == (n > 16384), desc
+
+
+@pytest.mark.parametrize("y_types", [("int8", "int8"), ("int4", "int8"), ("int8", "int4"),
+                                     ("int4", "int4"), ("int8", None), ("int4", None)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_long_rows_every_output_variant(y_types, dtype):
+    """Rows of 16385..32768 columns run the row kernel with four vectors per
+    thread (parameters partly read at use, x and the inputs recomputed per
+    pass): every output combination, a ragged last vector group (24584 =
+    3073 vectors) and more rows than workgroups."""
+    m, n = 300, 24584
+    _announce(f"long rows {m}x{n} {dtype} {y_types}")
+    x1, x2, g, b, s1, s2 = _case_inputs(m, n, dtype, seed=4242)
+    two = y_types[1] is not None
+    yt = (y_types[0], y_types[1] if two else "int8")
+    mask = (True, two)
+    outs, desc = run_v2(x1, x2, g, b, s1, s2 if two else None, 1e-6, mask, yt, dtype)
+    assert "path=row" in desc and "vpt=4" in desc, desc
+    ora = oracle_v2(x1, x2, g, b, s1, s2 if two else None, 1e-6, mask, yt, dtype)
+    compare_v2(outs, ora, yt)
 
 
 # ---- the option matrix --------------------------------------------------------
@@ -228,7 +249,7 @@ def test_option_matrix(row, y_types, dtype):
 @pytest.mark.parametrize("y_type", ["int8", "int4"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("smooth", [False, True])
-@pytest.mark.parametrize("n", [1024, 1000])
+@pytest.mark.parametrize("n", [1024, 1000, 20480])
 def test_rms_norm_dq_variants(y_type, dtype, smooth, n):
     w = synth.Workload("rms", "rmsnorm", 33, n, dtype, 5, None, True, 1 if smooth else 0)
     x, _ = synth.inputs(w)
