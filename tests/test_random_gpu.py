@@ -3,8 +3,9 @@ operation checked against the oracle, beyond the hand-picked shapes of the
 other GPU tests.
 
  - AddRmsNormDynamicQuantV2 / RmsNormDynamicQuant: random row counts, row
-   lengths (multiples of 8 up to the row kernel's limit, longer rows for the
-   split-row kernel, and arbitrary lengths for the generic kernel), dtypes,
+   lengths (multiples of 8 up to 16384 columns, rows of 16392..24576 columns
+   for the row kernel's four-vectors-per-thread instances, and arbitrary
+   lengths for the generic kernel), dtypes,
    valid output-option combinations, INT8/INT4 outputs, beta present or not,
    outlier columns; compared under the parity rules.
  - W8A8 GEMM: random m, n and k (a multiple of 16), output dtype and bias;
@@ -49,7 +50,7 @@ def _row_length(rng):
     if kind == 1:
         return int(rng.integers(1, 5000))              # any length: generic kernel
     if kind == 2:
-        return int(rng.integers(2049, 3073)) * 8       # longer rows: split-row kernel
+        return int(rng.integers(2049, 3073)) * 8       # longer rows: four vectors per thread
     return int(rng.integers(1, 64)) * 8                # short rows
 
 
