@@ -239,8 +239,9 @@ void adq_executor_destroy(adq_executor* executor);
  * Kernel path of an executor.  ADQ_PATH_AUTO is chosen by phase 1 from the
  * shape; the others force a path (for tests and tuning).  ADQ_PATH_ROW:
  * one workgroup per row, 128-bit accesses (n % 8 == 0, 16-byte aligned
- * tensors, n <= 32768).  ADQ_PATH_SPLIT: several workgroups per row (same
- * conditions; few-row shapes).  ADQ_PATH_GENERIC: any n and alignment.
+ * tensors, n <= 32768).  ADQ_PATH_SPLIT: several workgroups per row (n % 8
+ * == 0, 16-byte aligned tensors; AUTO takes it for rows longer than 32768
+ * columns).  ADQ_PATH_GENERIC: any n and alignment.
  * GEMM executors: ADQ_PATH_GEMM_TILE128 (128 x 128 output tiles) and
  * ADQ_PATH_GEMM_TILE256 (256 x 256 tiles); AUTO takes 256 once the
  * 256-tiles cover the compute units.  Either accepts any valid GEMM shape;
