@@ -71,6 +71,7 @@ struct adq_executor {
   int gemm_tile;
   adq::LoraArgs lora;
   bool lora_tiled_ok;
+  int64_t lora_chunk_rows;  // tiled path: rows per launch sequence
   int64_t m;
   int device;
   int cus;
@@ -416,6 +417,22 @@ adq_status finish_plan(adq_executor* proto, uint64_t* workspace_size, adq_execut
   return ok();
 }
 
+// Rows [r0, r0 + lora_chunk_rows) of an AddLora call (fewer for the last
+// range) as arguments of their own: the tiled kernels address y, out and x
+// with 32-bit byte offsets, so a batch beyond 4 GiB runs as consecutive
+// launch sequences over row ranges below it.  Rows are independent of one
+// another, and each sequence lays its own tables out in the workspace.
+adq::LoraArgs lora_part(const adq_executor& e, int64_t r0) {
+  adq::LoraArgs c = e.lora;
+  const int64_t left = e.lora.rows - r0;
+  c.rows = left < e.lora_chunk_rows ? left : e.lora_chunk_rows;
+  c.y = static_cast<const char*>(c.y) + r0 * c.h3 * 2;
+  c.out = static_cast<char*>(c.out) + r0 * c.h3 * 2;
+  c.x = static_cast<const char*>(c.x) + r0 * c.h1 * 2;
+  c.indices += r0;
+  return c;
+}
+
 adq_status run(void* workspace, uint64_t workspace_size, adq_executor* e, void* stream, int op) {
   if (!e) return fail(ADQ_ERR_NULLPTR, "executor is NULL");
   if (e->op != op) return fail(ADQ_ERR_PARAM_INVALID, "executor was built for another operator");
@@ -436,10 +453,15 @@ adq_status run(void* workspace, uint64_t workspace_size, adq_executor* e, void* 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t err = hipErrorInvalidValue;
   if (op == kOpGemm || op == kOpLora) {
-    err = op == kOpGemm ? adq::launch_w8a8(e->gemm, e->gemm_tile, s)
-                        : adq::launch_lora(e->lora, e->path == ADQ_PATH_GENERIC
-                                                        ? adq::kLoraGeneric
-                                                        : adq::kLoraTiled, workspace, s);
+    if (op == kOpGemm) {
+      err = adq::launch_w8a8(e->gemm, e->gemm_tile, s);
+    } else if (e->path == ADQ_PATH_GENERIC) {
+      err = adq::launch_lora(e->lora, adq::kLoraGeneric, workspace, s);
+    } else {
+      err = hipSuccess;
+      for (int64_t r0 = 0; r0 < e->lora.rows && err == hipSuccess; r0 += e->lora_chunk_rows)
+        err = adq::launch_lora(lora_part(*e, r0), adq::kLoraTiled, workspace, s);
+    }
     if (cur != e->device) (void)hipSetDevice(cur);
     if (err != hipSuccess)
       return fail(ADQ_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(err));
@@ -785,33 +807,41 @@ adq_status adq_add_lora_get_workspace_size(const adq_tensor* y, const adq_tensor
   a.elem = y->dtype == ADQ_BF16 ? adq::kBF16 : adq::kF16;
   a.in_place = out->data == y->data;
   e.m = rows;
+  // Rows per launch sequence of the tiled path: y and out ([rows, h3]) and
+  // x ([rows, h1]) of one sequence stay below 4 GiB.
+  const int64_t below4g = ((int64_t)1 << 32) - 1;
+  int64_t chunk_rows = rows;
+  if (chunk_rows > below4g / (h3 * 2)) chunk_rows = below4g / (h3 * 2);
+  if (weight_a && chunk_rows > below4g / (h1 * 2)) chunk_rows = below4g / (h1 * 2);
+  if (chunk_rows < rows) chunk_rows -= chunk_rows % adq::kLoraTileRows;  // whole tiles
+  e.lora_chunk_rows = chunk_rows;
   e.lora_tiled_ok = h1 % 8 == 0 &&
                     (rank == 8 || rank == 16 || rank == 32 || rank == 64 || rank == 128) &&
                     h2 % 4 == 0 && h3 % 8 == 0 && y_offset % 8 == 0 && aligned(x->data, 16) &&
                     (!weight_a || aligned(weight_a->data, 16)) && aligned(weight_b->data, 8) &&
-                    aligned(y->data, 16) && aligned(out->data, 8) &&
-                    rows * h3 * 2 < (int64_t)1 << 32 &&  // 32-bit offsets into y,
-                    rank * h2 * 2 < (int64_t)1 << 32 &&  // into weightB[g, layer]
-                    (!weight_a || rows * h1 * 2 < (int64_t)1 << 32);  // and into x
+                    aligned(y->data, 16) && aligned(out->data, 8) && chunk_rows >= 1 &&
+                    rank * h2 * 2 < (int64_t)1 << 32;  // 32-bit offsets into weightB[g, layer]
   {
     // Tiles are only known on the device (they depend on the index values);
     // estimate them as rows / 64 plus one partial tile per adapter in use.
     // Slices of h1 per tile (shrink) are chosen for about four workgroups
     // per CU, each slice at least 256 k; the expand takes ranges of 1024
     // columns of the slice.
-    const int64_t est_tiles = (rows + adq::kLoraTileRows - 1) / adq::kLoraTileRows +
-                              (w < rows ? w : rows);
+    const int64_t est_tiles = (chunk_rows + adq::kLoraTileRows - 1) / adq::kLoraTileRows +
+                              (w < chunk_rows ? w : chunk_rows);
     // ... but no more than fit on the chip at once (ranks whose shrink
     // holds fewer workgroups per CU would otherwise run a second round)
     int64_t want = (2 * (int64_t)e.cus + est_tiles - 1) / est_tiles;
-    const int64_t fit = (int64_t)adq::lora_shrink_blocks_per_cu(a) * e.cus / est_tiles;
+    adq::LoraArgs part = a;
+    part.rows = chunk_rows;
+    const int64_t fit = (int64_t)adq::lora_shrink_blocks_per_cu(part) * e.cus / est_tiles;
     if (fit >= 1 && fit < want) want = fit;
     auto clamp = [](int64_t v, int64_t hi) { return (int)(v < 1 ? 1 : v > hi ? hi : v); };
     a.ksplit = clamp(ADQ_LORA_KSPLIT_MULT * want, h1 / 256 > 1 ? h1 / 256 : 1);
     a.chunks = adq::lora_expand_chunks(h2);
   }
   e.path = e.lora_tiled_ok ? ADQ_PATH_AUTO : ADQ_PATH_GENERIC;
-  e.ws_bytes = e.lora_tiled_ok ? adq::lora_workspace_bytes(a) : 0;
+  e.ws_bytes = e.lora_tiled_ok ? adq::lora_workspace_bytes(lora_part(e, 0)) : 0;
   adq_executor* ex = new (std::nothrow) adq_executor(e);
   if (!ex) return fail(ADQ_ERR_RUNTIME, "out of host memory");
   *workspace_size = e.ws_bytes;
@@ -842,7 +872,7 @@ adq_status adq_executor_set_path(adq_executor* executor, int32_t path, uint64_t*
     else if (path == ADQ_PATH_GENERIC) executor->path = ADQ_PATH_GENERIC;
     else return fail(ADQ_ERR_PARAM_INVALID, "an AddLora executor takes AUTO or GENERIC");
     executor->ws_bytes =
-        executor->path == ADQ_PATH_GENERIC ? 0 : adq::lora_workspace_bytes(executor->lora);
+        executor->path == ADQ_PATH_GENERIC ? 0 : adq::lora_workspace_bytes(lora_part(*executor, 0));
     *workspace_size = executor->ws_bytes;
     return ok();
   }
@@ -861,16 +891,18 @@ int32_t adq_executor_describe(const adq_executor* e, char* buf, uint64_t len) {
   if (e->op == kOpLora) {
     if (buf && len > 0) {
       const adq::LoraArgs& a = e->lora;
+      const adq::LoraArgs part = lora_part(*e, 0);
       const bool tiled = e->path != ADQ_PATH_GENERIC;
       snprintf(buf, (size_t)len,
                "path=%s rows=%lld h1=%lld rank=%lld h2=%lld h3=%lld adapters=%lld layers=%lld "
-               "weight_a=%d in_place=%d ksplit=%d chunks=%d tiles<=%lld workspace=%llu cus=%d "
-               "kernels=%s",
+               "weight_a=%d in_place=%d ksplit=%d chunks=%d row_ranges=%lld tiles<=%lld "
+               "workspace=%llu cus=%d kernels=%s",
                tiled ? "lora-tiled" : "lora-generic", (long long)a.rows, (long long)a.h1,
                (long long)a.rank, (long long)a.h2, (long long)a.h3, (long long)a.w,
                (long long)a.l, a.wa != nullptr, a.in_place, a.ksplit, a.chunks,
-               (long long)adq::lora_max_tiles(a), (unsigned long long)e->ws_bytes, e->cus,
-               tiled ? adq::lora_tiled_kernels(a) : "generic");
+               tiled ? (long long)((a.rows + e->lora_chunk_rows - 1) / e->lora_chunk_rows) : 1LL,
+               (long long)adq::lora_max_tiles(part), (unsigned long long)e->ws_bytes, e->cus,
+               tiled ? adq::lora_tiled_kernels(part) : "generic");
     }
     return e->path;
   }

@@ -288,8 +288,9 @@ def test_paths():
 
 @pytest.mark.parametrize("h2,kind", [((1 << 24) - 8, "lora-tiled"), (1 << 24, "lora-generic")])
 def test_offset_limits_select_the_kernel(h2, kind):
-    """The tiled kernels address y, x and weightB[g, layer] with 32-bit byte
-    offsets: a rank-128 weightB slice of 2^32 bytes (2^24 columns) is planned
+    """The tiled kernels address weightB[g, layer] with 32-bit byte offsets
+    (y and x are taken in row ranges below 4 GiB): a rank-128 weightB slice
+    of 2^32 bytes (2^24 columns) is planned
     on the generic kernel, one just below on the tiled kernels.  Planning
     only (tensors left uninitialised)."""
     rank = 128
