@@ -48,6 +48,7 @@ namespace {
 
 constexpr int kThreads = 256;         // generic, shrink and expand kernels
 constexpr int kGroupThreads = 1024;   // group kernel
+constexpr int kGroupBatch = 8;        // indices per thread loaded together by the group kernel
 constexpr int kTile = kLoraTileRows;  // 64 rows
 constexpr int kKSub = 128;            // k per shrink stage
 // Transposed weightA rows in LDS: 128 k + 32 of padding (320 bytes, 16 banks
@@ -163,10 +164,37 @@ __global__ void __launch_bounds__(kGroupThreads) lora_group_kernel(const LoraArg
   __shared__ int scan_tmp[NW];
   const int tid = threadIdx.x;
   const int64_t W = a.w;
+  // Indices are read kGroupBatch per thread at a time, all loads in flight
+  // before the first is used (one memory latency per batch rather than per
+  // index); the first batch's classes stay in registers for the placement.
+  constexpr int64_t kStep = (int64_t)kGroupThreads * kGroupBatch;
+  auto load_batch = [&](int64_t base, int (&c)[kGroupBatch]) {
+#pragma unroll
+    for (int u = 0; u < kGroupBatch; ++u) {
+      const int64_t i = base + (int64_t)u * kGroupThreads + tid;
+      c[u] = i < a.rows ? a.indices[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kGroupBatch; ++u) {
+      const int64_t i = base + (int64_t)u * kGroupThreads + tid;
+      c[u] = i < a.rows ? adapter_class(c[u], W) : -1;
+    }
+  };
+  auto count_batch = [&](const int (&c)[kGroupBatch]) {
+#pragma unroll
+    for (int u = 0; u < kGroupBatch; ++u)
+      if (c[u] >= 0) atomicAdd(&cnt[c[u]], 1);
+  };
+  int c0[kGroupBatch];
+  load_batch(0, c0);
   for (int g = tid; g <= W; g += kGroupThreads) cnt[g] = 0;
   __syncthreads();
-  for (int64_t i = tid; i < a.rows; i += kGroupThreads)
-    atomicAdd(&cnt[adapter_class(a.indices[i], W)], 1);
+  count_batch(c0);
+  for (int64_t base = kStep; base < a.rows; base += kStep) {
+    int c[kGroupBatch];
+    load_batch(base, c);
+    count_batch(c);
+  }
   __syncthreads();
   // rows without an adapter are only listed when out is not y (to be copied)
   auto placed = [&](int g) -> int { return (g < W || !a.in_place) ? cnt[g] : 0; };
@@ -191,12 +219,21 @@ __global__ void __launch_bounds__(kGroupThreads) lora_group_kernel(const LoraArg
   }
   if (tid == 0) ws.header[0] = ntiles;
   __syncthreads();
-  for (int64_t i = tid; i < a.rows; i += kGroupThreads) {
-    const int c = adapter_class(a.indices[i], W);
-    if (c < W || !a.in_place) {
-      const int p = atomicAdd(&cur[c], 1);  // place within the class
-      ws.rows[(first_tile[c] + p / kTile) * kTile + p % kTile] = (int32_t)i;
+  auto place_batch = [&](int64_t base, const int (&c)[kGroupBatch]) {
+#pragma unroll
+    for (int u = 0; u < kGroupBatch; ++u) {
+      if (c[u] >= 0 && (c[u] < W || !a.in_place)) {
+        const int p = atomicAdd(&cur[c[u]], 1);  // place within the class
+        ws.rows[(first_tile[c[u]] + p / kTile) * kTile + p % kTile] =
+            (int32_t)(base + (int64_t)u * kGroupThreads + tid);
+      }
     }
+  };
+  place_batch(0, c0);
+  for (int64_t base = kStep; base < a.rows; base += kStep) {
+    int c[kGroupBatch];
+    load_batch(base, c);
+    place_batch(base, c);
   }
 }
 
