@@ -215,8 +215,9 @@ adq_status adq_w8a8_gemm(void* workspace, uint64_t workspace_size, adq_executor*
  * entering as three bf16 pieces whose sum is exactly Z1); each slice value is
  * rounded once to the storage type.  W <= 2048, rank <= 1024.
  * Workspace: the tiled path (see adq_path) needs one, 8-byte aligned, whose
- * contents need not be initialised (tile table, grouped row order and
- * partial sums, rewritten by every launch; calls that share a workspace
+ * contents need not be initialised (tile table, grouped row order, partial
+ * sums and, above 8192 rows, class counts per 8192 rows, all rewritten by
+ * every launch before they are read; calls that share a workspace
  * must not overlap); the generic path needs none.  Errors as for the other
  * phase-1 calls.
  */

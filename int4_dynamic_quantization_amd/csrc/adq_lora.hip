@@ -123,14 +123,18 @@ struct Workspace {
   int4* table;      // per tile: {class, 0, rows, 0}
   int32_t* rows;    // per tile, 64 slots of row ids
   float* z1p;       // [ksplit][tile slot][rank] partial shrink sums
+  int* hist;        // batches above kGroupRowsPerWg rows: [workgroup][class] row counts
 };
 
 __host__ __device__ inline uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
 
 // byte offsets of the table, the row list and the partial sums
 struct WsOffsets {
-  uint64_t table, rows, z1p, end;
+  uint64_t table, rows, z1p, hist, end;
 };
+
+// Rows grouped by one workgroup of the grouping launches (8 per thread).
+constexpr int64_t kGroupRowsPerWg = (int64_t)kGroupThreads * kGroupBatch;
 
 __host__ __device__ inline WsOffsets ws_offsets(const LoraArgs& a) {
   const int64_t tiles = (a.rows + kTile - 1) / kTile + a.w + 1;
@@ -138,8 +142,10 @@ __host__ __device__ inline WsOffsets ws_offsets(const LoraArgs& a) {
   o.table = 256;
   o.rows = align256(o.table + (uint64_t)tiles * 16);
   o.z1p = align256(o.rows + (uint64_t)tiles * kTile * 4);
-  o.end = o.z1p +
-          (a.wa ? (uint64_t)a.ksplit * (uint64_t)tiles * kTile * (uint64_t)a.rank * 4 : 0);
+  o.hist = align256(o.z1p +
+                   (a.wa ? (uint64_t)a.ksplit * (uint64_t)tiles * kTile * (uint64_t)a.rank * 4 : 0));
+  const int64_t wgs = a.rows > kGroupRowsPerWg ? (a.rows + kGroupRowsPerWg - 1) / kGroupRowsPerWg : 0;
+  o.end = o.hist + (uint64_t)wgs * (uint64_t)(a.w + 1) * 4;
   return o;
 }
 
@@ -151,53 +157,44 @@ inline Workspace ws_layout(void* base, const LoraArgs& a) {
   w.table = reinterpret_cast<int4*>(p + o.table);
   w.rows = reinterpret_cast<int32_t*>(p + o.rows);
   w.z1p = reinterpret_cast<float*>(p + o.z1p);
+  w.hist = reinterpret_cast<int*>(p + o.hist);
   return w;
 }
 
 // ---- 1. grouping
-__global__ void __launch_bounds__(kGroupThreads) lora_group_kernel(const LoraArgs a,
-                                                                   Workspace ws) {
+// Batches of up to kGroupRowsPerWg rows: one workgroup counts the rows of
+// each adapter class (W + 1, the last for rows without an adapter), lays out
+// the tiles and places every row into its tile's slot.  Larger batches: a
+// counting launch (one workgroup per kGroupRowsPerWg rows) and a placing
+// launch in which each workgroup adds up the counts of the workgroups before
+// it, so the rows of a class keep the order of the workgroups that hold them.
+
+// Classes of rows base + u * kGroupThreads + tid (-1 past the end).  All
+// loads are in flight before the first is used.
+__device__ __forceinline__ void load_classes(const LoraArgs& a, int64_t base,
+                                             int (&c)[kGroupBatch]) {
+#pragma unroll
+  for (int u = 0; u < kGroupBatch; ++u) {
+    const int64_t i = base + (int64_t)u * kGroupThreads + threadIdx.x;
+    c[u] = i < a.rows ? a.indices[i] : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < kGroupBatch; ++u) {
+    const int64_t i = base + (int64_t)u * kGroupThreads + threadIdx.x;
+    c[u] = i < a.rows ? adapter_class(c[u], a.w) : -1;
+  }
+}
+
+// Tiles of up to kTile rows of one class, classes in order, from the row
+// counts n[g] of each class: first_tile[g] for every class and, when
+// `write`, the table entries and the tile count.  Rows without an adapter are
+// only listed when out is not y (to be copied).
+__device__ void lay_out_tiles(const LoraArgs& a, const int* n, int* first_tile, int* scan_tmp,
+                              const Workspace& ws, bool write) {
   constexpr int NW = kGroupThreads / 64;
-  __shared__ int cnt[kLoraMaxAdapters + 1];
-  __shared__ int cur[kLoraMaxAdapters + 1];
-  __shared__ int first_tile[kLoraMaxAdapters + 1];
-  __shared__ int scan_tmp[NW];
   const int tid = threadIdx.x;
   const int64_t W = a.w;
-  // Indices are read kGroupBatch per thread at a time, all loads in flight
-  // before the first is used (one memory latency per batch rather than per
-  // index); the first batch's classes stay in registers for the placement.
-  constexpr int64_t kStep = (int64_t)kGroupThreads * kGroupBatch;
-  auto load_batch = [&](int64_t base, int (&c)[kGroupBatch]) {
-#pragma unroll
-    for (int u = 0; u < kGroupBatch; ++u) {
-      const int64_t i = base + (int64_t)u * kGroupThreads + tid;
-      c[u] = i < a.rows ? a.indices[i] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < kGroupBatch; ++u) {
-      const int64_t i = base + (int64_t)u * kGroupThreads + tid;
-      c[u] = i < a.rows ? adapter_class(c[u], W) : -1;
-    }
-  };
-  auto count_batch = [&](const int (&c)[kGroupBatch]) {
-#pragma unroll
-    for (int u = 0; u < kGroupBatch; ++u)
-      if (c[u] >= 0) atomicAdd(&cnt[c[u]], 1);
-  };
-  int c0[kGroupBatch];
-  load_batch(0, c0);
-  for (int g = tid; g <= W; g += kGroupThreads) cnt[g] = 0;
-  __syncthreads();
-  count_batch(c0);
-  for (int64_t base = kStep; base < a.rows; base += kStep) {
-    int c[kGroupBatch];
-    load_batch(base, c);
-    count_batch(c);
-  }
-  __syncthreads();
-  // rows without an adapter are only listed when out is not y (to be copied)
-  auto placed = [&](int g) -> int { return (g < W || !a.in_place) ? cnt[g] : 0; };
+  auto placed = [&](int g) -> int { return (g < W || !a.in_place) ? n[g] : 0; };
   const int per = (int)((W + 1 + kGroupThreads - 1) / kGroupThreads);
   int tl = 0;
   for (int q = 0; q < per; ++q) {
@@ -209,32 +206,106 @@ __global__ void __launch_bounds__(kGroupThreads) lora_group_kernel(const LoraArg
   for (int q = 0; q < per; ++q) {
     const int g = tid * per + q;
     if (g <= W) {
-      const int n = placed(g);
-      for (int t = 0; t * kTile < n; ++t)
-        ws.table[tb + t] = int4{g, 0, n - t * kTile < kTile ? n - t * kTile : kTile, 0};
-      cur[g] = 0;
+      const int m = placed(g);
+      if (write)
+        for (int t = 0; t * kTile < m; ++t)
+          ws.table[tb + t] = int4{g, 0, m - t * kTile < kTile ? m - t * kTile : kTile, 0};
       first_tile[g] = tb;
-      tb += (n + kTile - 1) / kTile;
+      tb += (m + kTile - 1) / kTile;
     }
   }
-  if (tid == 0) ws.header[0] = ntiles;
-  __syncthreads();
-  auto place_batch = [&](int64_t base, const int (&c)[kGroupBatch]) {
+  if (write && tid == 0) ws.header[0] = ntiles;
+}
+
+// Rows base + u * kGroupThreads + tid of classes c[u] into their tiles' slots;
+// cur[g] is the next position within class g.
+__device__ __forceinline__ void place_rows(const LoraArgs& a, const Workspace& ws, int64_t base,
+                                           const int (&c)[kGroupBatch], int* cur,
+                                           const int* first_tile) {
 #pragma unroll
-    for (int u = 0; u < kGroupBatch; ++u) {
-      if (c[u] >= 0 && (c[u] < W || !a.in_place)) {
-        const int p = atomicAdd(&cur[c[u]], 1);  // place within the class
-        ws.rows[(first_tile[c[u]] + p / kTile) * kTile + p % kTile] =
-            (int32_t)(base + (int64_t)u * kGroupThreads + tid);
+  for (int u = 0; u < kGroupBatch; ++u) {
+    if (c[u] >= 0 && (c[u] < a.w || !a.in_place)) {
+      const int p = atomicAdd(&cur[c[u]], 1);
+      ws.rows[(int64_t)(first_tile[c[u]] + p / kTile) * kTile + p % kTile] =
+          (int32_t)(base + (int64_t)u * kGroupThreads + threadIdx.x);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kGroupThreads) lora_group_kernel(const LoraArgs a,
+                                                                   Workspace ws) {
+  __shared__ int cnt[kLoraMaxAdapters + 1];
+  __shared__ int cur[kLoraMaxAdapters + 1];
+  __shared__ int first_tile[kLoraMaxAdapters + 1];
+  __shared__ int scan_tmp[kGroupThreads / 64];
+  const int tid = threadIdx.x;
+  const int64_t W = a.w;
+  int c[kGroupBatch];
+  load_classes(a, 0, c);
+  for (int g = tid; g <= W; g += kGroupThreads) cnt[g] = 0, cur[g] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kGroupBatch; ++u)
+    if (c[u] >= 0) atomicAdd(&cnt[c[u]], 1);
+  __syncthreads();
+  lay_out_tiles(a, cnt, first_tile, scan_tmp, ws, true);
+  __syncthreads();
+  place_rows(a, ws, 0, c, cur, first_tile);
+}
+
+// Larger batches, first launch: the class counts of this workgroup's rows.
+__global__ void __launch_bounds__(kGroupThreads) lora_count_kernel(const LoraArgs a,
+                                                                   Workspace ws) {
+  __shared__ int cnt[kLoraMaxAdapters + 1];
+  const int tid = threadIdx.x;
+  const int64_t W = a.w;
+  int c[kGroupBatch];
+  load_classes(a, (int64_t)blockIdx.x * kGroupRowsPerWg, c);
+  for (int g = tid; g <= W; g += kGroupThreads) cnt[g] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kGroupBatch; ++u)
+    if (c[u] >= 0) atomicAdd(&cnt[c[u]], 1);
+  __syncthreads();
+  for (int g = tid; g <= W; g += kGroupThreads) ws.hist[(int64_t)blockIdx.x * (W + 1) + g] = cnt[g];
+}
+
+// Larger batches, second launch: class totals and this workgroup's first
+// position in each class from the counts of every workgroup, the tiles
+// (written by workgroup 0; every workgroup derives the same layout), then
+// this workgroup's rows placed.
+__global__ void __launch_bounds__(kGroupThreads) lora_place_kernel(const LoraArgs a,
+                                                                   Workspace ws) {
+  __shared__ int tot[kLoraMaxAdapters + 1];
+  __shared__ int cur[kLoraMaxAdapters + 1];
+  __shared__ int first_tile[kLoraMaxAdapters + 1];
+  __shared__ int scan_tmp[kGroupThreads / 64];
+  const int tid = threadIdx.x;
+  const int64_t W = a.w;
+  const int wg = (int)blockIdx.x, nwg = (int)gridDim.x;
+  const int64_t base = (int64_t)wg * kGroupRowsPerWg;
+  int c[kGroupBatch];
+  load_classes(a, base, c);
+  for (int g = tid; g <= W; g += kGroupThreads) {
+    int total = 0, before = 0;
+    for (int w0 = 0; w0 < nwg; w0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = w0 + u < nwg ? ws.hist[(int64_t)(w0 + u) * (W + 1) + g] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        total += v[u];
+        if (w0 + u < wg) before += v[u];
       }
     }
-  };
-  place_batch(0, c0);
-  for (int64_t base = kStep; base < a.rows; base += kStep) {
-    int c[kGroupBatch];
-    load_batch(base, c);
-    place_batch(base, c);
+    tot[g] = total;
+    cur[g] = before;
   }
+  __syncthreads();
+  lay_out_tiles(a, tot, first_tile, scan_tmp, ws, wg == 0);
+  __syncthreads();
+  place_rows(a, ws, base, c, cur, first_tile);
 }
 
 // ---- 1'. grouping inside the shrink, for small batches
@@ -1053,7 +1124,13 @@ hipError_t launch_tiled(const LoraArgs& a, const Workspace& ws, hipStream_t s) {
     hipLaunchKernelGGL((lora_shrink_kernel<E, R, true>), dim3((unsigned)(tiles * a.ksplit)),
                        dim3(kThreads), 0, s, a, ws);
   } else {
-    hipLaunchKernelGGL(lora_group_kernel, dim3(1), dim3(kGroupThreads), 0, s, a, ws);
+    if (a.rows > kGroupRowsPerWg) {
+      const unsigned wgs = (unsigned)((a.rows + kGroupRowsPerWg - 1) / kGroupRowsPerWg);
+      hipLaunchKernelGGL(lora_count_kernel, dim3(wgs), dim3(kGroupThreads), 0, s, a, ws);
+      hipLaunchKernelGGL(lora_place_kernel, dim3(wgs), dim3(kGroupThreads), 0, s, a, ws);
+    } else {
+      hipLaunchKernelGGL(lora_group_kernel, dim3(1), dim3(kGroupThreads), 0, s, a, ws);
+    }
     if (a.wa)
       hipLaunchKernelGGL((lora_shrink_kernel<E, R, false>), dim3((unsigned)(tiles * a.ksplit)),
                          dim3(kThreads), 0, s, a, ws);
@@ -1118,6 +1195,10 @@ int lora_shrink_blocks_per_cu(const LoraArgs& a) {
 const char* lora_tiled_kernels(const LoraArgs& a) {
   const bool mx = a.elem == kBF16 && a.rank >= kMxMinRank;
   if (a.wa && a.rows <= kSmallRows) return mx ? "shrink+mfma-expand" : "shrink+expand";
+  if (a.rows > kGroupRowsPerWg) {
+    if (a.wa) return mx ? "count+place+shrink+mfma-expand" : "count+place+shrink+expand";
+    return mx ? "count+place+mfma-expand" : "count+place+expand";
+  }
   if (a.wa) return mx ? "group+shrink+mfma-expand" : "group+shrink+expand";
   return mx ? "group+mfma-expand" : "group+expand";
 }

@@ -134,6 +134,10 @@ EXACT = [
     (777, 264, 16, 68, 136, 6, 2, 1, 40, True, "fp16"),
     (50, 64, 64, 96, 160, 3, 1, 0, 32, False, "bf16"),  # matrix-core expand without weightA
     (600, 128, 128, 64, 128, 2, 1, 0, 0, False, "bf16"),
+    # above 8192 rows: the counting and placing launches (3, 2 and 2 workgroups)
+    (20000, 64, 16, 48, 104, 5, 2, 1, 24, True, "bf16"),
+    (16385, 64, 64, 64, 128, 3, 1, 0, 64, False, "bf16"),
+    (8193, 64, 8, 44, 96, 4, 1, 0, 8, True, "fp16"),
     (37, 64, 16, 48, 100, 3, 2, 1, 20, True, "bf16"),   # y rows not 16-byte aligned: generic
     (5, 30, 5, 7, 13, 2, 2, 1, 3, True, "fp16"),        # generic only (ragged)
 ]
@@ -157,6 +161,8 @@ def test_exact_integers(case, path):
     got, desc = run_lora(y, x, wa, wb, idx, layer, 0.5, off, dt, path)
     tiled = path == adq.PATH_AUTO and tiled_expected(h1, rank, h2, h3, off)
     assert ("lora-tiled" if tiled else "lora-generic") in desc, desc
+    if tiled:
+        assert ("count+place" in desc) == (rows > 8192), desc
     ref, _ = oracle.add_lora(y, x, wb, idx, wa, layer, 0.5, off, dt)
     assert np.array_equal(got, ref), desc
 
