@@ -147,3 +147,59 @@ def test_lora_beyond_4gib(rank, dt, in_place):
     assert_periodic(out, "out")
     del out
     torch.cuda.empty_cache()
+
+
+def _gemm_sampled(a, w, out, rows, cols):
+    """The GEMM's outputs at (rows[t], cols[t]) against the oracle's exact
+    sums (unit scales, float32 output: the sum rounded once on both sides)."""
+    sums, _ = oracle.w8a8_gemm_at(a, np.ones(a.shape[0], np.float32), w,
+                                  np.ones(w.shape[0], np.float32), None, rows, cols)
+    got = out[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy()
+    assert np.array_equal(got, sums.astype(np.float32))
+
+
+def test_gemm_largest_k():
+    """k = 131072, the largest accepted (127 * 127 * 2^17 still fits int32):
+    rows and columns of +-127 reach the int32 extremes.  Every output of the
+    extreme rows and columns, and 2000 random ones, against the oracle."""
+    m, n, k = 300, 260, 1 << 17
+    _announce(f"gemm m={m} n={n} k={k}")
+    a = synth.int8_codes(4245, 1, m, k, -127, 127)
+    w = synth.int8_codes(4245, 2, n, k, -127, 127)
+    a[0], a[1], w[0], w[1] = 127, -127, 127, -127
+    out = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    ex, out = adq.plan_w8a8_gemm(torch.from_numpy(a).cuda(), torch.ones(m, device="cuda"),
+                                 torch.from_numpy(w).cuda(), torch.ones(n, device="cuda"), None,
+                                 out=out)
+    ex.run()
+    torch.cuda.synchronize()
+    ex.close()
+    assert not bool(out.isnan().any())
+    assert float(out[0, 0]) == 127 * 127 * k and float(out[1, 0]) == -127 * 127 * k
+    rng = np.random.default_rng(4245)
+    rows = np.concatenate([np.zeros(n, np.int64), np.ones(n, np.int64), np.arange(m),
+                           np.arange(m), rng.integers(0, m, 2000)])
+    cols = np.concatenate([np.arange(n), np.arange(n), np.zeros(m, np.int64),
+                           np.ones(m, np.int64), rng.integers(0, n, 2000)])
+    _gemm_sampled(a, w, out, rows, cols)
+
+
+def test_gemm_largest_n():
+    """n = 2^20 columns, the largest accepted: every output written, the last
+    300 columns of every row and 5000 random outputs against the oracle."""
+    m, n, k = 40, 1 << 20, 64
+    _announce(f"gemm m={m} n={n} k={k}")
+    a = synth.int8_codes(4246, 1, m, k, -127, 127)
+    w = synth.int8_codes(4246, 2, n, k, -127, 127)
+    out = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    ex, out = adq.plan_w8a8_gemm(torch.from_numpy(a).cuda(), torch.ones(m, device="cuda"),
+                                 torch.from_numpy(w).cuda(), torch.ones(n, device="cuda"), None,
+                                 out=out)
+    ex.run()
+    torch.cuda.synchronize()
+    ex.close()
+    assert not bool(out.isnan().any())
+    rng = np.random.default_rng(4246)
+    rows = np.concatenate([np.repeat(np.arange(m), 300), rng.integers(0, m, 5000)])
+    cols = np.concatenate([np.tile(np.arange(n - 300, n), m), rng.integers(0, n, 5000)])
+    _gemm_sampled(a, w, out, rows, cols)

@@ -138,6 +138,7 @@ EXACT = [
     (20000, 64, 16, 48, 104, 5, 2, 1, 24, True, "bf16"),
     (16385, 64, 64, 64, 128, 3, 1, 0, 64, False, "bf16"),
     (8193, 64, 8, 44, 96, 4, 1, 0, 8, True, "fp16"),
+    (12000, 64, 16, 48, 104, 1500, 1, 0, 24, True, "fp16"),  # two classes per thread in the layout
     (37, 64, 16, 48, 100, 3, 2, 1, 20, True, "bf16"),   # y rows not 16-byte aligned: generic
     (5, 30, 5, 7, 13, 2, 2, 1, 3, True, "fp16"),        # generic only (ragged)
 ]
