@@ -838,7 +838,7 @@ adq_status adq_add_lora_get_workspace_size(const adq_tensor* y, const adq_tensor
     if (fit >= 1 && fit < want) want = fit;
     auto clamp = [](int64_t v, int64_t hi) { return (int)(v < 1 ? 1 : v > hi ? hi : v); };
     a.ksplit = clamp(ADQ_LORA_KSPLIT_MULT * want, h1 / 256 > 1 ? h1 / 256 : 1);
-    a.chunks = adq::lora_expand_chunks(h2);
+    a.chunks = adq::lora_expand_chunks(h2, rank);
   }
   e.path = e.lora_tiled_ok ? ADQ_PATH_AUTO : ADQ_PATH_GENERIC;
   e.ws_bytes = e.lora_tiled_ok ? adq::lora_workspace_bytes(lora_part(e, 0)) : 0;

@@ -115,7 +115,7 @@ constexpr int kLoraMaxRankGeneric = 1024;
 // ceil(count / 64) <= rows / 64 + w + 1), and the workspace it needs (tile
 // table, grouped row order, per-slice partial shrink results).
 int64_t lora_max_tiles(const LoraArgs& a);
-int lora_expand_chunks(int64_t h2);  // column ranges per tile in the expand
+int lora_expand_chunks(int64_t h2, int64_t rank);  // column ranges per tile in the expand
 const char* lora_tiled_kernels(const LoraArgs& a);  // the tiled path's launches
 int lora_shrink_blocks_per_cu(const LoraArgs& a);   // resident shrink workgroups per CU
 uint64_t lora_workspace_bytes(const LoraArgs& a);

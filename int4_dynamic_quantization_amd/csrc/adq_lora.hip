@@ -556,11 +556,17 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
 // the ranks, one fma into y, one rounding, an 8-byte store.
 constexpr int kQRows = 16;                  // rows per workgroup
 constexpr int kQuarters = kTile / kQRows;   // workgroups per tile and column range
-constexpr int kQCols = 4 * kThreads;        // columns per workgroup
+// Threads of an expand workgroup (4 columns each): 256, or fewer for
+// slices that would leave waves of a 256-thread workgroup without columns:
+// 64 / 128 for up to 256 / 512 columns at ranks up to 16, 128 for up to 512
+// at rank 32 (with 64 its partial sums would be fetched in 4 rounds).
+__host__ __device__ constexpr int expand_threads(int64_t h2, int64_t rank) {
+  if (rank <= 16) return h2 <= 256 ? 64 : h2 <= 512 ? 128 : kThreads;
+  return rank <= 32 && h2 <= 512 ? 128 : kThreads;
+}
 
-template <int E, int R>
-__global__ void __launch_bounds__(kThreads) lora_expand_kernel(const LoraArgs a,
-                                                                 Workspace ws) {
+template <int E, int R, int NT>
+__global__ void __launch_bounds__(NT) lora_expand_kernel(const LoraArgs a, Workspace ws) {
   __shared__ __attribute__((aligned(16))) float z1[kQRows][R];
   const int tid = threadIdx.x;
   // workgroup b runs on XCD b % 8 (the dispatcher deals workgroups to the XCDs
@@ -600,13 +606,13 @@ __global__ void __launch_bounds__(kThreads) lora_expand_kernel(const LoraArgs a,
   if (g >= a.w) {  // rows without an adapter (listed only when out is not y): copy
     for (int i = 0; i < n; ++i) {
       const int64_t row = rows[i];
-      for (int64_t c4 = c0 + tid; c4 < c1; c4 += kThreads)
+      for (int64_t c4 = c0 + tid; c4 < c1; c4 += NT)
         *reinterpret_cast<uint2*>(out + row * h3 + 4 * c4) =
             *reinterpret_cast<const uint2*>(y + row * h3 + 4 * c4);
     }
     return;
   }
-  const int64_t col = (int64_t)chunk * kQCols + 4 * tid;  // first column of the slice
+  const int64_t col = (int64_t)chunk * (4 * NT) + 4 * tid;  // first column of the slice
   const bool col_ok = col < a.h2;
 
   // y: every row's 4 values, all loads in flight together (rows*h3*2 < 2^32);
@@ -642,15 +648,15 @@ __global__ void __launch_bounds__(kThreads) lora_expand_kernel(const LoraArgs a,
   // weightA).  The first kZS slices are loaded together, behind y and
   // weightB, with no wait in between; indices past the valid ones are
   // clamped to a valid slot and their values dropped.
-  constexpr int ZP = (kQRows * R + kThreads - 1) / kThreads;  // elements per thread
-  constexpr int kZS = R <= 16 ? 16 : 256 / R;  // slices loaded together (kZS * ZP <= 16)
+  constexpr int ZP = (kQRows * R + NT - 1) / NT;  // elements per thread
+  constexpr int kZS = ZP >= 16 ? 1 : 16 / ZP;  // slices loaded together (kZS * ZP <= 16)
   if (a.wa) {
     const int ksn = a.ksplit;
     float zs[ZP];
     int64_t zi[ZP];
 #pragma unroll
     for (int u = 0; u < ZP; ++u) {
-      const int t = tid + u * kThreads;
+      const int t = tid + u * NT;
       const int i = t / R < n ? t / R : 0, r = t % R;
       zi[u] = ((int64_t)tile * kTile + qt * kQRows + i) * R + r;
     }
@@ -677,11 +683,11 @@ __global__ void __launch_bounds__(kThreads) lora_expand_kernel(const LoraArgs a,
       for (int u = 0; u < ZP; ++u) zs[u] += ws.z1p[k * kstride + zi[u]];
 #pragma unroll
     for (int u = 0; u < ZP; ++u) {
-      const int t = tid + u * kThreads;
+      const int t = tid + u * NT;
       if (t < kQRows * R) z1[t / R][t % R] = t / R < n ? zs[u] : 0.0f;
     }
   } else {
-    for (int t = tid; t < kQRows * R; t += kThreads) {
+    for (int t = tid; t < kQRows * R; t += NT) {
       const int i = t / R, r = t % R;
       z1[i][r] = i < n ? widen1<E>(static_cast<const T*>(a.x)[(int64_t)rows[i] * a.h1 + r])
                        : 0.0f;
@@ -765,7 +771,7 @@ __global__ void __launch_bounds__(kThreads) lora_expand_kernel(const LoraArgs a,
     const int64_t s0 = a.y_offset / 4, s1 = (a.y_offset + a.h2) / 4;
     for (int i = 0; i < n; ++i) {
       const int64_t row = rows[i];
-      for (int64_t c4 = c0 + tid; c4 < c1; c4 += kThreads)
+      for (int64_t c4 = c0 + tid; c4 < c1; c4 += NT)
         if (c4 < s0 || c4 >= s1)
           *reinterpret_cast<uint2*>(out + row * h3 + 4 * c4) =
               *reinterpret_cast<const uint2*>(y + row * h3 + 4 * c4);
@@ -1141,9 +1147,20 @@ hipError_t launch_tiled(const LoraArgs& a, const Workspace& ws, hipStream_t s) {
                        dim3(kThreads), 0, s, a, ws);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((lora_expand_kernel<E, R>),
-                     dim3((unsigned)((tiles + 7) / 8 * 8 * kQuarters * a.chunks)), dim3(kThreads),
-                     0, s, a, ws);
+  const unsigned grid = (unsigned)((tiles + 7) / 8 * 8 * kQuarters * a.chunks);
+  if constexpr (R <= 32) {
+    const int nt = expand_threads(a.h2, R);
+    if (nt == 64) {
+      hipLaunchKernelGGL((lora_expand_kernel<E, R, 64>), dim3(grid), dim3(64), 0, s, a, ws);
+      return hipGetLastError();
+    }
+    if (nt == 128) {
+      hipLaunchKernelGGL((lora_expand_kernel<E, R, 128>), dim3(grid), dim3(128), 0, s, a, ws);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((lora_expand_kernel<E, R, kThreads>), dim3(grid), dim3(kThreads), 0, s, a,
+                     ws);
   return hipGetLastError();
 }
 
@@ -1203,8 +1220,9 @@ const char* lora_tiled_kernels(const LoraArgs& a) {
   return mx ? "group+mfma-expand" : "group+expand";
 }
 
-int lora_expand_chunks(int64_t h2) {
-  const int64_t c = (h2 + kQCols - 1) / kQCols;
+int lora_expand_chunks(int64_t h2, int64_t rank) {
+  const int64_t cols = 4 * expand_threads(h2, rank);
+  const int64_t c = (h2 + cols - 1) / cols;
   return (int)(c < 1 ? 1 : c);
 }
 

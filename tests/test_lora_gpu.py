@@ -139,6 +139,10 @@ EXACT = [
     (16385, 64, 64, 64, 128, 3, 1, 0, 64, False, "bf16"),
     (8193, 64, 8, 44, 96, 4, 1, 0, 8, True, "fp16"),
     (12000, 64, 16, 48, 104, 1500, 1, 0, 24, True, "fp16"),  # two classes per thread in the layout
+    # slices of 257..512 columns: 128-thread expand workgroups (up to 256: 64 threads)
+    (700, 64, 16, 400, 480, 3, 2, 1, 64, True, "fp16"),
+    (300, 64, 32, 300, 320, 4, 1, 0, 16, True, "fp16"),
+    (130, 8, 8, 260, 264, 2, 1, 0, 0, False, "bf16"),
     (37, 64, 16, 48, 100, 3, 2, 1, 20, True, "bf16"),   # y rows not 16-byte aligned: generic
     (5, 30, 5, 7, 13, 2, 2, 1, 3, True, "fp16"),        # generic only (ragged)
 ]
