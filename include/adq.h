@@ -44,15 +44,13 @@
  * thread-local message for the last non-OK status of the calling thread.
  * Phase 2 never allocates and never synchronizes.
  *
- * Threads: phase-1 calls and different executors may be used from any
- * threads at once.  One executor is run from one host thread at a time
- * (a split-row run records its launch tag in the executor); it may be run
- * any number of times on any streams.
+ * Threads: phase-1 calls and executors may be used from any threads at
+ * once; an executor may be run any number of times, on any streams.
+ * Phase-2 calls that share a workspace must be ordered by the caller.
  *
- * Graphs: a phase-2 call may be captured into a HIP graph and the graph
- * replayed, on every path except the split-row one (ADQ_PATH_SPLIT): its
- * launches tag their exchange slots with a value the host makes fresh for
- * each call, and a replay would repeat the captured tag.
+ * Graphs: every phase-2 call may be captured into a HIP graph and the graph
+ * replayed; no call records a memset, and no kernel keeps state between
+ * launches.
  *
  * Determinism: results are bitwise reproducible run to run (fixed
  * reduction order, no floating-point atomics), as the pages' Constraints
@@ -126,7 +124,10 @@ typedef struct adq_executor adq_executor;
  * An output that is produced needs its tensors (else ADQ_ERR_NULLPTR).  An
  * output that is not produced may be NULL; if given, it is never written.
  * Empty tensors (a zero dimension) are rejected ("aclnnRmsNormDynamicQuant",
- * Constraints: no empty input or output).
+ * Constraints: no empty input or output).  A produced output that shares
+ * memory with an input or with another produced output is rejected
+ * (ADQ_ERR_PARAM_INVALID): some paths read x1 and x2 again after writing
+ * xOut and the codes.
  */
 adq_status adq_add_rms_norm_dynamic_quant_v2_get_workspace_size(
     const adq_tensor* x1, const adq_tensor* x2, const adq_tensor* gamma,
@@ -139,7 +140,10 @@ adq_status adq_add_rms_norm_dynamic_quant_v2_get_workspace_size(
  * AddRmsNormDynamicQuantV2, phase 2: enqueue the work on `hip_stream` (a
  * hipStream_t; NULL = the default stream of the executor's device).
  * `workspace` is caller-owned device memory of at least the phase-1 size
- * (may be NULL when that size is 0).  Concurrent launches that share a
+ * (may be NULL when that size is 0), 8-byte aligned, with any contents: the
+ * split-row path (ADQ_PATH_SPLIT) keeps its per-chunk partial sums and
+ * maxima there between its launches, and every value it reads was written
+ * by an earlier launch of the same call.  Concurrent launches that share a
  * workspace must be ordered by the caller.  Returns without waiting.
  */
 adq_status adq_add_rms_norm_dynamic_quant_v2(void* workspace, uint64_t workspace_size,
@@ -240,9 +244,13 @@ void adq_executor_destroy(adq_executor* executor);
  * Kernel path of an executor.  ADQ_PATH_AUTO is chosen by phase 1 from the
  * shape; the others force a path (for tests and tuning).  ADQ_PATH_ROW:
  * one workgroup per row, 128-bit accesses (n % 8 == 0, 16-byte aligned
- * tensors, n <= 32768).  ADQ_PATH_SPLIT: several workgroups per row (n % 8
- * == 0, 16-byte aligned tensors; AUTO takes it for rows longer than 32768
- * columns).  ADQ_PATH_GENERIC: any n and alignment.
+ * tensors, n <= 32768).  ADQ_PATH_SPLIT: S workgroups per row, each on a
+ * chunk of the row, in two or three launches per batch of rows that hand
+ * the per-chunk partial sums of squares and maxima over through the
+ * workspace (n % 8 == 0, 16-byte aligned tensors; AUTO takes it for rows
+ * longer than 32768 columns, and for rows of at least 4096 columns when
+ * there are at most a quarter as many rows as compute units).
+ * ADQ_PATH_GENERIC: any n and alignment.
  * GEMM executors: ADQ_PATH_GEMM_TILE128 (128 x 128 output tiles) and
  * ADQ_PATH_GEMM_TILE256 (256 x 256 tiles); AUTO takes 256 once the
  * 256-tiles cover the compute units.  Either accepts any valid GEMM shape;
@@ -270,6 +278,22 @@ typedef enum adq_path {
  */
 adq_status adq_executor_set_path(adq_executor* executor, int32_t path,
                                  uint64_t* workspace_size);
+
+/*
+ * Split-row geometry of an operator executor (AddRmsNormDynamicQuantV2 or
+ * RmsNormDynamicQuant): moves it to ADQ_PATH_SPLIT with `splits` chunks per
+ * row (0 = the planner's choice; otherwise it must be a count that cuts n
+ * into whole chunks of at most 2048 8-column vectors, each chunk but the
+ * last the same size) and `launches` 2 (the last launch takes each row's
+ * maxima over the whole row) or 3 (a launch of its own for the partial
+ * maxima), or 0 for the planner's choice; returns the new workspace size.
+ * For one chunk count the two launch forms give the same bits (the row's
+ * sum of squares is added up chunk by chunk in the same order); another
+ * chunk count adds it up in another order.  For tests and tuning;
+ * ADQ_ERR_PARAM_INVALID leaves the executor unchanged.
+ */
+adq_status adq_executor_set_split(adq_executor* executor, int32_t splits, int32_t launches,
+                                  uint64_t* workspace_size);
 
 /*
  * Write a one-line description of the plan (path, kernel variant, block,

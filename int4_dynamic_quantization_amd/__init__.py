@@ -40,6 +40,7 @@ EXPORTED = (
     "adq_add_lora",
     "adq_executor_destroy",
     "adq_executor_set_path",
+    "adq_executor_set_split",
     "adq_executor_describe",
     "adq_last_error",
 )
@@ -99,6 +100,7 @@ def _load():
     lib.adq_executor_destroy.argtypes = [vp]
     lib.adq_executor_destroy.restype = None
     lib.adq_executor_set_path.argtypes = [vp, ctypes.c_int32, u64p]
+    lib.adq_executor_set_split.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, u64p]
     lib.adq_executor_describe.argtypes = [vp, ctypes.c_char_p, ctypes.c_uint64]
     lib.adq_executor_describe.restype = ctypes.c_int32
     lib.adq_last_error.argtypes = []
@@ -107,7 +109,8 @@ def _load():
                  "adq_add_rms_norm_dynamic_quant_v2",
                  "adq_rms_norm_dynamic_quant_get_workspace_size", "adq_rms_norm_dynamic_quant",
                  "adq_w8a8_gemm_get_workspace_size", "adq_w8a8_gemm",
-                 "adq_add_lora_get_workspace_size", "adq_add_lora", "adq_executor_set_path"):
+                 "adq_add_lora_get_workspace_size", "adq_add_lora", "adq_executor_set_path",
+                 "adq_executor_set_split"):
         getattr(lib, name).restype = ctypes.c_int
     runtimes = _hip_runtimes_mapped()
     if len(runtimes) > 1:
@@ -189,6 +192,15 @@ class Executor:
     def set_path(self, path: int) -> int:
         ws = ctypes.c_uint64(0)
         _check(_lib().adq_executor_set_path(self.handle, int(path), ctypes.byref(ws)))
+        self.workspace_size = int(ws.value)
+        return self.workspace_size
+
+    def set_split(self, splits: int = 0, launches: int = 0) -> int:
+        """Split-row path with `splits` chunks per row and a 2- or 3-launch
+        form (0 = the planner's choice); returns the new workspace size."""
+        ws = ctypes.c_uint64(0)
+        _check(_lib().adq_executor_set_split(self.handle, int(splits), int(launches),
+                                             ctypes.byref(ws)))
         self.workspace_size = int(ws.value)
         return self.workspace_size
 
@@ -310,6 +322,21 @@ def _workspace(ex, device):
     return torch.empty(ex.workspace_size, dtype=torch.uint8, device=device)
 
 
+def _run_once(ex, device, stream, made):
+    """Phase 2 with a workspace allocated here.  The workspace and the
+    tensors in `made` (allocated here, on torch's current stream) are marked
+    as used on the launch stream, so that torch's caching allocator does not
+    hand their memory out again before the launched work has finished when
+    that stream is not the current one."""
+    ws = _workspace(ex, device)
+    ex.run(ws, stream)
+    if stream is not None:
+        for t in [ws] + list(made):
+            if t is not None:
+                t.record_stream(stream)
+    ex.close()
+
+
 def add_rms_norm_dynamic_quant_v2(x1, x2, gamma, beta=None, smooth_scale1=None,
                                   smooth_scale2=None, epsilon=1e-6, output_mask=None,
                                   y1_type="int8", y2_type="int8", stream=None, path=PATH_AUTO):
@@ -317,9 +344,7 @@ def add_rms_norm_dynamic_quant_v2(x1, x2, gamma, beta=None, smooth_scale1=None,
     ex, outs = plan_add_rms_norm_dynamic_quant_v2(
         x1, x2, gamma, beta, smooth_scale1, smooth_scale2, epsilon, output_mask, y1_type,
         y2_type, path=path)
-    ws = _workspace(ex, x1.device)
-    ex.run(ws, stream)
-    ex.close()
+    _run_once(ex, x1.device, stream, outs.values())
     return outs["y1"], outs["y2"], outs["scale1"], outs["scale2"], outs["x_out"]
 
 
@@ -348,9 +373,7 @@ def rms_norm_dynamic_quant(x, gamma, beta=None, smooth_scales=None, epsilon=1e-6
     """Both phases on torch tensors; returns (y, scale)."""
     ex, outs = plan_rms_norm_dynamic_quant(x, gamma, beta, smooth_scales, epsilon, y_type,
                                            path=path)
-    ws = _workspace(ex, x.device)
-    ex.run(ws, stream)
-    ex.close()
+    _run_once(ex, x.device, stream, outs.values())
     return outs["y"], outs["scale"]
 
 
@@ -387,8 +410,7 @@ def plan_w8a8_gemm(a, a_scale, w, w_scale, bias=None, out_dtype=None, out=None,
 def w8a8_gemm(a, a_scale, w, w_scale, bias=None, out_dtype=None, stream=None):
     """Both GEMM phases on torch tensors; returns out."""
     ex, out = plan_w8a8_gemm(a, a_scale, w, w_scale, bias, out_dtype)
-    ex.run(None, stream)
-    ex.close()
+    _run_once(ex, a.device, stream, [out])
     return out
 
 
@@ -424,7 +446,7 @@ def plan_add_lora(y, x, weight_b, indices, weight_a=None, layer_idx=0, scale=1.0
 def add_lora(y, x, weight_b, indices, weight_a=None, layer_idx=0, scale=1.0, y_offset=0,
              out=None, stream=None):
     """Both AddLora phases on torch tensors (workspace allocated here); returns out."""
+    allocated = out is None
     ex, out = plan_add_lora(y, x, weight_b, indices, weight_a, layer_idx, scale, y_offset, out)
-    ex.run(_workspace(ex, y.device), stream)
-    ex.close()
+    _run_once(ex, y.device, stream, [out] if allocated else [])
     return out

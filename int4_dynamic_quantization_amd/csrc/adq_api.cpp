@@ -7,8 +7,6 @@
 // Formula cases and Constraints section.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
-#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -81,9 +79,11 @@ struct adq_executor {
   int block;
   int grid;
   int splits;
-  int row_groups;
+  int launches;        // split-row path: 2 or 3 launches per batch of rows
+  int64_t batch_rows;  // split-row path: rows per batch
+  int split_req;       // split-row path: requested chunks per row (0 = planner's)
+  int launch_req;      // split-row path: requested launch form (0 = planner's)
   uint64_t ws_bytes;
-  uint64_t last_epoch;
 };
 
 namespace {
@@ -185,6 +185,36 @@ adq_status check_output(const adq_tensor* y, const adq_tensor* s, const char* yn
 
 bool aligned(const void* p, uintptr_t a) { return p == nullptr || (uintptr_t)p % a == 0; }
 
+// Bytes of a tensor's storage.
+uint64_t tensor_bytes(const adq_tensor* t) {
+  uint64_t esz = 2;
+  if (t->dtype == ADQ_F32 || t->dtype == ADQ_INT32) esz = 4;
+  else if (t->dtype == ADQ_INT8 || t->dtype == ADQ_INT4X2) esz = 1;
+  return (uint64_t)numel(t) * esz;
+}
+
+bool overlaps(const adq_tensor* a, const adq_tensor* b) {
+  if (!a || !b || !a->data || !b->data) return false;
+  const uintptr_t a0 = (uintptr_t)a->data, b0 = (uintptr_t)b->data;
+  return a0 < b0 + tensor_bytes(b) && b0 < a0 + tensor_bytes(a);
+}
+
+// Outputs must not share memory with inputs or with each other: the
+// split-row and generic kernels read x1 and x2 again after xOut and the codes
+// of the same row are written.
+adq_status check_no_overlap(const adq_tensor* const* ins, int nin, const adq_tensor* const* outs,
+                            int nout) {
+  for (int o = 0; o < nout; ++o) {
+    for (int i = 0; i < nin; ++i)
+      if (overlaps(outs[o], ins[i]))
+        return fail(ADQ_ERR_PARAM_INVALID, "an output shares memory with an input");
+    for (int p = 0; p < o; ++p)
+      if (overlaps(outs[o], outs[p]))
+        return fail(ADQ_ERR_PARAM_INVALID, "two outputs share memory");
+  }
+  return ADQ_OK;
+}
+
 struct DeviceInfo {
   int cus = 0;
 };
@@ -216,59 +246,51 @@ adq_status current_device(int* dev, int* cus) {
 
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
-// Per-launch epochs for the split-row exchange: unique within the process,
-// starting from a value mixed from the clock and an address so that stale
-// workspace contents from another process do not repeat them.
-uint64_t next_epoch() {
-  static std::atomic<uint64_t> counter{[] {
-    uint64_t z = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
-                 (uint64_t)(uintptr_t)&g_last_error;
-    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
-    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
-    return z ^ (z >> 31);
-  }()};
-  return counter.fetch_add(0x9E3779B97F4A7C15ULL, std::memory_order_relaxed);
-}
+// ---- planning constants (each measured on an MI355X; the numbers behind
+// them are in the design notes of the repository)
 
-// Row-kernel geometry: vectors per thread and block size for n / 8 vectors.
-#ifndef ADQ_VPT1_MAX_NVEC
-#define ADQ_VPT1_MAX_NVEC 64
-#endif
-#ifndef ADQ_MAX_WG_PER_CU
-#define ADQ_MAX_WG_PER_CU 0
-#endif
-#ifndef ADQ_LORA_KSPLIT_MULT
-#define ADQ_LORA_KSPLIT_MULT 1
-#endif
-#ifndef ADQ_GEMM_BIG_TILE
-#define ADQ_GEMM_BIG_TILE 2
-#endif
-#ifndef ADQ_ROW_GRID_MULT
-#define ADQ_ROW_GRID_MULT 1
-#endif
-#ifndef ADQ_SHORT_ROW_MAX_N
-#define ADQ_SHORT_ROW_MAX_N 6144
-#endif
-#ifndef ADQ_SHORT_ROW_MIN_ROWS_PER_WG
-#define ADQ_SHORT_ROW_MIN_ROWS_PER_WG 16
-#endif
-#ifndef ADQ_SHORT_ROW_GRID_MULT
-#define ADQ_SHORT_ROW_GRID_MULT 24
-#endif
+// Row kernel: rows of up to 64 8-column vectors take one vector per thread,
+// up to 2048 two, up to 4096 (32768 columns) four; longer rows do not fit
+// one workgroup's registers.
+constexpr int64_t kRowVpt1MaxVec = 64;
+constexpr int64_t kRowVpt2MaxVec = 2048;
+constexpr int64_t kRowMaxVec = 4096;
+// Short rows (up to 6144 columns) that a grid filling every resident slot
+// once would stream 16 or more times per workgroup run faster with 24 times
+// as many workgroups of a few rows each, which the dispatcher hands to CUs
+// as they free up (65536 x 5120: 410.6 -> 376.6 us).  Longer rows keep the
+// persistent grid (16384 x 8192 is slower with more workgroups).
+constexpr int64_t kShortRowMaxN = 6144;
+constexpr int64_t kShortRowMinRowsPerWg = 16;
+constexpr int64_t kShortRowGridMult = 24;
 
-// Rows of up to ADQ_ROW_MAX_NVEC 8-column vectors (32768 columns) fit one
-// workgroup of the row kernel (VPT 4 above 16384 columns).
-#ifndef ADQ_ROW_MAX_NVEC
-#define ADQ_ROW_MAX_NVEC 4096
-#endif
+// Split-row path: chunks of at least one wave of vectors (512 columns) and
+// at most 1024 threads x 2 vectors (16384 columns); enough chunks per row
+// for about two workgroups per CU; batches of rows whose x1 and x2 take at
+// most 64 MiB, so that the chunks the later launches read again are still
+// in the 256 MB memory-side cache.
+constexpr int64_t kSplitMinChunkVec = 64;
+constexpr int64_t kSplitMaxChunkVec = 2048;
+constexpr int64_t kSplitWgPerCu = 2;
+constexpr int64_t kSplitBatchBytes = (int64_t)64 << 20;
+// The two-launch form (each workgroup of the last launch takes the row
+// maxima over the whole row) up to this many chunks per row and this row
+// length; beyond, the three-launch form.
+constexpr int64_t kSplitWholeRowMaxSplits = 8;
+constexpr int64_t kSplitWholeRowMaxVec = 4096;
+// AUTO sends rows that fit the row kernel to the split-row path when they
+// are too few to give each CU a quarter of a row (the row kernel would
+// leave most CUs idle) and at least 4096 columns long.
+constexpr int64_t kFewRowsCuDiv = 4;
+constexpr int64_t kFewRowsMinVec = 512;
 
 bool row_geometry(int64_t nvec, int* vpt, int* block) {
   if (nvec <= 0) return false;
-  if (nvec <= ADQ_VPT1_MAX_NVEC) {
+  if (nvec <= kRowVpt1MaxVec) {
     *vpt = 1, *block = round_up((int)nvec, 64);
-  } else if (nvec <= 2048) {
+  } else if (nvec <= kRowVpt2MaxVec) {
     *vpt = 2, *block = round_up((int)((nvec + 1) / 2), 64);
-  } else if (nvec <= ADQ_ROW_MAX_NVEC) {
+  } else if (nvec <= kRowMaxVec) {
     *vpt = 4, *block = round_up((int)((nvec + 3) / 4), 64);
   } else {
     return false;
@@ -276,73 +298,60 @@ bool row_geometry(int64_t nvec, int* vpt, int* block) {
   return true;
 }
 
-#ifndef ADQ_SPLIT_MAX_BLOCK
-#define ADQ_SPLIT_MAX_BLOCK 512
-#endif
-#ifndef ADQ_SPLIT_MAX_WANT
-#define ADQ_SPLIT_MAX_WANT 8
-#endif
-#ifndef ADQ_SPLIT_TARGET_WG_PER_CU
-#define ADQ_SPLIT_TARGET_WG_PER_CU 2
-#endif
-
-// Split-row geometry: S workgroups of `block` threads (one 8-column vector
-// per thread, two when a split would need more than ADQ_SPLIT_MAX_BLOCK
-// threads) per row, enough of them to give every CU about
-// ADQ_SPLIT_TARGET_WG_PER_CU workgroups but at most ADQ_SPLIT_MAX_WANT per
-// row (every split adds a partner to each exchange), and all resident at
-// once.  Rows are processed 8 * row_groups at a time.  512-thread
-// workgroups let two share a CU, so one computes while the other waits.
+// Split-row geometry: S chunks per row (requested, or enough for about
+// kSplitWgPerCu workgroups per CU), each of block x vpt vectors; the launch
+// form (requested, or by the rule above); rows per batch.
 bool split_geometry(adq_executor* e) {
   const int64_t nvec = e->args.n / 8;
+  if (nvec < 1) return false;
   const int64_t rows8 = (e->m + 7) / 8 * 8;
-  int64_t want = (int64_t)e->cus * ADQ_SPLIT_TARGET_WG_PER_CU / rows8;  // splits per row
-  if (want > ADQ_SPLIT_MAX_WANT) want = ADQ_SPLIT_MAX_WANT;
-  if (want < 1) want = 1;
-  int vpt = 1;
-  int64_t block = round_up((int)((nvec + want - 1) / want), 64);
-  if (block < 64) block = 64;
-  if (block > ADQ_SPLIT_MAX_BLOCK) {
-    vpt = 2;
-    block = round_up((int)((nvec + 2 * want - 1) / (2 * want)), 64);
-    if (block > ADQ_SPLIT_MAX_BLOCK) block = ADQ_SPLIT_MAX_BLOCK;
+  int64_t S = e->split_req;
+  if (S <= 0) {
+    S = ((int64_t)e->cus * kSplitWgPerCu + rows8 - 1) / rows8;
+    const int64_t most = nvec / kSplitMinChunkVec > 1 ? nvec / kSplitMinChunkVec : 1;
+    if (S > most) S = most;
+    if (S < 1) S = 1;
   }
-  const int64_t chunk = block * vpt;
-  const int64_t splits = (nvec + chunk - 1) / chunk;
-  if (splits > 64) return false;
-  const int occ = adq::split_max_blocks_per_cu(e->var, vpt, (int)block);
-  if (occ <= 0) return false;
-  const int64_t capacity = (int64_t)occ * e->cus;
-  int64_t groups = (e->m + 7) / 8;
-  if (groups * 8 * splits > capacity) groups = capacity / (8 * splits);
-  if (groups < 1) return false;
+  if (S > nvec) S = nvec;
+  const int64_t least = (nvec + kSplitMaxChunkVec - 1) / kSplitMaxChunkVec;
+  if (S < least) S = least;
+  const int64_t chunk = (nvec + S - 1) / S;
+  int vpt = 1;
+  int64_t block = round_up((int)chunk, 64);
+  if (block > 1024) {
+    vpt = 2;
+    block = round_up((int)((chunk + 1) / 2), 64);
+  }
+  S = (nvec + block * vpt - 1) / (block * vpt);
+  int launches = e->launch_req;
+  if (launches == 0)
+    launches = S <= kSplitWholeRowMaxSplits && nvec <= kSplitWholeRowMaxVec ? 2 : 3;
+  const int64_t row_bytes = (int64_t)e->var.nin * 2 * e->args.n;
+  int64_t batch = kSplitBatchBytes / row_bytes;
+  if (batch >= 8) batch -= batch % 8;
+  if (batch < 1) batch = 1;
+  if (batch > e->m) batch = e->m;
+  while (batch > 1 && adq::split_grid(batch, (int)S) > INT32_MAX) batch /= 2;
+  if (adq::split_grid(batch, (int)S) > INT32_MAX) return false;
   e->vpt = vpt;
   e->block = (int)block;
-  e->splits = (int)splits;
-  e->row_groups = (int)groups;
-  e->grid = (int)(8 * groups * splits);
-  e->ws_bytes = adq::split_workspace_bytes(e->m, (int)splits);
+  e->splits = (int)S;
+  e->launches = launches;
+  e->batch_rows = batch;
+  e->grid = (int)adq::split_grid(batch, (int)S);
+  e->ws_bytes = adq::split_workspace_bytes(batch, (int)S, launches);
   return true;
 }
-
-// Few-row shapes stay on the row kernel: on gfx950 one workgroup streaming
-// a whole row (up to 32768 columns) beats S workgroups that must exchange
-// partial results twice through agent-coherent memory, and the cooperative
-// launch the exchange needs costs more than the kernel itself.  Set above 0
-// to send shapes with at most this many rows (and n >= 2048) to the
-// split-row kernel.
-#ifndef ADQ_SPLIT_MAX_ROWS
-#define ADQ_SPLIT_MAX_ROWS 0
-#endif
 
 adq_status plan(adq_executor* e, int path) {
   const int64_t n = e->args.n;
   if (path == ADQ_PATH_AUTO) {
-    // Row kernel when it holds a row; split-row for longer rows; generic
-    // for rows that are not whole 16-byte vectors or unaligned tensors.
+    // Row kernel when it holds a row and there are rows enough for the
+    // CUs; split-row for few or long rows; generic for rows that are not
+    // whole 16-byte vectors or unaligned tensors.
     int vpt = 0, block = 0;
     const bool row_ok = e->vector_ok && row_geometry(n / 8, &vpt, &block);
-    const bool few_rows = e->m <= ADQ_SPLIT_MAX_ROWS && n >= 2048;
+    const bool few_rows = e->m * kFewRowsCuDiv <= e->cus && n / 8 >= kFewRowsMinVec;
     if (e->vector_ok && (!row_ok || few_rows)) {
       adq_executor trial = *e;
       if (split_geometry(&trial)) path = ADQ_PATH_SPLIT;
@@ -353,20 +362,17 @@ adq_status plan(adq_executor* e, int path) {
     int vpt = 0, block = 0;
     if (!e->vector_ok || !row_geometry(n / 8, &vpt, &block))
       return fail(ADQ_ERR_PARAM_INVALID,
-                  "row path needs n %% 8 == 0, n <= %d and 16-byte aligned tensors",
-                  ADQ_ROW_MAX_NVEC * 8);
-    int occ = adq::row_max_blocks_per_cu(e->var, vpt, block);
-    if (ADQ_MAX_WG_PER_CU > 0 && occ > ADQ_MAX_WG_PER_CU) occ = ADQ_MAX_WG_PER_CU;
+                  "row path needs n %% 8 == 0, n <= %lld and 16-byte aligned tensors",
+                  (long long)(kRowMaxVec * 8));
+    const int occ = adq::row_max_blocks_per_cu(e->var, vpt, block);
     if (occ <= 0) return fail(ADQ_ERR_RUNTIME, "row kernel does not fit block %d", block);
     // A grid that fills every slot once (each workgroup then streams
-    // rows / slots rows) suits long rows.  Short rows (up to 6144 columns)
-    // that would be streamed 16 or more times per workgroup go faster with
-    // ADQ_SHORT_ROW_GRID_MULT times as many workgroups of a few rows each,
-    // which the dispatcher hands to CUs as they free up.
-    int64_t slots = (int64_t)occ * e->cus * ADQ_ROW_GRID_MULT;
+    // rows / slots rows) suits long rows; short rows streamed many times per
+    // workgroup take kShortRowGridMult times as many workgroups.
+    int64_t slots = (int64_t)occ * e->cus;
     int64_t per = (e->m + slots - 1) / slots;
-    if (n <= ADQ_SHORT_ROW_MAX_N && per >= ADQ_SHORT_ROW_MIN_ROWS_PER_WG) {
-      slots *= ADQ_SHORT_ROW_GRID_MULT;
+    if (n <= kShortRowMaxN && per >= kShortRowMinRowsPerWg) {
+      slots *= kShortRowGridMult;
       per = (e->m + slots - 1) / slots;
     }
     e->path = ADQ_PATH_ROW;
@@ -374,7 +380,8 @@ adq_status plan(adq_executor* e, int path) {
     e->block = block;
     e->grid = (int)((e->m + per - 1) / per);
     e->splits = 1;
-    e->row_groups = 0;
+    e->launches = 1;
+    e->batch_rows = e->m;
     e->ws_bytes = 0;
     return ADQ_OK;
   }
@@ -384,7 +391,8 @@ adq_status plan(adq_executor* e, int path) {
     e->block = 256;
     e->grid = (int)(e->m < (int64_t)e->cus * 8 ? e->m : (int64_t)e->cus * 8);
     e->splits = 1;
-    e->row_groups = 0;
+    e->launches = 1;
+    e->batch_rows = e->m;
     e->ws_bytes = 0;
     return ADQ_OK;
   }
@@ -392,7 +400,7 @@ adq_status plan(adq_executor* e, int path) {
     if (!e->vector_ok)
       return fail(ADQ_ERR_PARAM_INVALID,
                   "split-row path needs n %% 8 == 0 and 16-byte aligned tensors");
-    if (!split_geometry(e)) return fail(ADQ_ERR_RUNTIME, "split-row kernel does not fit");
+    if (!split_geometry(e)) return fail(ADQ_ERR_PARAM_INVALID, "split-row geometry does not fit");
     e->path = ADQ_PATH_SPLIT;
     return ADQ_OK;
   }
@@ -473,9 +481,8 @@ adq_status run(void* workspace, uint64_t workspace_size, adq_executor* e, void* 
       break;
     case ADQ_PATH_GENERIC: err = adq::launch_generic(e->var, e->block, e->grid, e->args, s); break;
     case ADQ_PATH_SPLIT:
-      e->last_epoch = next_epoch();
-      err = adq::launch_split(e->var, e->vpt, e->block, e->splits, e->row_groups, e->args,
-                              workspace, e->last_epoch, s);
+      err = adq::launch_split(e->var, e->vpt, e->block, e->splits, e->launches, e->batch_rows,
+                              e->args, workspace, s);
       break;
     default: break;
   }
@@ -547,6 +554,12 @@ adq_status adq_add_rms_norm_dynamic_quant_v2_get_workspace_size(
     return st;
   if (act2 && (st = check_output(y2_out, scale2_out, "y2_out", "scale2_out", x1, &q2)) != ADQ_OK)
     return st;
+  {
+    const adq_tensor* ins[] = {x1, x2, gamma, beta, smooth_scale1, smooth_scale2};
+    const adq_tensor* outs[] = {x_out, act1 ? y1_out : nullptr, act1 ? scale1_out : nullptr,
+                                act2 ? y2_out : nullptr, act2 ? scale2_out : nullptr};
+    if ((st = check_no_overlap(ins, 6, outs, 5)) != ADQ_OK) return st;
+  }
 
   adq_executor e{};
   e.op = kOpV2;
@@ -611,6 +624,11 @@ adq_status adq_rms_norm_dynamic_quant_get_workspace_size(
     return fail(ADQ_ERR_PARAM_INVALID, "epsilon must be a finite value");
   int q = adq::kQNone;
   if ((st = check_output(y_out, scale_out, "y_out", "scale_out", x, &q)) != ADQ_OK) return st;
+  {
+    const adq_tensor* ins[] = {x, gamma, beta, smooth_scales};
+    const adq_tensor* outs[] = {y_out, scale_out};
+    if ((st = check_no_overlap(ins, 4, outs, 2)) != ADQ_OK) return st;
+  }
 
   adq_executor e{};
   e.op = kOpRmsNorm;
@@ -638,7 +656,7 @@ adq_status adq_rms_norm_dynamic_quant(void* workspace, uint64_t workspace_size,
 // large tiles once there are enough of them to occupy every compute unit
 static int gemm_auto_tile(const adq_executor& e) {
   const int64_t big = ((e.gemm.m + 255) / 256) * ((e.gemm.n + 255) / 256);
-  return big >= e.cus ? ADQ_GEMM_BIG_TILE : adq::kGemmTile128;
+  return big >= e.cus ? adq::kGemmTile256 : adq::kGemmTile128;
 }
 
 adq_status adq_w8a8_gemm_get_workspace_size(const adq_tensor* a, const adq_tensor* a_scale,
@@ -837,7 +855,7 @@ adq_status adq_add_lora_get_workspace_size(const adq_tensor* y, const adq_tensor
     const int64_t fit = (int64_t)adq::lora_shrink_blocks_per_cu(part) * e.cus / est_tiles;
     if (fit >= 1 && fit < want) want = fit;
     auto clamp = [](int64_t v, int64_t hi) { return (int)(v < 1 ? 1 : v > hi ? hi : v); };
-    a.ksplit = clamp(ADQ_LORA_KSPLIT_MULT * want, h1 / 256 > 1 ? h1 / 256 : 1);
+    a.ksplit = clamp(want, h1 / 256 > 1 ? h1 / 256 : 1);
     a.chunks = adq::lora_expand_chunks(h2, rank);
   }
   e.path = e.lora_tiled_ok ? ADQ_PATH_AUTO : ADQ_PATH_GENERIC;
@@ -886,6 +904,27 @@ adq_status adq_executor_set_path(adq_executor* executor, int32_t path, uint64_t*
   return ok();
 }
 
+adq_status adq_executor_set_split(adq_executor* executor, int32_t splits, int32_t launches,
+                                  uint64_t* workspace_size) {
+  if (!executor || !workspace_size)
+    return fail(ADQ_ERR_NULLPTR, "executor and workspace_size are required");
+  if (executor->op != kOpV2 && executor->op != kOpRmsNorm)
+    return fail(ADQ_ERR_PARAM_INVALID, "split geometry applies to the operator's executors only");
+  if (splits < 0 || (launches != 0 && launches != 2 && launches != 3))
+    return fail(ADQ_ERR_PARAM_INVALID, "splits must be >= 0 and launches 0, 2 or 3");
+  adq_executor trial = *executor;
+  trial.split_req = splits;
+  trial.launch_req = launches;
+  adq_status st = plan(&trial, ADQ_PATH_SPLIT);
+  if (st != ADQ_OK) return st;
+  if (splits > 0 && trial.splits != splits)
+    return fail(ADQ_ERR_PARAM_INVALID, "%d chunks per row do not fit n = %d (nearest: %d)",
+                splits, trial.args.n, trial.splits);
+  *executor = trial;
+  *workspace_size = trial.ws_bytes;
+  return ok();
+}
+
 int32_t adq_executor_describe(const adq_executor* e, char* buf, uint64_t len) {
   if (!e) return -1;
   if (e->op == kOpLora) {
@@ -917,11 +956,11 @@ int32_t adq_executor_describe(const adq_executor* e, char* buf, uint64_t len) {
     static const char* names[] = {"auto", "row", "split", "generic"};
     snprintf(buf, (size_t)len,
              "path=%s elem=%s nin=%d q1=%d q2=%d rows=%lld n=%d vpt=%d block=%d grid=%d "
-             "splits=%d row_groups=%d workspace=%llu cus=%d epoch=%llu",
+             "splits=%d launches=%d batch_rows=%lld workspace=%llu cus=%d",
              names[e->path & 3], e->var.elem == adq::kBF16 ? "bf16" : "fp16", e->var.nin,
              e->var.q1, e->var.q2, (long long)e->m, e->args.n, e->vpt, e->block, e->grid,
-             e->splits, e->row_groups, (unsigned long long)e->ws_bytes, e->cus,
-             (unsigned long long)e->last_epoch);
+             e->splits, e->launches, (long long)e->batch_rows, (unsigned long long)e->ws_bytes,
+             e->cus);
   }
   return e->path;
 }

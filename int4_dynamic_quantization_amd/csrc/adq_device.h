@@ -34,15 +34,10 @@ __device__ __forceinline__ void* row_ptr(void* base, int64_t row, uint32_t row_b
 }
 
 // Cache policy bits of streamed (read-once / write-once) buffer accesses:
-// 2 = non-temporal.
-#ifndef ADQ_LOAD_POLICY
-#define ADQ_LOAD_POLICY 2
-#endif
-#ifndef ADQ_STORE_POLICY
-#define ADQ_STORE_POLICY 2
-#endif
-constexpr int kStreamLoad = ADQ_LOAD_POLICY;
-constexpr int kStreamStore = ADQ_STORE_POLICY;
+// 2 = non-temporal (measured 2-9% faster than cached accesses on the row
+// kernel; the sc0 / sc1 combinations measured the same within noise).
+constexpr int kStreamLoad = 2;
+constexpr int kStreamStore = 2;
 
 // Two packed 16-bit values (element 0 in the low half) -> two floats.
 template <int E>

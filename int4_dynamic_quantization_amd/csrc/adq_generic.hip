@@ -3,9 +3,12 @@
 // a time, elementwise 16-bit accesses, three passes that re-read the row's
 // inputs from cache.  This is the correctness path for shapes the vector
 // kernels do not take; the arithmetic per element is the same as theirs:
-// fp32 add, sum of squares, rinv = 1/sqrt(ss/n + eps), y = fma(x*rinv,
+// fp32 add, sum of squares, rinv = rsq(fma(ss, 1/n, eps)), y = fma(x*rinv,
 // gamma, beta), input_k = y * smooth_k, scale_k = max|input_k| / Q,
-// code = round_half_even(input_k * (1/scale_k)).
+// code = round_half_even(input_k * (1/scale_k)).  Only the order in which
+// the sum of squares is added up differs between the kernels (each fixed),
+// so a row's results are reproducible bit for bit within one path and agree
+// across paths to the last bits of the scale.
 //
 // Operator: "aclnnAddRmsNormDynamicQuantV2", Formula section, and
 // "aclnnRmsNormDynamicQuant", formula section.
@@ -58,7 +61,7 @@ __global__ void __launch_bounds__(256) generic_kernel(const Args a) {
     __syncthreads();
     float tot = 0.0f;
     for (int w = 0; w < nwaves; ++w) tot += red_ss[w];
-    const float rinv = 1.0f / __builtin_sqrtf(tot / (float)a.n + a.eps);
+    const float rinv = __builtin_amdgcn_rsqf(__builtin_fmaf(tot, a.inv_n, a.eps));
 
     auto inputs = [&](int64_t j, float& in1, float& in2) {
       const float y = __builtin_fmaf(xval(j) * rinv, param<E>(a.gamma, j, 0.0f),

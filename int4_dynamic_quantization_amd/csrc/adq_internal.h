@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI host layer (adq_api.cpp) and the
-// HIP kernels (adq_row.hip, adq_split.hip, adq_generic.hip).  Not installed.
+// HIP kernels (adq_row_*.hip, adq_split.hip, adq_generic.hip, adq_gemm.hip,
+// adq_lora.hip).  Not installed.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -47,19 +48,20 @@ struct Variant {
 };
 
 // Row kernel: one workgroup per row at a time, `vpt` 8-element vectors per
-// thread (1 or 2), grid-strided over rows, next row prefetched.
+// thread (1, 2 or 4), grid-strided over rows, next row prefetched.
 hipError_t launch_row(const Variant& v, int vpt, int block, int grid, const Args& a,
                       hipStream_t stream);
 int row_max_blocks_per_cu(const Variant& v, int vpt, int block);
 
-// Split-row kernel: `splits` workgroups share each row (a chunk of block *
-// vpt 8-column vectors each); grid = 8 * row_groups * splits, launched
-// cooperatively.  `ws` is the launch's workspace (split_workspace_bytes,
-// 8-byte aligned, any contents), `epoch` a value unique to this launch.
-hipError_t launch_split(const Variant& v, int vpt, int block, int splits, int row_groups,
-                        const Args& a, void* ws, uint64_t epoch, hipStream_t stream);
-int split_max_blocks_per_cu(const Variant& v, int vpt, int block);
-uint64_t split_workspace_bytes(int64_t rows, int splits);
+// Split-row path: S workgroups share each row (a chunk of block * vpt
+// 8-column vectors each); `launches` 2 or 3 plain kernels per batch of
+// `batch_rows` rows hand the partial results over through `ws`
+// (split_workspace_bytes(batch_rows, splits, launches) bytes, 4-byte
+// aligned, any contents) at kernel boundaries.
+hipError_t launch_split(const Variant& v, int vpt, int block, int splits, int launches,
+                        int64_t batch_rows, const Args& a, void* ws, hipStream_t stream);
+uint64_t split_workspace_bytes(int64_t batch_rows, int splits, int launches);
+int64_t split_grid(int64_t batch_rows, int splits);  // workgroups per launch
 
 // Generic kernel: any n (odd widths, unaligned pointers); correctness path.
 hipError_t launch_generic(const Variant& v, int block, int grid, const Args& a,

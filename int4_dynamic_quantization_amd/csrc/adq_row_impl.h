@@ -37,10 +37,6 @@
 
 #include "adq_device.h"
 
-#ifndef ADQ_ROW_BLOCKED
-#define ADQ_ROW_BLOCKED 0
-#endif
-
 namespace adq {
 
 // Keeps the compiler from hoisting per-use conversions of a loop-invariant
@@ -117,18 +113,11 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
     }
   };
 
-  // Rows of this workgroup: strided (blockIdx.x, + gridDim.x, ...) or one
-  // contiguous block of rows.
-#if ADQ_ROW_BLOCKED
-  const int64_t per = (a.rows + gridDim.x - 1) / gridDim.x;
-  const int64_t first = (int64_t)blockIdx.x * per;
-  const int64_t rend = first + per < a.rows ? first + per : a.rows;
-  const int64_t step = 1;
-#else
+  // Rows of this workgroup: blockIdx.x, + gridDim.x, ... (strided rows
+  // measured 3-9% faster than one contiguous block of rows per workgroup).
   const int64_t first = blockIdx.x;
   const int64_t rend = a.rows;
   const int64_t step = gridDim.x;
-#endif
   auto clamp_row = [&](int64_t r) { return r < rend ? r : rend - 1; };
 
   int64_t row = first;

@@ -1,36 +1,39 @@
-// Split-row kernel: fused (Add)RmsNorm + dynamic quantization with S
-// workgroups sharing each row, for shapes with few rows (decode steps) or
-// rows longer than one workgroup holds.
+// Split-row path: fused (Add)RmsNorm + dynamic quantization with S
+// workgroups sharing each row, for shapes whose rows are too few to occupy
+// the chip one row per workgroup (decode steps) or too long for one
+// workgroup to hold.
 //
 // Operator: "aclnnAddRmsNormDynamicQuantV2", Formula section, and
-// "aclnnRmsNormDynamicQuant", formula section.  Both the row sum of squares
-// (inside Rms) and the row maximum (row_max) span the whole row, so the S
-// workgroups of a row exchange partial results twice per row:
-//   A  chunk loads, x = x1 + x2, xOut, partial sum of squares -> publish
-//   -- wait for the S partial sums; add them in split order (every
-//      workgroup gets the same bits, so results are deterministic)
-//   B  y, quantizer inputs, partial row maxima -> publish
-//   -- wait for the S partial maxima (max is exact in any order)
-//   C  scales (split 0 stores them), codes, packed stores
+// "aclnnRmsNormDynamicQuant", formula section.  The sum of squares inside
+// Rms and the row maximum (row_max) both span the whole row, so a row cut
+// into S chunks needs two whole-row results before its codes exist.  They
+// are handed over at kernel boundaries, never inside a launch:
 //
-// Exchange slots live in the caller's workspace and need no clearing: each
-// launch carries a 64-bit epoch unique within the process, and a slot is
-// two 64-bit words {epoch low half, value}, {epoch high half, value'}
-// written with single-copy-atomic stores.  A reader accepts a slot only
-// when both words carry this launch's halves, so a slot written by an
-// earlier launch or holding unrelated data is never taken (a 64-bit match
-// by chance is the only exception).  No memory fences are needed: each
-// value travels in the same atomic word as its tag.
+//   K1 sumsq  workgroup (row, s): chunk s of x1, x2 -> x = x1 + x2 (fp32),
+//             xOut, partial sum of squares -> ss[row][s]
+//   K2 max    workgroup (row, s): total = ss[row][0] + ... + ss[row][S-1]
+//             in split order (the same bits in every workgroup of the
+//             row); rinv; chunk s again; quantizer inputs; partial row
+//             maxima -> mx[row][s][k]
+//   K3 quant  workgroup (row, s): rinv as in K2; M_k = max over
+//             mx[row][.][k] (a maximum is exact in any order); scales
+//             (split 0 stores them); chunk s again; codes -> y_k
 //
-// All workgroups of the grid are resident at once (cooperative launch), so
-// every wait ends; each wait is also bounded, and a workgroup that gives up
-// records an error word in the workspace and continues.
+// Two-launch form: K2 is left out and each K3 workgroup takes the row
+// maxima itself over the whole row.  That costs S reads of each row from
+// the cache instead of one launch, which pays for few short rows.
 //
-// Workgroup -> (row, split) mapping keeps the S workgroups of a row on one
-// XCD (workgroups are dealt to the 8 XCDs round robin), so their exchange
-// stays within one L2 when the dispatcher follows that order; a wait that
-// keeps failing invalidates its L2 now and then, so that a slot written
-// from another XCD is still seen.
+// Every chunk is re-read from the caches (K1 loads with the default cache
+// policy so the lines stay in L2 and the memory-side cache), and every
+// quantizer input is recomputed from the same loaded values with the same
+// fp32 operations in each kernel, so K3 quantizes exactly the values whose
+// maximum K2 took.  The kernels never read a location that another
+// workgroup of the same launch writes: there are no waits, no flags and no
+// atomics, and the workspace needs no clearing (each kernel reads only what
+// an earlier launch of the same call wrote).  Kernel boundaries on one
+// stream order the launches; large inputs run as batches of rows (each
+// batch's three launches before the next batch's), so the re-read chunks
+// of a batch still sit in the 256 MB memory-side cache.
 #include <type_traits>
 
 #include "adq_device.h"
@@ -39,305 +42,380 @@ namespace adq {
 
 namespace {
 
-constexpr uint32_t kSpinLimit = 1u << 14;  // polls (about 2 us each) before a wait gives up
 constexpr int kXcds = 8;
 
 struct SplitArgs {
   Args a;
-  uint64_t* ws;      // workspace base (header + slots)
-  uint64_t epoch;    // unique per launch
-  int32_t splits;    // S
-  int32_t chunk;     // 8-column vectors per split (block * VPT)
-  int32_t row_groups;  // grid = kXcds * row_groups * splits
+  float* ss;       // [rows, S] partial sums of squares
+  float* mx;       // [rows, S, 2] partial row maxima (three-launch form)
+  int64_t row0;    // first row of this batch
+  int32_t rows;    // rows of this batch
+  int32_t splits;  // S
+  int32_t chunk;   // 8-column vectors per split (block * VPT)
 };
 
-// Workspace: 32-byte header (word 0: error flag = epoch of a launch whose
-// wait timed out), then for each (row, split) two 16-byte slots (sum of
-// squares; the two maxima).
-__device__ __forceinline__ uint64_t* slot_ptr(const SplitArgs& p, int64_t row, int s, int phase) {
-  return p.ws + 4 + ((row * p.splits + s) * 2 + phase) * 2;
-}
+// blockIdx -> (row of the batch, split).  Workgroups are dealt to the XCDs
+// round robin (b % 8); the S workgroups of a row share b % 8, so in each
+// launch of a batch (all with the same grid) a row's chunks are read on the
+// same XCD, whose L2 then still holds them for the next launch.
+struct Place {
+  int32_t local;  // row within the batch
+  int32_t s;      // split
+  bool valid;
+};
 
-__device__ __forceinline__ void publish(uint64_t* slot, uint64_t epoch, float v0, float v1) {
-  const uint64_t w0 = ((uint64_t)__float_as_uint(v0) << 32) | (uint32_t)epoch;
-  const uint64_t w1 = ((uint64_t)__float_as_uint(v1) << 32) | (uint32_t)(epoch >> 32);
-  __hip_atomic_store(slot, w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(slot + 1, w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wave 0, lane s < S: wait for split s's slot of this row and return its
-// two values.  Returns false when the wait gave up.
-__device__ __forceinline__ bool collect(const SplitArgs& p, int64_t row, int phase, int lane,
-                                        float& v0, float& v1) {
-  const bool mine = lane < p.splits;
-  uint64_t* slot = slot_ptr(p, row, mine ? lane : 0, phase);
-  const uint32_t lo = (uint32_t)p.epoch, hi = (uint32_t)(p.epoch >> 32);
-  bool done = !mine;
-  uint64_t w0 = 0, w1 = 0;
-  for (uint32_t it = 0; it < kSpinLimit; ++it) {
-    if (!done) {
-      w0 = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      w1 = __hip_atomic_load(slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      done = (uint32_t)w0 == lo && (uint32_t)w1 == hi;
-    }
-    if (__builtin_amdgcn_ballot_w64(!done) == 0) {
-      v0 = __uint_as_float((uint32_t)(w0 >> 32));
-      v1 = __uint_as_float((uint32_t)(w1 >> 32));
-      return true;
-    }
-    __builtin_amdgcn_s_sleep(1);
-    // Each XCD has its own L2, and a slot polled before it was written can
-    // stay cached there; the mapping keeps a row's workgroups on one XCD,
-    // but only through the dispatcher's order.  After every 64 unsuccessful
-    // polls (far beyond a normal wait) the wavefront invalidates its L2 so
-    // that a slot written from another XCD is read afresh.
-    if ((it & 63u) == 63u) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
-  v0 = v1 = 0.0f;
-  return false;
-}
-
-template <int E, int NIN, int Q1, int Q2, int VPT>
-__global__ void __launch_bounds__(1024) split_kernel(const SplitArgs p) {
-  static_assert(VPT == 1 || VPT == 2, "split kernel holds at most 16 columns per thread");
-  constexpr bool kTwo = Q2 != kQNone;
-  constexpr int kQ2 = kTwo ? Q2 : kQInt8;
-  const Args& a = p.a;
-  const int tid = threadIdx.x;
-  const int bs = blockDim.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int nwaves = bs >> 6;
-  const int S = p.splits;
-
-  // blockIdx -> (xcd, row group, split); rows xcd + 8*group, then + stride
+__device__ __forceinline__ Place place_of(const SplitArgs& p) {
   const int b = blockIdx.x;
-  const int xcd = b % kXcds;
   const int q = b / kXcds;
-  const int s = q % S;
-  const int group = q / S;
-  const int64_t row_stride = (int64_t)kXcds * p.row_groups;
+  Place r;
+  r.s = q % p.splits;
+  r.local = (q / p.splits) * kXcds + b % kXcds;
+  r.valid = r.local < p.rows;
+  return r;
+}
 
-  const uint32_t n = (uint32_t)a.n;
-  const uint32_t nvec = n >> 3;
-  const uint32_t v0 = (uint32_t)s * (uint32_t)p.chunk;  // first vector of this split
+// Chunk s of a row: vectors [v0, vend) of the row's n / 8.
+struct Chunk {
+  uint32_t v0;
+  uint32_t nv;  // vectors in the chunk (the last one may be short)
+};
+
+__device__ __forceinline__ Chunk chunk_of(const SplitArgs& p, int s) {
+  const uint32_t nvec = (uint32_t)p.a.n >> 3;
+  const uint32_t v0 = (uint32_t)s * (uint32_t)p.chunk;
   const uint32_t vend = v0 + (uint32_t)p.chunk < nvec ? v0 + (uint32_t)p.chunk : nvec;
-  const uint32_t chunk_bytes16 = (vend - v0) * 16u;  // bytes of 16-bit data in this split
-  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
-  const u32x4 one4 = u32x4{kOnePair<E>, kOnePair<E>, kOnePair<E>, kOnePair<E>};
+  return Chunk{v0, vend - v0};
+}
 
-  __shared__ float red_a[16], red_b[2][16];
-  __shared__ float bcast[2];
-  __shared__ int failed;
-  if (tid == 0) failed = 0;
+// Descriptor over the chunk's bytes of a row of 16-bit data (or of the
+// parameter vectors when row_bytes == 0): vectors past the chunk read 0 and
+// their stores are dropped.
+__device__ __forceinline__ rsrc_t chunk_rsrc(const void* base, int64_t row, uint32_t row_bytes,
+                                            Chunk c, uint32_t vbytes) {
+  return make_rsrc(static_cast<const char*>(base) + row * (int64_t)row_bytes +
+                       (size_t)c.v0 * vbytes,
+                   c.nv * vbytes);
+}
 
-  uint32_t vj[VPT];  // vector index within this split's chunk
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) vj[k] = (uint32_t)(tid + k * bs);
-
-  auto param_rsrc = [&](const void* base) {
-    return make_rsrc(static_cast<const char*>(base) + (size_t)v0 * 16u, chunk_bytes16);
-  };
-  u32x4 pg[VPT], pb[VPT], p1[VPT], p2[VPT];
+// Raw x1 / x2 vectors of this thread in a chunk (vector tid + k * block).
+template <int NIN, int VPT>
+__device__ __forceinline__ void load_x(const Args& a, int64_t row, Chunk c,
+                                       const uint32_t (&vj)[VPT], u32x4 (&c1)[VPT],
+                                       u32x4 (&c2)[VPT]) {
+  const uint32_t row_bytes = (uint32_t)a.n * 2u;
+  const rsrc_t r1 = chunk_rsrc(a.x1, row, row_bytes, c, 16u);
+  const rsrc_t r2 = chunk_rsrc(NIN == 2 ? a.x2 : a.x1, row, row_bytes, c, 16u);
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    pg[k] = __builtin_amdgcn_raw_buffer_load_b128(param_rsrc(a.gamma), vj[k] * 16u, 0, 0);
-    pb[k] = a.beta ? __builtin_amdgcn_raw_buffer_load_b128(param_rsrc(a.beta), vj[k] * 16u, 0, 0)
-                   : zero4;
-    // smooth absent: 1 inside the chunk, 0 past its end
-    p1[k] = a.smooth1
-                ? __builtin_amdgcn_raw_buffer_load_b128(param_rsrc(a.smooth1), vj[k] * 16u, 0, 0)
-                : (v0 + vj[k] < vend ? one4 : zero4);
-    p2[k] = !kTwo ? zero4
-            : a.smooth2
-                ? __builtin_amdgcn_raw_buffer_load_b128(param_rsrc(a.smooth2), vj[k] * 16u, 0, 0)
-                : (v0 + vj[k] < vend ? one4 : zero4);
+    c1[k] = __builtin_amdgcn_raw_buffer_load_b128(r1, vj[k] * 16u, 0, 0);
+    if constexpr (NIN == 2) c2[k] = __builtin_amdgcn_raw_buffer_load_b128(r2, vj[k] * 16u, 0, 0);
   }
+}
 
-  // the next row's chunk is requested before this row's exchanges, so its
-  // loads are in flight while the workgroup waits for the other splits
-  const uint32_t row_bytes = n * 2u;
-  u32x4 n1[VPT], n2[VPT];
-  auto load_row = [&](int64_t r) {
-    const rsrc_t r1 = make_rsrc(
-        static_cast<const char*>(row_ptr(a.x1, r, row_bytes)) + (size_t)v0 * 16u, chunk_bytes16);
-    const rsrc_t r2 = make_rsrc(
-        static_cast<const char*>(row_ptr(a.x2, r, row_bytes)) + (size_t)v0 * 16u, chunk_bytes16);
+// x = x1 + x2 (fp32) of one raw vector pair.
+template <int E, int NIN>
+__device__ __forceinline__ void xvec(const u32x4& r1, const u32x4& r2, float (&x)[8]) {
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      n1[k] = __builtin_amdgcn_raw_buffer_load_b128(r1, vj[k] * 16u, 0, kStreamLoad);
-      if constexpr (NIN == 2)
-        n2[k] = __builtin_amdgcn_raw_buffer_load_b128(r2, vj[k] * 16u, 0, kStreamLoad);
-    }
+  for (int w = 0; w < 4; ++w) {
+    f32x2 v = widen2<E>(r1[w]);
+    if constexpr (NIN == 2) v += widen2<E>(r2[w]);
+    x[2 * w] = v.x;
+    x[2 * w + 1] = v.y;
+  }
+}
+
+// Parameter vectors of a chunk (gamma, beta, smooth1, smooth2 as 16-bit
+// pairs; an absent beta reads 0, an absent smooth scale 1).
+template <int VPT>
+struct Params {
+  u32x4 g[VPT], b[VPT], s1[VPT], s2[VPT];
+};
+
+template <int E, bool TWO, int VPT>
+__device__ __forceinline__ void load_params(const Args& a, Chunk c, const uint32_t (&vj)[VPT],
+                                            Params<VPT>& pr) {
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  const u32x4 one4 = u32x4{kOnePair<E>, kOnePair<E>, kOnePair<E>, kOnePair<E>};
+  auto ld = [&](const void* base, int k, u32x4 absent) -> u32x4 {
+    if (!base) return absent;
+    return __builtin_amdgcn_raw_buffer_load_b128(chunk_rsrc(base, 0, 0u, c, 16u), vj[k] * 16u,
+                                                 0, 0);
   };
-  const int64_t row0 = (int64_t)group * kXcds + xcd;
-  if (row0 < a.rows) load_row(row0);
-  for (int64_t row = row0; row < a.rows; row += row_stride) {
-    u32x4 c1[VPT], c2[VPT];
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      c1[k] = n1[k];
-      if constexpr (NIN == 2) c2[k] = n2[k];
-    }
-    if (row + row_stride < a.rows) load_row(row + row_stride);
+  for (int k = 0; k < VPT; ++k) {
+    pr.g[k] = ld(a.gamma, k, zero4);
+    pr.b[k] = ld(a.beta, k, zero4);
+    pr.s1[k] = ld(a.smooth1, k, one4);
+    pr.s2[k] = TWO ? ld(a.smooth2, k, one4) : zero4;
+  }
+}
 
-    // ---- A
-    float x[VPT][8];
-    float ss = 0.0f;
-    const rsrc_t rxo = make_rsrc(
-        static_cast<char*>(row_ptr(a.x_out, row, row_bytes)) + (size_t)v0 * 16u, chunk_bytes16);
+// Quantizer inputs of one vector: y = fma(x * rinv, gamma, beta),
+// input_k = y * smooth_k.  The same operations as in the row kernel.
+template <int E, bool TWO>
+__device__ __forceinline__ void inputs_of(const float (&x)[8], float rinv, const u32x4& g,
+                                          const u32x4& b, const u32x4& s1, const u32x4& s2,
+                                          float (&i1)[8], float (&i2)[8]) {
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        f32x2 v = widen2<E>(c1[k][w]);
-        if constexpr (NIN == 2) v += widen2<E>(c2[k][w]);
-        x[k][2 * w] = v.x;
-        x[k][2 * w + 1] = v.y;
-        acc = __builtin_fmaf(v.x, v.x, acc);
-        acc = __builtin_fmaf(v.y, v.y, acc);
-      }
-      ss += acc;
-      if constexpr (NIN == 2) {
-        __builtin_amdgcn_raw_buffer_store_b128(
-            u32x4{narrow2<E>(x[k][0], x[k][1]), narrow2<E>(x[k][2], x[k][3]),
-                  narrow2<E>(x[k][4], x[k][5]), narrow2<E>(x[k][6], x[k][7])},
-            rxo, vj[k] * 16u, 0, kStreamStore);
-      }
+  for (int w = 0; w < 4; ++w) {
+    const f32x2 gg = widen2<E>(g[w]), bb = widen2<E>(b[w]), t1 = widen2<E>(s1[w]);
+    const float y0 = __builtin_fmaf(x[2 * w] * rinv, gg.x, bb.x);
+    const float y1 = __builtin_fmaf(x[2 * w + 1] * rinv, gg.y, bb.y);
+    i1[2 * w] = y0 * t1.x;
+    i1[2 * w + 1] = y1 * t1.y;
+    if constexpr (TWO) {
+      const f32x2 t2 = widen2<E>(s2[w]);
+      i2[2 * w] = y0 * t2.x;
+      i2[2 * w + 1] = y1 * t2.y;
     }
-    ss = wave_sum(ss);
-    if (lane == 0) red_a[wave] = ss;
-    __syncthreads();
-    if (wave == 0) {
-      if (lane == 0) {
-        float part = 0.0f;
-        for (int w = 0; w < nwaves; ++w) part += red_a[w];
-        publish(slot_ptr(p, row, s, 0), p.epoch, part, part);
-      }
-      float mine = 0.0f, dup = 0.0f;
-      const bool ok = collect(p, row, 0, lane, mine, dup);
-      float tot = 0.0f;  // in split order, the same bits in every workgroup of the row
-      for (int t = 0; t < S; ++t) tot += lane_value(mine, t);
-      if (lane == 0) {
-        bcast[0] = tot;
-        if (!ok) failed = 1;
-      }
-    }
-    __syncthreads();
-    const float rinv = __builtin_amdgcn_rsqf(__builtin_fmaf(bcast[0], a.inv_n, a.eps));
+  }
+}
 
-    // ---- B
-    float in1[VPT][8], in2[VPT][8];
-    float m1 = 0.0f, m2 = 0.0f;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const f32x2 g = widen2<E>(pg[k][w]), bb = widen2<E>(pb[k][w]);
-        const f32x2 s1 = widen2<E>(p1[k][w]);
-        const float y0 = __builtin_fmaf(x[k][2 * w] * rinv, g.x, bb.x);
-        const float y1 = __builtin_fmaf(x[k][2 * w + 1] * rinv, g.y, bb.y);
-        in1[k][2 * w] = y0 * s1.x;
-        in1[k][2 * w + 1] = y1 * s1.y;
-        m1 = fmaxf(m1, fmaxf(fabsf(in1[k][2 * w]), fabsf(in1[k][2 * w + 1])));
-        if constexpr (kTwo) {
-          const f32x2 s2 = widen2<E>(p2[k][w]);
-          in2[k][2 * w] = y0 * s2.x;
-          in2[k][2 * w + 1] = y1 * s2.y;
-          m2 = fmaxf(m2, fmaxf(fabsf(in2[k][2 * w]), fabsf(in2[k][2 * w + 1])));
-        }
-      }
-    }
-    m1 = wave_max(m1);
-    if constexpr (kTwo) m2 = wave_max(m2);
-    if (lane == 0) red_b[0][wave] = m1, red_b[1][wave] = m2;
-    __syncthreads();
-    if (wave == 0) {
-      if (lane == 0) {
-        float pm1 = 0.0f, pm2 = 0.0f;
-        for (int w = 0; w < nwaves; ++w) pm1 = fmaxf(pm1, red_b[0][w]), pm2 = fmaxf(pm2, red_b[1][w]);
-        publish(slot_ptr(p, row, s, 1), p.epoch, pm1, pm2);
-      }
-      float q1 = 0.0f, q2 = 0.0f;
-      const bool ok = collect(p, row, 1, lane, q1, q2);
-      q1 = wave_max(q1);  // lanes >= S hold 0; maxima are >= 0
-      q2 = wave_max(q2);
-      if (lane == 0) {
-        bcast[0] = q1;
-        bcast[1] = q2;
-        if (!ok) failed = 1;
-      }
-    }
-    __syncthreads();
-    const float M1 = bcast[0], M2 = bcast[1];
+// Workgroup sum in a fixed order (DPP + readlane per wave, waves in order).
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  v = wave_sum(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.0f;
+  for (int w = 0; w < nwaves; ++w) t += red[w];
+  return t;
+}
 
-    // ---- C
-    const RowScale rs1 = row_scale<Q1>(M1);
-    const RowScale rs2 = row_scale<kQ2>(M2);
-    if (s == 0 && tid == 0) {
-      a.scale1[row] = rs1.scale;
-      if constexpr (kTwo) a.scale2[row] = rs2.scale;
+__device__ __forceinline__ float block_max(float v, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  v = wave_max(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.0f;
+  for (int w = 0; w < nwaves; ++w) t = fmaxf(t, red[w]);
+  return t;
+}
+
+// 1 / Rms of a row from its S partial sums, added in split order (the same
+// bits in every workgroup of the row and in every kernel).
+__device__ __forceinline__ float row_rinv(const SplitArgs& p, int32_t local, float* bcast) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    const int S = p.splits;
+    float tot = 0.0f;
+    for (int t0 = 0; t0 < S; t0 += 64) {
+      const float v = t0 + lane < S ? p.ss[(int64_t)local * S + t0 + lane] : 0.0f;
+      const int cnt = S - t0 < 64 ? S - t0 : 64;
+      for (int t = 0; t < cnt; ++t) tot += lane_value(v, t);
     }
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      apply_boost(in1[k], rs1);
-      if constexpr (kTwo) apply_boost(in2[k], rs2);
-    }
-    auto codes = [&](const float (&in)[8], float inv, void* out, auto qtag) {
-      constexpr int Q = decltype(qtag)::value;
-      uint32_t c[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = code_bits(in[e], inv);
-      return Q == kQInt8 ? pack_int8x8(c) : u32x2{pack_int4x8(c), 0u};
-    };
-    {
-      const uint32_t ybytes = Q1 == kQInt4 ? n / 2u : n;
-      const uint32_t vb = Q1 == kQInt4 ? 4u : 8u;  // bytes per vector
-      const rsrc_t ry = make_rsrc(static_cast<char*>(row_ptr(a.y1, row, ybytes)) + (size_t)v0 * vb,
-                                  (vend - v0) * vb);
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const u32x2 c = codes(in1[k], rs1.inv, a.y1, std::integral_constant<int, Q1>{});
-        if constexpr (Q1 == kQInt8)
-          __builtin_amdgcn_raw_buffer_store_b64(c, ry, vj[k] * 8u, 0, kStreamStore);
-        else
-          __builtin_amdgcn_raw_buffer_store_b32(c.x, ry, vj[k] * 4u, 0, kStreamStore);
-      }
-    }
-    if constexpr (kTwo) {
-      const uint32_t ybytes = kQ2 == kQInt4 ? n / 2u : n;
-      const uint32_t vb = kQ2 == kQInt4 ? 4u : 8u;
-      const rsrc_t ry = make_rsrc(static_cast<char*>(row_ptr(a.y2, row, ybytes)) + (size_t)v0 * vb,
-                                  (vend - v0) * vb);
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const u32x2 c = codes(in2[k], rs2.inv, a.y2, std::integral_constant<int, kQ2>{});
-        if constexpr (kQ2 == kQInt8)
-          __builtin_amdgcn_raw_buffer_store_b64(c, ry, vj[k] * 8u, 0, kStreamStore);
-        else
-          __builtin_amdgcn_raw_buffer_store_b32(c.x, ry, vj[k] * 4u, 0, kStreamStore);
-      }
-    }
+    if (lane == 0) *bcast = tot;
   }
   __syncthreads();
-  if (tid == 0 && failed)
-    __hip_atomic_store(p.ws, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_amdgcn_rsqf(__builtin_fmaf(*bcast, p.a.inv_n, p.a.eps));
 }
+
+// ---- K1: xOut and partial sums of squares
+
+template <int E, int NIN, int VPT>
+__global__ void __launch_bounds__(1024) split_sumsq_kernel(const SplitArgs p) {
+  const Place pl = place_of(p);
+  if (!pl.valid) return;  // the whole workgroup
+  __shared__ float red[16];
+  const Args& a = p.a;
+  const int64_t row = p.row0 + pl.local;
+  const Chunk c = chunk_of(p, pl.s);
+  uint32_t vj[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) vj[k] = threadIdx.x + k * blockDim.x;
+  u32x4 c1[VPT], c2[VPT];
+  load_x<NIN, VPT>(a, row, c, vj, c1, c2);
+  const rsrc_t rxo = chunk_rsrc(a.x_out, row, (uint32_t)a.n * 2u, c, 16u);
+  float ss = 0.0f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    float x[8];
+    xvec<E, NIN>(c1[k], c2[k], x);
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(x[e], x[e], acc);
+    ss += acc;
+    if constexpr (NIN == 2) {
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{narrow2<E>(x[0], x[1]), narrow2<E>(x[2], x[3]), narrow2<E>(x[4], x[5]),
+                narrow2<E>(x[6], x[7])},
+          rxo, vj[k] * 16u, 0, kStreamStore);
+    }
+  }
+  ss = block_sum(ss, red);
+  if (threadIdx.x == 0) p.ss[(int64_t)pl.local * p.splits + pl.s] = ss;
+}
+
+// ---- K2: partial row maxima
+
+template <int E, int NIN, bool TWO, int VPT>
+__global__ void __launch_bounds__(1024) split_max_kernel(const SplitArgs p) {
+  const Place pl = place_of(p);
+  if (!pl.valid) return;
+  __shared__ float red[2][16];
+  __shared__ float bcast;
+  const Args& a = p.a;
+  const int64_t row = p.row0 + pl.local;
+  const Chunk c = chunk_of(p, pl.s);
+  uint32_t vj[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) vj[k] = threadIdx.x + k * blockDim.x;
+  u32x4 c1[VPT], c2[VPT];
+  load_x<NIN, VPT>(a, row, c, vj, c1, c2);
+  Params<VPT> pr;
+  load_params<E, TWO, VPT>(a, c, vj, pr);
+  const float rinv = row_rinv(p, pl.local, &bcast);
+  float m1 = 0.0f, m2 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    float x[8], i1[8], i2[8];
+    xvec<E, NIN>(c1[k], c2[k], x);
+    inputs_of<E, TWO>(x, rinv, pr.g[k], pr.b[k], pr.s1[k], pr.s2[k], i1, i2);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      m1 = fmaxf(m1, fabsf(i1[e]));
+      if constexpr (TWO) m2 = fmaxf(m2, fabsf(i2[e]));
+    }
+  }
+  m1 = block_max(m1, red[0]);
+  if constexpr (TWO) m2 = block_max(m2, red[1]);
+  if (threadIdx.x == 0) {
+    float* slot = p.mx + ((int64_t)pl.local * p.splits + pl.s) * 2;
+    slot[0] = m1;
+    slot[1] = m2;
+  }
+}
+
+// ---- K3: scales and codes
+
+template <int Q>
+__device__ __forceinline__ void store_chunk_codes(const float (&in)[8], float inv, rsrc_t out,
+                                                  uint32_t j) {
+  uint32_t q[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q[e] = code_bits(in[e], inv);
+  if constexpr (Q == kQInt8)
+    __builtin_amdgcn_raw_buffer_store_b64(pack_int8x8(q), out, j * 8u, 0, kStreamStore);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(pack_int4x8(q), out, j * 4u, 0, kStreamStore);
+}
+
+// Row maxima over the whole row, taken by one workgroup (two-launch form):
+// each thread covers vectors tid, tid + block, ... of the row, two at a
+// time with all their loads in flight.  Which thread takes which vector does
+// not matter: each input is computed by the same operations wherever it is
+// computed, and a maximum is exact in any order.
+template <int E, int NIN, bool TWO>
+__device__ __forceinline__ void whole_row_max(const Args& a, int64_t row, float rinv, float& m1,
+                                              float& m2) {
+  const uint32_t nvec = (uint32_t)a.n >> 3;
+  const Chunk all{0u, nvec};
+  const uint32_t bs = blockDim.x;
+  for (uint32_t base = 0; base < nvec; base += 2 * bs) {
+    const uint32_t vj[2] = {base + threadIdx.x, base + bs + threadIdx.x};
+    u32x4 c1[2], c2[2];
+    load_x<NIN, 2>(a, row, all, vj, c1, c2);
+    Params<2> pr;
+    load_params<E, TWO, 2>(a, all, vj, pr);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      float x[8], i1[8], i2[8];
+      xvec<E, NIN>(c1[k], c2[k], x);
+      inputs_of<E, TWO>(x, rinv, pr.g[k], pr.b[k], pr.s1[k], pr.s2[k], i1, i2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        m1 = fmaxf(m1, fabsf(i1[e]));
+        if constexpr (TWO) m2 = fmaxf(m2, fabsf(i2[e]));
+      }
+    }
+  }
+}
+
+template <int E, int NIN, int Q1, int Q2, int VPT, bool WHOLE>
+__global__ void __launch_bounds__(1024) split_quant_kernel(const SplitArgs p) {
+  constexpr bool kTwo = Q2 != kQNone;
+  constexpr int kQ2 = kTwo ? Q2 : kQInt8;
+  const Place pl = place_of(p);
+  if (!pl.valid) return;
+  __shared__ float red[2][16];
+  __shared__ float bcast;
+  const Args& a = p.a;
+  const int64_t row = p.row0 + pl.local;
+  const Chunk c = chunk_of(p, pl.s);
+  uint32_t vj[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) vj[k] = threadIdx.x + k * blockDim.x;
+  u32x4 c1[VPT], c2[VPT];
+  load_x<NIN, VPT>(a, row, c, vj, c1, c2);
+  Params<VPT> pr;
+  load_params<E, kTwo, VPT>(a, c, vj, pr);
+  const float rinv = row_rinv(p, pl.local, &bcast);
+
+  float M1 = 0.0f, M2 = 0.0f;
+  if constexpr (WHOLE) {
+    whole_row_max<E, NIN, kTwo>(a, row, rinv, M1, M2);
+    M1 = block_max(M1, red[0]);
+    if constexpr (kTwo) M2 = block_max(M2, red[1]);
+  } else {
+    // the S partial maxima of the row, read by wave 0 and reduced in it
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const float* mx = p.mx + (int64_t)pl.local * p.splits * 2;
+      for (int t = lane; t < p.splits; t += 64) {
+        M1 = fmaxf(M1, mx[2 * t]);
+        if constexpr (kTwo) M2 = fmaxf(M2, mx[2 * t + 1]);
+      }
+      M1 = wave_max(M1);
+      M2 = wave_max(M2);
+      if (lane == 0) red[0][0] = M1, red[1][0] = M2;
+    }
+    __syncthreads();
+    M1 = red[0][0];
+    M2 = red[1][0];
+  }
+
+  const RowScale r1 = row_scale<Q1>(M1);
+  const RowScale r2 = row_scale<kQ2>(M2);
+  if (pl.s == 0 && threadIdx.x == 0) {
+    a.scale1[row] = r1.scale;
+    if constexpr (kTwo) a.scale2[row] = r2.scale;
+  }
+  const uint32_t n = (uint32_t)a.n;
+  const rsrc_t ry1 = chunk_rsrc(a.y1, row, Q1 == kQInt4 ? n / 2u : n, c, Q1 == kQInt4 ? 4u : 8u);
+  const rsrc_t ry2 = kTwo ? chunk_rsrc(a.y2, row, kQ2 == kQInt4 ? n / 2u : n, c,
+                                       kQ2 == kQInt4 ? 4u : 8u)
+                          : make_rsrc(a.y1, 0u);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    float x[8], i1[8], i2[8];
+    xvec<E, NIN>(c1[k], c2[k], x);
+    inputs_of<E, kTwo>(x, rinv, pr.g[k], pr.b[k], pr.s1[k], pr.s2[k], i1, i2);
+    apply_boost(i1, r1);
+    store_chunk_codes<Q1>(i1, r1.inv, ry1, vj[k]);
+    if constexpr (kTwo) {
+      apply_boost(i2, r2);
+      store_chunk_codes<kQ2>(i2, r2.inv, ry2, vj[k]);
+    }
+  }
+}
+
+// ---- launch tables
 
 template <int E, int NIN, int Q1, int Q2, int VPT>
 struct SplitInst {
-  static hipError_t launch(int block, int grid, const SplitArgs& p, hipStream_t s) {
-    void* args[] = {const_cast<SplitArgs*>(&p)};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&split_kernel<E, NIN, Q1, Q2, VPT>),
-                                      dim3(grid), dim3(block), args, 0, s);
-  }
-  static int occupancy(int block) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split_kernel<E, NIN, Q1, Q2, VPT>, block,
-                                                     0) != hipSuccess)
-      return 0;
-    return n;
+  static constexpr bool kTwo = Q2 != kQNone;
+  static hipError_t launch(int block, int grid, int launches, const SplitArgs& p,
+                           hipStream_t s) {
+    hipLaunchKernelGGL((split_sumsq_kernel<E, NIN, VPT>), dim3(grid), dim3(block), 0, s, p);
+    if (launches == 3) {
+      hipLaunchKernelGGL((split_max_kernel<E, NIN, kTwo, VPT>), dim3(grid), dim3(block), 0, s, p);
+      hipLaunchKernelGGL((split_quant_kernel<E, NIN, Q1, Q2, VPT, false>), dim3(grid),
+                         dim3(block), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((split_quant_kernel<E, NIN, Q1, Q2, VPT, true>), dim3(grid),
+                         dim3(block), 0, s, p);
+    }
+    return hipGetLastError();
   }
 };
 
@@ -366,38 +444,46 @@ bool dispatch(int nin, int q1, int q2, int vpt, F&& f) {
   return false;
 }
 
-template <typename F>
-bool dispatch_any(const Variant& v, int vpt, F&& f) {
-  return v.elem == kBF16 ? dispatch<kBF16>(v.nin, v.q1, v.q2, vpt, f)
-                         : dispatch<kF16>(v.nin, v.q1, v.q2, vpt, f);
-}
-
 }  // namespace
 
-uint64_t split_workspace_bytes(int64_t rows, int splits) {
-  return 32u + (uint64_t)rows * (uint64_t)splits * 32u;
+uint64_t split_workspace_bytes(int64_t batch_rows, int splits, int launches) {
+  const uint64_t slots = (uint64_t)batch_rows * (uint64_t)splits;
+  const uint64_t ss = (slots * 4u + 255u) / 256u * 256u;
+  return ss + (launches == 3 ? slots * 8u : 0u);
 }
 
-int split_max_blocks_per_cu(const Variant& v, int vpt, int block) {
-  int occ = 0;
-  dispatch_any(v, vpt, [&]<typename I>() { occ = I::occupancy(block); });
-  return occ;
+int64_t split_grid(int64_t batch_rows, int splits) {
+  return (batch_rows + kXcds - 1) / kXcds * kXcds * splits;
 }
 
-hipError_t launch_split(const Variant& v, int vpt, int block, int splits, int row_groups,
-                        const Args& a, void* ws, uint64_t epoch, hipStream_t stream) {
-  if (splits < 1 || splits > 64 || row_groups < 1 || block < 64 || block > 1024 || block % 64)
+hipError_t launch_split(const Variant& v, int vpt, int block, int splits, int launches,
+                        int64_t batch_rows, const Args& a, void* ws, hipStream_t stream) {
+  if (splits < 1 || batch_rows < 1 || block < 64 || block > 1024 || block % 64 ||
+      (launches != 2 && launches != 3) || (vpt != 1 && vpt != 2) ||
+      (int64_t)splits * block * vpt < a.n / 8 || split_grid(batch_rows, splits) > INT32_MAX)
     return hipErrorInvalidValue;
   SplitArgs p;
   p.a = a;
-  p.ws = static_cast<uint64_t*>(ws);
-  p.epoch = epoch;
+  p.ss = static_cast<float*>(ws);
+  p.mx = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                  split_workspace_bytes(batch_rows, splits, 2));
   p.splits = splits;
   p.chunk = block * vpt;
-  p.row_groups = row_groups;
-  const int grid = kXcds * row_groups * splits;
-  hipError_t err = hipErrorInvalidValue;
-  dispatch_any(v, vpt, [&]<typename I>() { err = I::launch(block, grid, p, stream); });
+  hipError_t err = hipSuccess;
+  for (int64_t r0 = 0; r0 < a.rows && err == hipSuccess; r0 += batch_rows) {
+    const int64_t rows = a.rows - r0 < batch_rows ? a.rows - r0 : batch_rows;
+    p.row0 = r0;
+    p.rows = (int32_t)rows;
+    const int grid = (int)split_grid(rows, splits);
+    bool found = false;
+    auto go = [&]<typename I>() {
+      found = true;
+      err = I::launch(block, grid, launches, p, stream);
+    };
+    if (v.elem == kBF16) dispatch<kBF16>(v.nin, v.q1, v.q2, vpt, go);
+    else dispatch<kF16>(v.nin, v.q1, v.q2, vpt, go);
+    if (!found) err = hipErrorInvalidValue;
+  }
   return err;
 }
 

@@ -16,10 +16,10 @@
  * Uniform:  u = (d >> 11) * 2^-53  in [0, 1).
  * Normal:   Box-Muller (cosine branch) on draws 2i and 2i+1, computed in
  *           double: z = sqrt(-2 ln(1 - u0)) * cos(2 pi u1).
- * Storage:  each double value (after any outlier factor) is converted to
- *           float by the C cast (round to nearest even) and from float to
- *           the 16-bit storage type by integer round-to-nearest-even.
- *           Only the stored 16-bit patterns matter to the consumers.
+ * Storage:  each double value (after any outlier factor) is rounded once,
+ *           directly to the 16-bit storage type, to nearest with ties to
+ *           even (no intermediate float).  Only the stored 16-bit patterns
+ *           matter to the consumers.
  *
  * Build:  gcc -O2 -fPIC -shared -pthread synth_gen.c -o libsynth_gen.so -lm
  */
@@ -53,45 +53,57 @@ static inline double unit_double(uint64_t d) {
   return (double)(d >> 11) * (1.0 / 9007199254740992.0);
 }
 
-/* float -> bfloat16 bits, round to nearest even (inputs here are finite). */
-static uint16_t float_to_bf16_bits(float f) {
+/*
+ * Round a finite double to the nearest value of a binary format with
+ * `digits` significant bits, smallest normal exponent `emin` (the format's
+ * normal values lie in [2^emin, 2^(emax+1))) and largest finite value
+ * `maxval`; ties to even (nearbyint under the default rounding mode).  The
+ * value is cut at the format's spacing at |v| (2^(e - digits + 1) for
+ * |v| in [2^e, 2^(e+1)), or the subnormal spacing 2^(emin - digits + 1)),
+ * scaled to an integer count of that spacing, rounded, and scaled back:
+ * every step but the rounding is exact.  Values that round beyond maxval
+ * become infinite.
+ */
+static double round_to_format(double v, int digits, int emin, double maxval) {
+  if (v == 0.0) return v;
+  int e;
+  (void)frexp(v, &e); /* |v| in [2^(e-1), 2^e) */
+  int exp = e - 1;
+  if (exp < emin) exp = emin;
+  const double spacing = ldexp(1.0, exp - digits + 1);
+  const double r = nearbyint(v / spacing) * spacing;
+  if (fabs(r) > maxval) return r > 0 ? INFINITY : -INFINITY;
+  return r;
+}
+
+/* Bits of a float that is exactly a bfloat16 value (top half). */
+static uint16_t bf16_bits_exact(float f) {
   uint32_t u;
   memcpy(&u, &f, 4);
-  uint32_t lsb = (u >> 16) & 1u;
-  u += 0x7FFFu + lsb;
   return (uint16_t)(u >> 16);
 }
 
-/* float -> IEEE binary16 bits, round to nearest even, overflow to inf. */
-static uint16_t float_to_f16_bits(float f) {
+/* Bits of a float that is exactly a binary16 value (or infinite). */
+static uint16_t f16_bits_exact(float f) {
   uint32_t u;
   memcpy(&u, &f, 4);
-  uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
-  uint32_t exp = (u >> 23) & 0xFFu;
-  uint32_t man = u & 0x7FFFFFu;
-  if (exp == 0xFFu) return (uint16_t)(sign | 0x7C00u | (man ? 0x200u : 0u));
-  int e = (int)exp - 127 + 15;
-  if (e >= 31) return (uint16_t)(sign | 0x7C00u);
-  if (e <= 0) {
-    /* subnormal or zero in binary16: value = m * 2^-24 */
-    if (e < -10) return sign;
-    uint32_t m = man | 0x800000u;
-    int shift = 14 - e; /* 24-bit significand down to (11 - (1 - e)) bits */
-    uint32_t q = m >> shift;
-    uint32_t rem = m & ((1u << shift) - 1u);
-    uint32_t half = 1u << (shift - 1);
-    if (rem > half || (rem == half && (q & 1u))) q++;
-    return (uint16_t)(sign | q);
-  }
-  uint32_t q = ((uint32_t)e << 10) | (man >> 13);
-  uint32_t rem = man & 0x1FFFu;
-  if (rem > 0x1000u || (rem == 0x1000u && (q & 1u))) q++; /* carry may reach inf: correct */
-  return (uint16_t)(sign | q);
+  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  const uint32_t exp = (u >> 23) & 0xFFu;
+  const uint32_t man = u & 0x7FFFFFu;
+  if (exp == 0xFFu) return (uint16_t)(sign | 0x7C00u);
+  if (exp == 0 && man == 0) return sign;
+  const int e = (int)exp - 127;
+  if (e < -14) /* subnormal binary16: value = q * 2^-24 */
+    return (uint16_t)(sign | (uint32_t)ldexp(fabs((double)f), 24));
+  return (uint16_t)(sign | ((uint32_t)(e + 15) << 10) | (man >> 13));
 }
 
+/* bfloat16: 8 significant bits, normals from 2^-126, largest (2 - 2^-7) 2^127.
+ * binary16: 11 significant bits, normals from 2^-14, largest 65504. */
 static inline uint16_t to_storage(double v, int dtype) {
-  float f = (float)v;
-  return dtype == SYNTH_BF16 ? float_to_bf16_bits(f) : float_to_f16_bits(f);
+  if (dtype == SYNTH_BF16)
+    return bf16_bits_exact((float)round_to_format(v, 8, -126, 0x1.FEp127));
+  return f16_bits_exact((float)round_to_format(v, 11, -14, 65504.0));
 }
 
 static inline double sample(uint64_t base, uint64_t idx, int dist, double p0, double p1) {

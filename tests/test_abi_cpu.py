@@ -44,7 +44,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert set(names) == set(adq.EXPORTED)
     for name in names:
         assert hasattr(adq.lib, name), name
@@ -112,6 +112,22 @@ def test_mask_truth_table_through_phase_one():
                 assert st == adq.ERR_NULLPTR, (mask, has1, has2, k)
             else:
                 assert st in ACCEPTED, (mask, has1, has2, k, adq.last_error())
+
+
+@pytest.mark.parametrize("out,src", [("xo", "x1"), ("xo", "x2"), ("y1", "x1"), ("sc1", "gamma"),
+                                     ("y2", "s2"), ("y2", "y1"), ("sc2", "xo")])
+def test_outputs_sharing_memory_rejected(out, src):
+    """A produced output overlapping an input or another produced output
+    (same start, or a range that reaches into it) is rejected."""
+    for shift in (0, 3):
+        a = full_v2()
+        a[out].data = a[src].data + shift
+        assert v2_call(**a) == adq.ERR_PARAM_INVALID, (out, src, shift)
+        assert "share" in adq.last_error() and "memory" in adq.last_error()
+    # an output that is not produced may sit anywhere
+    a = full_v2(smooth=1)
+    a["y2"].data = a["x1"].data
+    assert v2_call(mask=(True, False), **a) in ACCEPTED
 
 
 @pytest.mark.parametrize("field", ["x1", "x2", "gamma", "xo"])

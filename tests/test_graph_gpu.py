@@ -5,8 +5,7 @@ capture them into a graph (torch.cuda.graph here) and replay it.  Each test
 captures one run, then replays it several times with new input values
 written in place between replays (eager work and synchronizations in
 between), and checks every replay bit for bit against an eager call on the
-same inputs.  The split-row path is left out: each of its launches needs a
-fresh tag for its exchange slots, and a replay would reuse the captured one.
+same inputs.
 """
 import numpy as np
 import pytest
@@ -68,6 +67,46 @@ def test_v2_replays_match_eager(m, n, dtype, y_types):
         assert previous is None or not np.array_equal(got[0], previous), "replay saw stale inputs"
         previous = got[0]
     ex.close()
+
+
+@pytest.mark.parametrize("launches", [2, 3])
+def test_v2_split_path_replays_match_eager(launches):
+    """The split-row path (decode shape 32 x 16384: several workgroups per
+    row, partial results handed over through the workspace between the
+    captured launches); the eager reference runs the same plan."""
+    m, n, dtype, y_types = 32, 16384, "bf16", ("int8", "int8")
+    w = synth.Workload("graph", "v2", m, n, dtype, 81, (True, True), True, 2)
+    g, b, s1, s2 = (dev(p, dtype) for p in synth.params(w))
+    x1, x2 = (dev(a, dtype) for a in synth.inputs(w))
+    ex, outs = adq.plan_add_rms_norm_dynamic_quant_v2(x1, x2, g, b, s1, s2, 1e-6, (True, True),
+                                                      y_types[0], y_types[1],
+                                                      path=adq.PATH_SPLIT)
+    ex.set_split(0, launches)
+    ref_ex, ref = adq.plan_add_rms_norm_dynamic_quant_v2(
+        x1, x2, g, b, s1, s2, 1e-6, (True, True), y_types[0], y_types[1], path=adq.PATH_SPLIT)
+    ref_ex.set_split(0, launches)
+    assert ex.describe() == ref_ex.describe() and f"launches={launches}" in ex.describe()
+    ws = torch.empty(ex.workspace_size, dtype=torch.uint8, device="cuda")
+    ref_ws = torch.empty(ex.workspace_size, dtype=torch.uint8, device="cuda")
+    graph = capture(lambda: ex.run(ws))
+    previous = None
+    for rep in range(REPLAYS):
+        n1, n2 = synth.inputs(w, seed=700 + rep)
+        x1.copy_(dev(n1, dtype))
+        x2.copy_(dev(n2, dtype))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [bits(outs[k]) for k in ("x_out", "y1", "y2", "scale1", "scale2")]
+        ref_ex.run(ref_ws)
+        torch.cuda.synchronize()
+        want = [bits(ref[k]) for k in ("x_out", "y1", "y2", "scale1", "scale2")]
+        for a_, b_ in zip(got, want):
+            assert np.array_equal(a_, b_), f"replay {rep} differs from the eager call"
+        assert previous is None or not np.array_equal(got[1], previous), "replay saw stale inputs"
+        previous = got[1]
+    ex.close()
+    ref_ex.close()
 
 
 def test_rms_norm_dq_replays_match_eager():

@@ -1,15 +1,16 @@
-"""GPU tests of the split-row path (several workgroups per row exchanging
-partial sums and maxima through the workspace), against the oracle."""
+"""GPU tests of the split-row path: S workgroups per row, each on a chunk,
+in two or three plain launches per batch of rows that hand the per-chunk
+partial sums of squares and maxima over through the workspace at kernel
+boundaries.  Compared with the oracle under the parity rules, through the
+C-ABI."""
 import numpy as np
 import pytest
 import torch
 
 import int4_dynamic_quantization_amd as adq
-import synth
-from gpu_helpers import (check_no_timeout, compare_v2, dev, host, host_bits, oracle_v2, run_rms,
-                         run_v2, workspace)
-from gpu_helpers import compare_rms
 import oracle
+import synth
+from gpu_helpers import compare_rms, compare_v2, dev, oracle_v2, run_rms, run_v2, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -20,6 +21,10 @@ def _gpu():
     yield
 
 
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
 def _inputs(m, n, dtype, seed, n_smooth=2):
     w = synth.Workload("split", "v2", m, n, dtype, seed, None, True, n_smooth)
     x1, x2 = synth.inputs(w)
@@ -27,36 +32,107 @@ def _inputs(m, n, dtype, seed, n_smooth=2):
     return x1, x2, g, b, s1, s2
 
 
+def _run_split(x1, x2, g, b, s1, s2, mask, y_types, dtype, splits=0, launches=0, ws_fill=None,
+               eps=1e-6):
+    ex, outs = adq.plan_add_rms_norm_dynamic_quant_v2(
+        dev(x1, dtype), dev(x2, dtype), dev(g, dtype), dev(b, dtype), dev(s1, dtype),
+        dev(s2, dtype), eps, mask, y_types[0], y_types[1], path=adq.PATH_SPLIT)
+    if splits or launches:
+        ex.set_split(splits, launches)
+    ws = workspace(ex, ws_fill)
+    ex.run(ws)
+    torch.cuda.synchronize()
+    desc = ex.describe()
+    ex.close()
+    return outs, desc
+
+
 SPLIT_SHAPES = [(1, 2048), (3, 4096), (32, 16384), (7, 16392), (5, 20000), (2, 65536),
-                (64, 8192), (257, 32768), (9, 8), (130, 1024)]
+                (64, 8192), (257, 32768), (9, 8), (130, 1024), (1, 262144), (3, 40008)]
 
 
+@pytest.mark.parametrize("launches", [2, 3])
 @pytest.mark.parametrize("m,n", SPLIT_SHAPES)
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-def test_split_path_parity(m, n, dtype):
-    print(f"\n[case] split {m}x{n} {dtype}", flush=True)
+def test_split_path_parity(m, n, dtype, launches):
+    _announce(f"split {m}x{n} {dtype} launches={launches}")
     y_types = ("int8", "int4")
     x1, x2, g, b, s1, s2 = _inputs(m, n, dtype, seed=300 + m + n)
-    outs, desc = run_v2(x1, x2, g, b, s1, s2, 1e-6, (True, True), y_types, dtype,
-                        path=adq.PATH_SPLIT)
-    assert "path=split" in desc, desc
+    outs, desc = _run_split(x1, x2, g, b, s1, s2, (True, True), y_types, dtype,
+                            launches=launches)
+    assert "path=split" in desc and f"launches={launches}" in desc, desc
     ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, (True, True), y_types, dtype)
     compare_v2(outs, ora, y_types)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 8, 64])
+def test_split_counts(splits):
+    """Explicit chunk counts on 9 x 32768 (4096 vectors per row): chunks of
+    2048, 1408 (ragged last chunk), 512 and 64 vectors."""
+    _announce(f"split 9x32768 bf16 splits={splits}")
+    x1, x2, g, b, s1, s2 = _inputs(9, 32768, "bf16", seed=31)
+    ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, None, ("int8", "int8"), "bf16")
+    for launches in (2, 3):
+        outs, desc = _run_split(x1, x2, g, b, s1, s2, None, ("int8", "int8"), "bf16",
+                                splits=splits, launches=launches)
+        assert f"splits={splits} " in desc, desc
+        compare_v2(outs, ora, ("int8", "int8"))
+
+
+def test_split_count_that_does_not_fit_is_rejected():
+    x1, x2, g, b, s1, s2 = _inputs(2, 32768, "bf16", seed=32)
+    ex, _ = adq.plan_add_rms_norm_dynamic_quant_v2(
+        dev(x1, "bf16"), dev(x2, "bf16"), dev(g, "bf16"), None, None, None, 1e-6, None)
+    before = ex.describe()
+    for splits, launches in ((1, 0), (0, 4), (-1, 2)):  # 1 chunk > 2048 vectors
+        with pytest.raises(adq.AdqError) as e:
+            ex.set_split(splits, launches)
+        assert e.value.status == adq.ERR_PARAM_INVALID
+        assert ex.describe() == before
+    ex.close()
+
+
+def test_launch_forms_agree_bit_for_bit():
+    """For one chunk count both launch forms quantize the same fp32 values
+    with the same scale, so every output is the same bits."""
+    x1, x2, g, b, s1, s2 = _inputs(40, 12288, "fp16", seed=33)
+    a, _ = _run_split(x1, x2, g, b, s1, s2, None, ("int8", "int4"), "fp16", splits=6,
+                      launches=2)
+    c, _ = _run_split(x1, x2, g, b, s1, s2, None, ("int8", "int4"), "fp16", splits=6,
+                      launches=3)
+    for k in ("x_out", "y1", "y2", "scale1", "scale2"):
+        assert torch.equal(a[k], c[k]), k
+
+
+def test_split_batches_of_rows():
+    """300 rows of 65536 bf16 columns: x1 and x2 take 256 KiB per row, so the
+    rows run as a batch of 256 and a batch of 44 (each batch's launches
+    before the next batch's), sharing one workspace."""
+    m, n = 300, 65536
+    _announce(f"split batches {m}x{n}")
+    x1, x2, g, b, s1, s2 = _inputs(m, n, "bf16", seed=34)
+    ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, None, ("int8", "int8"), "bf16")
+    for launches in (2, 3):
+        outs, desc = _run_split(x1, x2, g, b, s1, s2, None, ("int8", "int8"), "bf16",
+                                launches=launches)
+        assert "batch_rows=256 " in desc, desc
+        compare_v2(outs, ora, ("int8", "int8"))
 
 
 @pytest.mark.parametrize("fill", [None, 0x00, 0xFF, 0xA5])
 def test_split_workspace_contents_do_not_matter(fill):
     x1, x2, g, b, s1, s2 = _inputs(32, 16384, "bf16", seed=5)
     ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, None, ("int8", "int8"), "bf16")
-    outs, desc = run_v2(x1, x2, g, b, s1, s2, 1e-6, None, ("int8", "int8"), "bf16",
-                        path=adq.PATH_SPLIT, ws_fill=fill)
-    compare_v2(outs, ora, ("int8", "int8"))
+    for launches in (2, 3):
+        outs, desc = _run_split(x1, x2, g, b, s1, s2, None, ("int8", "int8"), "bf16",
+                                launches=launches, ws_fill=fill)
+        compare_v2(outs, ora, ("int8", "int8"))
 
 
 def test_split_reused_workspace_and_determinism():
     """Back-to-back launches on one workspace (which then holds the previous
-    launch's slots) give bitwise-identical results; new inputs in the same
-    buffers give the new results."""
+    launch's partial results) give bitwise-identical results; new inputs in
+    the same buffers give the new results."""
     x1, x2, g, b, s1, s2 = _inputs(16, 8192, "bf16", seed=6)
     d1, d2 = dev(x1, "bf16"), dev(x2, "bf16")
     ex, outs = adq.plan_add_rms_norm_dynamic_quant_v2(
@@ -65,12 +141,10 @@ def test_split_reused_workspace_and_determinism():
     ws = workspace(ex)
     ex.run(ws)
     torch.cuda.synchronize()
-    check_no_timeout(ex, ws)
     first = {k: v.clone() for k, v in outs.items() if v is not None}
     for _ in range(5):
         ex.run(ws)
     torch.cuda.synchronize()
-    check_no_timeout(ex, ws)
     for k, v in first.items():
         assert torch.equal(outs[k], v), k
     y1, y2, _, _, _, _ = _inputs(16, 8192, "bf16", seed=7)
@@ -78,7 +152,6 @@ def test_split_reused_workspace_and_determinism():
     d2.copy_(dev(y2, "bf16"))
     ex.run(ws)
     torch.cuda.synchronize()
-    check_no_timeout(ex, ws)
     ora = oracle_v2(y1, y2, g, b, s1, s2, 1e-6, None, ("int8", "int8"), "bf16")
     compare_v2(outs, ora, ("int8", "int8"))
     ex.close()
@@ -109,10 +182,28 @@ def test_split_output_options(mask, has1, has2):
     x1, x2, g, b, s1, s2 = _inputs(6, 4096, "bf16", seed=10)
     s1 = s1 if has1 else None
     s2 = s2 if has2 else None
-    outs, _ = run_v2(x1, x2, g, b, s1, s2, 1e-6, mask, ("int4", "int8"), "bf16",
-                     path=adq.PATH_SPLIT)
     ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, mask, ("int4", "int8"), "bf16")
-    compare_v2(outs, ora, ("int4", "int8"))
+    for launches in (2, 3):
+        outs, _ = _run_split(x1, x2, g, b, s1, s2, mask, ("int4", "int8"), "bf16",
+                             launches=launches)
+        compare_v2(outs, ora, ("int4", "int8"))
+
+
+@pytest.mark.parametrize("launches", [2, 3])
+def test_split_degenerate_rows(launches):
+    """gamma = beta = 0 (row maximum 0: scale 0, codes 0), and x = 0 with
+    epsilon = 0 (0/0 in the norm, read as row maximum 0), on the split path."""
+    m, n = 3, 4096
+    x1, x2, g, b, s1, s2 = _inputs(m, n, "bf16", seed=12)
+    zero = np.zeros(n, np.uint16)
+    outs, _ = _run_split(x1, x2, zero, zero, None, None, (True, True), ("int8", "int8"),
+                         "bf16", launches=launches)
+    for k in (1, 2):
+        assert torch.all(outs[f"scale{k}"] == 0) and torch.all(outs[f"y{k}"] == 0)
+    zx = np.zeros((m, n), np.uint16)
+    outs, _ = _run_split(zx, zx, g, zero, None, None, None, ("int8", "int8"), "bf16",
+                         launches=launches, eps=0.0)
+    assert torch.all(outs["scale1"] == 0) and torch.all(outs["y1"] == 0)
 
 
 def test_split_workspace_errors():
@@ -133,3 +224,30 @@ def test_split_workspace_errors():
                                                        ex.handle, None)
     assert status == adq.ERR_WORKSPACE
     ex.close()
+
+
+def test_one_shot_helper_on_side_stream_keeps_workspace():
+    """The one-shot helper allocates the workspace and the outputs on torch's
+    current stream and launches on a side stream; they are marked as used
+    there, so memory allocated on the current stream right after the call
+    (and filled before the side stream ends) does not take them over."""
+    m, n = 32, 16384
+    x1, x2, g, b, s1, s2 = _inputs(m, n, "bf16", seed=13)
+    ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, None, ("int8", "int8"), "bf16")
+    args = [dev(a, "bf16") for a in (x1, x2, g, b, s1, s2)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        # a long kernel first on the side stream, so the operator runs late
+        spin = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+        with torch.cuda.stream(side):
+            spin.fill_(1)
+        y1, y2, sc1, sc2, xo = adq.add_rms_norm_dynamic_quant_v2(
+            *args, 1e-6, None, path=adq.PATH_SPLIT, stream=side)
+        junk = [torch.full((1 << 16,), 0x7F, dtype=torch.uint8, device="cuda")
+                for _ in range(8)]
+        side.synchronize()
+        torch.cuda.synchronize()
+        outs = {"x_out": xo, "y1": y1, "y2": y2, "scale1": sc1, "scale2": sc2}
+        compare_v2(outs, ora, ("int8", "int8"))
+        del junk, spin
