@@ -168,25 +168,97 @@ def device_context(torch, step_bytes: int) -> dict:
     return ctx
 
 
-def make_case(w, torch, adq, synth, dev, path=0):
+def make_cases(w, torch, adq, synth, dev, path, n_sets):
+    """n_sets independent input/output sets of a workload (inputs uploaded
+    once and copied on the device), each with its executor and workspace;
+    returns (cases, host inputs, active outputs)."""
     x1, x2 = synth.inputs(w)
     g, b, s1, s2 = synth.params(w)
-    d = lambda a: None if a is None else torch.from_numpy(a.view("int16")).view(
-        {"bf16": torch.bfloat16, "fp16": torch.float16}[w.dtype]).to(dev)
+    td = {"bf16": torch.bfloat16, "fp16": torch.float16}[w.dtype]
+    d = lambda a: None if a is None else torch.from_numpy(a.view("int16")).view(td).to(dev)
+    base1, base2 = d(x1), d(x2)
+    params = [d(p) for p in (g, b, s1, s2)]
+    cases = []
+    for i in range(n_sets):
+        t1 = base1 if i == 0 else base1.clone()
+        t2 = None if base2 is None else (base2 if i == 0 else base2.clone())
+        if w.op == "v2":
+            ex, outs = adq.plan_add_rms_norm_dynamic_quant_v2(
+                t1, t2, *params, w.eps, w.mask, w.y_types[0], w.y_types[1], path=path)
+        else:
+            ex, outs = adq.plan_rms_norm_dynamic_quant(t1, params[0], params[1], params[2],
+                                                       w.eps, w.y_types[0], path=path)
+        ws = (torch.empty(ex.workspace_size, dtype=torch.uint8, device=dev)
+              if ex.workspace_size else None)
+        cases.append((ex, ws, outs))
     if w.op == "v2":
-        ex, outs = adq.plan_add_rms_norm_dynamic_quant_v2(
-            d(x1), d(x2), d(g), d(b), d(s1), d(s2), w.eps, w.mask, w.y_types[0], w.y_types[1],
-            path=path)
-    else:
-        ex, outs = adq.plan_rms_norm_dynamic_quant(d(x1), d(g), d(b), d(s1), w.eps,
-                                                   w.y_types[0], path=path)
-    ws = (torch.empty(ex.workspace_size, dtype=torch.uint8, device=dev)
-          if ex.workspace_size else None)
-    if w.op == "v2":
-        active = [outs["y1"] is not None, outs["y2"] is not None]
+        active = [cases[0][2]["y1"] is not None, cases[0][2]["y2"] is not None]
     else:
         active = [True, False]
-    return ex, ws, (x1, x2, g, b, s1, s2), active
+    return cases, (x1, x2, g, b, s1, s2), active
+
+
+def active_outputs(w):
+    """Which quantized outputs a workload produces (the V2 page's cases)."""
+    if w.op != "v2":
+        return [True, False]
+    if w.mask is not None:
+        return [bool(w.mask[0]), bool(w.mask[1])]
+    return [True, w.n_smooth >= 2]
+
+
+def time_operator(w, torch, adq, synth, path, steps, warmup, rotate=True, keep=False):
+    """Average launch time of one operator workload: `steps` back-to-back
+    launches between two HIP events on the launch stream, after `warmup`
+    launches, rotating through enough input/output sets that every launch
+    streams from HBM rather than the 256 MB last-level cache."""
+    dev = torch.device("cuda:0")
+    footprint = alg_bytes(w, active_outputs(w))
+    n_sets = max(1, math.ceil(512e6 / footprint)) if rotate else 1
+    cases, host_inputs, active = make_cases(w, torch, adq, synth, dev, path, n_sets)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        ex, ws, _ = cases[i % n_sets]
+        ex.run(ws, stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        ex, ws, _ = cases[i % n_sets]
+        ex.run(ws, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / steps
+    plan = cases[0][0].describe()
+    res = {"ms": ms, "wall": wall, "bytes": footprint, "sets": n_sets, "plan": plan,
+           "active": active, "host_inputs": host_inputs if keep else None}
+    for ex, _, _ in cases:
+        ex.close()
+    del cases
+    torch.cuda.empty_cache()
+    return res
+
+
+def config_entry(w, r, steps):
+    """Per-workload figures for the bench line's `configs` object."""
+    us = r["ms"] * 1e3
+    gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
+    return {
+        "op": "AddRmsNormDynamicQuantV2" if w.op == "v2" else "RmsNormDynamicQuant",
+        "rows": w.rows, "cols": w.cols, "storage": w.dtype,
+        "outputs": [t for t, a in zip(w.y_types, r["active"]) if a],
+        "algorithmic_bytes": r["bytes"], "launches_timed": steps, "rotating_sets": r["sets"],
+        "us_per_launch": round(us, 2), "gbs": round(gbs, 1),
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "rows_per_s": round(w.rows / (r["ms"] * 1e-3)),
+        "kernel_path": r["plan"].split()[0].split("=")[1],
+        "plan": " ".join(x for x in r["plan"].split()
+                         if x.split("=")[0] in ("vpt", "block", "grid", "splits", "launches")),
+        "traffic": measured_traffic(w.name),
+    }
 
 
 def cpu_baseline(w, active, host_inputs, budget_s: float):
@@ -242,6 +314,9 @@ def main():
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--path", choices=["auto", "row", "split", "generic"], default="auto",
                     help="kernel path (default: the library's own choice)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the chosen workload (by default every operator workload "
+                         "is also timed and reported under `configs`)")
     ap.add_argument("--no-rotate", action="store_true",
                     help="reuse one input/output set (cache-warm) instead of rotating sets "
                          "that do not fit the last-level cache")
@@ -275,40 +350,18 @@ def main():
     torch.cuda.set_device(dev)
     path = {"auto": adq.PATH_AUTO, "row": adq.PATH_ROW, "split": adq.PATH_SPLIT,
             "generic": adq.PATH_GENERIC}[args.path]
-    first = make_case(w, torch, adq, synth, dev, path)
-    active = first[3]
-    footprint = alg_bytes(w, active)
-    # Rotate input/output sets so that each launch streams from HBM rather
-    # than the 256 MB last-level cache.
-    n_sets = 1 if args.no_rotate else max(1, math.ceil(512e6 / footprint))
+    footprint = alg_bytes(w, active_outputs(w))
     print(f"[bench] workload {w.name} {w.rows}x{w.cols} {w.dtype}: {footprint / 1e6:.1f} MB "
-          f"per launch, {n_sets} rotating set(s)", file=sys.stderr, flush=True)
-    cases = [first] + [make_case(w, torch, adq, synth, dev, path) for _ in range(n_sets - 1)]
-    print(f"[bench] plan: {cases[0][0].describe()}", file=sys.stderr, flush=True)
-    stream = torch.cuda.current_stream()
-
-    for i in range(args.warmup):
-        ex, ws, _, _ = cases[i % n_sets]
-        ex.run(ws, stream)
-    torch.cuda.synchronize()
-
-    # Timed region: K back-to-back launches between two HIP events recorded
-    # on the launch stream; the average launch duration is their span / K.
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        ex, ws, _, _ = cases[i % n_sets]
-        ex.run(ws, stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / args.steps
+          f"per launch", file=sys.stderr, flush=True)
+    head = time_operator(w, torch, adq, synth, path, args.steps, args.warmup,
+                         rotate=not args.no_rotate, keep=args.cpu_budget > 0)
+    ms = head["ms"]
     gbs = footprint / (ms * 1e-3) / 1e9
+    print(f"[bench] plan: {head['plan']}", file=sys.stderr, flush=True)
     print(f"[bench] {args.steps} launches: avg {ms * 1e3:.1f} us per launch, "
-          f"wall {wall * 1e3:.1f} ms", file=sys.stderr, flush=True)
+          f"wall {head['wall'] * 1e3:.1f} ms", file=sys.stderr, flush=True)
+    n_sets = head["sets"]
+    active = head["active"]
 
     traffic = measured_traffic(w.name)
     result = {
@@ -334,7 +387,7 @@ def main():
             "rows_per_s": round(w.rows / (ms * 1e-3)),
             "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "parallelism": "single GPU",
-            "kernel_path": first[0].describe().split()[0].split("=")[1],
+            "kernel_path": head["plan"].split()[0].split("=")[1],
             "cache": "warm (one set)" if n_sets == 1 and args.no_rotate else
                      f"cold ({n_sets} rotating sets)" if n_sets > 1 else "cold (footprint > LLC)",
         },
@@ -342,13 +395,23 @@ def main():
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
     }
+    if not args.no_configs:
+        # every workload of the operator, measured the same way (the headline
+        # among them, in a run of its own)
+        configs = {}
+        for name, wc in synth.WORKLOADS.items():
+            steps = args.steps if alg_bytes(wc, active_outputs(wc)) >= 100e6 else max(args.steps, 200)
+            r = time_operator(wc, torch, adq, synth, adq.PATH_AUTO, steps, args.warmup)
+            configs[name] = config_entry(wc, r, steps)
+            print(f"[bench] config {name}: {configs[name]['us_per_launch']} us, "
+                  f"{configs[name]['gbs']} GB/s ({configs[name]['kernel_path']})",
+                  file=sys.stderr, flush=True)
+        result["configs"] = configs
     result["context"] = device_context(torch, footprint)
     if args.cpu_budget > 0:
-        result["cpu_baseline"] = cpu_baseline(w, active, cases[0][2], args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, active, head["host_inputs"], args.cpu_budget)
     else:
         result["cpu_baseline"] = None
-    for ex, _, _, _ in cases:
-        ex.close()
     print(json.dumps(result), flush=True)
 
 

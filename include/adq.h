@@ -50,7 +50,8 @@
  *
  * Graphs: every phase-2 call may be captured into a HIP graph and the graph
  * replayed; no call records a memset, and no kernel keeps state between
- * launches.
+ * launches (a split-row call captured on a stream runs its plain-launch
+ * form, whose results are the same bits as the one-launch form's).
  *
  * Determinism: results are bitwise reproducible run to run (fixed
  * reduction order, no floating-point atomics), as the pages' Constraints
@@ -245,11 +246,12 @@ void adq_executor_destroy(adq_executor* executor);
  * shape; the others force a path (for tests and tuning).  ADQ_PATH_ROW:
  * one workgroup per row, 128-bit accesses (n % 8 == 0, 16-byte aligned
  * tensors, n <= 32768).  ADQ_PATH_SPLIT: S workgroups per row, each on a
- * chunk of the row, in two or three launches per batch of rows that hand
- * the per-chunk partial sums of squares and maxima over through the
- * workspace (n % 8 == 0, 16-byte aligned tensors; AUTO takes it for rows
- * longer than 32768 columns, and for rows of at least 4096 columns when
- * there are at most a quarter as many rows as compute units).
+ * chunk of the row, handing the per-chunk partial sums of squares and
+ * maxima over through the workspace, in one launch or in two or three per
+ * batch of rows (see adq_executor_set_split; n % 8 == 0, 16-byte aligned
+ * tensors; AUTO takes it for rows longer than 32768 columns, and for rows
+ * of at least 4096 columns when there are at most a quarter as many rows
+ * as compute units).
  * ADQ_PATH_GENERIC: any n and alignment.
  * GEMM executors: ADQ_PATH_GEMM_TILE128 (128 x 128 output tiles) and
  * ADQ_PATH_GEMM_TILE256 (256 x 256 tiles); AUTO takes 256 once the
@@ -281,18 +283,41 @@ adq_status adq_executor_set_path(adq_executor* executor, int32_t path,
 
 /*
  * Split-row geometry of an operator executor (AddRmsNormDynamicQuantV2 or
- * RmsNormDynamicQuant): moves it to ADQ_PATH_SPLIT with `splits` chunks per
- * row (0 = the planner's choice; otherwise it must be a count that cuts n
- * into whole chunks of at most 2048 8-column vectors, each chunk but the
- * last the same size) and `launches` 2 (the last launch takes each row's
- * maxima over the whole row) or 3 (a launch of its own for the partial
- * maxima), or 0 for the planner's choice; returns the new workspace size.
- * For one chunk count the two launch forms give the same bits (the row's
- * sum of squares is added up chunk by chunk in the same order); another
- * chunk count adds it up in another order.  For tests and tuning;
- * ADQ_ERR_PARAM_INVALID leaves the executor unchanged.
+ * RmsNormDynamicQuant), for tests and tuning: moves it to ADQ_PATH_SPLIT
+ * and returns the new workspace size.  ADQ_ERR_PARAM_INVALID leaves the
+ * executor unchanged.
+ *
+ * splits    chunks per row, 0 = the planner's choice; otherwise a count that
+ *           cuts n into whole chunks of at most 2048 8-column vectors, all
+ *           but the last of one size (at most 64 for the one-launch form).
+ * launches  0 = the planner's choice (one launch when all workgroups of the
+ *           call fit on the chip at once, else two or three);
+ *           1 = one kernel whose workgroups exchange their chunks' partial
+ *           sums of squares and maxima through the workspace, each slot
+ *           tagged with a value the host makes for the call; a wait for a
+ *           slot ends after `wait_us` and the waiting workgroup then
+ *           computes the missing partial result itself (same code, same
+ *           bits), so results never depend on timing.  A call on a stream
+ *           that is being captured into a graph runs the plain two- or
+ *           three-launch form instead (a replay would repeat the tag);
+ *           2 = plain kernels; the last takes each row's maxima over the
+ *           whole row;  3 = plain kernels, one of them for the maxima.
+ * wait_us   one-launch form: longest wait per exchange in microseconds
+ *           (< 0: the default, 20; 0: one look, then compute what is missing).
+ * spread    nonzero: a row's chunks go to workgroups on different XCDs.
+ *
+ * For one chunk count every form, wait and placement gives the same bits
+ * (the row's sum of squares is added up chunk by chunk in the same order);
+ * another chunk count adds it up in another order.
  */
-adq_status adq_executor_set_split(adq_executor* executor, int32_t splits, int32_t launches,
+typedef struct adq_split_config {
+  int32_t splits;
+  int32_t launches;
+  int32_t wait_us;
+  int32_t spread;
+} adq_split_config;
+
+adq_status adq_executor_set_split(adq_executor* executor, const adq_split_config* config,
                                   uint64_t* workspace_size);
 
 /*

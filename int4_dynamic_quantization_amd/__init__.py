@@ -52,6 +52,12 @@ class Tensor(ctypes.Structure):
                 ("shape", ctypes.c_int64 * MAX_DIMS)]
 
 
+class SplitConfig(ctypes.Structure):
+    """adq_split_config: split-row geometry (tests and tuning)."""
+    _fields_ = [("splits", ctypes.c_int32), ("launches", ctypes.c_int32),
+                ("wait_us", ctypes.c_int32), ("spread", ctypes.c_int32)]
+
+
 class AdqError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -100,7 +106,7 @@ def _load():
     lib.adq_executor_destroy.argtypes = [vp]
     lib.adq_executor_destroy.restype = None
     lib.adq_executor_set_path.argtypes = [vp, ctypes.c_int32, u64p]
-    lib.adq_executor_set_split.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, u64p]
+    lib.adq_executor_set_split.argtypes = [vp, ctypes.POINTER(SplitConfig), u64p]
     lib.adq_executor_describe.argtypes = [vp, ctypes.c_char_p, ctypes.c_uint64]
     lib.adq_executor_describe.restype = ctypes.c_int32
     lib.adq_last_error.argtypes = []
@@ -195,12 +201,14 @@ class Executor:
         self.workspace_size = int(ws.value)
         return self.workspace_size
 
-    def set_split(self, splits: int = 0, launches: int = 0) -> int:
-        """Split-row path with `splits` chunks per row and a 2- or 3-launch
-        form (0 = the planner's choice); returns the new workspace size."""
+    def set_split(self, splits: int = 0, launches: int = 0, wait_us: int = -1,
+                  spread: bool = False) -> int:
+        """Split-row path with `splits` chunks per row and the 1-, 2- or
+        3-launch form (0 = the planner's choice), the one-launch form's wait
+        budget and chunk placement; returns the new workspace size."""
         ws = ctypes.c_uint64(0)
-        _check(_lib().adq_executor_set_split(self.handle, int(splits), int(launches),
-                                             ctypes.byref(ws)))
+        cfg = SplitConfig(int(splits), int(launches), int(wait_us), int(bool(spread)))
+        _check(_lib().adq_executor_set_split(self.handle, ctypes.byref(cfg), ctypes.byref(ws)))
         self.workspace_size = int(ws.value)
         return self.workspace_size
 

@@ -7,6 +7,8 @@
 // Formula cases and Constraints section.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -79,10 +81,13 @@ struct adq_executor {
   int block;
   int grid;
   int splits;
-  int launches;        // split-row path: 2 or 3 launches per batch of rows
+  int launches;        // split-row path: 1, 2 or 3 launches per batch of rows
+  int plain_launches;  // split-row path: the plain form (2 or 3) a captured call runs
   int64_t batch_rows;  // split-row path: rows per batch
   int split_req;       // split-row path: requested chunks per row (0 = planner's)
   int launch_req;      // split-row path: requested launch form (0 = planner's)
+  int spread;          // split-row path: a row's chunks on different XCDs (tests)
+  uint32_t wait_ticks; // split-row path, one-launch form: wait budget (10 ns ticks)
   uint64_t ws_bytes;
 };
 
@@ -246,6 +251,22 @@ adq_status current_device(int* dev, int* cus) {
 
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
+// Tags of the split-row path's one-launch form, `count` consecutive ones of
+// a sequence unique within the process (a Weyl sequence with an odd step
+// has period 2^64), starting from a value mixed from the clock and an
+// address, so that workspace contents left by another process do not repeat
+// them; one tag per batch of rows of a call.
+uint64_t next_tags(uint64_t count) {
+  static std::atomic<uint64_t> counter{[] {
+    uint64_t z = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
+                 (uint64_t)(uintptr_t)&g_last_error;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+  }()};
+  return counter.fetch_add(count * adq::kSplitTagStep, std::memory_order_relaxed);
+}
+
 // ---- planning constants (each measured on an MI355X; the numbers behind
 // them are in the design notes of the repository)
 
@@ -264,25 +285,34 @@ constexpr int64_t kShortRowMaxN = 6144;
 constexpr int64_t kShortRowMinRowsPerWg = 16;
 constexpr int64_t kShortRowGridMult = 24;
 
-// Split-row path: chunks of at least one wave of vectors (512 columns) and
-// at most 1024 threads x 2 vectors (16384 columns); enough chunks per row
-// for about two workgroups per CU; batches of rows whose x1 and x2 take at
-// most 64 MiB, so that the chunks the later launches read again are still
-// in the 256 MB memory-side cache.
-constexpr int64_t kSplitMinChunkVec = 64;
+// Split-row path: chunks of about 512 8-column vectors (4096 columns), at
+// most 1024 threads x 2 vectors (16384 columns); for few rows, no more
+// chunks than give each CU one workgroup.  Measured on 1-256 rows of
+// 16384 and 32768 bf16 columns (one-launch form, two INT8 outputs): 4096-
+// column chunks were the fastest or within 3% of it wherever rows x chunks
+// stayed within the CUs.  Plain-launch batches of rows whose x1 and x2 take
+// at most 64 MiB, so that the chunks the later launches read again are
+// still in the 256 MB memory-side cache.
+constexpr int64_t kSplitChunkVec = 512;
 constexpr int64_t kSplitMaxChunkVec = 2048;
-constexpr int64_t kSplitWgPerCu = 2;
 constexpr int64_t kSplitBatchBytes = (int64_t)64 << 20;
 // The two-launch form (each workgroup of the last launch takes the row
 // maxima over the whole row) up to this many chunks per row and this row
 // length; beyond, the three-launch form.
 constexpr int64_t kSplitWholeRowMaxSplits = 8;
 constexpr int64_t kSplitWholeRowMaxVec = 4096;
+// One-launch form: the planner takes it when every workgroup of the call
+// fits on the chip at once; a wait for another chunk's partial result gives
+// up after 20 us (the waiting workgroup then computes it itself).
+constexpr uint32_t kSplitWaitTicksDefault = 2000;  // 10 ns ticks
 // AUTO sends rows that fit the row kernel to the split-row path when they
-// are too few to give each CU a quarter of a row (the row kernel would
-// leave most CUs idle) and at least 4096 columns long.
-constexpr int64_t kFewRowsCuDiv = 4;
-constexpr int64_t kFewRowsMinVec = 512;
+// are at least 16384 columns long and few enough that two or more 4096-
+// column chunks per row still give each CU at most one workgroup.  Launch
+// to launch, cold, one-launch form against the row kernel (bf16, two INT8
+// outputs): 32 x 16384 7.0 against 9.0 us, 1 x 32768 6.7 against 10.9 us,
+// 128 x 16384 8.7 against 9.9 us; at 256 rows, and for rows of 4096 or
+// 8192 columns at any count, the row kernel was as fast or faster.
+constexpr int64_t kFewRowsMinVec = 2048;
 
 bool row_geometry(int64_t nvec, int* vpt, int* block) {
   if (nvec <= 0) return false;
@@ -298,18 +328,19 @@ bool row_geometry(int64_t nvec, int* vpt, int* block) {
   return true;
 }
 
-// Split-row geometry: S chunks per row (requested, or enough for about
-// kSplitWgPerCu workgroups per CU), each of block x vpt vectors; the launch
-// form (requested, or by the rule above); rows per batch.
+// Split-row geometry: S chunks per row (requested, or chunks of about
+// kSplitChunkVec vectors, no more per row than give each CU one workgroup
+// when the rows are few), each of block x vpt vectors; the launch form
+// (requested; else one launch when the call's workgroups all fit on the chip
+// at once, else two or three by the rule above); rows per batch.
 bool split_geometry(adq_executor* e) {
   const int64_t nvec = e->args.n / 8;
   if (nvec < 1) return false;
-  const int64_t rows8 = (e->m + 7) / 8 * 8;
   int64_t S = e->split_req;
   if (S <= 0) {
-    S = ((int64_t)e->cus * kSplitWgPerCu + rows8 - 1) / rows8;
-    const int64_t most = nvec / kSplitMinChunkVec > 1 ? nvec / kSplitMinChunkVec : 1;
-    if (S > most) S = most;
+    S = nvec / kSplitChunkVec;
+    const int64_t fill = e->cus / e->m;  // chunks per row that still fit one per CU
+    if (fill >= 1 && S > fill) S = fill;
     if (S < 1) S = 1;
   }
   if (S > nvec) S = nvec;
@@ -323,12 +354,24 @@ bool split_geometry(adq_executor* e) {
     block = round_up((int)((chunk + 1) / 2), 64);
   }
   S = (nvec + block * vpt - 1) / (block * vpt);
+  const int plain = S <= kSplitWholeRowMaxSplits && nvec <= kSplitWholeRowMaxVec ? 2 : 3;
+  // one-launch form when all workgroups of the call are resident at once
+  const int occ = adq::split_exchange_blocks_per_cu(e->var, vpt, (int)block);
+  const int64_t capacity = (int64_t)occ * e->cus;
   int launches = e->launch_req;
   if (launches == 0)
-    launches = S <= kSplitWholeRowMaxSplits && nvec <= kSplitWholeRowMaxVec ? 2 : 3;
-  const int64_t row_bytes = (int64_t)e->var.nin * 2 * e->args.n;
-  int64_t batch = kSplitBatchBytes / row_bytes;
-  if (batch >= 8) batch -= batch % 8;
+    launches = S <= 64 && adq::split_grid(e->m, (int)S) <= capacity ? 1 : plain;
+  if (launches == 1 && (S > 64 || occ <= 0)) return false;
+  int64_t batch;
+  if (launches == 1) {
+    // batches of rows whose workgroups fit on the chip at once
+    batch = capacity / S;
+    if (batch >= 8) batch -= batch % 8;
+  } else {
+    const int64_t row_bytes = (int64_t)e->var.nin * 2 * e->args.n;
+    batch = kSplitBatchBytes / row_bytes;
+    if (batch >= 8) batch -= batch % 8;
+  }
   if (batch < 1) batch = 1;
   if (batch > e->m) batch = e->m;
   while (batch > 1 && adq::split_grid(batch, (int)S) > INT32_MAX) batch /= 2;
@@ -337,9 +380,13 @@ bool split_geometry(adq_executor* e) {
   e->block = (int)block;
   e->splits = (int)S;
   e->launches = launches;
+  e->plain_launches = launches == 1 ? plain : launches;
   e->batch_rows = batch;
   e->grid = (int)adq::split_grid(batch, (int)S);
-  e->ws_bytes = adq::split_workspace_bytes(batch, (int)S, launches);
+  // a captured one-launch call runs the plain form on the same workspace
+  uint64_t ws = adq::split_workspace_bytes(batch, (int)S, launches);
+  const uint64_t ws_plain = adq::split_workspace_bytes(batch, (int)S, e->plain_launches);
+  e->ws_bytes = ws > ws_plain ? ws : ws_plain;
   return true;
 }
 
@@ -351,7 +398,9 @@ adq_status plan(adq_executor* e, int path) {
     // whole 16-byte vectors or unaligned tensors.
     int vpt = 0, block = 0;
     const bool row_ok = e->vector_ok && row_geometry(n / 8, &vpt, &block);
-    const bool few_rows = e->m * kFewRowsCuDiv <= e->cus && n / 8 >= kFewRowsMinVec;
+    int64_t few_splits = n / 8 / kSplitChunkVec;
+    if (e->cus / e->m < few_splits) few_splits = e->cus / e->m;
+    const bool few_rows = n / 8 >= kFewRowsMinVec && few_splits >= 2;
     if (e->vector_ok && (!row_ok || few_rows)) {
       adq_executor trial = *e;
       if (split_geometry(&trial)) path = ADQ_PATH_SPLIT;
@@ -381,6 +430,7 @@ adq_status plan(adq_executor* e, int path) {
     e->grid = (int)((e->m + per - 1) / per);
     e->splits = 1;
     e->launches = 1;
+    e->plain_launches = 1;
     e->batch_rows = e->m;
     e->ws_bytes = 0;
     return ADQ_OK;
@@ -392,6 +442,7 @@ adq_status plan(adq_executor* e, int path) {
     e->grid = (int)(e->m < (int64_t)e->cus * 8 ? e->m : (int64_t)e->cus * 8);
     e->splits = 1;
     e->launches = 1;
+    e->plain_launches = 1;
     e->batch_rows = e->m;
     e->ws_bytes = 0;
     return ADQ_OK;
@@ -411,6 +462,7 @@ adq_status plan(adq_executor* e, int path) {
 adq_status finish_plan(adq_executor* proto, uint64_t* workspace_size, adq_executor** executor) {
   adq_status st = current_device(&proto->device, &proto->cus);
   if (st != ADQ_OK) return st;
+  proto->wait_ticks = kSplitWaitTicksDefault;
   const Args& a = proto->args;
   proto->vector_ok = a.n % 8 == 0 && aligned(a.x1, 16) && aligned(a.x2, 16) &&
                      aligned(a.x_out, 16) && aligned(a.gamma, 16) && aligned(a.beta, 16) &&
@@ -480,10 +532,26 @@ adq_status run(void* workspace, uint64_t workspace_size, adq_executor* e, void* 
       err = adq::launch_row(e->var, e->vpt, e->block, e->grid, e->args, s);
       break;
     case ADQ_PATH_GENERIC: err = adq::launch_generic(e->var, e->block, e->grid, e->args, s); break;
-    case ADQ_PATH_SPLIT:
-      err = adq::launch_split(e->var, e->vpt, e->block, e->splits, e->launches, e->batch_rows,
-                              e->args, workspace, s);
+    case ADQ_PATH_SPLIT: {
+      adq::SplitPlan sp{e->vpt, e->block, e->splits, e->launches, e->batch_rows, e->spread,
+                        e->wait_ticks, 0};
+      if (sp.launches == 1) {
+        // the one-launch form's tag is made here for each call; a captured
+        // call (which a replay would repeat) runs the plain form instead,
+        // and so does a call whose capture state cannot be read
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+          (void)hipGetLastError();
+          cs = hipStreamCaptureStatusActive;
+        }
+        if (cs == hipStreamCaptureStatusNone)
+          sp.tag = next_tags((uint64_t)((e->m + e->batch_rows - 1) / e->batch_rows));
+        else
+          sp.launches = e->plain_launches;
+      }
+      err = adq::launch_split(e->var, sp, e->args, workspace, s);
       break;
+    }
     default: break;
   }
   if (cur != e->device) (void)hipSetDevice(cur);
@@ -904,22 +972,28 @@ adq_status adq_executor_set_path(adq_executor* executor, int32_t path, uint64_t*
   return ok();
 }
 
-adq_status adq_executor_set_split(adq_executor* executor, int32_t splits, int32_t launches,
+adq_status adq_executor_set_split(adq_executor* executor, const adq_split_config* config,
                                   uint64_t* workspace_size) {
-  if (!executor || !workspace_size)
-    return fail(ADQ_ERR_NULLPTR, "executor and workspace_size are required");
+  if (!executor || !config || !workspace_size)
+    return fail(ADQ_ERR_NULLPTR, "executor, config and workspace_size are required");
   if (executor->op != kOpV2 && executor->op != kOpRmsNorm)
     return fail(ADQ_ERR_PARAM_INVALID, "split geometry applies to the operator's executors only");
-  if (splits < 0 || (launches != 0 && launches != 2 && launches != 3))
-    return fail(ADQ_ERR_PARAM_INVALID, "splits must be >= 0 and launches 0, 2 or 3");
+  if (config->splits < 0 || config->launches < 0 || config->launches > 3)
+    return fail(ADQ_ERR_PARAM_INVALID, "splits must be >= 0 and launches 0, 1, 2 or 3");
+  if (config->launches == 1 && config->splits > 64)
+    return fail(ADQ_ERR_PARAM_INVALID, "the one-launch form takes at most 64 chunks per row");
   adq_executor trial = *executor;
-  trial.split_req = splits;
-  trial.launch_req = launches;
+  trial.split_req = config->splits;
+  trial.launch_req = config->launches;
+  trial.spread = config->spread != 0;
+  trial.wait_ticks = config->wait_us < 0 ? kSplitWaitTicksDefault
+                     : config->wait_us > 1000000 ? 100000000u
+                                                 : (uint32_t)config->wait_us * 100u;
   adq_status st = plan(&trial, ADQ_PATH_SPLIT);
   if (st != ADQ_OK) return st;
-  if (splits > 0 && trial.splits != splits)
+  if (config->splits > 0 && trial.splits != config->splits)
     return fail(ADQ_ERR_PARAM_INVALID, "%d chunks per row do not fit n = %d (nearest: %d)",
-                splits, trial.args.n, trial.splits);
+                config->splits, trial.args.n, trial.splits);
   *executor = trial;
   *workspace_size = trial.ws_bytes;
   return ok();
@@ -956,11 +1030,12 @@ int32_t adq_executor_describe(const adq_executor* e, char* buf, uint64_t len) {
     static const char* names[] = {"auto", "row", "split", "generic"};
     snprintf(buf, (size_t)len,
              "path=%s elem=%s nin=%d q1=%d q2=%d rows=%lld n=%d vpt=%d block=%d grid=%d "
-             "splits=%d launches=%d batch_rows=%lld workspace=%llu cus=%d",
+             "splits=%d launches=%d plain_launches=%d batch_rows=%lld spread=%d wait_us=%u "
+             "workspace=%llu cus=%d",
              names[e->path & 3], e->var.elem == adq::kBF16 ? "bf16" : "fp16", e->var.nin,
              e->var.q1, e->var.q2, (long long)e->m, e->args.n, e->vpt, e->block, e->grid,
-             e->splits, e->launches, (long long)e->batch_rows, (unsigned long long)e->ws_bytes,
-             e->cus);
+             e->splits, e->launches, e->plain_launches, (long long)e->batch_rows, e->spread,
+             e->wait_ticks / 100u, (unsigned long long)e->ws_bytes, e->cus);
   }
   return e->path;
 }

@@ -54,14 +54,32 @@ hipError_t launch_row(const Variant& v, int vpt, int block, int grid, const Args
 int row_max_blocks_per_cu(const Variant& v, int vpt, int block);
 
 // Split-row path: S workgroups share each row (a chunk of block * vpt
-// 8-column vectors each); `launches` 2 or 3 plain kernels per batch of
-// `batch_rows` rows hand the partial results over through `ws`
-// (split_workspace_bytes(batch_rows, splits, launches) bytes, 4-byte
-// aligned, any contents) at kernel boundaries.
-hipError_t launch_split(const Variant& v, int vpt, int block, int splits, int launches,
-                        int64_t batch_rows, const Args& a, void* ws, hipStream_t stream);
+// 8-column vectors each), one batch of `batch_rows` rows at a time.
+// launches 2 or 3: plain kernels hand the partial results over through the
+// workspace at kernel boundaries.  launches 1: one kernel whose workgroups
+// exchange them through the workspace, tagged with `tag` + b * kSplitTagStep
+// for batch b (the caller reserves one tag per batch, each unique to its
+// launch), waiting at most `wait_ticks` (10 ns) for each exchange before
+// computing a missing partial result themselves.  `spread` places a row's
+// chunks on different XCDs (tests).  The workspace takes
+// split_workspace_bytes(batch_rows, splits, launches) bytes, 8-byte
+// aligned, any contents.
+constexpr uint64_t kSplitTagStep = 0x9E3779B97F4A7C15ULL;
+struct SplitPlan {
+  int vpt;
+  int block;
+  int splits;
+  int launches;
+  int64_t batch_rows;
+  int spread;
+  uint32_t wait_ticks;
+  uint64_t tag;
+};
+hipError_t launch_split(const Variant& v, const SplitPlan& sp, const Args& a, void* ws,
+                        hipStream_t stream);
 uint64_t split_workspace_bytes(int64_t batch_rows, int splits, int launches);
 int64_t split_grid(int64_t batch_rows, int splits);  // workgroups per launch
+int split_exchange_blocks_per_cu(const Variant& v, int vpt, int block);
 
 // Generic kernel: any n (odd widths, unaligned pointers); correctness path.
 hipError_t launch_generic(const Variant& v, int block, int grid, const Args& a,

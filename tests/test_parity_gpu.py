@@ -164,8 +164,9 @@ def test_ragged_shapes(m, n, dtype):
     cus = int(desc.split("cus=")[1].split()[0])
     if n % 8 != 0:
         assert "path=generic" in desc, desc
-    elif n > 32768 or (m * 4 <= cus and n >= 4096):
-        # long rows, or too few rows to occupy the CUs one row per workgroup
+    elif n > 32768 or (n // 8 >= 2048 and min(n // 8 // 512, cus // m) >= 2):
+        # long rows, or rows of 16384+ columns too few to occupy the CUs one
+        # row per workgroup (two or more 4096-column chunks per row fit)
         assert "path=split" in desc, desc
     else:
         assert "path=row" in desc, desc

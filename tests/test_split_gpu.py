@@ -1,8 +1,8 @@
 """GPU tests of the split-row path: S workgroups per row, each on a chunk,
-in two or three plain launches per batch of rows that hand the per-chunk
-partial sums of squares and maxima over through the workspace at kernel
-boundaries.  Compared with the oracle under the parity rules, through the
-C-ABI."""
+handing the per-chunk partial sums of squares and maxima over through the
+workspace -- in one launch (tagged slots, bounded waits, missing partial
+results computed locally) or in two or three plain launches per batch of
+rows.  Compared with the oracle under the parity rules, through the C-ABI."""
 import numpy as np
 import pytest
 import torch
@@ -33,12 +33,12 @@ def _inputs(m, n, dtype, seed, n_smooth=2):
 
 
 def _run_split(x1, x2, g, b, s1, s2, mask, y_types, dtype, splits=0, launches=0, ws_fill=None,
-               eps=1e-6):
+               eps=1e-6, wait_us=-1, spread=False):
     ex, outs = adq.plan_add_rms_norm_dynamic_quant_v2(
         dev(x1, dtype), dev(x2, dtype), dev(g, dtype), dev(b, dtype), dev(s1, dtype),
         dev(s2, dtype), eps, mask, y_types[0], y_types[1], path=adq.PATH_SPLIT)
-    if splits or launches:
-        ex.set_split(splits, launches)
+    if splits or launches or wait_us >= 0 or spread:
+        ex.set_split(splits, launches, wait_us, spread)
     ws = workspace(ex, ws_fill)
     ex.run(ws)
     torch.cuda.synchronize()
@@ -51,7 +51,7 @@ SPLIT_SHAPES = [(1, 2048), (3, 4096), (32, 16384), (7, 16392), (5, 20000), (2, 6
                 (64, 8192), (257, 32768), (9, 8), (130, 1024), (1, 262144), (3, 40008)]
 
 
-@pytest.mark.parametrize("launches", [2, 3])
+@pytest.mark.parametrize("launches", [1, 2, 3])
 @pytest.mark.parametrize("m,n", SPLIT_SHAPES)
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_split_path_parity(m, n, dtype, launches):
@@ -72,7 +72,7 @@ def test_split_counts(splits):
     _announce(f"split 9x32768 bf16 splits={splits}")
     x1, x2, g, b, s1, s2 = _inputs(9, 32768, "bf16", seed=31)
     ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, None, ("int8", "int8"), "bf16")
-    for launches in (2, 3):
+    for launches in (1, 2, 3):
         outs, desc = _run_split(x1, x2, g, b, s1, s2, None, ("int8", "int8"), "bf16",
                                 splits=splits, launches=launches)
         assert f"splits={splits} " in desc, desc
@@ -84,7 +84,8 @@ def test_split_count_that_does_not_fit_is_rejected():
     ex, _ = adq.plan_add_rms_norm_dynamic_quant_v2(
         dev(x1, "bf16"), dev(x2, "bf16"), dev(g, "bf16"), None, None, None, 1e-6, None)
     before = ex.describe()
-    for splits, launches in ((1, 0), (0, 4), (-1, 2)):  # 1 chunk > 2048 vectors
+    # 1 chunk > 2048 vectors; no 4-launch form; negative count; > 64 chunks in one launch
+    for splits, launches in ((1, 0), (0, 4), (-1, 2), (65, 1)):
         with pytest.raises(adq.AdqError) as e:
             ex.set_split(splits, launches)
         assert e.value.status == adq.ERR_PARAM_INVALID
@@ -92,16 +93,27 @@ def test_split_count_that_does_not_fit_is_rejected():
     ex.close()
 
 
-def test_launch_forms_agree_bit_for_bit():
-    """For one chunk count both launch forms quantize the same fp32 values
-    with the same scale, so every output is the same bits."""
-    x1, x2, g, b, s1, s2 = _inputs(40, 12288, "fp16", seed=33)
-    a, _ = _run_split(x1, x2, g, b, s1, s2, None, ("int8", "int4"), "fp16", splits=6,
-                      launches=2)
-    c, _ = _run_split(x1, x2, g, b, s1, s2, None, ("int8", "int4"), "fp16", splits=6,
-                      launches=3)
-    for k in ("x_out", "y1", "y2", "scale1", "scale2"):
-        assert torch.equal(a[k], c[k]), k
+@pytest.mark.parametrize("m,n,dtype", [(40, 12288, "fp16"), (32, 16384, "bf16"),
+                                         (3, 40008, "bf16")])
+def test_launch_forms_agree_bit_for_bit(m, n, dtype):
+    """For one chunk count every form quantizes the same fp32 values with the
+    same scale, so every output is the same bits: the three launch forms, the
+    one-launch form with no waiting (partial results of chunks whose slots are
+    not there at the first look are computed by the waiting workgroup) and
+    with a row's chunks on different XCDs."""
+    _announce(f"forms {m}x{n} {dtype}")
+    x1, x2, g, b, s1, s2 = _inputs(m, n, dtype, seed=33)
+    ref, desc = _run_split(x1, x2, g, b, s1, s2, None, ("int8", "int4"), dtype, launches=3)
+    splits = int(desc.split("splits=")[1].split()[0])
+    ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, None, ("int8", "int4"), dtype)
+    compare_v2(ref, ora, ("int8", "int4"))
+    for launches, wait_us, spread in ((2, -1, False), (1, -1, False), (1, 0, False),
+                                      (1, -1, True), (1, 0, True)):
+        got, d = _run_split(x1, x2, g, b, s1, s2, None, ("int8", "int4"), dtype,
+                            splits=splits, launches=launches, wait_us=wait_us, spread=spread)
+        assert f"launches={launches} " in d and f"spread={int(spread)} " in d, d
+        for k in ("x_out", "y1", "y2", "scale1", "scale2"):
+            assert torch.equal(ref[k], got[k]), (k, launches, wait_us, spread)
 
 
 def test_split_batches_of_rows():
@@ -117,13 +129,17 @@ def test_split_batches_of_rows():
                                 launches=launches)
         assert "batch_rows=256 " in desc, desc
         compare_v2(outs, ora, ("int8", "int8"))
+    # the one-launch form in batches of rows whose workgroups fit on the chip
+    outs, desc = _run_split(x1, x2, g, b, s1, s2, None, ("int8", "int8"), "bf16", launches=1)
+    assert int(desc.split("batch_rows=")[1].split()[0]) < m, desc
+    compare_v2(outs, ora, ("int8", "int8"))
 
 
 @pytest.mark.parametrize("fill", [None, 0x00, 0xFF, 0xA5])
 def test_split_workspace_contents_do_not_matter(fill):
     x1, x2, g, b, s1, s2 = _inputs(32, 16384, "bf16", seed=5)
     ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, None, ("int8", "int8"), "bf16")
-    for launches in (2, 3):
+    for launches in (1, 2, 3):
         outs, desc = _run_split(x1, x2, g, b, s1, s2, None, ("int8", "int8"), "bf16",
                                 launches=launches, ws_fill=fill)
         compare_v2(outs, ora, ("int8", "int8"))
@@ -174,6 +190,15 @@ def test_split_rms_norm_dq(y_type):
     outs, desc = run_rms(x, g, b, s1, 1e-6, y_type, "fp16", path=adq.PATH_SPLIT)
     assert "path=split" in desc
     compare_rms(outs, oracle.rms_norm_dq(x, g, b, s1, 1e-6, y_type, "fp16"), y_type)
+    for launches in (1, 2, 3):
+        ex, o = adq.plan_rms_norm_dynamic_quant(dev(x, "fp16"), dev(g, "fp16"), dev(b, "fp16"),
+                                                dev(s1, "fp16"), 1e-6, y_type)
+        ex.set_split(0, launches)
+        ex.run(workspace(ex))
+        torch.cuda.synchronize()
+        ex.close()
+        for k in ("y", "scale"):
+            assert torch.equal(o[k], outs[k]), (k, launches)
 
 
 @pytest.mark.parametrize("mask,has1,has2", [((False, True), False, True), ((True, False), True, False),
@@ -183,13 +208,13 @@ def test_split_output_options(mask, has1, has2):
     s1 = s1 if has1 else None
     s2 = s2 if has2 else None
     ora = oracle_v2(x1, x2, g, b, s1, s2, 1e-6, mask, ("int4", "int8"), "bf16")
-    for launches in (2, 3):
+    for launches in (1, 2, 3):
         outs, _ = _run_split(x1, x2, g, b, s1, s2, mask, ("int4", "int8"), "bf16",
                              launches=launches)
         compare_v2(outs, ora, ("int4", "int8"))
 
 
-@pytest.mark.parametrize("launches", [2, 3])
+@pytest.mark.parametrize("launches", [1, 2, 3])
 def test_split_degenerate_rows(launches):
     """gamma = beta = 0 (row maximum 0: scale 0, codes 0), and x = 0 with
     epsilon = 0 (0/0 in the norm, read as row maximum 0), on the split path."""
