@@ -151,6 +151,28 @@ adq_status adq_add_rms_norm_dynamic_quant_v2(void* workspace, uint64_t workspace
                                              adq_executor* executor, void* hip_stream);
 
 /*
+ * AddRmsNormDynamicQuantV2, phase 2 without a workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving
+ * loops that may not allocate, harnesses that forbid allocation.  Runs
+ * `executor` exactly as adq_add_rms_norm_dynamic_quant_v2 does (same
+ * kernels, same results bit for bit), but the split-row path's partial
+ * results go to a buffer of ADQ_STATIC_SCRATCH_BYTES that the library keeps
+ * in each device's memory (a static device array, held until the process
+ * ends) instead of a caller's workspace.  Allocates nothing.  Returns
+ * ADQ_ERR_WORKSPACE when the executor needs a larger workspace than that
+ * buffer (the plan's workspace size, as phase 1 reported it),
+ * ADQ_ERR_PARAM_INVALID for an executor of another operator, and
+ * ADQ_ERR_RUNTIME when the buffer's address cannot be found (it is looked up
+ * once per device, on the first call there that needs it).  All calls on one
+ * device share the one buffer, which keeps the last call's contents (nothing
+ * in it needs clearing): calls that may run at the same time on one device
+ * (on different streams, or graphs replayed concurrently) race, and the
+ * caller must order them.
+ */
+#define ADQ_STATIC_SCRATCH_BYTES (1u << 20)
+adq_status adq_add_rms_norm_dynamic_quant_v2_no_alloc(adq_executor* executor, void* hip_stream);
+
+/*
  * RmsNormDynamicQuant, phase 1.
  * x [..., n] F16/BF16; gamma [n]; beta [n] or NULL; smooth_scales [n] or
  * NULL; y_out [..., n] ADQ_INT8 or [..., n/2] ADQ_INT4X2; scale_out F32

@@ -32,6 +32,7 @@ MAX_DIMS = 8
 EXPORTED = (
     "adq_add_rms_norm_dynamic_quant_v2_get_workspace_size",
     "adq_add_rms_norm_dynamic_quant_v2",
+    "adq_add_rms_norm_dynamic_quant_v2_no_alloc",
     "adq_rms_norm_dynamic_quant_get_workspace_size",
     "adq_rms_norm_dynamic_quant",
     "adq_w8a8_gemm_get_workspace_size",
@@ -94,6 +95,7 @@ def _load():
         P, P, P, P, P, P, ctypes.c_double, ctypes.POINTER(ctypes.c_bool), P, P, P, P, P, u64p,
         exp]
     lib.adq_add_rms_norm_dynamic_quant_v2.argtypes = [vp, ctypes.c_uint64, vp, vp]
+    lib.adq_add_rms_norm_dynamic_quant_v2_no_alloc.argtypes = [vp, vp]
     lib.adq_rms_norm_dynamic_quant_get_workspace_size.argtypes = [
         P, P, P, P, ctypes.c_double, P, P, u64p, exp]
     lib.adq_rms_norm_dynamic_quant.argtypes = [vp, ctypes.c_uint64, vp, vp]
@@ -113,6 +115,7 @@ def _load():
     lib.adq_last_error.restype = ctypes.c_char_p
     for name in ("adq_add_rms_norm_dynamic_quant_v2_get_workspace_size",
                  "adq_add_rms_norm_dynamic_quant_v2",
+                 "adq_add_rms_norm_dynamic_quant_v2_no_alloc",
                  "adq_rms_norm_dynamic_quant_get_workspace_size", "adq_rms_norm_dynamic_quant",
                  "adq_w8a8_gemm_get_workspace_size", "adq_w8a8_gemm",
                  "adq_add_lora_get_workspace_size", "adq_add_lora", "adq_executor_set_path",
@@ -230,6 +233,16 @@ class Executor:
               "rmsnorm": _lib().adq_rms_norm_dynamic_quant,
               "gemm": _lib().adq_w8a8_gemm, "lora": _lib().adq_add_lora}[self.op]
         _check(fn(ws_ptr, ws_size, self.handle, s))
+
+    def run_no_alloc(self, stream=None) -> None:
+        """AddRmsNormDynamicQuantV2 phase 2 without a workspace: the library's
+        static scratch buffer of the device takes the split-row path's
+        partial results (calls on one device must not overlap)."""
+        if self.op != "v2":
+            raise ValueError("only AddRmsNormDynamicQuantV2 executors run without a workspace")
+        if stream is None:
+            stream = _torch().cuda.current_stream(self.device)
+        _check(_lib().adq_add_rms_norm_dynamic_quant_v2_no_alloc(self.handle, stream.cuda_stream))
 
     def close(self) -> None:
         if self.handle:

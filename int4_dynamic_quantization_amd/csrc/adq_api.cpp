@@ -668,6 +668,36 @@ adq_status adq_add_rms_norm_dynamic_quant_v2(void* workspace, uint64_t workspace
   return run(workspace, workspace_size, executor, hip_stream, kOpV2);
 }
 
+adq_status adq_add_rms_norm_dynamic_quant_v2_no_alloc(adq_executor* executor, void* hip_stream) {
+  if (!executor) return fail(ADQ_ERR_NULLPTR, "executor is NULL");
+  if (executor->op != kOpV2)
+    return fail(ADQ_ERR_PARAM_INVALID, "executor was built for another operator");
+  if (executor->ws_bytes > ADQ_STATIC_SCRATCH_BYTES)
+    return fail(ADQ_ERR_WORKSPACE,
+                "this call needs %llu bytes of scratch; the library's static buffer holds %u",
+                (unsigned long long)executor->ws_bytes, (unsigned)ADQ_STATIC_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  if (executor->ws_bytes > 0) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(ADQ_ERR_RUNTIME, "no HIP device available");
+    }
+    if (cur != executor->device && hipSetDevice(executor->device) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(ADQ_ERR_RUNTIME, "cannot select device %d", executor->device);
+    }
+    const hipError_t err = adq::split_static_scratch(executor->device, &scratch);
+    if (cur != executor->device) (void)hipSetDevice(cur);
+    if (err != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(ADQ_ERR_RUNTIME, "cannot find the static scratch buffer on device %d: %s",
+                  executor->device, hipGetErrorString(err));
+    }
+  }
+  return run(scratch, ADQ_STATIC_SCRATCH_BYTES, executor, hip_stream, kOpV2);
+}
+
 adq_status adq_rms_norm_dynamic_quant_get_workspace_size(
     const adq_tensor* x, const adq_tensor* gamma, const adq_tensor* beta,
     const adq_tensor* smooth_scales, double epsilon, const adq_tensor* y_out,

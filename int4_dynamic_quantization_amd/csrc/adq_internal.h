@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "adq.h"
+
 namespace adq {
 
 enum ElemType : int { kBF16 = 0, kF16 = 1 };
@@ -80,6 +82,10 @@ hipError_t launch_split(const Variant& v, const SplitPlan& sp, const Args& a, vo
 uint64_t split_workspace_bytes(int64_t batch_rows, int splits, int launches);
 int64_t split_grid(int64_t batch_rows, int splits);  // workgroups per launch
 int split_exchange_blocks_per_cu(const Variant& v, int vpt, int block);
+// Device address of the library's static scratch buffer
+// (ADQ_STATIC_SCRATCH_BYTES) on `device`, which must be the current device;
+// looked up on the first call for each device.
+hipError_t split_static_scratch(int device, void** ptr);
 
 // Generic kernel: any n (odd widths, unaligned pointers); correctness path.
 hipError_t launch_generic(const Variant& v, int block, int grid, const Args& a,

@@ -51,15 +51,27 @@
 // stream order the launches; large inputs run as batches of rows (each
 // batch's three launches before the next batch's), so the re-read chunks
 // of a batch still sit in the 256 MB memory-side cache.
+#include <mutex>
 #include <type_traits>
 
 #include "adq_device.h"
+
+// Scratch memory of the entry point that allocates nothing
+// (adq_add_rms_norm_dynamic_quant_v2_no_alloc): a static device array that
+// every device the library runs on holds, at its own address, from module
+// load until the process ends.  Host code never passes this name to a
+// kernel (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[ADQ_STATIC_SCRATCH_BYTES];
 
 namespace adq {
 
 namespace {
 
 constexpr int kXcds = 8;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 struct SplitArgs {
   Args a;
@@ -694,6 +706,19 @@ int split_exchange_blocks_per_cu(const Variant& v, int vpt, int block) {
   if (v.elem == kBF16) dispatch<kBF16>(v.nin, v.q1, v.q2, vpt, q);
   else dispatch<kF16>(v.nin, v.q1, v.q2, vpt, q);
   return occ;
+}
+
+hipError_t split_static_scratch(int device, void** ptr) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    g_scratch_ptr[device] = p;
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
 }
 
 hipError_t launch_split(const Variant& v, const SplitPlan& sp, const Args& a, void* ws,

@@ -44,7 +44,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert set(names) == set(adq.EXPORTED)
     for name in names:
         assert hasattr(adq.lib, name), name
