@@ -20,15 +20,15 @@
 
 namespace adq {
 
-hipError_t launch_row_bf16(const Variant&, int, int, int, const Args&, hipStream_t);
-hipError_t launch_row_f16(const Variant&, int, int, int, const Args&, hipStream_t);
+hipError_t launch_row_bf16(const Variant&, int, bool, int, int, const Args&, hipStream_t);
+hipError_t launch_row_f16(const Variant&, int, bool, int, int, const Args&, hipStream_t);
 int row_occupancy_bf16(const Variant&, int, int);
 int row_occupancy_f16(const Variant&, int, int);
 
-hipError_t launch_row(const Variant& v, int vpt, int block, int grid, const Args& a,
+hipError_t launch_row(const Variant& v, int vpt, bool wt, int block, int grid, const Args& a,
                       hipStream_t s) {
-  return v.elem == kBF16 ? launch_row_bf16(v, vpt, block, grid, a, s)
-                         : launch_row_f16(v, vpt, block, grid, a, s);
+  return v.elem == kBF16 ? launch_row_bf16(v, vpt, wt, block, grid, a, s)
+                         : launch_row_f16(v, vpt, wt, block, grid, a, s);
 }
 
 int row_max_blocks_per_cu(const Variant& v, int vpt, int block) {
@@ -88,6 +88,7 @@ struct adq_executor {
   int launch_req;      // split-row path: requested launch form (0 = planner's)
   int spread;          // split-row path: a row's chunks on different XCDs (tests)
   uint32_t wait_ticks; // split-row path, one-launch form: wait budget (10 ns ticks)
+  bool write_through;  // row path: sc1 stores (launches that move little data)
   uint64_t ws_bytes;
 };
 
@@ -284,6 +285,13 @@ constexpr int64_t kRowMaxVec = 4096;
 constexpr int64_t kShortRowMaxN = 6144;
 constexpr int64_t kShortRowMinRowsPerWg = 16;
 constexpr int64_t kShortRowGridMult = 24;
+// Row kernel stores: sc1 instead of non-temporal for launches that move at
+// most this many bytes.  Launch to launch, cold (bf16, rows of 4096 columns
+// with one INT8 output or 8192 with two; nt against sc1): 117 MB 24.6 /
+// 22.7 us, 235 MB 47.5 / 45.2, 268 MB 50.7 / 47.2, 470 MB 88.0 / 90.9,
+// 805 MB 141.8 / 146.7, 940 MB 164.1 / 166.3; the headline 1.07 GB and the
+// 2.18 GB INT4 workload were 2-4% slower with sc1 stores.
+constexpr int64_t kRowWriteThroughMaxBytes = (int64_t)384 << 20;
 
 // Split-row path: chunks of about 512 8-column vectors (4096 columns), at
 // most 1024 threads x 2 vectors (16384 columns); for few rows, no more
@@ -313,6 +321,16 @@ constexpr uint32_t kSplitWaitTicksDefault = 2000;  // 10 ns ticks
 // 128 x 16384 8.7 against 9.9 us; at 256 rows, and for rows of 4096 or
 // 8192 columns at any count, the row kernel was as fast or faster.
 constexpr int64_t kFewRowsMinVec = 2048;
+
+// Bytes one launch of the operator moves: inputs read, xOut and the codes
+// and scales written (the parameter vectors aside).
+int64_t launch_bytes(const adq_executor& e) {
+  const int64_t n = e.args.n;
+  int64_t per_row = (int64_t)e.var.nin * 2 * n + (e.var.nin == 2 ? 2 * n : 0);
+  for (int q : {e.var.q1, e.var.q2})
+    if (q != adq::kQNone) per_row += (q == adq::kQInt4 ? n / 2 : n) + 4;
+  return e.m * per_row;
+}
 
 bool row_geometry(int64_t nvec, int* vpt, int* block) {
   if (nvec <= 0) return false;
@@ -428,6 +446,7 @@ adq_status plan(adq_executor* e, int path) {
     e->vpt = vpt;
     e->block = block;
     e->grid = (int)((e->m + per - 1) / per);
+    e->write_through = launch_bytes(*e) <= kRowWriteThroughMaxBytes;
     e->splits = 1;
     e->launches = 1;
     e->plain_launches = 1;
@@ -440,6 +459,7 @@ adq_status plan(adq_executor* e, int path) {
     e->vpt = 0;
     e->block = 256;
     e->grid = (int)(e->m < (int64_t)e->cus * 8 ? e->m : (int64_t)e->cus * 8);
+    e->write_through = false;
     e->splits = 1;
     e->launches = 1;
     e->plain_launches = 1;
@@ -453,6 +473,7 @@ adq_status plan(adq_executor* e, int path) {
                   "split-row path needs n %% 8 == 0 and 16-byte aligned tensors");
     if (!split_geometry(e)) return fail(ADQ_ERR_PARAM_INVALID, "split-row geometry does not fit");
     e->path = ADQ_PATH_SPLIT;
+    e->write_through = false;
     return ADQ_OK;
   }
   return fail(ADQ_ERR_PARAM_INVALID, "unknown path %d", path);
@@ -529,7 +550,7 @@ adq_status run(void* workspace, uint64_t workspace_size, adq_executor* e, void* 
   }
   switch (e->path) {
     case ADQ_PATH_ROW:
-      err = adq::launch_row(e->var, e->vpt, e->block, e->grid, e->args, s);
+      err = adq::launch_row(e->var, e->vpt, e->write_through, e->block, e->grid, e->args, s);
       break;
     case ADQ_PATH_GENERIC: err = adq::launch_generic(e->var, e->block, e->grid, e->args, s); break;
     case ADQ_PATH_SPLIT: {
@@ -1061,11 +1082,12 @@ int32_t adq_executor_describe(const adq_executor* e, char* buf, uint64_t len) {
     snprintf(buf, (size_t)len,
              "path=%s elem=%s nin=%d q1=%d q2=%d rows=%lld n=%d vpt=%d block=%d grid=%d "
              "splits=%d launches=%d plain_launches=%d batch_rows=%lld spread=%d wait_us=%u "
-             "workspace=%llu cus=%d",
+             "store=%s workspace=%llu cus=%d",
              names[e->path & 3], e->var.elem == adq::kBF16 ? "bf16" : "fp16", e->var.nin,
              e->var.q1, e->var.q2, (long long)e->m, e->args.n, e->vpt, e->block, e->grid,
              e->splits, e->launches, e->plain_launches, (long long)e->batch_rows, e->spread,
-             e->wait_ticks / 100u, (unsigned long long)e->ws_bytes, e->cus);
+             e->wait_ticks / 100u, e->write_through ? "sc1" : "nt",
+             (unsigned long long)e->ws_bytes, e->cus);
   }
   return e->path;
 }

@@ -38,6 +38,11 @@ __device__ __forceinline__ void* row_ptr(void* base, int64_t row, uint32_t row_b
 // kernel; the sc0 / sc1 combinations measured the same within noise).
 constexpr int kStreamLoad = 2;
 constexpr int kStreamStore = 2;
+// sc1 (no nt) on the stores of row-kernel launches that move at most a few
+// hundred MB (the planner's threshold, with its measurements, is in the host
+// layer): 4096 x 4096 bf16 (117 MB) 24.6 -> 22.7 us, while launches of 1 GB
+// and more run 2-4% slower with it than with nt stores.
+constexpr int kWriteThroughStore = 16;
 
 // Two packed 16-bit values (element 0 in the low half) -> two floats.
 template <int E>

@@ -50,8 +50,9 @@ struct Variant {
 };
 
 // Row kernel: one workgroup per row at a time, `vpt` 8-element vectors per
-// thread (1, 2 or 4), grid-strided over rows, next row prefetched.
-hipError_t launch_row(const Variant& v, int vpt, int block, int grid, const Args& a,
+// thread (1, 2 or 4), grid-strided over rows, next row prefetched; `wt`
+// selects sc1 stores instead of non-temporal ones.
+hipError_t launch_row(const Variant& v, int vpt, bool wt, int block, int grid, const Args& a,
                       hipStream_t stream);
 int row_max_blocks_per_cu(const Variant& v, int vpt, int block);
 

@@ -45,25 +45,28 @@ __device__ __forceinline__ void opaque(u32x4& v) { asm volatile("" : "+v"(v)); }
 
 // Codes of one 8-column vector into an INT8 (8 bytes) or INT4X2 (4 bytes)
 // output row, at vector index j of that row.  `in` is already boosted.
-template <int Q>
+template <int Q, int ST>
 __device__ __forceinline__ void store_codes(const float (&in)[8], float inv, rsrc_t out,
                                             uint32_t j) {
   uint32_t q[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) q[e] = code_bits(in[e], inv);
   if constexpr (Q == kQInt8) {
-    __builtin_amdgcn_raw_buffer_store_b64(pack_int8x8(q), out, j * 8u, 0, kStreamStore);
+    __builtin_amdgcn_raw_buffer_store_b64(pack_int8x8(q), out, j * 8u, 0, ST);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b32(pack_int4x8(q), out, j * 4u, 0, kStreamStore);
+    __builtin_amdgcn_raw_buffer_store_b32(pack_int4x8(q), out, j * 4u, 0, ST);
   }
 }
 
-template <int E, int NIN, int Q1, int Q2, int VPT>
+// WT: the stores' cache policy, non-temporal (false) or sc1 (true; chosen for
+// launches that move little data).
+template <int E, int NIN, int Q1, int Q2, int VPT, bool WT>
 __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
   static_assert(VPT == 1 || VPT == 2 || VPT == 4, "row kernel holds at most 32 columns per thread");
   constexpr bool kHold = VPT <= 2;  // x and the inputs kept between passes, next row prefetched
   constexpr bool kTwo = Q2 != kQNone;
   constexpr int kQ2 = kTwo ? Q2 : kQInt8;
+  constexpr int kSt = WT ? kWriteThroughStore : kStreamStore;
   const int tid = threadIdx.x;
   const int bs = blockDim.x;
   const int lane = tid & 63;
@@ -176,7 +179,7 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
         __builtin_amdgcn_raw_buffer_store_b128(
             u32x4{narrow2<E>(xk[0], xk[1]), narrow2<E>(xk[2], xk[3]),
                   narrow2<E>(xk[4], xk[5]), narrow2<E>(xk[6], xk[7])},
-            rxo, vj[k] * 16u, 0, kStreamStore);
+            rxo, vj[k] * 16u, 0, kSt);
       }
     }
     ss = wave_sum(ss);
@@ -265,10 +268,10 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
         if constexpr (kTwo) apply_boost(in2[k], r2);
       }
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) store_codes<Q1>(in1[k], r1.inv, ry1, vj[k]);
+      for (int k = 0; k < VPT; ++k) store_codes<Q1, kSt>(in1[k], r1.inv, ry1, vj[k]);
       if constexpr (kTwo) {
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) store_codes<kQ2>(in2[k], r2.inv, ry2, vj[k]);
+        for (int k = 0; k < VPT; ++k) store_codes<kQ2, kSt>(in2[k], r2.inv, ry2, vj[k]);
       }
     } else {
 #pragma unroll
@@ -276,10 +279,10 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
         float i1[8], i2[8];
         inputs(k, i1, i2);
         apply_boost(i1, r1);
-        store_codes<Q1>(i1, r1.inv, ry1, vj[k]);
+        store_codes<Q1, kSt>(i1, r1.inv, ry1, vj[k]);
         if constexpr (kTwo) {
           apply_boost(i2, r2);
-          store_codes<kQ2>(i2, r2.inv, ry2, vj[k]);
+          store_codes<kQ2, kSt>(i2, r2.inv, ry2, vj[k]);
         }
       }
     }
@@ -295,31 +298,34 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
 
 // ---- launch table for one element type
 
-template <int E, int NIN, int Q1, int Q2, int VPT>
+template <int E, int NIN, int Q1, int Q2, int VPT, bool WT>
 struct RowInst {
   static hipError_t launch(int block, int grid, const Args& a, hipStream_t s) {
-    hipLaunchKernelGGL((row_kernel<E, NIN, Q1, Q2, VPT>), dim3(grid), dim3(block), 0, s, a);
+    hipLaunchKernelGGL((row_kernel<E, NIN, Q1, Q2, VPT, WT>), dim3(grid), dim3(block), 0, s, a);
     return hipGetLastError();
   }
   static int occupancy(int block) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_kernel<E, NIN, Q1, Q2, VPT>, block,
-                                                     0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_kernel<E, NIN, Q1, Q2, VPT, WT>,
+                                                     block, 0) != hipSuccess)
       return 0;
     return n;
   }
 };
 
 // Calls f.template operator()<Inst>() for the instance matching (nin, q1,
-// q2, vpt); returns false when no such instance exists.
-template <int E, template <int, int, int, int, int> class Inst, typename F>
-bool dispatch_variant(int nin, int q1, int q2, int vpt, F&& f) {
-#define ADQ_VPT_CASES(NIN_, Q1_, Q2_)                                         \
-  switch (vpt) {                                                              \
-    case 1: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 1>>(); return true; \
-    case 2: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 2>>(); return true; \
-    case 4: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 4>>(); return true; \
-    default: return false;                                                    \
+// q2, vpt, wt); returns false when no such instance exists.
+template <int E, template <int, int, int, int, int, bool> class Inst, typename F>
+bool dispatch_variant(int nin, int q1, int q2, int vpt, bool wt, F&& f) {
+#define ADQ_VPT_CASES(NIN_, Q1_, Q2_)                                                     \
+  switch (vpt * 2 + (wt ? 1 : 0)) {                                                       \
+    case 2: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 1, false>>(); return true;      \
+    case 3: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 1, true>>(); return true;       \
+    case 4: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 2, false>>(); return true;      \
+    case 5: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 2, true>>(); return true;       \
+    case 8: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 4, false>>(); return true;      \
+    case 9: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 4, true>>(); return true;       \
+    default: return false;                                                                \
   }
   if (nin == 1) {
     if (q2 != kQNone) return false;
@@ -340,17 +346,17 @@ bool dispatch_variant(int nin, int q1, int q2, int vpt, F&& f) {
 
 // Entry points for one element type, used by launch_row() in adq_api.cpp.
 #define ADQ_DEFINE_ROW_ENTRY(E, SUFFIX)                                                     \
-  hipError_t launch_row_##SUFFIX(const Variant& v, int vpt, int block, int grid,           \
+  hipError_t launch_row_##SUFFIX(const Variant& v, int vpt, bool wt, int block, int grid,  \
                                  const Args& a, hipStream_t s) {                           \
     hipError_t err = hipErrorInvalidValue;                                                 \
-    dispatch_variant<E, RowInst>(v.nin, v.q1, v.q2, vpt, [&]<typename I>() {               \
+    dispatch_variant<E, RowInst>(v.nin, v.q1, v.q2, vpt, wt, [&]<typename I>() {           \
       err = I::launch(block, grid, a, s);                                                  \
     });                                                                                    \
     return err;                                                                            \
   }                                                                                        \
   int row_occupancy_##SUFFIX(const Variant& v, int vpt, int block) {                       \
     int occ = 0;                                                                           \
-    dispatch_variant<E, RowInst>(v.nin, v.q1, v.q2, vpt,                                   \
+    dispatch_variant<E, RowInst>(v.nin, v.q1, v.q2, vpt, false,                            \
                                  [&]<typename I>() { occ = I::occupancy(block); });        \
     return occ;                                                                            \
   }
