@@ -168,7 +168,7 @@ def device_context(torch, step_bytes: int) -> dict:
     return ctx
 
 
-def make_cases(w, torch, adq, synth, dev, path, n_sets):
+def make_cases(w, torch, adq, synth, dev, path, n_sets, split=(0, 0)):
     """n_sets independent input/output sets of a workload (inputs uploaded
     once and copied on the device), each with its executor and workspace;
     returns (cases, host inputs, active outputs)."""
@@ -188,6 +188,8 @@ def make_cases(w, torch, adq, synth, dev, path, n_sets):
         else:
             ex, outs = adq.plan_rms_norm_dynamic_quant(t1, params[0], params[1], params[2],
                                                        w.eps, w.y_types[0], path=path)
+        if path == adq.PATH_SPLIT and any(split):
+            ex.set_split(split[0], split[1])
         ws = (torch.empty(ex.workspace_size, dtype=torch.uint8, device=dev)
               if ex.workspace_size else None)
         cases.append((ex, ws, outs))
@@ -207,7 +209,8 @@ def active_outputs(w):
     return [True, w.n_smooth >= 2]
 
 
-def time_operator(w, torch, adq, synth, path, steps, warmup, rotate=True, keep=False):
+def time_operator(w, torch, adq, synth, path, steps, warmup, rotate=True, keep=False,
+                  split=(0, 0)):
     """Average launch time of one operator workload: `steps` back-to-back
     launches between two HIP events on the launch stream, after `warmup`
     launches, rotating through enough input/output sets that every launch
@@ -215,7 +218,7 @@ def time_operator(w, torch, adq, synth, path, steps, warmup, rotate=True, keep=F
     dev = torch.device("cuda:0")
     footprint = alg_bytes(w, active_outputs(w))
     n_sets = max(1, math.ceil(512e6 / footprint)) if rotate else 1
-    cases, host_inputs, active = make_cases(w, torch, adq, synth, dev, path, n_sets)
+    cases, host_inputs, active = make_cases(w, torch, adq, synth, dev, path, n_sets, split)
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         ex, ws, _ = cases[i % n_sets]
@@ -314,6 +317,11 @@ def main():
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--path", choices=["auto", "row", "split", "generic"], default="auto",
                     help="kernel path (default: the library's own choice)")
+    ap.add_argument("--splits", type=int, default=0, metavar="S",
+                    help="with --path split: S chunks per row (0 = the planner's choice)")
+    ap.add_argument("--launches", type=int, default=0, choices=[0, 1, 2, 3],
+                    help="with --path split: the one-, two- or three-launch form (0 = the "
+                         "planner's choice)")
     ap.add_argument("--no-configs", action="store_true",
                     help="time only the chosen workload (by default every operator workload "
                          "is also timed and reported under `configs`)")
@@ -354,7 +362,8 @@ def main():
     print(f"[bench] workload {w.name} {w.rows}x{w.cols} {w.dtype}: {footprint / 1e6:.1f} MB "
           f"per launch", file=sys.stderr, flush=True)
     head = time_operator(w, torch, adq, synth, path, args.steps, args.warmup,
-                         rotate=not args.no_rotate, keep=args.cpu_budget > 0)
+                         rotate=not args.no_rotate, keep=args.cpu_budget > 0,
+                         split=(args.splits, args.launches))
     ms = head["ms"]
     gbs = footprint / (ms * 1e-3) / 1e9
     print(f"[bench] plan: {head['plan']}", file=sys.stderr, flush=True)
@@ -388,6 +397,9 @@ def main():
             "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "parallelism": "single GPU",
             "kernel_path": head["plan"].split()[0].split("=")[1],
+            "plan": " ".join(x for x in head["plan"].split()
+                             if x.split("=")[0] in ("vpt", "block", "grid", "splits", "launches",
+                                                    "store")),
             "cache": "warm (one set)" if n_sets == 1 and args.no_rotate else
                      f"cold ({n_sets} rotating sets)" if n_sets > 1 else "cold (footprint > LLC)",
         },

@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
   constexpr bool kHold = VPT <= 2;  // x and the inputs kept between passes, next row prefetched
   constexpr bool kTwo = Q2 != kQNone;
   constexpr int kQ2 = kTwo ? Q2 : kQInt8;
-  constexpr int kSt = WT ? kWriteThroughStore : kStreamStore;
+  constexpr int kStBulk = WT ? kWriteThroughStore : kStreamStore;
   const int tid = threadIdx.x;
   const int bs = blockDim.x;
   const int lane = tid & 63;
@@ -128,11 +128,16 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
   u32x4 c1[VPT], c2[VPT];  // raw x1/x2 vectors of the row being computed
   if constexpr (kHold) load_row(row, c1, c2);
 
-  // One row: prefetch the next, compute and store this one.  The first row
-  // is peeled off the loop so that every entry to the loop header has the
-  // same outstanding memory operations (loads, then stores); the wait for
-  // the prefetched row then need not wait for stores.
-  auto body = [&](int64_t row) {
+  // One row: prefetch the next, compute and store this one, with the stores'
+  // cache policy kSt.  The first row is peeled off the loop so that every
+  // entry to the loop header has the same outstanding memory operations
+  // (loads, then stores); the wait for the prefetched row then need not wait
+  // for stores.  The last row is peeled too: its prefetch (of a row that is
+  // not this workgroup's) is dead there and dropped, and its stores use sc1
+  // so that the end of the kernel leaves less written data behind in the
+  // caches (65536 x 5120 INT4 390.9 -> 377.8 us, 4096 x 4096 23.1 -> 21.8 us,
+  // 16384 x 8192 190.7 -> 189.1 us).
+  auto body = [&]<int kSt>(int64_t row) {
     // Prefetch this workgroup's next row (its last row again when there is
     // none, so the loads are unconditional).
     // (VPT 4: the registers hold no second row, so this row is loaded here)
@@ -292,8 +297,12 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
       for (int k = 0; k < VPT; ++k) c1[k] = n1[k], c2[k] = n2[k];
     }
   };
-  body(row);
-  for (row += step; row < rend; row += step) body(row);
+  const int64_t last = first + (rend - 1 - first) / step * step;
+  if (row < last) {
+    body.template operator()<kStBulk>(row);
+    for (row += step; row < last; row += step) body.template operator()<kStBulk>(row);
+  }
+  body.template operator()<kWriteThroughStore>(last);
 }
 
 // ---- launch table for one element type
