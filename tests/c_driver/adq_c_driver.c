@@ -5,7 +5,11 @@
  * error reporting of phase 1.
  *
  * usage: adq_c_driver DIR
- *   DIR/shape.txt: "m n dtype" (dtype 1 = F16, 2 = BF16)
+ *   DIR/shape.txt: "m n dtype [mode]" (dtype 1 = F16, 2 = BF16; mode 0 =
+ *     the planner's path, 1 = the split-row path's one-launch form set with
+ *     adq_executor_set_split, then the same executor run again through the
+ *     entry point that allocates nothing, whose outputs must be the same
+ *     bytes)
  *   DIR/{x1,x2,gamma,beta,s1,s2}.bin: 16-bit values, row-major
  * writes DIR/{xout,y1,y2,scale1,scale2}.bin (y1 INT8, y2 INT4X2) and prints
  * the executor description, then "ok".
@@ -88,12 +92,13 @@ int main(int argc, char** argv) {
   if (argc != 2) { fprintf(stderr, "usage: %s DIR\n", argv[0]); return 1; }
   const char* dir = argv[1];
   long long m = 0, n = 0;
-  int dtype = 0;
+  int dtype = 0, mode = 0;
   {
     char path[4096];
     snprintf(path, sizeof path, "%s/shape.txt", dir);
     FILE* f = fopen(path, "r");
     if (!f || fscanf(f, "%lld %lld %d", &m, &n, &dtype) != 3) { fprintf(stderr, "bad shape.txt\n"); return 4; }
+    if (fscanf(f, "%d", &mode) != 1) mode = 0;
     fclose(f);
   }
   const size_t elems = (size_t)m * (size_t)n, row = (size_t)n * 2;
@@ -130,12 +135,42 @@ int main(int argc, char** argv) {
 
   CHECK_ADQ(adq_add_rms_norm_dynamic_quant_v2_get_workspace_size(
       &tx1, &tx2, &tg, &tb, &ts1, &ts2, 1e-6, mask, &ty1, &ty2, &tsc1, &tsc2, &txo, &ws_size, &ex));
+  if (mode == 1) {
+    const adq_split_config cfg = {0, 1, -1, 0};
+    CHECK_ADQ(adq_executor_set_split(ex, &cfg, &ws_size));
+  }
   void* ws = NULL;
   if (ws_size) CHECK_HIP(hipMalloc(&ws, ws_size));
   hipStream_t stream;
   CHECK_HIP(hipStreamCreate(&stream));
   CHECK_ADQ(adq_add_rms_norm_dynamic_quant_v2(ws, ws_size, ex, stream));
   CHECK_HIP(hipStreamSynchronize(stream));
+  if (mode == 1) {
+    /* the same plan through the entry point that allocates nothing: the
+       outputs must come out the same, byte for byte */
+    const size_t sizes[5] = {elems * 2, elems, elems / 2, (size_t)m * 4, (size_t)m * 4};
+    void* outs[5] = {xout, y1, y2, sc1, sc2};
+    void* first[5];
+    for (int i = 0; i < 5; ++i) {
+      first[i] = malloc(sizes[i]);
+      if (!first[i]) exit(4);
+      CHECK_HIP(hipMemcpy(first[i], outs[i], sizes[i], hipMemcpyDeviceToHost));
+      CHECK_HIP(hipMemset(outs[i], 0x5A, sizes[i]));
+    }
+    CHECK_ADQ(adq_add_rms_norm_dynamic_quant_v2_no_alloc(ex, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    for (int i = 0; i < 5; ++i) {
+      void* again = malloc(sizes[i]);
+      if (!again) exit(4);
+      CHECK_HIP(hipMemcpy(again, outs[i], sizes[i], hipMemcpyDeviceToHost));
+      if (memcmp(again, first[i], sizes[i]) != 0) {
+        fprintf(stderr, "output %d differs between the two entry points\n", i);
+        return 6;
+      }
+      free(again);
+      free(first[i]);
+    }
+  }
   char desc[512];
   adq_executor_describe(ex, desc, sizeof desc);
   adq_executor_destroy(ex);
