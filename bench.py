@@ -11,7 +11,7 @@ average launch time, HIP events on the launch stream), its fraction of the
 MI355X HBM3E peak, and the CPU oracle timed on a bounded sample of the same
 workload on the host cores.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload v2_outlier]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload v2_outlier]
 
 ``--workload w8a8_gemm`` instead times the INT8 GEMM that consumes the
 quantized rows (16384 x 8192 codes with per-row scales through an
@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 INT8_PEAK_TOPS = 5000.0  # MI355X dense INT8 MFMA, 5.0 POP/s
+SETTLE_MS = 50.0  # least time of untimed launches before a timed run
 
 
 def alg_bytes(w, active, rows=None):
@@ -124,8 +125,7 @@ def timed_copy_us(torch, nbytes: int, steps: int = 20) -> float:
     bufs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1),
              torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")) for _ in range(sets)]
     stream = torch.cuda.current_stream()
-    for i in range(3):
-        bufs[i % sets][1].copy_(bufs[i % sets][0])
+    settle(torch, lambda i: bufs[i % sets][1].copy_(bufs[i % sets][0]), 3, SETTLE_MS)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -209,21 +209,42 @@ def active_outputs(w):
     return [True, w.n_smooth >= 2]
 
 
+def settle(torch, launch, warmup, settle_ms):
+    """`warmup` launches, continued until at least `settle_ms` of back-to-back
+    launches have run: after an idle spell the GPU needs about 20 ms of
+    sustained load before its launch time settles (bf16 16384 x 8192, windows
+    of 10 launches after 0.5 s idle: 172 us, rising to 195 us by the 30th
+    launch, back to 165 us from about the 100th on).  Returns the number of
+    launches made."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or (time.perf_counter() - t0) * 1e3 < settle_ms:
+        launch(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()  # keeps the host clock on the GPU's work
+    torch.cuda.synchronize()
+    return i
+
+
 def time_operator(w, torch, adq, synth, path, steps, warmup, rotate=True, keep=False,
-                  split=(0, 0)):
+                  split=(0, 0), settle_ms=SETTLE_MS):
     """Average launch time of one operator workload: `steps` back-to-back
     launches between two HIP events on the launch stream, after `warmup`
-    launches, rotating through enough input/output sets that every launch
-    streams from HBM rather than the 256 MB last-level cache."""
+    launches that go on for at least `settle_ms`, rotating through enough
+    input/output sets that every launch streams from HBM rather than the
+    256 MB last-level cache."""
     dev = torch.device("cuda:0")
     footprint = alg_bytes(w, active_outputs(w))
     n_sets = max(1, math.ceil(512e6 / footprint)) if rotate else 1
     cases, host_inputs, active = make_cases(w, torch, adq, synth, dev, path, n_sets, split)
     stream = torch.cuda.current_stream()
-    for i in range(warmup):
+
+    def launch(i):
         ex, ws, _ = cases[i % n_sets]
         ex.run(ws, stream)
-    torch.cuda.synchronize()
+
+    warm = settle(torch, launch, warmup, settle_ms)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -237,7 +258,7 @@ def time_operator(w, torch, adq, synth, path, steps, warmup, rotate=True, keep=F
     ms = start.elapsed_time(end) / steps
     plan = cases[0][0].describe()
     res = {"ms": ms, "wall": wall, "bytes": footprint, "sets": n_sets, "plan": plan,
-           "active": active, "host_inputs": host_inputs if keep else None}
+           "active": active, "host_inputs": host_inputs if keep else None, "warm": warm}
     for ex, _, _ in cases:
         ex.close()
     del cases
@@ -253,7 +274,8 @@ def config_entry(w, r, steps):
         "op": "AddRmsNormDynamicQuantV2" if w.op == "v2" else "RmsNormDynamicQuant",
         "rows": w.rows, "cols": w.cols, "storage": w.dtype,
         "outputs": [t for t, a in zip(w.y_types, r["active"]) if a],
-        "algorithmic_bytes": r["bytes"], "launches_timed": steps, "rotating_sets": r["sets"],
+        "algorithmic_bytes": r["bytes"], "launches_timed": steps, "untimed_launches": r["warm"],
+        "rotating_sets": r["sets"],
         "us_per_launch": round(us, 2), "gbs": round(gbs, 1),
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "rows_per_s": round(w.rows / (r["ms"] * 1e-3)),
@@ -310,8 +332,10 @@ def cpu_baseline(w, active, host_inputs, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed launches before the timed ones; they go on for at least "
+                         f"{SETTLE_MS:.0f} ms however many that takes")
     ap.add_argument("--workload", default="v2_outlier")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
@@ -400,6 +424,8 @@ def main():
             "plan": " ".join(x for x in head["plan"].split()
                              if x.split("=")[0] in ("vpt", "block", "grid", "splits", "launches",
                                                     "store")),
+            "untimed_launches": head["warm"],
+            "settle_ms": SETTLE_MS,
             "cache": "warm (one set)" if n_sets == 1 and args.no_rotate else
                      f"cold ({n_sets} rotating sets)" if n_sets > 1 else "cold (footprint > LLC)",
         },
@@ -412,7 +438,7 @@ def main():
         # among them, in a run of its own)
         configs = {}
         for name, wc in synth.WORKLOADS.items():
-            steps = args.steps if alg_bytes(wc, active_outputs(wc)) >= 100e6 else max(args.steps, 200)
+            steps = args.steps if alg_bytes(wc, active_outputs(wc)) >= 100e6 else max(args.steps, 1000)
             r = time_operator(wc, torch, adq, synth, adq.PATH_AUTO, steps, args.warmup)
             configs[name] = config_entry(wc, r, steps)
             print(f"[bench] config {name}: {configs[name]['us_per_launch']} us, "
@@ -475,9 +501,7 @@ def bench_gemm(args, torch, adq, synth) -> None:
     print(f"[bench] workload {w8.name} m={w8.m} n={w8.n} k={w8.k} out {w8.out_dtype}; "
           f"plan: {ex.describe()}", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        ex.run(None, stream)
-    torch.cuda.synchronize()
+    settle(torch, lambda i: ex.run(None, stream), args.warmup, SETTLE_MS)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -595,9 +619,8 @@ def bench_lora(args, torch, adq, synth) -> None:
     print(f"[bench] workload {wl.name}: {alg / 1e6:.1f} MB per launch, {n_sets} rotating set(s); "
           f"plan: {cases[0][0].describe()}", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
-        cases[i % n_sets][0].run(cases[i % n_sets][1], stream)
-    torch.cuda.synchronize()
+    settle(torch, lambda i: cases[i % n_sets][0].run(cases[i % n_sets][1], stream), args.warmup,
+           SETTLE_MS)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -651,9 +674,7 @@ def calibrate_copy(torch, mib: int, steps: int, warmup: int) -> None:
     src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
     dst = torch.empty_like(src)
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        dst.copy_(src)
-    torch.cuda.synchronize()
+    settle(torch, lambda i: dst.copy_(src), warmup, SETTLE_MS)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)

@@ -277,14 +277,26 @@ uint64_t next_tags(uint64_t count) {
 constexpr int64_t kRowVpt1MaxVec = 64;
 constexpr int64_t kRowVpt2MaxVec = 2048;
 constexpr int64_t kRowMaxVec = 4096;
-// Short rows (up to 6144 columns) that a grid filling every resident slot
-// once would stream 16 or more times per workgroup run faster with 24 times
-// as many workgroups of a few rows each, which the dispatcher hands to CUs
-// as they free up (65536 x 5120: 410.6 -> 376.6 us).  Longer rows keep the
-// persistent grid (16384 x 8192 is slower with more workgroups).
-constexpr int64_t kShortRowMaxN = 6144;
-constexpr int64_t kShortRowMinRowsPerWg = 16;
-constexpr int64_t kShortRowGridMult = 24;
+// Rows per workgroup of the row kernel, from the rows each CU has to stream.
+// Fewer than 16 rows per CU, and rows of more than 8192 columns: one
+// persistent wave of workgroups (every resident slot once).  Otherwise
+// workgroups of a few rows each (grid-strided, each with its next row in
+// flight), which the dispatcher hands to CUs as slots free up: one row when
+// a row holds at most 4 KiB of input, else 8 rows for 16-32 rows per CU (4
+// for rows of up to 2048 columns, whose workgroups are small), 2 for 32-64,
+// 3 above.  Swept over 1, 2, 3, 4, 6, 8, 12, 16 rows and the persistent
+// wave on 50 shapes (1024-32768 columns, 4096-262144 rows, one and two INT8
+// outputs, INT4, RmsNormDynamicQuant), each timed after 40 ms of launches:
+// this rule is 1.6% slower than each shape's best on average; the
+// persistent wave is 11.6% slower, and 24 times the slots for 16 or more
+// rows per slot 6.5%.  bf16 16384 x 8192 with two INT8 outputs: 182.7 us
+// persistent, 165.0 with 2 rows per workgroup.
+constexpr int64_t kWaveRowsMaxN = 8192;
+constexpr int64_t kFewRowsPerCu = 16;
+constexpr int64_t kMidRowsPerCu = 32;
+constexpr int64_t kManyRowsPerCu = 64;
+constexpr int64_t kShortRowsMaxN = 2048;
+constexpr int64_t kOneRowMaxBytes = 4096;
 // Row kernel stores: sc1 instead of non-temporal for launches that move at
 // most this many bytes.  Launch to launch, cold (bf16, rows of 4096 columns
 // with one INT8 output or 8192 with two; nt against sc1): 117 MB 24.6 /
@@ -330,6 +342,14 @@ int64_t launch_bytes(const adq_executor& e) {
   for (int q : {e.var.q1, e.var.q2})
     if (q != adq::kQNone) per_row += (q == adq::kQInt4 ? n / 2 : n) + 4;
   return e.m * per_row;
+}
+
+int64_t row_rows_per_wg(int64_t m, int64_t n, int64_t row_in_bytes, int64_t cus, int64_t slots) {
+  const int64_t wave = (m + slots - 1) / slots;  // one persistent wave
+  if (n > kWaveRowsMaxN || m < kFewRowsPerCu * cus) return wave;
+  if (row_in_bytes <= kOneRowMaxBytes) return 1;
+  if (m <= kMidRowsPerCu * cus) return n <= kShortRowsMaxN ? 4 : 8;
+  return m <= kManyRowsPerCu * cus ? 2 : 3;
 }
 
 bool row_geometry(int64_t nvec, int* vpt, int* block) {
@@ -433,15 +453,11 @@ adq_status plan(adq_executor* e, int path) {
                   (long long)(kRowMaxVec * 8));
     const int occ = adq::row_max_blocks_per_cu(e->var, vpt, block);
     if (occ <= 0) return fail(ADQ_ERR_RUNTIME, "row kernel does not fit block %d", block);
-    // A grid that fills every slot once (each workgroup then streams
-    // rows / slots rows) suits long rows; short rows streamed many times per
-    // workgroup take kShortRowGridMult times as many workgroups.
-    int64_t slots = (int64_t)occ * e->cus;
-    int64_t per = (e->m + slots - 1) / slots;
-    if (n <= kShortRowMaxN && per >= kShortRowMinRowsPerWg) {
-      slots *= kShortRowGridMult;
-      per = (e->m + slots - 1) / slots;
-    }
+    int64_t per = row_rows_per_wg(e->m, n, (int64_t)e->var.nin * 2 * n, e->cus,
+                                  (int64_t)occ * e->cus);
+    // a dispatch holds fewer than 2^32 work-items
+    const int64_t max_grid = ((int64_t)1 << 31) / block;
+    if ((e->m + per - 1) / per > max_grid) per = (e->m + max_grid - 1) / max_grid;
     e->path = ADQ_PATH_ROW;
     e->vpt = vpt;
     e->block = block;
