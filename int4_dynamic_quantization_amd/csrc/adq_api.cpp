@@ -277,6 +277,16 @@ uint64_t next_tags(uint64_t count) {
 constexpr int64_t kRowVpt1MaxVec = 64;
 constexpr int64_t kRowVpt2MaxVec = 2048;
 constexpr int64_t kRowMaxVec = 4096;
+// Rows of 3840-4096 columns in launches of at most 16 rows per CU take one
+// vector per thread (480-512 threads) instead of two.  Launch to launch
+// after 40 ms of launches, two vectors -> one, us: bf16 4096 x 4096 with one
+// INT8 output 20.9 -> 20.0, with two 25.2 -> 23.8, 1024 rows 8.05 -> 7.6,
+// 256 rows 4.13 -> 3.9, 4096 x 3840 19.6 -> 19.2; fp16 INT4 4096 x 4096
+// 19.6 -> 18.9, RmsNormDynamicQuant 14.1 -> 13.8.  Not taken: 8192 rows
+// and more (within 1%, RmsNormDynamicQuant 8192 x 4096 3% slower), 3584 and
+// 3072 columns (2-9% slower).
+constexpr int64_t kRowVpt1WideMinVec = 480;
+constexpr int64_t kRowVpt1WideMaxVec = 512;
 // Rows per workgroup of the row kernel, from the rows each CU has to stream.
 // Fewer than 16 rows per CU, and rows of more than 8192 columns: one
 // persistent wave of workgroups (every resident slot once).  Otherwise
@@ -451,6 +461,11 @@ adq_status plan(adq_executor* e, int path) {
       return fail(ADQ_ERR_PARAM_INVALID,
                   "row path needs n %% 8 == 0, n <= %lld and 16-byte aligned tensors",
                   (long long)(kRowMaxVec * 8));
+    if (n / 8 >= kRowVpt1WideMinVec && n / 8 <= kRowVpt1WideMaxVec &&
+        e->m <= kFewRowsPerCu * e->cus) {
+      vpt = 1;
+      block = round_up((int)(n / 8), 64);
+    }
     const int occ = adq::row_max_blocks_per_cu(e->var, vpt, block);
     if (occ <= 0) return fail(ADQ_ERR_RUNTIME, "row kernel does not fit block %d", block);
     int64_t per = row_rows_per_wg(e->m, n, (int64_t)e->var.nin * 2 * n, e->cus,

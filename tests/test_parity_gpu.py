@@ -149,7 +149,11 @@ def _case_inputs(m, n, dtype, seed, n_smooth=2, beta=True, outlier=0.0):
 
 SHAPES = [(1, 8), (3, 8), (257, 16), (3, 24), (5, 100 * 8), (3, 1000), (257, 1000),
           (2, 5120), (3, 16384), (1, 1), (3, 7), (4, 2), (257, 100), (2, 16392), (1, 20000),
-          (300, 24584), (2, 32768), (3, 32776), (2, 65536), (64, 1032)]
+          (300, 24584), (2, 32768), (3, 32776), (2, 65536), (64, 1032),
+          # one vector per thread for rows of 3840-4096 columns (ragged: 3848)
+          (300, 3840), (5, 3848), (1000, 4096),
+          # rows per workgroup: 8 (ragged tail), 2, 3, and 1 for rows of <= 4 KiB
+          (4100, 3072), (8200, 2048), (16500, 1032), (4500, 1024)]
 
 
 @pytest.mark.parametrize("m,n", SHAPES)
@@ -171,6 +175,8 @@ def test_ragged_shapes(m, n, dtype):
     else:
         assert "path=row" in desc, desc
         assert ("vpt=4" in desc) == (n > 16384), desc
+        if 3840 <= n <= 4096 and m <= 16 * cus:
+            assert "vpt=1" in desc, desc
 
 
 @pytest.mark.parametrize("y_types", [("int8", "int8"), ("int4", "int8"), ("int8", "int4"),
