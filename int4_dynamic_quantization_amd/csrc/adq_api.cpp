@@ -293,20 +293,27 @@ constexpr int64_t kRowVpt1WideMaxVec = 512;
 // workgroups of a few rows each (grid-strided, each with its next row in
 // flight), which the dispatcher hands to CUs as slots free up: one row when
 // a row holds at most 4 KiB of input, else 8 rows for 16-32 rows per CU (4
-// for rows of up to 2048 columns, whose workgroups are small), 2 for 32-64,
-// 3 above.  Swept over 1, 2, 3, 4, 6, 8, 12, 16 rows and the persistent
-// wave on 50 shapes (1024-32768 columns, 4096-262144 rows, one and two INT8
+// for rows of up to 2048 columns, whose workgroups are small), 2 for 32-64
+// (and above, for rows of more than 6144 columns), and above that as many
+// as make about 16 workgroups per resident slot over the launch (at least
+// 3).  Swept over 1, 2, 3, 4, 6, 8, 12, 16 rows and the persistent wave on
+// 50 shapes (1024-32768 columns, 4096-262144 rows, one and two INT8
 // outputs, INT4, RmsNormDynamicQuant), each timed after 40 ms of launches:
-// this rule is 1.6% slower than each shape's best on average; the
-// persistent wave is 11.6% slower, and 24 times the slots for 16 or more
-// rows per slot 6.5%.  bf16 16384 x 8192 with two INT8 outputs: 182.7 us
-// persistent, 165.0 with 2 rows per workgroup.
+// this rule is 1.1% slower than each shape's best on average (12 or 20
+// workgroups per slot instead of 16: 1.2%, 1.6%); the persistent wave is
+// 11.6% slower, and 24 times the slots for 16 or more rows per slot 6.5%.
+// bf16 16384 x 8192 with two INT8 outputs: 182.7 us persistent, 165.0 with
+// 2 rows per workgroup; fp16 65536 x 5120 INT4: 416.4 persistent, 354.8
+// with 3, 343.0 with 4 (16 per slot).
 constexpr int64_t kWaveRowsMaxN = 8192;
 constexpr int64_t kFewRowsPerCu = 16;
 constexpr int64_t kMidRowsPerCu = 32;
 constexpr int64_t kManyRowsPerCu = 64;
 constexpr int64_t kShortRowsMaxN = 2048;
 constexpr int64_t kOneRowMaxBytes = 4096;
+constexpr int64_t kWgPerSlot = 16;
+constexpr int64_t kWgPerSlotMaxN = 6144;
+constexpr int64_t kManyRowsMinPerWg = 3;
 // Row kernel stores: sc1 instead of non-temporal for launches that move at
 // most this many bytes.  Launch to launch, cold (bf16, rows of 4096 columns
 // with one INT8 output or 8192 with two; nt against sc1): 117 MB 24.6 /
@@ -359,7 +366,9 @@ int64_t row_rows_per_wg(int64_t m, int64_t n, int64_t row_in_bytes, int64_t cus,
   if (n > kWaveRowsMaxN || m < kFewRowsPerCu * cus) return wave;
   if (row_in_bytes <= kOneRowMaxBytes) return 1;
   if (m <= kMidRowsPerCu * cus) return n <= kShortRowsMaxN ? 4 : 8;
-  return m <= kManyRowsPerCu * cus ? 2 : 3;
+  if (m <= kManyRowsPerCu * cus || n > kWgPerSlotMaxN) return 2;
+  const int64_t per = (m + kWgPerSlot * slots / 2) / (kWgPerSlot * slots);  // nearest
+  return per > kManyRowsMinPerWg ? per : kManyRowsMinPerWg;
 }
 
 bool row_geometry(int64_t nvec, int* vpt, int* block) {
