@@ -314,13 +314,18 @@ constexpr int64_t kOneRowMaxBytes = 4096;
 constexpr int64_t kWgPerSlot = 16;
 constexpr int64_t kWgPerSlotMaxN = 6144;
 constexpr int64_t kManyRowsMinPerWg = 3;
-// Row kernel stores: sc1 instead of non-temporal for launches that move at
-// most this many bytes.  Launch to launch, cold (bf16, rows of 4096 columns
-// with one INT8 output or 8192 with two; nt against sc1): 117 MB 24.6 /
-// 22.7 us, 235 MB 47.5 / 45.2, 268 MB 50.7 / 47.2, 470 MB 88.0 / 90.9,
-// 805 MB 141.8 / 146.7, 940 MB 164.1 / 166.3; the headline 1.07 GB and the
-// 2.18 GB INT4 workload were 2-4% slower with sc1 stores.
-constexpr int64_t kRowWriteThroughMaxBytes = (int64_t)384 << 20;
+// Row kernel stores: sc1 instead of non-temporal when the grid is one wave
+// (every workgroup resident at once) and the launch moves at most this many
+// bytes; non-temporal for grids of several generations of workgroups and
+// for larger launches.  Launch to launch after 40 ms of launches, bf16, nt
+// against sc1, us: one wave, 4096 x 16384 two INT8 outputs (537 MB) 95.1 /
+// 87.1, 2048 x 16384 51.5 / 48.9, 4096 x 4096 one output 21.3 / 20.1,
+// 4096 x 8192 two 46.6 / 42.8, 8192 x 12288 (805 MB) 140.2 / 143.0; several
+// generations, 16384 x 3072 one output (352 MB) 56.3 / 59.6, 12288 x 4096
+// 56.4 / 58.7, 16384 x 2048 39.2 / 40.8, 8192 x 8192 75.9 / 80.3, the
+// headline 16384 x 8192 165.0 / 185.6.  Exceptions measured: 8192 x 8192
+// with two outputs (two generations) 90.8 / 80.4, 20000 x 2048 47.3 / 45.9.
+constexpr int64_t kRowWriteThroughMaxBytes = (int64_t)640 << 20;
 
 // Split-row path: chunks of about 512 8-column vectors (4096 columns), at
 // most 1024 threads x 2 vectors (16384 columns); for few rows, no more
@@ -486,7 +491,8 @@ adq_status plan(adq_executor* e, int path) {
     e->vpt = vpt;
     e->block = block;
     e->grid = (int)((e->m + per - 1) / per);
-    e->write_through = launch_bytes(*e) <= kRowWriteThroughMaxBytes;
+    e->write_through =
+        e->grid <= (int64_t)occ * e->cus && launch_bytes(*e) <= kRowWriteThroughMaxBytes;
     e->splits = 1;
     e->launches = 1;
     e->plain_launches = 1;
