@@ -77,3 +77,36 @@ def test_lora_algorithmic_bytes_by_hand():
     assert ((idx >= 0) & (idx < wl.w)).all() and len(set(idx.tolist())) == 8
     want = 4096 * 4096 * 2 + 2 * 4096 * 4096 * 2 + 4 * 4096 + 8 * (4096 * 16 + 16 * 4096) * 2
     assert bench.lora_alg_bytes(wl, idx) == want == 102_776_832
+
+
+class _FakeCuda:
+    def __init__(self):
+        self.syncs = 0
+
+    def synchronize(self):
+        self.syncs += 1
+
+
+class _FakeTorch:
+    def __init__(self):
+        self.cuda = _FakeCuda()
+
+
+def test_settle_runs_the_warmup_count_and_the_time_floor():
+    """The untimed phase makes at least `warmup` launches, goes on until the
+    time floor has passed, keeps the host in step with the device, and ends
+    with a synchronization (so the timed launches start on an idle queue)."""
+    import time
+    calls = []
+    torch = _FakeTorch()
+    n = bench.settle(torch, lambda i: calls.append(i), 40, 0.0)
+    assert n == 40 and calls == list(range(40))
+    assert torch.cuda.syncs >= 40 // 16 + 1
+
+    calls.clear()
+    torch = _FakeTorch()
+    t0 = time.perf_counter()
+    n = bench.settle(torch, lambda i: (calls.append(i), time.sleep(0.001)), 3, 30.0)
+    assert (time.perf_counter() - t0) * 1e3 >= 30.0
+    assert n == len(calls) and n > 3
+    assert torch.cuda.syncs >= n // 16
