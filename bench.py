@@ -16,7 +16,9 @@ workload on the host cores.
 ``--workload w8a8_gemm`` instead times the INT8 GEMM that consumes the
 quantized rows (16384 x 8192 codes with per-row scales through an
 8192 -> 8192 projection with per-column weight scales, bf16 out) against
-the MI355X dense INT8 MFMA peak.  ``--workload lora_prefill`` (or
+the MI355X dense INT8 MFMA peak (``--gemm-rows M`` runs it with M rows of
+activations; few rows are bound by reading the weights and are reported
+against HBM bandwidth).  ``--workload lora_prefill`` (or
 lora_decode) times AddLora accumulating into y in place, against HBM
 bandwidth; ``--lora-rank R`` runs it at another rank.
 """
@@ -352,6 +354,10 @@ def main():
     ap.add_argument("--no-rotate", action="store_true",
                     help="reuse one input/output set (cache-warm) instead of rotating sets "
                          "that do not fit the last-level cache")
+    ap.add_argument("--gemm-rows", type=int, default=0, metavar="M",
+                    help="with --workload w8a8_gemm: M rows of activations instead of 16384 "
+                         "(few rows are bound by reading the weights; the bench line then "
+                         "reports HBM GB/s)")
     ap.add_argument("--lora-rank", type=int, default=0, metavar="R",
                     help="AddLora workloads: use rank R (8, 16, 32, 64, 128 take the tiled "
                          "kernels) instead of the workload's own")
@@ -453,9 +459,11 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def gemm_cpu_baseline(a, sa, w, sw, b, k: int, budget_s: float):
+def gemm_cpu_baseline(a, sa, w, sw, b, k: int, budget_s: float, step_bytes: int = 0):
     """The oracle (plain C, one thread, exact int64 sums) on a sample of the
-    outputs, as many as fit the time budget after a short pilot."""
+    outputs, as many as fit the time budget after a short pilot.  In TOPS;
+    with `step_bytes`, in GB/s instead: the step's bytes times the share of
+    its outputs computed per second."""
     import numpy as np
     import oracle
     rng = np.random.default_rng(0)
@@ -471,8 +479,10 @@ def gemm_cpu_baseline(a, sa, w, sw, b, k: int, budget_s: float):
     t = run(pilot)
     count = int(max(pilot, budget_s / max(t / pilot, 1e-9)))
     t = run(count)
-    tops = 2.0 * k * count / t / 1e12
-    single = {"value": round(tops, 6), "cores": 1,
+    outputs = a.shape[0] * w.shape[0]
+    rate = lambda c, secs: (step_bytes * c / outputs / secs / 1e9 if step_bytes
+                            else 2.0 * k * c / secs / 1e12)
+    single = {"value": round(rate(count, t), 6), "cores": 1,
               "sample": f"{count} randomly placed outputs, {t:.2f} s"}
     # the same oracle, the sampled outputs split over the host's cores
     threads = host_threads()
@@ -481,17 +491,21 @@ def gemm_cpu_baseline(a, sa, w, sw, b, k: int, budget_s: float):
     cols = rng.integers(0, w.shape[0], count_mt)
     t_mt = threaded_wall(lambda lo, hi: oracle.w8a8_gemm_at(a, sa, w, sw, b, rows[lo:hi],
                                                             cols[lo:hi]), count_mt, threads)
-    tops_mt = 2.0 * k * count_mt / t_mt / 1e12
-    return {"value": round(tops_mt, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+    return {"value": round(rate(count_mt, t_mt), 6), "unit": "GB/s" if step_bytes else "TOPS",
+            "cores": threads, "kind": "oracle",
             "sample": f"{count_mt} randomly placed outputs of the same seeded inputs "
                       f"(2*k ops each) split over {threads} threads, {t_mt:.2f} s wall, "
-                      f"plain-C int64 oracle",
+                      f"plain-C int64 oracle" +
+                      (f"; as GB/s: {step_bytes} bytes per step times the share of the "
+                       f"step's {outputs} outputs done per second" if step_bytes else ""),
             "single_thread": single}
 
 
 def bench_gemm(args, torch, adq, synth) -> None:
     """One step = one launch of the INT8 GEMM with its dequantizing epilogue."""
     w8 = synth.GEMM_WORKLOADS[args.workload]
+    if args.gemm_rows:
+        w8 = dataclasses.replace(w8, name=f"{w8.name}_m{args.gemm_rows}", m=args.gemm_rows)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     a, sa, wq, sw, b = synth.gemm_inputs(w8)
@@ -514,12 +528,22 @@ def bench_gemm(args, torch, adq, synth) -> None:
     ms = start.elapsed_time(end) / args.steps
     ops = 2.0 * w8.m * w8.n * w8.k
     tops = ops / (ms * 1e-3) / 1e12
+    # bytes the product must move: both operands, the scales (and bias), the output
+    out_bytes = {"bf16": 2, "fp16": 2, "f32": 4}[w8.out_dtype]
+    nbytes = (w8.m * w8.k + w8.n * w8.k + 4 * w8.m + 4 * w8.n * (2 if w8.has_bias else 1) +
+              out_bytes * w8.m * w8.n)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    # the roofline of whichever resource bounds the shape: matrix cores for
+    # many rows, reading the weights for few
+    mfma_bound = ops / (INT8_PEAK_TOPS * 1e12) >= nbytes / (HBM_PEAK_GBS * 1e9)
     print(f"[bench] {args.steps} launches: avg {ms * 1e3:.1f} us per launch, "
           f"wall {wall * 1e3:.1f} ms", file=sys.stderr, flush=True)
     result = {
-        "metric": "achieved INT8 TOPS (% of dense MFMA peak), W8A8 GEMM 16384x8192x8192",
-        "value": round(tops, 1),
-        "unit": "TOPS",
+        "metric": (f"achieved INT8 TOPS (% of dense MFMA peak), W8A8 GEMM "
+                   f"{w8.m}x{w8.n}x{w8.k}" if mfma_bound else
+                   f"achieved HBM GB/s (% of peak), W8A8 GEMM {w8.m}x{w8.n}x{w8.k}"),
+        "value": round(tops, 1) if mfma_bound else round(gbs, 1),
+        "unit": "TOPS" if mfma_bound else "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -532,18 +556,24 @@ def bench_gemm(args, torch, adq, synth) -> None:
         "config": {
             "workload": w8.name, "op": "W8A8 GEMM (per-row x per-column scales)",
             "m": w8.m, "n": w8.n, "k": w8.k, "out": w8.out_dtype, "bias": w8.has_bias,
-            "algorithmic_ops_per_step": ops,
-            "pct_of_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
+            "algorithmic_ops_per_step": ops, "algorithmic_bytes_per_step": nbytes,
+            "tops": round(tops, 1), "gbs": round(gbs, 1),
+            "pct_of_peak": round(100 * tops / INT8_PEAK_TOPS, 2) if mfma_bound else
+                           round(100 * gbs / HBM_PEAK_GBS, 2),
             "parallelism": "single GPU",
             "plan": ex.describe(),
         },
-        "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS,
-                     "unit": "TOPS", "frac": round(tops / INT8_PEAK_TOPS, 4),
-                     "traffic": measured_traffic(w8.name)},
+        "roofline": ({"bound": "mfma", "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS,
+                      "unit": "TOPS", "frac": round(tops / INT8_PEAK_TOPS, 4),
+                      "traffic": measured_traffic(w8.name)} if mfma_bound else
+                     {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "traffic": measured_traffic(w8.name)}),
     }
     ex.close()
     result["context"] = device_context(torch, 0)
-    result["cpu_baseline"] = (gemm_cpu_baseline(a, sa, wq, sw, b, w8.k, args.cpu_budget)
+    result["cpu_baseline"] = (gemm_cpu_baseline(a, sa, wq, sw, b, w8.k, args.cpu_budget,
+                                                0 if mfma_bound else nbytes)
                               if args.cpu_budget > 0 else None)
     print(json.dumps(result), flush=True)
 

@@ -275,10 +275,13 @@ void adq_executor_destroy(adq_executor* executor);
  * of at least 4096 columns when there are at most a quarter as many rows
  * as compute units).
  * ADQ_PATH_GENERIC: any n and alignment.
- * GEMM executors: ADQ_PATH_GEMM_TILE128 (128 x 128 output tiles) and
- * ADQ_PATH_GEMM_TILE256 (256 x 256 tiles); AUTO takes 256 once the
- * 256-tiles cover the compute units.  Either accepts any valid GEMM shape;
- * the operator paths are rejected for a GEMM executor and vice versa.
+ * GEMM executors: ADQ_PATH_GEMM_TILE128 (128 x 128 output tiles),
+ * ADQ_PATH_GEMM_TILE256 (256 x 256 tiles) and ADQ_PATH_GEMM_TILE32 (32
+ * columns and up to 128 rows per tile, K split over the wavefronts of the
+ * workgroup, for few rows); AUTO takes the 32-column tiles for few rows,
+ * else 256 once the 256-tiles cover the compute units, else 128.  Each
+ * accepts any valid GEMM shape; the operator paths are rejected for a GEMM
+ * executor and vice versa.
  * AddLora executors: AUTO (the tiled kernel when the shapes and alignments
  * allow it: h1 % 8 == 0, rank 8, 16, 32, 64 or 128, h2 a multiple of 4, h3 and
  * y_offset multiples of 8, aligned tensors, one weight_b[g, layer] under
@@ -292,7 +295,8 @@ typedef enum adq_path {
   ADQ_PATH_SPLIT = 2,
   ADQ_PATH_GENERIC = 3,
   ADQ_PATH_GEMM_TILE128 = 4,
-  ADQ_PATH_GEMM_TILE256 = 5
+  ADQ_PATH_GEMM_TILE256 = 5,
+  ADQ_PATH_GEMM_TILE32 = 6
 } adq_path;
 
 /*

@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "ADQ_OK", 1: "ADQ_ERR_NULLPTR", 2: "ADQ_ERR_PARAM_INVALID",
                 3: "ADQ_ERR_UNSUPPORTED", 4: "ADQ_ERR_WORKSPACE", 5: "ADQ_ERR_RUNTIME"}
 # adq_path
 PATH_AUTO, PATH_ROW, PATH_SPLIT, PATH_GENERIC = 0, 1, 2, 3
-PATH_GEMM_TILE128, PATH_GEMM_TILE256 = 4, 5
+PATH_GEMM_TILE128, PATH_GEMM_TILE256, PATH_GEMM_TILE32 = 4, 5, 6
 MAX_DIMS = 8
 
 EXPORTED = (
@@ -413,7 +413,7 @@ def plan_w8a8_gemm(a, a_scale, w, w_scale, bias=None, out_dtype=None, out=None,
     """Allocate out (unless given) and run GEMM phase 1 on torch tensors:
     a int8 [..., k], a_scale float32 (one per row), w int8 [n, k],
     w_scale float32 [n], bias float32 [n] or None.  `path` may force a tile
-    size (PATH_GEMM_TILE128 / PATH_GEMM_TILE256)."""
+    size (PATH_GEMM_TILE128 / PATH_GEMM_TILE256 / PATH_GEMM_TILE32)."""
     torch = _torch()
     if out is None:
         out = torch.empty(tuple(a.shape[:-1]) + (w.shape[0],),

@@ -818,8 +818,12 @@ adq_status adq_rms_norm_dynamic_quant(void* workspace, uint64_t workspace_size,
   return run(workspace, workspace_size, executor, hip_stream, kOpRmsNorm);
 }
 
-// large tiles once there are enough of them to occupy every compute unit
+// 32-column tiles for few rows (the product is then bound by reading the
+// weights, and larger tiles leave CUs idle); large tiles once there are
+// enough of them to occupy every compute unit
+constexpr int64_t kGemmSkinnyMaxRows = 128;
 static int gemm_auto_tile(const adq_executor& e) {
+  if (e.gemm.m <= kGemmSkinnyMaxRows) return adq::kGemmTileSkinny;
   const int64_t big = ((e.gemm.m + 255) / 256) * ((e.gemm.n + 255) / 256);
   return big >= e.cus ? adq::kGemmTile256 : adq::kGemmTile128;
 }
@@ -1045,6 +1049,7 @@ adq_status adq_executor_set_path(adq_executor* executor, int32_t path, uint64_t*
     if (path == ADQ_PATH_AUTO) executor->gemm_tile = gemm_auto_tile(*executor);
     else if (path == ADQ_PATH_GEMM_TILE128) executor->gemm_tile = adq::kGemmTile128;
     else if (path == ADQ_PATH_GEMM_TILE256) executor->gemm_tile = adq::kGemmTile256;
+    else if (path == ADQ_PATH_GEMM_TILE32) executor->gemm_tile = adq::kGemmTileSkinny;
     else return fail(ADQ_ERR_PARAM_INVALID, "a GEMM executor takes AUTO or a GEMM tile path");
     executor->path = path;
     *workspace_size = 0;
@@ -1059,7 +1064,8 @@ adq_status adq_executor_set_path(adq_executor* executor, int32_t path, uint64_t*
     *workspace_size = executor->ws_bytes;
     return ok();
   }
-  if (path == ADQ_PATH_GEMM_TILE128 || path == ADQ_PATH_GEMM_TILE256)
+  if (path == ADQ_PATH_GEMM_TILE128 || path == ADQ_PATH_GEMM_TILE256 ||
+      path == ADQ_PATH_GEMM_TILE32)
     return fail(ADQ_ERR_PARAM_INVALID, "GEMM tile paths apply to GEMM executors only");
   adq_executor trial = *executor;
   adq_status st = plan(&trial, path);
@@ -1120,7 +1126,8 @@ int32_t adq_executor_describe(const adq_executor* e, char* buf, uint64_t len) {
     if (buf && len > 0)
       snprintf(buf, (size_t)len, "path=gemm m=%lld n=%lld k=%lld tile=%d out=%d cus=%d",
                (long long)e->gemm.m, (long long)e->gemm.n, (long long)e->gemm.k,
-               e->gemm_tile == adq::kGemmTile256 ? 256 : 128, e->gemm.out_type, e->cus);
+               e->gemm_tile == adq::kGemmTile256 ? 256 : e->gemm_tile == adq::kGemmTileSkinny ? 32 : 128,
+               e->gemm.out_type, e->cus);
     return e->path;
   }
   if (buf && len > 0) {

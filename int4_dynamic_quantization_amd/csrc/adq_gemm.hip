@@ -472,6 +472,147 @@ __global__ void __launch_bounds__(256) w8a8_big_kernel(const GemmArgs g) {
     }
 }
 
+// ---- few rows: w8a8_skinny_kernel
+// With few rows the product is bound by reading the weights (n x k bytes),
+// and output tiles of 128 rows or more leave most CUs idle.  Here a
+// workgroup owns 32 columns and all rows of a 32 * TM row block, and its four
+// wavefronts split K: wavefront w takes the 128-byte K chunks w, w + 4, ...
+// (4 MFMA steps each), requested D chunks ahead into a ring of registers
+// (every load is issued, past K or the tile's rows it reads 0 through the
+// buffer range check, so each wait counts exactly).  The four int32 partial
+// sums of every output meet in LDS and are added exactly (integer addition);
+// the epilogue is the same as the other kernels'.  Workgroups of one column
+// block are consecutive on one XCD, so a weight block read by several row
+// blocks is shared in that XCD's L2.
+constexpr int kSkinnyCols = 32;
+constexpr int kSkinnyChunk = 128;  // K bytes per chunk (4 MFMA steps)
+
+template <int TM> constexpr int skinny_depth() { return TM >= 4 ? 3 : 4; }
+
+template <int TM, int OUT>
+__global__ void __launch_bounds__(256) w8a8_skinny_kernel(const GemmArgs g) {
+  constexpr int D = skinny_depth<TM>();
+  constexpr int BM = 32 * TM;
+  __shared__ int32_t part[4][TM][16][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  // ---- tile: column blocks dealt to XCDs in contiguous ranges, the row
+  // blocks of a column block consecutive
+  const int64_t tiles_m = (g.m + BM - 1) / BM;
+  const int64_t tiles_n = (g.n + kSkinnyCols - 1) / kSkinnyCols;
+  const int64_t tiles = tiles_m * tiles_n;
+  const int64_t b = blockIdx.x;
+  const int64_t per_xcd = (tiles + kXcdCount - 1) / kXcdCount;
+  const int64_t t = (b % kXcdCount) * per_xcd + b / kXcdCount;
+  if (t >= tiles) return;
+  const int64_t tn = t / tiles_m, tm = t % tiles_m;
+  const int64_t m0 = tm * BM, n0 = tn * kSkinnyCols;
+  const int64_t a_rows = g.m - m0 < BM ? g.m - m0 : BM;
+  const int64_t w_rows = g.n - n0 < kSkinnyCols ? g.n - n0 : kSkinnyCols;
+  const rsrc_t ra = make_rsrc(g.a + m0 * g.k, (uint32_t)(a_rows * g.k));
+  const rsrc_t rw = make_rsrc(g.w + n0 * g.k, (uint32_t)(w_rows * g.k));
+  constexpr uint32_t kOut = 0x80000000u;  // beyond any tile descriptor
+
+  // this lane's fragment row (A) / column (W) and its 16 bytes of each
+  // 32-byte MFMA step
+  const uint32_t frow = (uint32_t)(lane & 31);
+  const int64_t fk = (lane >> 5) * 16;
+  const int64_t nchunks = (g.k + kSkinnyChunk - 1) / kSkinnyChunk;
+  const int64_t rounds = (nchunks + 3) / 4;  // chunks per wavefront (the last ones may be past K)
+
+  i32x4 ra_[D][TM][4], rw_[D][4];
+  auto issue = [&](int slot, int64_t round) {
+    const int64_t c = round * 4 + wave;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int64_t k = c * kSkinnyChunk + s * 32 + fk;
+      const bool in = k < g.k;
+      rw_[slot][s] = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, in ? (uint32_t)(frow * g.k + k) : kOut, 0, 0));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        ra_[slot][i][s] = __builtin_bit_cast(
+            i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       ra, in ? (uint32_t)((i * 32 + frow) * g.k + k) : kOut, 0, 0));
+    }
+  };
+
+  i32x16 acc[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) acc[i] = i32x16{};
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d, d);
+  for (int64_t r = 0; r < rounds; r += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ra_[d][i][s], rw_[d][s], acc[i], 0, 0, 0);
+      issue(d, r + d + D);  // past the last round: reads 0, never used
+    }
+  }
+
+  // ---- the four wavefronts' partial sums, added in LDS
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) part[wave][i][e][lane] = acc[i][e];
+  __syncthreads();
+
+  // ---- epilogue: out = float(sum) * a_scale[row] * w_scale[col] (+ bias[col])
+  const rsrc_t rsa = make_rsrc(g.a_scale + m0, (uint32_t)(a_rows * 4));
+  const rsrc_t rsw = make_rsrc(g.w_scale + n0, (uint32_t)(w_rows * 4));
+  const rsrc_t rb = make_rsrc(g.bias ? g.bias + n0 : g.w_scale + n0,
+                              g.bias ? (uint32_t)(w_rows * 4) : 0u);
+  constexpr int OB = OUT == kGemmOutF32 ? 4 : 2;  // output bytes
+  const int64_t out_bytes = a_rows * g.n * OB;
+  const rsrc_t ro = make_rsrc(static_cast<int8_t*>(g.out) + m0 * g.n * OB,
+                              (uint32_t)(out_bytes < 0x7FFFFFFF ? out_bytes : 0x7FFFFFFF));
+  const int col = lane & 31;
+  const uint32_t col_off = n0 + col < g.n ? (uint32_t)((n0 + col) * OB) : kOut;
+  const float swv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsw, col * 4, 0, 0));
+  const float bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, col * 4, 0, 0));
+#pragma unroll
+  for (int q = 0; q < 4 * TM; ++q) {
+    const int idx = q * 256 + tid;  // (i, e, lane) of the accumulator layout
+    const int i = idx >> 10, e = (idx >> 6) & 15;
+    const int32_t sum = part[0][i][e][lane] + part[1][i][e][lane] + part[2][i][e][lane] +
+                        part[3][i][e][lane];
+    const int row = i * 32 + (e / 4) * 8 + (lane >> 5) * 4 + (e & 3);
+    const float sa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, row * 4, 0, 0));
+    const float v = (float)sum * sa * swv + bv;
+    const uint32_t off = col_off == kOut ? kOut : (uint32_t)(row * g.n * OB) + col_off;
+    if constexpr (OUT == kGemmOutF32) {
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ro, off, 0, kStreamStore);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b16(narrow1<OUT == kGemmOutBF16 ? kBF16 : kF16>(v), ro,
+                                            off, 0, kStreamStore);
+    }
+  }
+}
+
+template <int TM, int OUT>
+hipError_t launch_skinny(const GemmArgs& g, hipStream_t s) {
+  const int64_t tiles = ((g.m + 32 * TM - 1) / (32 * TM)) * ((g.n + kSkinnyCols - 1) / kSkinnyCols);
+  const int64_t grid = (tiles + kXcdCount - 1) / kXcdCount * kXcdCount;
+  hipLaunchKernelGGL((w8a8_skinny_kernel<TM, OUT>), dim3((unsigned)grid), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+template <int TM>
+hipError_t launch_skinny_out(const GemmArgs& g, hipStream_t s) {
+  switch (g.out_type) {
+    case kGemmOutF32: return launch_skinny<TM, kGemmOutF32>(g, s);
+    case kGemmOutBF16: return launch_skinny<TM, kGemmOutBF16>(g, s);
+    case kGemmOutF16: return launch_skinny<TM, kGemmOutF16>(g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int BK, int STAGES, int OUT>
 hipError_t launch_big(const GemmArgs& g, hipStream_t s) {
   const int64_t tiles = ((g.m + 255) / 256) * ((g.n + 255) / 256);
@@ -517,6 +658,10 @@ hipError_t launch_w8a8(const GemmArgs& g, int tile, hipStream_t stream) {
   switch (tile) {
     case kGemmTile128: return launch_out<2, 2, 128>(g, stream);
     case kGemmTile256: return launch_big_out<kBigTileK, kBigTileStages>(g, stream);
+    case kGemmTileSkinny:
+      return g.m <= 32 ? launch_skinny_out<1>(g, stream)
+             : g.m <= 64 ? launch_skinny_out<2>(g, stream)
+                         : launch_skinny_out<4>(g, stream);
     default: return hipErrorInvalidValue;
   }
 }

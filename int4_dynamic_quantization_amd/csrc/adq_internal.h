@@ -94,7 +94,7 @@ hipError_t launch_generic(const Variant& v, int block, int grid, const Args& a,
 
 // INT8 x INT8 GEMM with per-row / per-column scales (consumer of the codes).
 enum GemmOut : int { kGemmOutF32 = 0, kGemmOutBF16 = 1, kGemmOutF16 = 2 };
-enum GemmTile : int { kGemmTile128 = 1, kGemmTile256 = 2 };
+enum GemmTile : int { kGemmTile128 = 1, kGemmTile256 = 2, kGemmTileSkinny = 3 };
 
 struct GemmArgs {
   const int8_t* a;        // [m, k] row-major (activation codes)

@@ -13,9 +13,10 @@ Bars:
        |got - exact| <= 5 * 2^-24 * (|P| + |bias|) + u_s * |exact| + sub
    with exact = the oracle's double result;
  - every output is written (outputs are pre-filled with NaN).
-Shapes span several tiles of both tile sizes, ragged M, N and K (K a
-multiple of 16), leading dimensions, and the full projection size
-16384 x 8192 x 8192 on sampled outputs.
+Shapes span several tiles of every tile size, ragged M, N and K (K a
+multiple of 16), leading dimensions, the full projection size
+16384 x 8192 x 8192 and the few-row projections that follow decode-sized
+batches (1 to 200 rows of 8192 x 8192) on sampled outputs.
 """
 import numpy as np
 import pytest
@@ -36,8 +37,9 @@ def codes(seed, tid, rows, cols, lo=-127, hi=127):
     return synth.int8_codes(seed, tid, rows, cols, lo, hi)
 
 
-TILES = [adq.PATH_GEMM_TILE128, adq.PATH_GEMM_TILE256]
-TILE_IDS = ["tile128", "tile256"]
+TILES = [adq.PATH_GEMM_TILE128, adq.PATH_GEMM_TILE256, adq.PATH_GEMM_TILE32]
+TILE_IDS = ["tile128", "tile256", "tile32"]
+TILE_SIZE = {adq.PATH_GEMM_TILE128: 128, adq.PATH_GEMM_TILE256: 256, adq.PATH_GEMM_TILE32: 32}
 
 
 def run_gemm(a, sa, w, sw, bias=None, out="bf16", lead=None, path=adq.PATH_AUTO):
@@ -99,7 +101,7 @@ def test_integer_sums_exact(m, n, k, path):
     w = codes(11, 9, n, k)
     ones_m, ones_n = np.ones(m, np.float32), np.ones(n, np.float32)
     got, desc = run_gemm(a, ones_m, w, ones_n, out="f32", path=path)
-    assert tile_of(desc) == (128 if path == adq.PATH_GEMM_TILE128 else 256), desc
+    assert tile_of(desc) == TILE_SIZE[path], desc
     sums, _ = oracle.w8a8_gemm(a, ones_m, w, ones_n)
     assert np.abs(sums).max() <= 2 ** 24
     assert np.array_equal(got, sums.astype(np.float32)), desc
@@ -187,7 +189,7 @@ def test_large_ragged_sampled(m, n, k, out, path):
     w8 = synth.GemmWorkload("t", m, n, k, 31, out, True)
     a, sa, w, sw, b = synth.gemm_inputs(w8)
     got, desc = run_gemm(a, sa, w, sw, b, out=out, path=path)
-    assert tile_of(desc) in (128, 256), desc
+    assert tile_of(desc) in (32, 128, 256), desc
     assert np.isfinite(got).all(), "output not written"
     rows, cols = sample_positions(m, n, tile_of(desc), np.random.default_rng(m))
     sums, exact = oracle.w8a8_gemm_at(a, sa, w, sw, b, rows, cols)
@@ -234,12 +236,17 @@ def test_paths():
     sa = torch.ones(4, device="cuda")
     sw = torch.ones(8, device="cuda")
     ex, _ = adq.plan_w8a8_gemm(a, sa, w, sw)
-    assert tile_of(ex.describe()) == 128  # one tile: too few for the large tiles
-    for p in (adq.PATH_ROW, adq.PATH_SPLIT, adq.PATH_GENERIC, 6):
+    assert tile_of(ex.describe()) == 32  # few rows: 32-column tiles
+    for p in (adq.PATH_ROW, adq.PATH_SPLIT, adq.PATH_GENERIC, 7):
         with pytest.raises(adq.AdqError):
             ex.set_path(p)
     assert ex.set_path(adq.PATH_GEMM_TILE256) == 0 and tile_of(ex.describe()) == 256
-    assert ex.set_path(adq.PATH_AUTO) == 0 and tile_of(ex.describe()) == 128
+    assert ex.set_path(adq.PATH_GEMM_TILE128) == 0 and tile_of(ex.describe()) == 128
+    assert ex.set_path(adq.PATH_AUTO) == 0 and tile_of(ex.describe()) == 32
+    ex.close()
+    a = torch.zeros(300, 32, dtype=torch.int8, device="cuda")
+    ex, _ = adq.plan_w8a8_gemm(a, torch.ones(300, device="cuda"), w, sw)
+    assert tile_of(ex.describe()) == 128  # more rows, still too few 256-tiles
     ex.close()
     # and the operator's executors refuse the GEMM tile paths
     x = torch.zeros(4, 64, dtype=torch.bfloat16, device="cuda")
@@ -249,3 +256,37 @@ def test_paths():
         with pytest.raises(adq.AdqError):
             ex.set_path(p)
     ex.close()
+
+
+# ---- few rows (32-column tiles, K split over the wavefronts)
+
+SKINNY_EXACT = [(1, 1, 16), (1, 33, 112), (17, 31, 4096), (32, 64, 8208), (33, 40, 1040),
+                (64, 96, 2064), (65, 32, 4096), (100, 70, 528), (128, 33, 4112), (200, 65, 1040)]
+
+
+@pytest.mark.parametrize("m,n,k", SKINNY_EXACT)
+def test_few_rows_integer_sums_exact(m, n, k):
+    """Every row block size (32, 64, 128 rows and several blocks), ragged N,
+    K past and short of a whole number of 128-byte chunks per wavefront."""
+    a = codes(13, 7, m, k)
+    w = codes(13, 9, n, k)
+    ones_m, ones_n = np.ones(m, np.float32), np.ones(n, np.float32)
+    got, desc = run_gemm(a, ones_m, w, ones_n, out="f32", path=adq.PATH_GEMM_TILE32)
+    assert tile_of(desc) == 32, desc
+    sums, _ = oracle.w8a8_gemm(a, ones_m, w, ones_n)
+    assert np.abs(sums).max() <= 2 ** 24
+    assert np.array_equal(got, sums.astype(np.float32)), desc
+
+
+@pytest.mark.parametrize("m", [1, 32, 64, 128, 200])
+def test_few_rows_projection_sampled(m):
+    """8192 x 8192 projections of decode-sized batches (AUTO), bf16 out with
+    bias, against the oracle on sampled outputs (every output written)."""
+    w8 = synth.GemmWorkload("t", m, 8192, 8192, 51 + m, "bf16", True)
+    a, sa, w, sw, b = synth.gemm_inputs(w8)
+    got, desc = run_gemm(a, sa, w, sw, b, out="bf16")
+    assert tile_of(desc) == (32 if m <= 128 else 128), desc
+    assert np.isfinite(got).all(), "output not written"
+    rows, cols = sample_positions(m, 8192, 32, np.random.default_rng(m), count=3000)
+    sums, exact = oracle.w8a8_gemm_at(a, sa, w, sw, b, rows, cols)
+    check_scaled(got[rows, cols], sums, exact, sa[rows], sw[cols], b[cols], "bf16")
