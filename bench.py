@@ -68,10 +68,12 @@ _PATH_SOURCES = {
 
 
 def path_of(workload: str) -> str:
+    """Kernel family of a workload, also of the names derived from one
+    (w8a8_gemm_m32: another row count; lora_prefill_rank64: another rank)."""
     import synth
-    if workload in synth.GEMM_WORKLOADS:
+    if workload.startswith(tuple(synth.GEMM_WORKLOADS)):
         return "gemm"
-    return "lora" if workload in synth.LORA_WORKLOADS else "operator"
+    return "lora" if workload.startswith(tuple(synth.LORA_WORKLOADS)) else "operator"
 
 
 def kernel_source_hash(workload: str = "v2_outlier") -> str:
