@@ -477,15 +477,19 @@ __global__ void __launch_bounds__(256) w8a8_big_kernel(const GemmArgs g) {
 // and output tiles of 128 rows or more leave most CUs idle.  Here a
 // workgroup owns 32 columns and all rows of a 32 * TM row block, and its four
 // wavefronts split K: wavefront w takes the 128-byte K chunks w, w + 4, ...
-// (4 MFMA steps each), requested D chunks ahead into a ring of registers
-// (every load is issued, past K or the tile's rows it reads 0 through the
-// buffer range check, so each wait counts exactly).  The four int32 partial
-// sums of every output meet in LDS and are added exactly (integer addition);
-// the epilogue is the same as the other kernels'.  Workgroups of one column
+// (two 64-byte MFMA steps each), requested D chunks ahead into a ring of
+// registers straight from global memory (every load is issued, past K or
+// the tile's rows it reads 0 through the buffer range check, so each wait
+// counts exactly).  The products are v_mfma_i32_16x16x64_i8: its fragments
+// are 16 rows of 64 contiguous bytes (lane l: row l % 16, bytes
+// 16 (l / 16) .. + 16), so a fragment load touches 16 rows' cache lines,
+// half as many as the 32 x 32 x 32 form's.  The four int32 partial sums of
+// every output meet in LDS and are added exactly (integer addition); the
+// epilogue is the same as the other kernels'.  Workgroups of one column
 // block are consecutive on one XCD, so a weight block read by several row
 // blocks is shared in that XCD's L2.
 constexpr int kSkinnyCols = 32;
-constexpr int kSkinnyChunk = 128;  // K bytes per chunk (4 MFMA steps)
+constexpr int kSkinnyChunk = 128;  // K bytes per chunk (2 MFMA steps of 64)
 
 template <int TM> constexpr int skinny_depth() { return TM >= 4 ? 3 : 4; }
 
@@ -493,7 +497,8 @@ template <int TM, int OUT>
 __global__ void __launch_bounds__(256) w8a8_skinny_kernel(const GemmArgs g) {
   constexpr int D = skinny_depth<TM>();
   constexpr int BM = 32 * TM;
-  __shared__ int32_t part[4][TM][16][64];
+  constexpr int RB = 2 * TM;  // 16-row blocks
+  __shared__ int32_t part[4][RB][2][4][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -515,55 +520,65 @@ __global__ void __launch_bounds__(256) w8a8_skinny_kernel(const GemmArgs g) {
   const rsrc_t rw = make_rsrc(g.w + n0 * g.k, (uint32_t)(w_rows * g.k));
   constexpr uint32_t kOut = 0x80000000u;  // beyond any tile descriptor
 
-  // this lane's fragment row (A) / column (W) and its 16 bytes of each
-  // 32-byte MFMA step
-  const uint32_t frow = (uint32_t)(lane & 31);
-  const int64_t fk = (lane >> 5) * 16;
+  // this lane's fragment row (of a 16-row block) and its 16 bytes of each
+  // 64-byte MFMA step
+  const uint32_t frow = (uint32_t)(lane & 15);
+  const int64_t fk = (lane >> 4) * 16;
   const int64_t nchunks = (g.k + kSkinnyChunk - 1) / kSkinnyChunk;
   const int64_t rounds = (nchunks + 3) / 4;  // chunks per wavefront (the last ones may be past K)
 
-  i32x4 ra_[D][TM][4], rw_[D][4];
+  i32x4 ra_[D][2][RB], rw_[D][2][2];
   auto issue = [&](int slot, int64_t round) {
     const int64_t c = round * 4 + wave;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int64_t k = c * kSkinnyChunk + s * 32 + fk;
+    for (int s = 0; s < 2; ++s) {
+      const int64_t k = c * kSkinnyChunk + s * 64 + fk;
       const bool in = k < g.k;
-      rw_[slot][s] = __builtin_bit_cast(
-          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, in ? (uint32_t)(frow * g.k + k) : kOut, 0, 0));
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        ra_[slot][i][s] = __builtin_bit_cast(
+      for (int j = 0; j < 2; ++j)
+        rw_[slot][s][j] = __builtin_bit_cast(
             i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                       ra, in ? (uint32_t)((i * 32 + frow) * g.k + k) : kOut, 0, 0));
+                       rw, in ? (uint32_t)((j * 16 + frow) * g.k + k) : kOut, 0, 0));
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+        ra_[slot][s][i] = __builtin_bit_cast(
+            i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       ra, in ? (uint32_t)((i * 16 + frow) * g.k + k) : kOut, 0, 0));
     }
   };
 
-  i32x16 acc[TM];
+  i32x4 acc[RB][2];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) acc[i] = i32x16{};
+  for (int i = 0; i < RB; ++i) acc[i][0] = acc[i][1] = i32x4{};
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d, d);
   for (int64_t r = 0; r < rounds; r += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-          acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ra_[d][i][s], rw_[d][s], acc[i], 0, 0, 0);
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra_[d][s][i], rw_[d][s][j], acc[i][j],
+                                                              0, 0, 0);
       issue(d, r + d + D);  // past the last round: reads 0, never used
     }
   }
 
   // ---- the four wavefronts' partial sums, added in LDS
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < RB; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) part[wave][i][e][lane] = acc[i][e];
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part[wave][i][j][e][lane] = acc[i][j][e];
   __syncthreads();
 
-  // ---- epilogue: out = float(sum) * a_scale[row] * w_scale[col] (+ bias[col])
+  // ---- epilogue: out = float(sum) * a_scale[row] * w_scale[col] (+ bias[col]);
+  // element e of lane l in block (i, j) is row 16 i + 4 (l / 16) + e, column
+  // 16 j + l % 16
   const rsrc_t rsa = make_rsrc(g.a_scale + m0, (uint32_t)(a_rows * 4));
   const rsrc_t rsw = make_rsrc(g.w_scale + n0, (uint32_t)(w_rows * 4));
   const rsrc_t rb = make_rsrc(g.bias ? g.bias + n0 : g.w_scale + n0,
@@ -572,20 +587,20 @@ __global__ void __launch_bounds__(256) w8a8_skinny_kernel(const GemmArgs g) {
   const int64_t out_bytes = a_rows * g.n * OB;
   const rsrc_t ro = make_rsrc(static_cast<int8_t*>(g.out) + m0 * g.n * OB,
                               (uint32_t)(out_bytes < 0x7FFFFFFF ? out_bytes : 0x7FFFFFFF));
-  const int col = lane & 31;
-  const uint32_t col_off = n0 + col < g.n ? (uint32_t)((n0 + col) * OB) : kOut;
-  const float swv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsw, col * 4, 0, 0));
-  const float bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, col * 4, 0, 0));
 #pragma unroll
   for (int q = 0; q < 4 * TM; ++q) {
-    const int idx = q * 256 + tid;  // (i, e, lane) of the accumulator layout
-    const int i = idx >> 10, e = (idx >> 6) & 15;
-    const int32_t sum = part[0][i][e][lane] + part[1][i][e][lane] + part[2][i][e][lane] +
-                        part[3][i][e][lane];
-    const int row = i * 32 + (e / 4) * 8 + (lane >> 5) * 4 + (e & 3);
+    const int idx = q * 256 + tid;  // (i, j, e, lane) of the accumulator layout
+    const int i = idx >> 9, j = (idx >> 8) & 1, e = (idx >> 6) & 3;
+    const int32_t sum = part[0][i][j][e][lane] + part[1][i][j][e][lane] +
+                        part[2][i][j][e][lane] + part[3][i][j][e][lane];
+    const int row = i * 16 + 4 * (lane >> 4) + e;
+    const int col = j * 16 + (lane & 15);
     const float sa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, row * 4, 0, 0));
+    const float swv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsw, col * 4, 0, 0));
+    const float bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, col * 4, 0, 0));
     const float v = (float)sum * sa * swv + bv;
-    const uint32_t off = col_off == kOut ? kOut : (uint32_t)(row * g.n * OB) + col_off;
+    const uint32_t off = n0 + col < g.n ? (uint32_t)(row * g.n * OB) + (uint32_t)((n0 + col) * OB)
+                                        : kOut;
     if constexpr (OUT == kGemmOutF32) {
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ro, off, 0, kStreamStore);
     } else {
