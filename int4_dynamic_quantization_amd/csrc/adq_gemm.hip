@@ -8,9 +8,11 @@
 //
 // with the integer sum exact in int32 (|k| <= 2^17 keeps it in range).
 //
-// Two kernels, both built on v_mfma_i32_32x32x32_i8 with a workgroup of 2 x 2
-// wavefronts: w8a8_kernel (128 x 128 tiles, for problems with few tiles) and
-// w8a8_big_kernel (256 x 256 tiles, described at its definition).
+// Three kernels with workgroups of four wavefronts: w8a8_kernel (128 x 128
+// tiles, for problems with few tiles) and w8a8_big_kernel (256 x 256 tiles,
+// described at its definition), both on v_mfma_i32_32x32x32_i8, and
+// w8a8_skinny_kernel (32 columns and up to 128 rows, for few rows, on
+// v_mfma_i32_16x16x64_i8; described at its definition).
 //
 // w8a8_kernel: each wavefront owns (32*TM) x (32*TN) outputs as TM x TN MFMA
 // blocks.  K advances in steps of BK bytes through a double buffer in LDS:
