@@ -285,7 +285,7 @@ void adq_executor_destroy(adq_executor* executor);
  * AddLora executors: AUTO (the tiled kernel when the shapes and alignments
  * allow it: h1 % 8 == 0, rank 8, 16, 32, 64 or 128, h2 a multiple of 4, h3 and
  * y_offset multiples of 8, aligned tensors, one weight_b[g, layer] under
- * 4 GiB; a batch whose y or x reaches 4 GiB runs as consecutive launch
+ * 4 GiB and one weight_a[g, layer] under 2 GiB; a batch whose y or x reaches 4 GiB runs as consecutive launch
  * sequences over row ranges below it, on the same stream and workspace) or
  * ADQ_PATH_GENERIC (one workgroup per row, any shape).
  */

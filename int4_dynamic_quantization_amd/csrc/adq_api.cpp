@@ -905,6 +905,15 @@ adq_status adq_w8a8_gemm(void* workspace, uint64_t workspace_size, adq_executor*
   return run(workspace, workspace_size, executor, hip_stream, kOpGemm);
 }
 
+// Shrink workgroups aimed at per two CUs when h1 is cut into slices (the
+// slices are further capped so that all workgroups are resident at once);
+// half as many at rank 128, where every slice adds 64 x 128 partial sums
+// per tile that each expand workgroup of the tile reads.  Step time on 4096
+// rows, h1 4096 -> h2 4096, 8 adapters (72 tiles), slices 3 / 4 / 6 / 8:
+// rank 16 40.2 / 38.9 / 37.8 / 37.8 us, rank 64 56.2 / 56.6 / 55.4 / 57.8,
+// rank 128 70.3 / 74.9 / 73.6 / 78.2 (3 slices: one workgroup per CU).
+constexpr int64_t kShrinkWgPerTwoCus = 3;
+
 adq_status adq_add_lora_get_workspace_size(const adq_tensor* y, const adq_tensor* x,
                                            const adq_tensor* weight_b,
                                            const adq_tensor* indices,
@@ -1007,18 +1016,20 @@ adq_status adq_add_lora_get_workspace_size(const adq_tensor* y, const adq_tensor
                     h2 % 4 == 0 && h3 % 8 == 0 && y_offset % 8 == 0 && aligned(x->data, 16) &&
                     (!weight_a || aligned(weight_a->data, 16)) && aligned(weight_b->data, 8) &&
                     aligned(y->data, 16) && aligned(out->data, 8) && chunk_rows >= 1 &&
-                    rank * h2 * 2 < (int64_t)1 << 32;  // 32-bit offsets into weightB[g, layer]
+                    rank * h2 * 2 < (int64_t)1 << 32 &&  // 32-bit offsets into weightB[g, layer]
+                    h1 * rank * 2 < (int64_t)1 << 31;    // and into weightA[g, layer]
   {
     // Tiles are only known on the device (they depend on the index values);
     // estimate them as rows / 64 plus one partial tile per adapter in use.
-    // Slices of h1 per tile (shrink) are chosen for about four workgroups
-    // per CU, each slice at least 256 k; the expand takes ranges of 1024
+    // Slices of h1 per tile (shrink) are chosen for the workgroups per CU
+    // above, each slice at least 256 k; the expand takes ranges of 1024
     // columns of the slice.
     const int64_t est_tiles = (chunk_rows + adq::kLoraTileRows - 1) / adq::kLoraTileRows +
                               (w < chunk_rows ? w : chunk_rows);
     // ... but no more than fit on the chip at once (ranks whose shrink
     // holds fewer workgroups per CU would otherwise run a second round)
-    int64_t want = (2 * (int64_t)e.cus + est_tiles - 1) / est_tiles;
+    const int64_t slots = kShrinkWgPerTwoCus * (int64_t)e.cus / (rank >= 128 ? 4 : 2);
+    int64_t want = (slots + est_tiles - 1) / est_tiles;
     adq::LoraArgs part = a;
     part.rows = chunk_rows;
     const int64_t fit = (int64_t)adq::lora_shrink_blocks_per_cu(part) * e.cus / est_tiles;

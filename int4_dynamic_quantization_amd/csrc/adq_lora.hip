@@ -20,8 +20,8 @@
 //     The stage of weightA[g, layer] (stored [h1, rank], rank contiguous) is
 //     staged in LDS transposed, so each MFMA operand is one 16-byte read; the
 //     stage of x (64 rows) reaches LDS through direct-to-LDS loads in whole
-//     row pieces, double-buffered (the next stage requested before the
-//     current one is staged and multiplied); 4 wavefronts each take 16 rows
+//     row pieces, through a ring of LDS buffers (two stages in flight while
+//     a third is multiplied; weightA one stage ahead); 4 wavefronts each take 16 rows
 //     (v_mfma_f32_16x16x32_{bf16,f16}) and write fp32 partial sums to the
 //     workspace.
 //  3. expand: one workgroup per (16 rows of a tile, 1024 columns of the
@@ -388,14 +388,14 @@ template <int E, int R, bool G>
 __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a, Workspace ws) {
   constexpr int RP = padded_rank<R>();
   constexpr int KS = stage_k<R>();
-  // x stage in LDS: 64 rows of KS k, filled by direct-to-LDS loads (1 KB
-  // per instruction: RPS whole rows of CPR 16-byte chunks); the chunk c of
-  // row r sits at position c ^ (r % 16), so the 16-byte MFMA fragment reads
-  // of 16 rows hit distinct banks
+  // x stage in LDS: 64 rows of KS k, each wave's 16-byte loads landing as
+  // 1 KB pieces (RPS whole rows of CPR 16-byte chunks, lane l at byte 16 l);
+  // the chunk c of row r sits at position c ^ (r % 16), so the 16-byte MFMA
+  // fragment reads of 16 rows hit distinct banks
   constexpr int CPR = KS / 8, RPS = 64 / CPR, SPW = kTile / RPS / 4;
   __shared__ int64_t rows_lds[kTile];
   __shared__ __attribute__((aligned(16))) uint16_t at[RP][at_stride<R>()];
-  __shared__ __attribute__((aligned(1024))) uint16_t xs[2 * kTile * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kTile * KS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -456,87 +456,94 @@ __global__ void __launch_bounds__(kThreads) lora_shrink_kernel(const LoraArgs a,
     xk[i] = 8 * c;
     xo[i] = r < n ? (uint32_t)(rows_lds[r] * h1 * 2) + 16u * c : 0xFFFFFFFFu;
   }
-  using lds_ptr = __attribute__((address_space(3))) void*;
-  uint8_t* xs_wave = reinterpret_cast<uint8_t*>(xs) + wave * SPW * 1024;
-  // x stages are double-buffered: stage st + 1 is requested before stage
-  // st's weightA is staged and its products run.  Barriers carry no memory
-  // fence (which would wait for the stage in flight too): stage st is
-  // awaited explicitly (loads complete in order, so it has landed once at
-  // most the SPW loads of stage st + 1 are outstanding), LDS writes and
-  // reads complete (lgkmcnt) before each barrier.
+  // Pipeline: x and weightA of stage st + 1 are requested, into registers,
+  // while stage st is staged and multiplied (more stages ahead measured
+  // slower: rank 16 shrink 10.95 us with one, 11.84 with two, 13.68 with
+  // three on 4096 rows, h1 4096).  Stages reach LDS through ordinary LDS
+  // writes, not direct-to-LDS loads: a read of LDS that such a load might
+  // still be writing makes the compiler wait for all loads in flight, which
+  // drained the pipeline before every stage (11.43 us).
+  // Lanes with nothing to fetch (rows past the tile, k past the slice) read
+  // past the end of a buffer descriptor, which yields zeros; weightA is
+  // fetched by the threads that stage it only (at rank 16, half a wave: each
+  // load instruction costs issue time whether or not its lanes fetch).
   // weightA stage: blocks of 8 k x 8 ranks, one per thread (threads t and
   // t + 1 take neighbouring 8-k groups of the same 8 ranks), loaded as 8
   // rows of 16 bytes, transposed in registers and written as 8 rank rows
   // of 16 bytes: 16 lanes of a row group write 16 distinct 16-byte slots
   constexpr int KG = KS / 8, NBLK = KG * (R / 8);
   static_assert(NBLK <= kThreads, "one weightA block per thread");
-  auto issue_x = [&](int64_t sub, int buf) {
-    const int sub_n = (int)(k_hi - sub < KS ? k_hi - sub : KS);
+  const int bkg = tid % KG, brg = tid / KG;
+  const bool blk = tid < NBLK;
+  const rsrc_t rwa = make_rsrc(wa, (uint32_t)(h1 * rank * 2));
+  auto stage_n = [&](int64_t sub) -> int {  // k of a stage inside the slice (<= 0 past it)
+    const int64_t v = k_hi - sub;
+    return (int)(v < KS ? (v > 0 ? v : 0) : KS);
+  };
+  auto load_x = [&](int64_t sub, u32x4(&xv)[SPW]) {
+    const int sub_n = stage_n(sub);
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const uint32_t off =
           xo[i] != 0xFFFFFFFFu && xk[i] < sub_n ? xo[i] + (uint32_t)(sub * 2) : 0xFFFFFFF0u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (lds_ptr)(xs_wave + buf * (kTile * KS * 2) + i * 1024), 16, off, 0, 0, kStreamLoad);
+      xv[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, kStreamLoad);
     }
   };
-  auto barrier = [] {
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    __asm__ __volatile__("" ::: "memory");
-  };
-  issue_x(k_lo, 0);
-  int buf = 0;
-  for (int64_t sub = k_lo; sub < k_hi; sub += KS, buf ^= 1) {
-    const int sub_n = (int)(k_hi - sub < KS ? k_hi - sub : KS);
-    const int steps = (sub_n + 31) / 32;
-    const bool more = sub + KS < k_hi;
-    // weightA[sub .. sub + KS) (zeros past the slice), then the next x stage
-    const int bkg = tid % KG, brg = tid / KG;
-    const bool blk = tid < NBLK;
-    u16x8 wv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int k = 8 * bkg + e;
-      wv[e] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (blk && k < sub_n) wv[e] = *reinterpret_cast<const u16x8*>(wa + (sub + k) * rank + 8 * brg);
-    }
-    if (more) issue_x(sub + KS, buf ^ 1);
-    // weightA staged transposed
+  auto load_wa = [&](int64_t sub, u16x8(&w)[8]) {  // threads with a block only
+    const int sub_n = stage_n(sub);
     if (blk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = 8 * bkg + e;
+        const uint32_t off = k < sub_n ? (uint32_t)((sub + k) * rank * 2) + 16u * brg : 0xFFFFFFF0u;
+        w[e] = __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(rwa, off, 0, 0));
+      }
+    }
+  };
+  u32x4* xs_lane = reinterpret_cast<u32x4*>(xs) + (wave * SPW * 64 + lane);
+  auto stage = [&](int st, u32x4(&xv)[SPW], u16x8(&w)[8]) {
+    const int64_t sub = k_lo + (int64_t)st * KS;
+    const int steps = (stage_n(sub) + 31) / 32;
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) xs_lane[i * 64] = xv[i];
+    if (blk) {  // weightA staged transposed
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         u16x8 t;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = wv[e][q];
+        for (int e = 0; e < 8; ++e) t[e] = w[e][q];
         const int r = 8 * brg + q;
         *reinterpret_cast<u16x8*>(&at[r][8 * (bkg ^ (((r >> 3) & 1) << 1))]) = t;
       }
     }
-    if (more) wait_vmcnt<SPW>();
-    else wait_vmcnt<0>();
-    barrier();
-    const uint16_t* xb = xs + buf * (kTile * KS);
+    load_wa(sub + KS, w);
+    load_x(sub + KS, xv);
+    __syncthreads();
     if (rb < n) {  // wavefront-uniform
 #pragma unroll
       for (int u = 0; u < KS / 32; ++u) {
         if (u < steps) {
           const int kg = 4 * u + fk;
-          const u16x8 xa = *reinterpret_cast<const u16x8*>(&xb[(rb + fi) * KS + 8 * (kg ^ fi)]);
+          const u16x8 xa = *reinterpret_cast<const u16x8*>(&xs[(rb + fi) * KS + 8 * (kg ^ fi)]);
 #pragma unroll
           for (int b = 0; b < nb; ++b) {
-            {
-              const int r = 16 * b + fi;
-              const u16x8 bv =
-                  *reinterpret_cast<const u16x8*>(&at[r][8 * (kg ^ (((r >> 3) & 1) << 1))]);
-              acc[b] = mfma16<E>(xa, bv, acc[b]);
-            }
+            const int r = 16 * b + fi;
+            const u16x8 bv =
+                *reinterpret_cast<const u16x8*>(&at[r][8 * (kg ^ (((r >> 3) & 1) << 1))]);
+            acc[b] = mfma16<E>(xa, bv, acc[b]);
           }
         }
       }
     }
-    barrier();  // before the next stage overwrites `at` and this x buffer is refilled
-  }
+    __syncthreads();  // before the next stage overwrites `at` and x
+  };
+  const int nst = k_hi > k_lo ? (int)((k_hi - k_lo + KS - 1) / KS) : 0;
+  u32x4 xv[SPW];
+  u16x8 wv[8];
+  load_wa(k_lo, wv);
+  load_x(k_lo, xv);
+  for (int st = 0; st < nst; ++st) stage(st, xv, wv);
+  wait_vmcnt<0>();  // the requests past the last stage
   // element e of lane l: row rb + 4 * (l / 16) + e, rank l % 16 (+ 16 * block)
   float* zp = ws.z1p + ((int64_t)ks * lora_max_tiles_dev(a) + tile) * kTile * rank;
 #pragma unroll
