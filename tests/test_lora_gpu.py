@@ -119,6 +119,10 @@ EXACT = [
     # rows, h1, rank, h2, h3, w, layers, layer, off, has_a, dt
     (37, 64, 16, 48, 104, 3, 2, 1, 24, True, "bf16"),
     (700, 64, 16, 48, 104, 3, 2, 1, 24, True, "bf16"),  # above 512 rows: grouping launch
+    (700, 64, 16, 48, 104, 100, 2, 1, 24, True, "bf16"),  # 100 adapters
+    (8192, 64, 16, 48, 104, 64, 1, 0, 24, True, "bf16"),  # the largest one-workgroup grouping
+    (5000, 64, 16, 48, 104, 1, 1, 0, 24, True, "fp16"),   # one adapter
+    (4000, 128, 128, 64, 128, 9, 1, 0, 0, True, "bf16"),  # rank 128, 3 slices of h1
     (100, 256, 32, 128, 256, 5, 3, 2, 128, True, "fp16"),
     (17, 16, 16, 64, 64, 2, 1, 0, 0, False, "bf16"),
     (300, 512, 64, 96, 400, 7, 2, 0, 296, True, "bf16"),
@@ -168,6 +172,9 @@ def test_exact_integers(case, path):
     assert ("lora-tiled" if tiled else "lora-generic") in desc, desc
     if tiled:
         assert ("count+place" in desc) == (rows > 8192), desc
+        # up to 512 rows with weightA, the shrink groups the rows itself
+        in_shrink = has_a and rows <= 512
+        assert desc.split("kernels=")[1].startswith("shrink") == in_shrink, desc
     ref, _ = oracle.add_lora(y, x, wb, idx, wa, layer, 0.5, off, dt)
     assert np.array_equal(got, ref), desc
 
