@@ -304,6 +304,27 @@ def test_paths():
     ex.close()
 
 
+@pytest.mark.parametrize("rank,rows,slices", [(16, 4096, 6), (64, 4096, 6), (128, 4096, 3),
+                                               (16, 64, 16), (128, 64, 16)])
+def test_slices_of_h1(rank, rows, slices):
+    """Slices of h1 per tile planned for the prefill and decode shapes (h1
+    4096, 8 adapters) on a 256-CU device: 1.5 shrink workgroups per CU, 0.75 at
+    rank 128, over rows / 64 + 8 estimated tiles, every slice at least 256 k
+    (so at most 16); fewer when the shrink instance holds fewer per CU."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("slice counts stated for 256 CUs")
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(rows, 12288, **bf)
+    x = torch.empty(rows, 4096, **bf)
+    wb = torch.empty(8, 32, rank, 4096, **bf)
+    wa = torch.empty(8, 32, 4096, rank, **bf)
+    idx = torch.zeros(rows, dtype=torch.int32, device="cuda")
+    ex, _ = adq.plan_add_lora(y, x, wb, idx, wa, 7, 0.5, 4096, out=y)
+    desc = ex.describe()
+    ex.close()
+    assert f" ksplit={slices} " in desc, desc
+
+
 @pytest.mark.parametrize("h2,kind", [((1 << 24) - 8, "lora-tiled"), (1 << 24, "lora-generic")])
 def test_offset_limits_select_the_kernel(h2, kind):
     """The tiled kernels address weightB[g, layer] with 32-bit byte offsets
