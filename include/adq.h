@@ -267,11 +267,11 @@ void adq_executor_destroy(adq_executor* executor);
  * Kernel path of an executor.  ADQ_PATH_AUTO is chosen by phase 1 from the
  * shape; the others force a path (for tests and tuning).  ADQ_PATH_ROW:
  * one workgroup per row, 128-bit accesses (n % 8 == 0, 16-byte aligned
- * tensors, n <= 32768).  ADQ_PATH_SPLIT: S workgroups per row, each on a
+ * tensors, n <= 65536).  ADQ_PATH_SPLIT: S workgroups per row, each on a
  * chunk of the row, handing the per-chunk partial sums of squares and
  * maxima over through the workspace, in one launch or in two or three per
  * batch of rows (see adq_executor_set_split; n % 8 == 0, 16-byte aligned
- * tensors; AUTO takes it for rows longer than 32768 columns, and for rows
+ * tensors; AUTO takes it for rows longer than 65536 columns, and for rows
  * of at least 4096 columns when there are at most a quarter as many rows
  * as compute units).
  * ADQ_PATH_GENERIC: any n and alignment.

@@ -272,11 +272,13 @@ uint64_t next_tags(uint64_t count) {
 // them are in the design notes of the repository)
 
 // Row kernel: rows of up to 64 8-column vectors take one vector per thread,
-// up to 2048 two, up to 4096 (32768 columns) four; longer rows do not fit
-// one workgroup's registers.
+// up to 2048 two, up to 4096 (32768 columns) four, up to 8192 (65536
+// columns) eight, half of them held in LDS; longer rows do not fit one
+// workgroup.
 constexpr int64_t kRowVpt1MaxVec = 64;
 constexpr int64_t kRowVpt2MaxVec = 2048;
-constexpr int64_t kRowMaxVec = 4096;
+constexpr int64_t kRowVpt4MaxVec = 4096;
+constexpr int64_t kRowMaxVec = 8192;
 // Rows of 3840-4096 columns in launches of at most 16 rows per CU take one
 // vector per thread (480-512 threads) instead of two.  Launch to launch
 // after 40 ms of launches, two vectors -> one, us: bf16 4096 x 4096 with one
@@ -382,8 +384,10 @@ bool row_geometry(int64_t nvec, int* vpt, int* block) {
     *vpt = 1, *block = round_up((int)nvec, 64);
   } else if (nvec <= kRowVpt2MaxVec) {
     *vpt = 2, *block = round_up((int)((nvec + 1) / 2), 64);
-  } else if (nvec <= kRowMaxVec) {
+  } else if (nvec <= kRowVpt4MaxVec) {
     *vpt = 4, *block = round_up((int)((nvec + 3) / 4), 64);
+  } else if (nvec <= kRowMaxVec) {
+    *vpt = 8, *block = round_up((int)((nvec + 7) / 8), 64);
   } else {
     return false;
   }

@@ -22,7 +22,7 @@
 //   C  scale_k = max_k / Q_k; code = round_half_even(input_k * (1/scale_k));
 //      pack (INT8: 1 byte, INT4: 1 nibble, even column low) and store.
 //
-// VPT (8-column vectors per thread) is 1, 2 or 4, so a row of up to 32768
+// VPT (8-column vectors per thread) is 1, 2, 4 or 8, so a row of up to 65536
 // columns fits one workgroup of at most 1024 threads.  With VPT 1 or 2 the
 // parameters (gamma, beta, smooth) stay in registers as packed 16-bit values
 // for the whole row loop and are converted at use, and x and the quantizer
@@ -30,7 +30,9 @@
 // registers of 1024 threads: the parameters are read at use (from L2, they
 // are shared by all rows) and x and the quantizer inputs are recomputed in
 // each pass from the row's raw 16-bit data, with the same operations, so
-// every pass sees the same values.
+// every pass sees the same values.  VPT 8 keeps the raw data of vectors 0-3
+// in registers and of vectors 4-7 in LDS (direct-to-LDS loads; 128 KiB for
+// two inputs at 1024 threads), and reads gamma and beta at use too.
 #pragma once
 
 #include <type_traits>
@@ -62,8 +64,11 @@ __device__ __forceinline__ void store_codes(const float (&in)[8], float inv, rsr
 // launches that move little data).
 template <int E, int NIN, int Q1, int Q2, int VPT, bool WT>
 __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
-  static_assert(VPT == 1 || VPT == 2 || VPT == 4, "row kernel holds at most 32 columns per thread");
+  static_assert(VPT == 1 || VPT == 2 || VPT == 4 || VPT == 8,
+                "row kernel holds at most 64 columns per thread");
   constexpr bool kHold = VPT <= 2;  // x and the inputs kept between passes, next row prefetched
+  constexpr int RV = VPT == 8 ? 4 : VPT;  // vectors whose raw data stay in registers
+  constexpr bool kHoldGB = VPT <= 4;      // gamma and beta held in registers
   constexpr bool kTwo = Q2 != kQNone;
   constexpr int kQ2 = kTwo ? Q2 : kQInt8;
   constexpr int kStBulk = WT ? kWriteThroughStore : kStreamStore;
@@ -79,40 +84,57 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
 
   __shared__ float red_ss[16];
   __shared__ float red_mx[2][16];
+  // VPT 8: raw data of vectors 4-7, input i of vector k at
+  // xl[((k - 4) * NIN + i) * 1024 + thread]
+  __shared__ __attribute__((aligned(16))) u32x4 xl[VPT == 8 ? (VPT - RV) * NIN * 1024 : 1];
 
   // This thread's 8-column vectors: j = tid + k * bs.  Vectors past the end
   // of the row read as 0 and their stores are dropped by the buffer range
   // check (the row is a whole number of 16-byte vectors).
-  uint32_t vj[VPT];
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) vj[k] = (uint32_t)(tid + k * bs);
+  auto vj = [&](int k) -> uint32_t { return (uint32_t)(tid + k * bs); };
 
   // Parameters, kept as 16-bit pairs (1 for an absent smooth scale).
   auto load_param = [&](const void* p, int k, u32x4 absent) -> u32x4 {
     if (!p) return absent;
-    return __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(p, row_bytes), vj[k] * 16u, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(p, row_bytes), vj(k) * 16u, 0, 0);
   };
   constexpr int PH = kHold ? VPT : 1;  // x / input vectors kept between passes
   // VPT 4 holds gamma and beta, and smooth1 when there is one output; the
   // smooth scales it does not hold are read at use (from L2)
-  constexpr bool kHoldS1 = kHold || !kTwo;
-  u32x4 pg[VPT], pb[VPT], p1[kHoldS1 ? VPT : 1], p2[PH];
+  constexpr bool kHoldS1 = kHoldGB && (kHold || !kTwo);
+  u32x4 pg[kHoldGB ? VPT : 1], pb[kHoldGB ? VPT : 1], p1[kHoldS1 ? VPT : 1], p2[PH];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    pg[k] = load_param(a.gamma, k, zero4);
-    pb[k] = load_param(a.beta, k, zero4);
+    if constexpr (kHoldGB) {
+      pg[k] = load_param(a.gamma, k, zero4);
+      pb[k] = load_param(a.beta, k, zero4);
+    }
     if constexpr (kHoldS1) p1[k] = load_param(a.smooth1, k, one4);
     if constexpr (kHold) p2[k] = kTwo ? load_param(a.smooth2, k, one4) : zero4;
   }
 
-  auto load_row = [&](int64_t row, u32x4 (&c1)[VPT], u32x4 (&c2)[VPT]) {
+  using lds_ptr = __attribute__((address_space(3))) void*;
+  auto load_row = [&](int64_t row, u32x4 (&c1)[RV], u32x4 (&c2)[RV]) {
     const rsrc_t r1 = make_rsrc(row_ptr(a.x1, row, row_bytes), row_bytes);
     const rsrc_t r2 = make_rsrc(row_ptr(a.x2, row, row_bytes), row_bytes);
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      c1[k] = __builtin_amdgcn_raw_buffer_load_b128(r1, vj[k] * 16u, 0, kStreamLoad);
+    for (int k = 0; k < RV; ++k) {
+      c1[k] = __builtin_amdgcn_raw_buffer_load_b128(r1, vj(k) * 16u, 0, kStreamLoad);
       if constexpr (NIN == 2)
-        c2[k] = __builtin_amdgcn_raw_buffer_load_b128(r2, vj[k] * 16u, 0, kStreamLoad);
+        c2[k] = __builtin_amdgcn_raw_buffer_load_b128(r2, vj(k) * 16u, 0, kStreamLoad);
+    }
+    // VPT 8: vectors 4-7 straight to LDS, each wave's 64 lanes as 1 KiB at
+    // its own threads' slots (issued after the register loads, so waiting
+    // for those does not wait for these)
+    uint8_t* xl_wave = reinterpret_cast<uint8_t*>(xl) + 16 * (tid & ~63);
+#pragma unroll
+    for (int k = RV; k < VPT; ++k) {
+      const uint32_t off = vj(k) * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r1, (lds_ptr)(xl_wave + 16 * 1024 * ((k - RV) * NIN)),
+                                               16, off, 0, 0, kStreamLoad);
+      if constexpr (NIN == 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r2, (lds_ptr)(xl_wave + 16 * 1024 * ((k - RV) * NIN + 1)), 16, off, 0, 0, kStreamLoad);
     }
   };
 
@@ -125,7 +147,7 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
 
   int64_t row = first;
   if (row >= rend) return;
-  u32x4 c1[VPT], c2[VPT];  // raw x1/x2 vectors of the row being computed
+  u32x4 c1[RV], c2[RV];  // raw x1/x2 vectors of the row being computed (in registers)
   if constexpr (kHold) load_row(row, c1, c2);
 
   // One row: prefetch the next, compute and store this one, with the stores'
@@ -144,8 +166,10 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
     u32x4 n1[PH], n2[PH];
     if constexpr (kHold) load_row(clamp_row(row + step), n1, n2);
     else load_row(row, c1, c2);
+    if constexpr (kHoldGB) {
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) opaque(pg[k]), opaque(pb[k]);
+      for (int k = 0; k < VPT; ++k) opaque(pg[k]), opaque(pb[k]);
+    }
     if constexpr (kHoldS1) {
 #pragma unroll
       for (int k = 0; k < VPT; ++k) opaque(p1[k]);
@@ -154,14 +178,27 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
 #pragma unroll
       for (int k = 0; k < VPT; ++k) opaque(p2[k]);
     }
-    // x of column vector k from the row's raw data
-    auto xvec = [&](int k, float (&xk)[8]) {
+    // x of a column vector from its raw data
+    auto xvec = [&](const u32x4& v1, const u32x4& v2, float (&xk)[8]) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        f32x2 v = widen2<E>(c1[k][w]);
-        if constexpr (NIN == 2) v += widen2<E>(c2[k][w]);
+        f32x2 v = widen2<E>(v1[w]);
+        if constexpr (NIN == 2) v += widen2<E>(v2[w]);
         xk[2 * w] = v.x;
         xk[2 * w + 1] = v.y;
+      }
+    };
+    // f(k, raw x1, raw x2) for every column vector: the register-held ones
+    // unrolled, those held in LDS (VPT 8) in a loop, one at a time, so that
+    // their loads and parameters are not all in flight at once
+    auto for_vectors = [&](auto&& f) {
+#pragma unroll
+      for (int k = 0; k < RV; ++k) f(k, c1[k], c2[k]);
+#pragma unroll 1
+      for (int k = RV; k < VPT; ++k) {
+        const u32x4 v1 = xl[((k - RV) * NIN) * 1024 + tid];
+        const u32x4 v2 = NIN == 2 ? xl[((k - RV) * NIN + 1) * 1024 + tid] : zero4;
+        f(k, v1, v2);
       }
     };
 
@@ -169,10 +206,9 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
     float x[PH][8];
     float ss = 0.0f;
     const rsrc_t rxo = make_rsrc(row_ptr(a.x_out, row, row_bytes), row_bytes);
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
+    for_vectors([&](int k, const u32x4& v1, const u32x4& v2) {
       float xk[8];
-      xvec(k, xk);
+      xvec(v1, v2, xk);
       float acc = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -184,9 +220,9 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
         __builtin_amdgcn_raw_buffer_store_b128(
             u32x4{narrow2<E>(xk[0], xk[1]), narrow2<E>(xk[2], xk[3]),
                   narrow2<E>(xk[4], xk[5]), narrow2<E>(xk[6], xk[7])},
-            rxo, vj[k] * 16u, 0, kSt);
+            rxo, vj(k) * 16u, 0, kSt);
       }
-    }
+    });
     ss = wave_sum(ss);
     if (lane == 0) red_ss[wave] = ss;
     __syncthreads();
@@ -196,15 +232,17 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
 
     // ---- B: y = x * rinv * gamma + beta, quantizer inputs, row maxima
     // inputs of column vector k (x held or recomputed)
-    auto inputs = [&](int k, float (&i1)[8], float (&i2)[8]) {
+    auto inputs = [&](int k, const u32x4& v1, const u32x4& v2, float (&i1)[8], float (&i2)[8]) {
       float xk[8];
       if constexpr (kHold) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) xk[e] = x[k][e];
       } else {
-        xvec(k, xk);
+        xvec(v1, v2, xk);
       }
-      u32x4 p1k, p2k = zero4;
+      u32x4 pgk, pbk, p1k, p2k = zero4;
+      if constexpr (kHoldGB) pgk = pg[k], pbk = pb[k];
+      else pgk = load_param(a.gamma, k, zero4), pbk = load_param(a.beta, k, zero4);
       if constexpr (kHoldS1) p1k = p1[k];
       else p1k = load_param(a.smooth1, k, one4);
       if constexpr (kTwo) {
@@ -213,7 +251,7 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
       }
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const f32x2 g = widen2<E>(pg[k][w]), b = widen2<E>(pb[k][w]);
+        const f32x2 g = widen2<E>(pgk[w]), b = widen2<E>(pbk[w]);
         const f32x2 s1 = widen2<E>(p1k[w]);
         const float y0 = __builtin_fmaf(xk[2 * w] * rinv, g.x, b.x);
         const float y1 = __builtin_fmaf(xk[2 * w + 1] * rinv, g.y, b.y);
@@ -228,10 +266,9 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
     };
     float in1[PH][8], in2[PH][8];
     float m1 = 0.0f, m2 = 0.0f;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
+    for_vectors([&](int k, const u32x4& v1, const u32x4& v2) {
       float i1[8], i2[8];
-      inputs(k, i1, i2);
+      inputs(k, v1, v2, i1, i2);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         m1 = fmaxf(m1, fabsf(i1[e]));
@@ -241,7 +278,7 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
           if constexpr (kTwo) in2[k][e] = i2[e];
         }
       }
-    }
+    });
     m1 = wave_max(m1);
     if constexpr (kTwo) m2 = wave_max(m2);
     if (lane == 0) {
@@ -273,23 +310,22 @@ __global__ void __launch_bounds__(1024) row_kernel(const Args a) {
         if constexpr (kTwo) apply_boost(in2[k], r2);
       }
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) store_codes<Q1, kSt>(in1[k], r1.inv, ry1, vj[k]);
+      for (int k = 0; k < VPT; ++k) store_codes<Q1, kSt>(in1[k], r1.inv, ry1, vj(k));
       if constexpr (kTwo) {
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) store_codes<kQ2, kSt>(in2[k], r2.inv, ry2, vj[k]);
+        for (int k = 0; k < VPT; ++k) store_codes<kQ2, kSt>(in2[k], r2.inv, ry2, vj(k));
       }
     } else {
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
+      for_vectors([&](int k, const u32x4& v1, const u32x4& v2) {
         float i1[8], i2[8];
-        inputs(k, i1, i2);
+        inputs(k, v1, v2, i1, i2);
         apply_boost(i1, r1);
-        store_codes<Q1, kSt>(i1, r1.inv, ry1, vj[k]);
+        store_codes<Q1, kSt>(i1, r1.inv, ry1, vj(k));
         if constexpr (kTwo) {
           apply_boost(i2, r2);
-          store_codes<kQ2, kSt>(i2, r2.inv, ry2, vj[k]);
+          store_codes<kQ2, kSt>(i2, r2.inv, ry2, vj(k));
         }
-      }
+      });
     }
 
     if constexpr (kHold) {
@@ -334,6 +370,8 @@ bool dispatch_variant(int nin, int q1, int q2, int vpt, bool wt, F&& f) {
     case 5: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 2, true>>(); return true;       \
     case 8: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 4, false>>(); return true;      \
     case 9: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 4, true>>(); return true;       \
+    case 16: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 8, false>>(); return true;     \
+    case 17: f.template operator()<Inst<E, NIN_, Q1_, Q2_, 8, true>>(); return true;      \
     default: return false;                                                                \
   }
   if (nin == 1) {

@@ -150,6 +150,9 @@ def _case_inputs(m, n, dtype, seed, n_smooth=2, beta=True, outlier=0.0):
 SHAPES = [(1, 8), (3, 8), (257, 16), (3, 24), (5, 100 * 8), (3, 1000), (257, 1000),
           (2, 5120), (3, 16384), (1, 1), (3, 7), (4, 2), (257, 100), (2, 16392), (1, 20000),
           (300, 24584), (2, 32768), (3, 32776), (2, 65536), (64, 1032),
+          # rows of 32769-65536 columns, enough of them for the row kernel
+          # (eight vectors per thread, half in LDS; ragged: 40968 = 5121 vectors)
+          (300, 65536), (257, 40968), (300, 32776), (2, 65544),
           # one vector per thread for rows of 3840-4096 columns (ragged: 3848)
           (300, 3840), (5, 3848), (1000, 4096),
           # rows per workgroup: 8 (ragged tail), 2, 3, and 1 for rows of <= 4 KiB
@@ -168,15 +171,37 @@ def test_ragged_shapes(m, n, dtype):
     cus = int(desc.split("cus=")[1].split()[0])
     if n % 8 != 0:
         assert "path=generic" in desc, desc
-    elif n > 32768 or (n // 8 >= 2048 and min(n // 8 // 512, cus // m) >= 2):
-        # long rows, or rows of 16384+ columns too few to occupy the CUs one
-        # row per workgroup (two or more 4096-column chunks per row fit)
+    elif n > 65536 or (n // 8 >= 2048 and min(n // 8 // 512, cus // m) >= 2):
+        # rows longer than a workgroup holds, or rows of 16384+ columns too
+        # few to occupy the CUs one row per workgroup (two or more
+        # 4096-column chunks per row fit)
         assert "path=split" in desc, desc
     else:
         assert "path=row" in desc, desc
-        assert ("vpt=4" in desc) == (n > 16384), desc
+        assert ("vpt=4" in desc) == (16384 < n <= 32768), desc
+        assert ("vpt=8" in desc) == (n > 32768), desc
         if 3840 <= n <= 4096 and m <= 16 * cus:
             assert "vpt=1" in desc, desc
+
+
+@pytest.mark.parametrize("y_types", [("int8", "int8"), ("int4", "int8"), ("int8", "int4"),
+                                     ("int4", "int4"), ("int8", None), ("int4", None)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_longest_rows_every_output_variant(y_types, dtype):
+    """Rows of 32769..65536 columns run the row kernel with eight vectors
+    per thread, vectors 4-7 of the row held in LDS between the passes: every
+    output combination, a ragged last vector group (49160 = 6145 vectors,
+    832 threads) and more rows than workgroups."""
+    m, n = 260, 49160
+    _announce(f"longest rows {m}x{n} {dtype} {y_types}")
+    x1, x2, g, b, s1, s2 = _case_inputs(m, n, dtype, seed=4343)
+    two = y_types[1] is not None
+    yt = (y_types[0], y_types[1] if two else "int8")
+    mask = (True, two)
+    outs, desc = run_v2(x1, x2, g, b, s1, s2 if two else None, 1e-6, mask, yt, dtype)
+    assert "path=row" in desc and "vpt=8" in desc and "block=832" in desc, desc
+    ora = oracle_v2(x1, x2, g, b, s1, s2 if two else None, 1e-6, mask, yt, dtype)
+    compare_v2(outs, ora, yt)
 
 
 @pytest.mark.parametrize("y_types", [("int8", "int8"), ("int4", "int8"), ("int8", "int4"),
@@ -236,12 +261,14 @@ def test_option_matrix(row, y_types, dtype):
 @pytest.mark.parametrize("y_type", ["int8", "int4"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("smooth", [False, True])
-@pytest.mark.parametrize("n", [1024, 1000, 20480])
-def test_rms_norm_dq_variants(y_type, dtype, smooth, n):
-    w = synth.Workload("rms", "rmsnorm", 33, n, dtype, 5, None, True, 1 if smooth else 0)
+@pytest.mark.parametrize("m,n", [(33, 1024), (33, 1000), (33, 20480), (300, 49152)])
+def test_rms_norm_dq_variants(y_type, dtype, smooth, m, n):
+    w = synth.Workload("rms", "rmsnorm", m, n, dtype, 5, None, True, 1 if smooth else 0)
     x, _ = synth.inputs(w)
     g, b, s1, _ = synth.params(w)
-    outs, _ = run_rms(x, g, b, s1, 1e-6, y_type, dtype)
+    outs, desc = run_rms(x, g, b, s1, 1e-6, y_type, dtype)
+    if n > 32768:  # one input, eight vectors per thread (half in LDS)
+        assert "path=row" in desc and "vpt=8" in desc, desc
     ora = oracle.rms_norm_dq(x, g, b, s1, 1e-6, y_type, dtype)
     compare_rms(outs, ora, y_type)
 
