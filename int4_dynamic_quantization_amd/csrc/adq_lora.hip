@@ -35,7 +35,7 @@
 //     without an adapter and, when out is not y, the columns outside the
 //     slice are copied here.  bf16 at ranks 32, 64 and 128 takes an expand
 //     on the matrix cores instead (z1 split exactly into three bf16 pieces;
-//     one workgroup per 64-row tile and 256 columns).
+//     one workgroup per 64-row tile and 512 columns).
 // Generic kernel: one workgroup per row, any sizes and alignments, same
 // arithmetic with block reductions in a fixed order.
 #include "adq_device.h"
@@ -794,7 +794,7 @@ __global__ void __launch_bounds__(NT) lora_expand_kernel(const LoraArgs a, Works
 // 8 + 8 + 8 significant bits), every product of a piece with a weightB value
 // is exact, and the sums run in fp32 inside the matrix unit.
 //
-// One workgroup per (tile of up to 64 rows, 256 columns of the slice), all
+// One workgroup per (tile of up to 64 rows, 64 columns per wavefront of the slice), all
 // workgroups of a tile on one XCD, so weightB is read once per 64 rows.  Wave
 // w takes 64 columns and every 16-row block of the tile.  MFMA operand A is
 // weightB: lane l reads the 4 adjacent columns c(l % 16) of 8 ranks with
@@ -804,10 +804,15 @@ __global__ void __launch_bounds__(NT) lora_expand_kernel(const LoraArgs a, Works
 // 8 (l / 16) + {0..7} and 32 + 8 (l / 16) + {0..7} of the wave's 64.
 // Operand B is z1's pieces, staged in LDS once per workgroup as three bf16
 // planes [64 rows][rank]; per chunk of 32 ranks one MFMA per piece.  y and
-// out cross LDS so that memory is read and written in whole 512-byte row
+// out cross LDS so that memory is read and written in whole row pieces
 // pieces; y is loaded after the products, which keeps the registers (and so
 // the occupancy) of the kernel low.
-constexpr int kMxCols = 256;    // columns per workgroup
+// Wavefronts per workgroup, 64 columns each: every workgroup of a tile reads
+// all of the tile's partial sums, so wider workgroups read them fewer times.
+// Step time on 4096 rows, h1 4096 -> h2 4096 (bf16, 8 adapters), 4 / 8 / 16
+// wavefronts: rank 32 42.5 / 40.0 / 41.9 us, rank 64 55.3 / 47.8 / 49.3,
+// rank 128 70.4 / 61.1 / 63.8 (16: one workgroup per CU, 288 of them).
+constexpr int kMxWaves = 8;
 constexpr int kMxMinRank = 32;  // below, the kernel above is faster (measured)
 
 // first of the 4 columns that MFMA row m of a wave's 64 columns holds
@@ -819,18 +824,19 @@ __device__ __forceinline__ int mx_col(int m) {
 template <int R> constexpr int mx_stride() { return R + 8; }
 
 int lora_mx_col_blocks(int64_t h2) {
-  const int64_t c = (h2 + kMxCols - 1) / kMxCols;
+  const int64_t c = (h2 + 64 * kMxWaves - 1) / (64 * kMxWaves);
   return (int)(c < 1 ? 1 : c);
 }
 
-template <int R>
-__global__ void __launch_bounds__(kThreads) lora_expand_mx_kernel(const LoraArgs a,
-                                                                    Workspace ws) {
+template <int R, int NW>
+__global__ void __launch_bounds__(64 * NW) lora_expand_mx_kernel(const LoraArgs a,
+                                                                   Workspace ws) {
   static_assert(R >= 32 && R % 32 == 0, "ranks of 32 and above");
+  constexpr int NT = 64 * NW, kMxCols = 64 * NW;  // threads, columns per workgroup
   constexpr int NP = 3, ZS = mx_stride<R>();  // pieces, plane row stride
   constexpr int RC = 32;                      // ranks per chunk
   // LDS: z1's pieces during the products, then the tile's y / out block
-  // [64 rows][256 columns + 8] (rows 16 bytes apart modulo 256 bytes)
+  // [64 rows][64 NW columns + 8] (rows 16 bytes apart modulo 256 bytes)
   constexpr int YS = kMxCols + 8;
   constexpr int kZBytes = NP * kTile * ZS * 2, kYBytes = kTile * YS * 2;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kZBytes > kYBytes ? kZBytes : kYBytes];
@@ -863,7 +869,7 @@ __global__ void __launch_bounds__(kThreads) lora_expand_mx_kernel(const LoraArgs
   if (g >= a.w) {  // rows without an adapter (listed only when out is not y): copy
     for (int i = 0; i < n; ++i) {
       const int64_t row = trows[i];
-      for (int64_t c4 = c0 + tid; c4 < c1; c4 += kThreads)
+      for (int64_t c4 = c0 + tid; c4 < c1; c4 += NT)
         *reinterpret_cast<uint2*>(out + row * h3 + 4 * c4) =
             *reinterpret_cast<const uint2*>(y + row * h3 + 4 * c4);
     }
@@ -894,7 +900,7 @@ __global__ void __launch_bounds__(kThreads) lora_expand_mx_kernel(const LoraArgs
   // weightA), 4 ranks per access, split into its pieces in LDS; rows past
   // the tile's are zero
   constexpr int NV4 = kTile * R / 4;                         // groups of 4 ranks
-  constexpr int ZP4 = (NV4 + kThreads - 1) / kThreads;       // groups per thread
+  constexpr int ZP4 = (NV4 + NT - 1) / NT;       // groups per thread
   constexpr int KB = ZP4 >= 8 ? 1 : 8 / ZP4;                // slices loaded together
   f32x4 zs[ZP4];
   if (a.wa) {
@@ -904,7 +910,7 @@ __global__ void __launch_bounds__(kThreads) lora_expand_mx_kernel(const LoraArgs
     int zi[ZP4];
 #pragma unroll
     for (int u = 0; u < ZP4; ++u) {
-      const int v = tid + u * kThreads;
+      const int v = tid + u * NT;
       zi[u] = v < NV4 && 4 * v / R < n ? v : 0;
       zs[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -934,7 +940,7 @@ __global__ void __launch_bounds__(kThreads) lora_expand_mx_kernel(const LoraArgs
   } else {
 #pragma unroll
     for (int u = 0; u < ZP4; ++u) {
-      const int v = tid + u * kThreads;
+      const int v = tid + u * NT;
       const int i = v < NV4 && 4 * v / R < n ? 4 * v / R : 0;
       const u16x4 xv = *reinterpret_cast<const u16x4*>(static_cast<const T*>(a.x) +
                                                         (int64_t)trows[i] * a.h1 + 4 * v % R);
@@ -944,7 +950,7 @@ __global__ void __launch_bounds__(kThreads) lora_expand_mx_kernel(const LoraArgs
   }
 #pragma unroll
   for (int u = 0; u < ZP4; ++u) {
-    const int v = tid + u * kThreads, i = 4 * v / R, r = 4 * v % R;
+    const int v = tid + u * NT, i = 4 * v / R, r = 4 * v % R;
     if (v < NV4) {
       u16x4 hi, mid, lo;
 #pragma unroll
@@ -998,18 +1004,19 @@ __global__ void __launch_bounds__(kThreads) lora_expand_mx_kernel(const LoraArgs
   // out = y + scale * sum, one rounding: y goes through LDS into the MFMA
   // layout, each lane turns its values into out in place, and the block is
   // stored row by row as it was loaded
-  // y: the block's rows, 16 bytes per access, 32 threads per row (512
+  // y: the block's rows, 16 bytes per access, TPR threads per row (16 TPR
   // contiguous bytes), issued first.  An 8-column group that starts inside
   // the slice stays inside y's row (h3 and y_offset are multiples of 8).
-  constexpr int kYChunks = kTile * kMxCols / 8 / kThreads;  // 8 per thread
+  constexpr int TPR = kMxCols / 8;                     // threads per row piece
+  constexpr int kYChunks = kTile * kMxCols / 8 / NT;  // 8 per thread
   const rsrc_t rout = make_rsrc(out, (uint32_t)(a.rows * h3 * 2));
   const rsrc_t ry = make_rsrc(y, (uint32_t)(a.rows * h3 * 2));
-  const int64_t colb = (int64_t)cb * kMxCols + 8 * (tid % 32);  // this thread's 8 columns
+  const int64_t colb = (int64_t)cb * kMxCols + 8 * (tid % TPR);  // this thread's 8 columns
   u16x8 yv[kYChunks];
   int32_t yrow[kYChunks];
 #pragma unroll
   for (int k = 0; k < kYChunks; ++k) {
-    const int rs = tid / 32 + 8 * k;
+    const int rs = tid / TPR + NT / TPR * k;
     yrow[k] = trows[rs];
     const bool ok = rs < n && colb < a.h2;
     yv[k] = __builtin_bit_cast(
@@ -1020,7 +1027,7 @@ __global__ void __launch_bounds__(kThreads) lora_expand_mx_kernel(const LoraArgs
   __syncthreads();  // every wave is done with z1's pieces
 #pragma unroll
   for (int k = 0; k < kYChunks; ++k)
-    *reinterpret_cast<u16x8*>(&yb[tid / 32 + 8 * k][8 * (tid % 32)]) = yv[k];
+    *reinterpret_cast<u16x8*>(&yb[tid / TPR + NT / TPR * k][8 * (tid % TPR)]) = yv[k];
   __syncthreads();
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
@@ -1041,9 +1048,9 @@ __global__ void __launch_bounds__(kThreads) lora_expand_mx_kernel(const LoraArgs
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < kYChunks; ++k) {
-    const int rs = tid / 32 + 8 * k;
+    const int rs = tid / TPR + NT / TPR * k;
     if (rs < n && colb < a.h2) {
-      const u16x8 o = *reinterpret_cast<const u16x8*>(&yb[rs][8 * (tid % 32)]);
+      const u16x8 o = *reinterpret_cast<const u16x8*>(&yb[rs][8 * (tid % TPR)]);
       const uint32_t off = (uint32_t)(((int64_t)yrow[k] * h3 + a.y_offset + colb) * 2);
       if (colb + 8 <= a.h2)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rout, off, 0,
@@ -1058,7 +1065,7 @@ __global__ void __launch_bounds__(kThreads) lora_expand_mx_kernel(const LoraArgs
     const int64_t s0 = a.y_offset / 4, s1 = (a.y_offset + a.h2) / 4;
     for (int i = 0; i < n; ++i) {
       const int64_t row = trows[i];
-      for (int64_t c4 = c0 + tid; c4 < c1; c4 += kThreads)
+      for (int64_t c4 = c0 + tid; c4 < c1; c4 += NT)
         if (c4 < s0 || c4 >= s1)
           *reinterpret_cast<uint2*>(out + row * h3 + 4 * c4) =
               *reinterpret_cast<const uint2*>(y + row * h3 + 4 * c4);
@@ -1149,9 +1156,9 @@ hipError_t launch_tiled(const LoraArgs& a, const Workspace& ws, hipStream_t s) {
                          dim3(kThreads), 0, s, a, ws);
   }
   if constexpr (E == kBF16 && R >= kMxMinRank) {
-    hipLaunchKernelGGL((lora_expand_mx_kernel<R>),
+    hipLaunchKernelGGL((lora_expand_mx_kernel<R, kMxWaves>),
                        dim3((unsigned)((tiles + 7) / 8 * 8 * lora_mx_col_blocks(a.h2))),
-                       dim3(kThreads), 0, s, a, ws);
+                       dim3(64 * kMxWaves), 0, s, a, ws);
     return hipGetLastError();
   }
   const unsigned grid = (unsigned)((tiles + 7) / 8 * 8 * kQuarters * a.chunks);
