@@ -179,6 +179,36 @@ def test_exact_integers(case, path):
     assert np.array_equal(got, ref), desc
 
 
+# In place (out is y, so rows without an adapter are not listed), above 512
+# rows (the grouping launch), ranks 8 / 16, slices wider than 512 columns:
+# partial tiles, slices that end inside a 1024-column range, more than 8
+# slices of h1, indices outside [0, w), the counting and placing launches.
+IN_PLACE = [
+    # rows, h1, rank, h2, h3, w, layers, layer, off, dt
+    (700, 64, 16, 1100, 1200, 3, 2, 1, 40, "bf16"),
+    (2000, 64, 8, 2048, 2304, 5, 1, 0, 256, "fp16"),
+    (600, 4096, 16, 1024, 1536, 4, 1, 0, 512, "bf16"),
+    (1031, 128, 16, 516, 1032, 7, 2, 1, 8, "fp16"),
+    (9000, 64, 16, 600, 608, 2, 1, 0, 0, "bf16"),  # counting and placing launches
+]
+
+
+@pytest.mark.parametrize("case", IN_PLACE,
+                         ids=[f"{c[0]}x{c[1]}r{c[2]}h{c[3]}" for c in IN_PLACE])
+def test_exact_integers_in_place(case):
+    rows, h1, rank, h2, h3, w, layers, layer, off, dt = case
+    s = 31 * rows + h2
+    x = small_ints(s, 12, (rows, h1), -2, 2, dt)
+    y = small_ints(s, 13, (rows, h3), -8, 8, dt)
+    wa = small_ints(s, 14, (w, layers, h1, rank), -2, 2, dt)
+    wb = small_ints(s, 15, (w, layers, rank, h2), -2, 2, dt)
+    idx = synth.int32s(s, 16, -1, w, rows)
+    got, desc = run_lora(y, x, wa, wb, idx, layer, 0.5, off, dt, in_place=True)
+    assert "lora-tiled" in desc and "+expand" in desc, desc
+    ref, _ = oracle.add_lora(y, x, wb, idx, wa, layer, 0.5, off, dt)
+    assert np.array_equal(got, ref), desc
+
+
 @pytest.mark.parametrize("rank", [8, 16, 32, 128])
 def test_many_slices_of_h1(rank):
     """Few rows and a long h1: the shrink splits h1 into more than 16 slices,
