@@ -190,6 +190,8 @@ IN_PLACE = [
     (600, 4096, 16, 1024, 1536, 4, 1, 0, 512, "bf16"),
     (1031, 128, 16, 516, 1032, 7, 2, 1, 8, "fp16"),
     (9000, 64, 16, 600, 608, 2, 1, 0, 0, "bf16"),  # counting and placing launches
+    (24576, 1024, 16, 64, 128, 4, 1, 0, 32, "bf16"),  # one slice of 1024 k (8 whole stages)
+    (3000, 1000, 8, 96, 104, 5, 2, 1, 8, "fp16"),  # slices ending inside a stage
 ]
 
 
