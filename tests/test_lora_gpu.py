@@ -138,6 +138,10 @@ EXACT = [
     (1000, 256, 16, 200, 264, 3, 2, 1, 64, True, "bf16"),
     (777, 264, 16, 68, 136, 6, 2, 1, 40, True, "fp16"),
     (50, 64, 64, 96, 160, 3, 1, 0, 32, False, "bf16"),  # matrix-core expand without weightA
+    # bf16 at ranks 8 / 16, slices wider than 512 columns
+    (800, 64, 16, 640, 1024, 3, 2, 1, 128, True, "bf16"),
+    (800, 64, 8, 1100, 1200, 5, 1, 0, 72, True, "bf16"),   # a partial 64-column group
+    (40, 16, 16, 2048, 2048, 2, 1, 0, 0, False, "bf16"),   # without weightA
     (600, 128, 128, 64, 128, 2, 1, 0, 0, False, "bf16"),
     # above 8192 rows: the counting and placing launches (3, 2 and 2 workgroups)
     (20000, 64, 16, 48, 104, 5, 2, 1, 24, True, "bf16"),
@@ -193,6 +197,7 @@ IN_PLACE = [
     (9000, 64, 16, 600, 608, 2, 1, 0, 0, "bf16"),  # counting and placing launches
     (24576, 1024, 16, 64, 128, 4, 1, 0, 32, "bf16"),  # one slice of 1024 k (8 whole stages)
     (3000, 1000, 8, 96, 104, 5, 2, 1, 8, "fp16"),  # slices ending inside a stage
+    (1500, 128, 8, 1028, 1104, 3, 1, 0, 40, "bf16"),
 ]
 
 
@@ -207,7 +212,7 @@ def test_exact_integers_in_place(case):
     wb = small_ints(s, 15, (w, layers, rank, h2), -2, 2, dt)
     idx = synth.int32s(s, 16, -1, w, rows)
     got, desc = run_lora(y, x, wa, wb, idx, layer, 0.5, off, dt, in_place=True)
-    assert "lora-tiled" in desc and "+expand" in desc, desc
+    assert "lora-tiled" in desc and "expand" in desc, desc
     ref, _ = oracle.add_lora(y, x, wb, idx, wa, layer, 0.5, off, dt)
     assert np.array_equal(got, ref), desc
 
